@@ -1,0 +1,179 @@
+"""Oracle: the fused optimizer step (AdamW and momentum SGD) over split weights
+and companded states.
+
+TEST INFRASTRUCTURE ONLY -- see the package docstring for who may import it.
+
+What the pages fix: FlashOptim's optimizers compute the same updates as the
+usual torch.optim ones while storing less (FlashOptim thread, Davis Blalock,
+the launch post and the post on doing the same updates; blog "FlashOptim:
+Breaking the Memory Wall ...", Conclusion & Perspective: drop-in replacements
+for torch.optim).  Gradients stay in the backward pass's 16-bit precision
+(thread, the post on gradients).  The pages print no update equations, so the
+textbook AdamW / SGD-with-momentum definitions are used.
+
+Readings (listed in the design doc):
+
+U1  AdamW = torch.optim.AdamW defaults: decoupled weight decay, bias
+    correction, step t counted from 1, amsgrad off.  The update uses the fresh
+    float32 m and v (before they are re-quantised).
+U2  Host scalars are computed in float64 and rounded once to float32:
+    b1, b2, 1-b1, 1-b2, decay = 1 - lr*wd, step_size = lr / (1 - b1^t),
+    ibc2 = 1 / sqrt(1 - b2^t), eps.
+U3  Per-element float32 operation order, every operation rounded once (no
+    fused multiply-add):
+        m = b1*m + (1-b1)*g
+        v = b2*v + (1-b2)*(g*g)
+        theta = theta*decay
+        d = sqrt(v)*ibc2 + eps
+        theta = theta - step_size*(m/d)
+U4  SGD-M = torch.optim.SGD defaults: coupled L2 weight decay, dampening 0,
+    no Nesterov:  d = g + wd*theta;  b = mu*b + d;  theta = theta - lr*b.
+    With a zero-initialised buffer the first step gives b = d, as torch does.
+U5  The momentum buffer of SGD-M uses the momentum codec.
+
+Parity status: pinned (unquantised update against torch.optim.AdamW / SGD in
+float64 and a float64 textbook loop; bf16+16 ECC reproduces a plain float32
+master bit for bit; first-step closed form; tests/test_oracle_optim.py).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+from .codecs import (
+    block_scales,
+    decode_momentum,
+    decode_variance,
+    encode_momentum,
+    encode_variance,
+)
+from .numerics import bf16_bits_to_f32, f16_bits_to_f32, reconstruct_weights, split_weights
+
+F32 = np.float32
+
+
+@dataclass(frozen=True)
+class AdamWScalars:
+    b1: np.float32
+    b2: np.float32
+    omb1: np.float32
+    omb2: np.float32
+    decay: np.float32
+    step_size: np.float32
+    ibc2: np.float32
+    eps: np.float32
+
+
+@dataclass(frozen=True)
+class SGDMScalars:
+    lr: np.float32
+    mu: np.float32
+    wd: np.float32
+
+
+def adamw_scalars(lr: float, beta1: float, beta2: float, eps: float, weight_decay: float, step: int) -> AdamWScalars:
+    """U2: float64 -> one float32 rounding each."""
+    if step < 1:
+        raise ValueError("step counts from 1")
+    bc1 = 1.0 - beta1 ** step
+    bc2 = 1.0 - beta2 ** step
+    return AdamWScalars(
+        b1=F32(beta1), b2=F32(beta2), omb1=F32(1.0 - beta1), omb2=F32(1.0 - beta2),
+        decay=F32(1.0 - lr * weight_decay), step_size=F32(lr / bc1),
+        ibc2=F32(1.0 / math.sqrt(bc2)), eps=F32(eps),
+    )
+
+
+def sgdm_scalars(lr: float, momentum: float, weight_decay: float) -> SGDMScalars:
+    return SGDMScalars(lr=F32(lr), mu=F32(momentum), wd=F32(weight_decay))
+
+
+def adamw_update(theta, g, m, v, S: AdamWScalars):
+    """U3 on float32 arrays.  Returns (theta, m, v, sqrt(v))."""
+    theta = np.asarray(theta, F32); g = np.asarray(g, F32)
+    m = np.asarray(m, F32); v = np.asarray(v, F32)
+    with np.errstate(all="ignore"):
+        m1 = S.b1 * m + S.omb1 * g
+        v1 = S.b2 * v + S.omb2 * (g * g)
+        th = theta * S.decay
+        w = np.sqrt(v1)
+        d = w * S.ibc2 + S.eps
+        th = th - S.step_size * (m1 / d)
+    return th.astype(F32), m1.astype(F32), v1.astype(F32), w.astype(F32)
+
+
+def sgdm_update(theta, g, b, S: SGDMScalars):
+    """U4 on float32 arrays.  Returns (theta, b)."""
+    theta = np.asarray(theta, F32); g = np.asarray(g, F32); b = np.asarray(b, F32)
+    with np.errstate(all="ignore"):
+        d = g + S.wd * theta
+        b1 = S.mu * b + d
+        th = theta - S.lr * b1
+    return th.astype(F32), b1.astype(F32)
+
+
+def widen_grad(grad_bits: np.ndarray, fmt: str) -> np.ndarray:
+    """16-bit gradient pattern -> float32 (exact)."""
+    return bf16_bits_to_f32(grad_bits) if fmt == "bf16" else f16_bits_to_f32(grad_bits)
+
+
+def adamw_step(state: dict, grad_bits: np.ndarray, hp: dict, fmt: str = "bf16",
+               ecc_bits: int = 8, codec: str = "companded") -> dict:
+    """One fused AdamW step on one tensor.
+
+    state: {"w16": uint16, "ecc": int8|int16, "m_q": int8, "m_s": uint16 (fp16 bits),
+            "v_q": uint8, "v_s": uint16}; hp: lr, beta1, beta2, eps, weight_decay, step.
+    Returns the new state (same keys).  Steps: widen grad, reconstruct master,
+    decode states, update (U3), split, block scales, encode.
+    """
+    S = adamw_scalars(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"], hp["step"])
+    theta = reconstruct_weights(state["w16"], state["ecc"], fmt, ecc_bits)
+    g = widen_grad(grad_bits, fmt)
+    m = decode_momentum(state["m_q"], state["m_s"], codec)
+    v = decode_variance(state["v_q"], state["v_s"], codec)
+    th, m1, v1, _ = adamw_update(theta, g, m, v, S)
+    w16, ecc = split_weights(th, fmt, ecc_bits)
+    m_s = block_scales(m1, "m")
+    v_s = block_scales(v1, "v")
+    return {
+        "w16": w16, "ecc": ecc,
+        "m_q": encode_momentum(m1, m_s, codec), "m_s": m_s,
+        "v_q": encode_variance(v1, v_s, codec), "v_s": v_s,
+    }
+
+
+def sgdm_step(state: dict, grad_bits: np.ndarray, hp: dict, fmt: str = "bf16",
+              ecc_bits: int = 8, codec: str = "companded") -> dict:
+    """One fused SGD-with-momentum step on one tensor.
+
+    state: {"w16", "ecc", "b_q": int8, "b_s": uint16}; hp: lr, momentum, weight_decay.
+    """
+    S = sgdm_scalars(hp["lr"], hp["momentum"], hp["weight_decay"])
+    theta = reconstruct_weights(state["w16"], state["ecc"], fmt, ecc_bits)
+    g = widen_grad(grad_bits, fmt)
+    b = decode_momentum(state["b_q"], state["b_s"], codec)
+    th, b1 = sgdm_update(theta, g, b, S)
+    w16, ecc = split_weights(th, fmt, ecc_bits)
+    b_s = block_scales(b1, "m")
+    return {"w16": w16, "ecc": ecc, "b_q": encode_momentum(b1, b_s, codec), "b_s": b_s}
+
+
+def fresh_adamw_state(x32: np.ndarray, fmt: str = "bf16", ecc_bits: int = 8) -> dict:
+    """Split an f32 weight and attach zero states (zero codes and zero scales
+    decode to exactly 0)."""
+    w16, ecc = split_weights(x32, fmt, ecc_bits)
+    n = w16.size
+    nb = -(-n // 32)
+    return {"w16": w16, "ecc": ecc,
+            "m_q": np.zeros(n, np.int8), "m_s": np.zeros(nb, np.uint16),
+            "v_q": np.zeros(n, np.uint8), "v_s": np.zeros(nb, np.uint16)}
+
+
+def fresh_sgdm_state(x32: np.ndarray, fmt: str = "bf16", ecc_bits: int = 8) -> dict:
+    w16, ecc = split_weights(x32, fmt, ecc_bits)
+    n = w16.size
+    return {"w16": w16, "ecc": ecc,
+            "b_q": np.zeros(n, np.int8), "b_s": np.zeros(-(-n // 32), np.uint16)}

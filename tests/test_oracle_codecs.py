@@ -1,0 +1,195 @@
+"""Pins for the oracle's blockwise state codecs (CPU only).
+
+Anchors: hand-derived golden codes, exact rational arithmetic near every code
+threshold, numpy's binary16 cast for the round-up scale, invertibility and
+monotonicity of the companders, the half-step bound, and the pages' claim
+that companding cuts quantisation error on heavy-tailed states.
+"""
+
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle as O
+from oracle.codecs import K255, momentum_lut
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "codec_cases.txt")
+
+
+def _golden():
+    rows = []
+    with open(GOLDEN) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            head, vals, codes = [p.strip() for p in line.split("|")]
+            kind, codec, scale = head.split()
+            rows.append((kind, codec, int(scale, 16),
+                         [float(v) for v in vals.split()], [int(c) for c in codes.split()]))
+    return rows
+
+
+@pytest.mark.parametrize("row", _golden(), ids=lambda r: f"{r[0]}-{r[1]}-{r[2]:04x}")
+def test_golden_codes(row):
+    kind, codec, scale, vals, codes = row
+    x = np.zeros(32, np.float32)
+    x[: len(vals)] = vals
+    q, s = O.quantize_state(x, kind, codec)
+    assert int(s[0]) == scale
+    assert [int(c) for c in q[: len(codes)]] == codes
+    assert np.all(q[len(codes):] == 0)
+
+
+def test_ru_fp16_against_numpy_cast():
+    # RU16(x) = the numpy binary16 cast (RNE) bumped up when it landed below x
+    rng = np.random.default_rng(10)
+    pats = np.arange(0, 0x7C00, dtype=np.uint16)
+    h = pats.view(np.float16).astype(np.float32)
+    x = np.concatenate([h, np.nextafter(h, np.float32(np.inf)), np.nextafter(h, np.float32(0)),
+                        (rng.random(200_000) * rng.choice([1e-7, 1e-4, 1.0, 6e4], 200_000)).astype(np.float32)])
+    x = x[(x >= 0) & (x <= 65504)]
+    ref = x.astype(np.float16)
+    below = ref.astype(np.float32) < x
+    ref[below] = np.nextafter(ref[below], np.float16(np.inf))
+    assert np.array_equal(O.ru_fp16_bits(x), ref.view(np.uint16))
+    # saturation and NaN
+    assert list(O.ru_fp16_bits(np.array([65504.5, 1e9, np.inf, np.nan], np.float32))) == [0x7BFF] * 3 + [0x7E00]
+
+
+def test_momentum_code_exact_near_thresholds():
+    # The exact code of a float32 a is round(127 * 2a/(1+a)).  Compare the
+    # oracle with Fraction arithmetic for float32 values within a few ulps of
+    # every threshold (2k+1)/(507-2k), where any evaluation error would show.
+    zs = []
+    for k in range(127):
+        t = np.array([float(Fraction(2 * k + 1, 507 - 2 * k))], np.float32).view(np.int32)[0]
+        zs.extend(int(t) + d for d in range(-3, 4))
+    a32 = np.array(zs, np.int32).view(np.float32)
+    a32 = a32[(a32 >= 0) & (a32 <= 1)]
+    q = O.encode_momentum(a32, np.full(-(-a32.size // 32), 0x3C00, np.uint16))   # scale 1.0
+    for ai, qi in zip(a32, q):
+        fa = Fraction(float(ai))
+        y = 254 * fa / (1 + fa)
+        k = int(y)
+        want = k + (1 if y - k > Fraction(1, 2) else 0)
+        assert y - k != Fraction(1, 2)          # no exact ties exist
+        assert int(qi) == want, (float(ai), int(qi), want)
+
+
+def test_momentum_invertible_and_monotone():
+    lut = momentum_lut()
+    assert lut[127] == 0.0 and lut[0] == -1.0 and lut[254] == 1.0      # phi^-1(0)=0, phi^-1(+-1)=+-1
+    assert np.all(np.diff(lut) > 0)
+    rng = np.random.default_rng(11)
+    scales = np.concatenate([np.array([0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF], np.uint16),
+                             rng.integers(1, 0x7C00, 300).astype(np.uint16)])
+    codes = np.arange(-127, 128, dtype=np.int8)
+    for s in scales:
+        nb = -(-codes.size // 32)
+        sb = np.full(nb, s, np.uint16)
+        m = O.decode_momentum(codes, sb)
+        assert np.all(np.diff(m.astype(np.float64)) > 0)
+        assert np.array_equal(O.encode_momentum(m, sb), codes)
+        m2 = O.decode_momentum(codes, sb, "linear")
+        assert np.array_equal(O.encode_momentum(m2, sb, "linear"), codes)
+
+
+def test_variance_invertible_and_monotone():
+    rng = np.random.default_rng(12)
+    scales = np.concatenate([np.array([0x0001, 0x0400, 0x3C00, 0x7BFF], np.uint16),
+                             rng.integers(1, 0x7C00, 300).astype(np.uint16)])
+    codes = np.arange(0, 256).astype(np.uint8)
+    for s in scales:
+        sb = np.full(8, s, np.uint16)
+        for codec in ("companded", "linear"):
+            v = O.decode_variance(codes, sb, codec)
+            assert v[0] == 0.0
+            assert np.all(np.diff(v.astype(np.float64)) >= 0)
+            assert np.array_equal(O.encode_variance(v, sb, codec), codes), (hex(s), codec)
+
+
+def test_half_step_bound_companded_domain():
+    # every float32 z in a dense sweep of [0, 1]: |127*phi(z) - q| <= 1/2, i.e.
+    # the code is the nearest level in the companded domain; and the decoded
+    # level is within half a level spacing of z in the raw domain.
+    z = np.arange(0x00000000, 0x3F800001, 97, dtype=np.int64).astype(np.int32).view(np.float32)
+    sb = np.full(-(-z.size // 32), 0x3C00, np.uint16)
+    q = O.encode_momentum(z, sb).astype(np.float64)
+    zz = z.astype(np.float64)
+    y = 254 * zz / (1 + zz)
+    assert np.max(np.abs(y - q)) <= 0.5
+    dec = O.decode_momentum(q.astype(np.int8), sb).astype(np.float64)
+    # raw domain: the error is bounded by the distance from the level to the
+    # preimages of the companded half-way points, phi^-1(y) = y / (2 - y)
+    inv = lambda y: y / (2 - y)
+    lvl = inv(q / 127)
+    t_hi = inv(np.minimum(q + 0.5, 127) / 127)
+    t_lo = inv(np.maximum(q - 0.5, 0) / 127)
+    bound = np.maximum(t_hi - lvl, lvl - t_lo)
+    assert np.all(np.abs(dec - zz) <= bound * (1 + 1e-6) + 1e-12)
+
+
+def test_variance_half_step_bound():
+    rng = np.random.default_rng(13)
+    v = (rng.standard_t(3, 32 * 20000) * 1e-3).astype(np.float32) ** 2
+    q, s = O.quantize_state(v, "v")
+    sv = np.repeat(s.view(np.float16).astype(np.float64), 32)
+    w = np.sqrt(v.astype(np.float64))
+    # in the sqrt domain the code is within half a step (plus float32 rounding)
+    assert np.all(np.abs(w / sv * 255 - q) <= 0.5 + 1e-5)
+
+
+def test_zero_state_roundtrip():
+    z = np.zeros(100, np.float32)
+    for kind in ("m", "v"):
+        for codec in ("companded", "linear"):
+            q, s = O.quantize_state(z, kind, codec)
+            assert np.all(q == 0) and np.all(s == 0)
+            assert np.all(O.dequantize_state(q, s, kind, codec) == 0)
+
+
+def test_scale_never_zero_for_nonzero_block_and_sqrt_domain():
+    # the variance scale lives in the sqrt domain: squared gradients of 1e-3
+    # (v ~ 1e-9) would underflow binary16 directly, their square roots do not
+    rng = np.random.default_rng(14)
+    g = (rng.standard_t(3, 32 * 1000) * 1e-3).astype(np.float32)
+    v = np.float32(0.001) * g * g
+    s = O.block_scales(v, "v")
+    assert np.all(s > 0)
+    assert np.mean(v.reshape(-1, 32).max(1).astype(np.float16) == 0) > 0.3   # direct fp16 would underflow often
+
+
+def test_companding_reduces_error_heavy_tailed():
+    # the pages: companding cuts quantisation error versus linear codes
+    rng = np.random.default_rng(15)
+    g = (rng.standard_t(3, 32 * 50000) * 1e-3).astype(np.float32)
+    m = np.float32(0.1) * g
+    v = np.float32(0.05) * g * g
+    def med_rel(kind, codec, x):
+        q, s = O.quantize_state(x, kind, codec)
+        d = O.dequantize_state(q, s, kind, codec).astype(np.float64)
+        nz = x != 0
+        return np.median(np.abs(d[nz] - x[nz]) / np.abs(x[nz]))
+    assert med_rel("m", "companded", m) < med_rel("m", "linear", m)
+    assert med_rel("v", "companded", v) < 0.5 * med_rel("v", "linear", v)
+
+
+def test_tail_block_covers_valid_elements_only():
+    x = np.zeros(37, np.float32)
+    x[33] = 0.5                  # only element of the short last block
+    x[0] = 4.0
+    q, s = O.quantize_state(x, "m")
+    assert s.size == 2 and s[1] == np.float16(0.5).view(np.uint16) and s[0] == np.float16(4.0).view(np.uint16)
+    assert q[33] == 127
+
+
+def test_variance_decode_definition():
+    # decode = (RN32(RN32(s * RN32(1/255)) * q))^2, pinned by hand for s = 1
+    sb = np.array([0x3C00], np.uint16)
+    q = np.array([0, 1, 255] + [0] * 29, np.uint8)
+    v = O.decode_variance(q, sb)
+    t255 = np.float32(K255) * np.float32(255)
+    assert v[0] == 0 and v[1] == np.float32(K255) * np.float32(K255) and v[2] == t255 * t255

@@ -1,0 +1,178 @@
+"""Pins for the oracle's update rules and full fused step (CPU only).
+
+Anchors: torch.optim.AdamW / torch.optim.SGD in float64 (a library routine),
+a float64 textbook loop written here, the first-step closed form, the
+bf16 + 16-bit ECC identity (a lossless split must reproduce a plain float32
+master bit for bit), and the storage byte count the pages give.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from oracle.optim import fresh_adamw_state, fresh_sgdm_state
+
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+
+
+def _torch_adamw(x0, grads, hp):
+    p = torch.nn.Parameter(torch.tensor(x0, dtype=torch.float64))
+    opt = torch.optim.AdamW([p], lr=hp["lr"], betas=(hp["beta1"], hp["beta2"]), eps=hp["eps"],
+                            weight_decay=hp["weight_decay"], foreach=False)
+    out = []
+    for g in grads:
+        p.grad = torch.tensor(g, dtype=torch.float64)
+        opt.step()
+        out.append(p.detach().numpy().copy())
+    return out
+
+
+def _oracle_unquantised_adamw(x0, grads, hp):
+    th = x0.astype(np.float32)
+    m = np.zeros_like(th); v = np.zeros_like(th)
+    out = []
+    for t, g in enumerate(grads, start=1):
+        S = O.adamw_scalars(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"], t)
+        th, m, v, _ = O.adamw_update(th, g.astype(np.float32), m, v, S)
+        out.append(th.copy())
+    return out
+
+
+def _textbook_adamw(x0, grads, hp):
+    # plain float64 AdamW, written from the textbook definition
+    th = x0.astype(np.float64); m = np.zeros_like(th); v = np.zeros_like(th)
+    out = []
+    for t, g in enumerate(grads, start=1):
+        g = g.astype(np.float64)
+        th = th - hp["lr"] * hp["weight_decay"] * th
+        m = hp["beta1"] * m + (1 - hp["beta1"]) * g
+        v = hp["beta2"] * v + (1 - hp["beta2"]) * g * g
+        mh = m / (1 - hp["beta1"] ** t)
+        vh = v / (1 - hp["beta2"] ** t)
+        th = th - hp["lr"] * mh / (np.sqrt(vh) + hp["eps"])
+        out.append(th.copy())
+    return out
+
+
+@pytest.mark.parametrize("hp", [HP, dict(lr=6e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)])
+def test_unquantised_adamw_matches_torch_and_textbook(hp):
+    rng = np.random.default_rng(20)
+    x0 = (rng.standard_normal((7, 5)) * 0.02).astype(np.float32)
+    grads = [(rng.standard_t(3, (7, 5)) * 1e-3).astype(np.float32) for _ in range(10)]
+    a = _oracle_unquantised_adamw(x0, grads, hp)
+    b = _torch_adamw(x0.astype(np.float64), [g.astype(np.float64) for g in grads], hp)
+    c = _textbook_adamw(x0, grads, hp)
+    # float32 trajectory vs float64 references: normwise 1e-6, and the
+    # accumulated update itself within 1e-4 (a dropped bias correction, a
+    # wrong sign or a misplaced eps changes it by far more)
+    for x, y, z in zip(a, b, c):
+        for ref in (y, z):
+            assert np.max(np.abs(x - ref)) <= 1e-6 * np.max(np.abs(ref))
+            assert np.max(np.abs((x - x0) - (ref - x0))) <= 1e-4 * np.max(np.abs(ref - x0))
+
+
+def test_unquantised_sgdm_matches_torch():
+    rng = np.random.default_rng(21)
+    x0 = (rng.standard_normal((7, 5)) * 0.02).astype(np.float32)
+    grads = [(rng.standard_normal((7, 5)) * 1e-2).astype(np.float32) for _ in range(10)]
+    p = torch.nn.Parameter(torch.tensor(x0, dtype=torch.float64))
+    opt = torch.optim.SGD([p], lr=0.1, momentum=0.9, weight_decay=1e-4, foreach=False)
+    S = O.sgdm_scalars(0.1, 0.9, 1e-4)
+    th = x0.copy(); b = np.zeros_like(th)
+    for g in grads:
+        p.grad = torch.tensor(g, dtype=torch.float64)
+        opt.step()
+        th, b = O.sgdm_update(th, g, b, S)
+        ref = p.detach().numpy()
+        assert np.max(np.abs(th - ref)) <= 1e-6 * np.max(np.abs(ref))
+        assert np.max(np.abs((th - x0) - (ref - x0))) <= 1e-4 * np.max(np.abs(ref - x0))
+
+
+def test_first_step_closed_form():
+    # from zero states, m = (1-b1) g and v = (1-b2) g^2, so the update is
+    # lr * g / (|g| + eps*sqrt(1-b2)/(1-b1)...) ~= lr * sign(g) for |g| >> eps
+    rng = np.random.default_rng(22)
+    th0 = (rng.standard_normal(1000) * 0.02).astype(np.float32)
+    g = (rng.standard_t(3, 1000) * 1e-3).astype(np.float32)
+    S = O.adamw_scalars(1e-3, 0.9, 0.999, 1e-8, 0.0, 1)
+    th, m, v, _ = O.adamw_update(th0, g, np.zeros(1000, np.float32), np.zeros(1000, np.float32), S)
+    big = np.abs(g) > 1e-5
+    assert np.allclose((th0 - th)[big], 1e-3 * np.sign(g[big]), rtol=2e-3, atol=0)
+    assert np.array_equal(m, np.float32(0.9) * np.float32(0) + np.float32(1.0 - 0.9) * g)
+
+
+def _run_ecc16_vs_plain(fmt_bits=16, steps=8):
+    # bf16 + 16-bit ECC is lossless, so storing the master as (theta', rho)
+    # between steps must reproduce a plain float32 master bit for bit.
+    rng = np.random.default_rng(23)
+    x0 = (rng.standard_normal(4096) * 0.02).astype(np.float32)
+    plain = x0.copy(); m1 = np.zeros_like(x0); v1 = np.zeros_like(x0)
+    w16, ecc = O.split_weights(x0, "bf16", fmt_bits)
+    m2 = np.zeros_like(x0); v2 = np.zeros_like(x0)
+    for t in range(1, steps + 1):
+        g = (rng.standard_t(3, 4096) * 1e-3).astype(np.float32)
+        S = O.adamw_scalars(1e-3, 0.9, 0.999, 1e-8, 0.01, t)
+        plain, m1, v1, _ = O.adamw_update(plain, g, m1, v1, S)
+        th = O.reconstruct_weights(w16, ecc, "bf16", fmt_bits)
+        th, m2, v2, _ = O.adamw_update(th, g, m2, v2, S)
+        w16, ecc = O.split_weights(th, "bf16", fmt_bits)
+    return plain, O.reconstruct_weights(w16, ecc, "bf16", fmt_bits)
+
+
+def test_bf16_ecc16_reproduces_fp32_master_bitwise():
+    plain, split = _run_ecc16_vs_plain(16)
+    assert np.array_equal(plain.view(np.uint32), split.view(np.uint32))
+    # and the 8-bit ECC does NOT (it is a 24-bit master), but stays close
+    plain8, split8 = _run_ecc16_vs_plain(8)
+    assert not np.array_equal(plain8, split8)
+    # each step re-rounds the master to a 16-bit significand (8 + 8 bits)
+    assert np.max(np.abs(plain8 - split8)) < 8 * 2 ** -16 * np.max(np.abs(plain8))
+
+
+def test_full_step_tracks_unquantised():
+    # sanity: the quantised step stays close to the unquantised trajectory
+    rng = np.random.default_rng(24)
+    n = 32 * 500 + 7
+    x0 = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    st = fresh_adamw_state(x0)
+    th = x0.copy(); m = np.zeros(n, np.float32); v = np.zeros(n, np.float32)
+    hp = dict(HP)
+    for t in range(1, 11):
+        g = (rng.standard_t(3, n) * 1e-3).astype(np.float32)
+        gb = (g.astype(np.float32).view(np.uint32) + 0x8000 >> 16).astype(np.uint16)   # test-side bf16 cast
+        gw = (gb.astype(np.uint32) << 16).view(np.float32)
+        hp["step"] = t
+        st = O.adamw_step(st, gb, hp)
+        th, m, v, _ = O.adamw_update(th, gw, m, v, O.adamw_scalars(1e-3, 0.9, 0.999, 1e-8, 0.01, t))
+    q = O.reconstruct_weights(st["w16"], st["ecc"])
+    # ten steps of ~lr each: parameters move ~1e-2 relative; quantised states
+    # perturb the update by at most a few percent of that
+    assert np.median(np.abs(q - th)) < 0.05 * 1e-3 * 10
+
+
+def test_sgdm_full_step_first_step_equals_torch_buffer():
+    rng = np.random.default_rng(25)
+    x0 = (rng.standard_normal(64) * 0.02).astype(np.float32)
+    st = fresh_sgdm_state(x0)
+    g = (rng.standard_normal(64) * 1e-2).astype(np.float32)
+    gb = (g.view(np.uint32) + 0x8000 >> 16).astype(np.uint16)
+    gw = (gb.astype(np.uint32) << 16).view(np.float32)
+    st2 = O.sgdm_step(st, gb, dict(lr=0.1, momentum=0.9, weight_decay=1e-4))
+    th0 = O.reconstruct_weights(st["w16"], st["ecc"])
+    d = gw + np.float32(1e-4) * th0
+    want = th0 - np.float32(0.1) * d
+    w16, ecc = O.split_weights(want)
+    assert np.array_equal(st2["w16"], w16) and np.array_equal(st2["ecc"], ecc)
+
+
+def test_bytes_per_param():
+    # 16-bit weight + 8-bit ECC + 16-bit grad + 8-bit m + 8-bit v = 7 B/param,
+    # plus one 16-bit scale per 32 elements for each of m and v: 7.125 B/param
+    n = 32 * 1024
+    st = fresh_adamw_state(np.zeros(n, np.float32))
+    grad = np.zeros(n, np.uint16)
+    total = sum(a.nbytes for a in st.values()) + grad.nbytes
+    assert total / n == 7.125
+    # the fp32 mixed-precision baseline: 4 master + 4 grad + 8 Adam = 16
+    assert (4 + 4 + 8) == 16
