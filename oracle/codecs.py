@@ -43,8 +43,9 @@ C5  Linear ablation (no companding), same scales as C2:
              decode RN32(RN32(s * K127) * q), K127 = RN32(1/127);
     variance q = clamp(rint(RN32(v * RN32(255/(s*s)))), 0, 255),
              decode RN32(RN32(RN32(s*s) * K255) * q).
-C6  Codes of non-finite elements: NaN momentum -> +127 (companded) or 0
-    (linear), NaN variance -> 0.  Codes are otherwise clamped to range.
+C6  Codes are clamped to range before rounding (IEEE minNum/maxNum, which
+    send NaN to the upper bound): a NaN momentum element gets +127 and a NaN
+    variance element 255, under either codec.
 
 RN32(.) is one IEEE float32 rounding; numpy float32 arithmetic provides it.
 Where floating point decides a code, the decision is taken in float32 (the
@@ -140,7 +141,8 @@ def encode_momentum(m: np.ndarray, scale_bits: np.ndarray, codec: str = "compand
         elif codec == "linear":
             c = np.where(s > 0, np.float32(127.0) / np.where(s > 0, s, np.float32(1)), np.float32(0))
             y = (m * c).astype(np.float32)
-            q = np.where(np.isnan(y), 0.0, np.clip(np.rint(y), -127, 127))
+            y = np.fmax(np.fmin(y, np.float32(127)), np.float32(-127))     # NaN -> 127 (C6)
+            q = np.rint(y)
         else:
             raise ValueError(codec)
     return np.clip(q, -127, 127).astype(np.int8)
@@ -171,7 +173,8 @@ def encode_variance(v: np.ndarray, scale_bits: np.ndarray, codec: str = "compand
             y = (v * c).astype(np.float32)
         else:
             raise ValueError(codec)
-        q = np.where(np.isnan(y), 0.0, np.clip(np.rint(y), 0, 255))
+        y = np.fmin(y, np.float32(255))                                    # NaN -> 255 (C6)
+        q = np.clip(np.rint(y), 0, 255)
     return q.astype(np.uint8)
 
 

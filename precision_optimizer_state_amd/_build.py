@@ -1,0 +1,42 @@
+"""Build the HIP library in-tree (gfx950).  Used by __graft_entry__.build()."""
+
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(PKG, "csrc", "fo_lib.hip")
+OUT_DIR = os.path.join(PKG, "lib")
+OUT = os.path.join(OUT_DIR, "libfoamd.so")
+
+# -ffp-contract=off: every float operation is rounded once (no FMA formation),
+# which the fixed operation order of the update relies on.  Division and square
+# root stay IEEE correctly rounded, denormals are preserved.  Packed-FP32
+# instruction selection is disabled.
+FLAGS = [
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-fno-gpu-flush-denormals-to-zero", "-fno-fast-math",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-variable", "-Wno-unknown-pragmas",
+]
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    os.makedirs(OUT_DIR, exist_ok=True)
+    tmp = OUT + ".tmp"
+    cmd = ["/opt/rocm/bin/hipcc", *FLAGS, *extra, SRC, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed building libfoamd.so")
+    if verbose and res.stderr.strip():
+        print("\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)[:4000])
+    os.replace(tmp, OUT)
+    return OUT
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

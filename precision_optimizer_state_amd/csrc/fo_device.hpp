@@ -1,0 +1,233 @@
+// fo_device.hpp -- device-side numerics of the fused low-precision optimizer
+// step for gfx950 (CDNA4, wave64).
+//
+// Everything here works on IEEE-754 bit patterns with integer arithmetic where
+// that is exact and cheap; the floating-point operations that remain are
+// single IEEE operations (compiled without contraction, with correctly
+// rounded division and square root, f32 and f16 denormals preserved).
+//
+// Weight split (16-bit theta' + N-bit ECC): Davis Blalock's FlashOptim
+// thread, posts on weight splitting and the ECC bits; blog "FlashOptim:
+// Breaking the Memory Wall with 24-bit Weights and Companded States",
+// Methodology section 1.  The ECC is the signed offset of the f32 value from
+// theta' in units of 2^-N of the 16-bit spacing on the value's side, rounded
+// half to even; theta' is the f32 value rounded to nearest with ties away
+// from zero.
+//
+// Key identity used for bf16: the f32 encoding of a bf16 value is its bit
+// pattern shifted left by 16, and inside any binade (and across the binade
+// boundary below a power of two, where both the bf16 spacing and the f32
+// spacing halve) one bf16 spacing is exactly 2^16 f32 spacings.  Hence the
+// side-aware offset is the signed difference of the magnitude bit patterns:
+//     bits(|x|) - bits(|theta'|) = sext16(low 16 bits of bits(|x|))
+// and reconstruction is a single integer add on the f32 pattern (valid for
+// either sign, because the sign bit is untouched).  fp16 has the same
+// property with 2^13 f32 spacings per fp16 spacing, except below the smallest
+// fp16 normal, where a float path is used.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fo {
+
+enum { BF16 = 0, FP16 = 1 };
+enum { COMPANDED = 0, LINEAR = 1 };
+
+__device__ __forceinline__ uint32_t f2u(float x) { return __float_as_uint(x); }
+__device__ __forceinline__ float u2f(uint32_t x) { return __uint_as_float(x); }
+
+__device__ __forceinline__ float h2f(uint32_t h) {  // binary16 pattern -> f32 (exact)
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
+}
+
+// ---------------------------------------------------------------------------
+// 16-bit element access inside packed dwords
+// ---------------------------------------------------------------------------
+template <int WFMT> struct W16;
+template <> struct W16<BF16> {
+  static __device__ __forceinline__ float lo(uint32_t w) { return u2f(w << 16); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return u2f(w & 0xFFFF0000u); }
+};
+template <> struct W16<FP16> {
+  static __device__ __forceinline__ float lo(uint32_t w) { return h2f(w & 0xFFFFu); }
+  static __device__ __forceinline__ float hi(uint32_t w) { return h2f(w >> 16); }
+};
+
+template <int WFMT>
+__device__ __forceinline__ float widen(uint32_t w, int half) {
+  return half ? W16<WFMT>::hi(w) : W16<WFMT>::lo(w);
+}
+
+// ---------------------------------------------------------------------------
+// ECC decode: theta' (already widened to f32, exact) + rho -> f32 master
+// ---------------------------------------------------------------------------
+template <int WFMT, int ECC>
+__device__ __forceinline__ float ecc_decode(float t, int32_t rho) {
+  if constexpr (WFMT == BF16) {
+    // one bf16 spacing = 2^16 f32 spacings; rho counts 2^-N of it
+    constexpr int SH = 16 - ECC;
+    return u2f(f2u(t) + ((uint32_t)rho << SH));
+  } else {
+    static_assert(ECC == 8, "fp16 supports an 8-bit ECC");
+    const uint32_t a = f2u(t) & 0x7FFFFFFFu;
+    if (a > 0x38800000u)                         // |theta'| above the smallest fp16 normal
+      return u2f(f2u(t) + ((uint32_t)rho << 5)); // one fp16 spacing = 2^13 f32 spacings
+    // zero, subnormal and the smallest normal: spacing 2^-24 on both sides
+    return t + copysignf((float)rho * 0x1p-32f, t);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// ECC encode (split): f32 -> (theta' pattern in the low 16 bits, rho)
+// ---------------------------------------------------------------------------
+struct SplitOut { uint32_t h; int32_t rho; };
+
+// round-half-to-even of a signed integer divided by 2^r, 1 <= r <= 30
+__device__ __forceinline__ int32_t rne_shift(int32_t d, int r) {
+  return (d + ((1 << (r - 1)) - 1) + ((d >> r) & 1)) >> r;
+}
+
+template <int WFMT, int ECC>
+__device__ __forceinline__ SplitOut ecc_encode(float x) {
+  const uint32_t xb = f2u(x);
+  const uint32_t ab = xb & 0x7FFFFFFFu;
+  SplitOut o;
+  if constexpr (WFMT == BF16) {
+    o.h = (ab + 0x8000u) >> 16;                        // RNA on the magnitude
+    const int32_t L = ((int32_t)(ab << 16)) >> 16;     // bits(|x|) - bits(|theta'|)
+    if constexpr (ECC == 8) {
+      o.rho = min(rne_shift(L, 8), 127);
+    } else {
+      o.rho = L;                                       // exact: in [-2^15, 2^15)
+    }
+    if (ab >= 0x7F7F8000u) {                           // RNA overflow, inf, nan (rare)
+      if (ab > 0x7F800000u)       { o.h = 0x7FC0u; o.rho = 0; }
+      else if (ab == 0x7F800000u) { o.h = 0x7F80u; o.rho = 0; }
+      else                        { o.h = 0x7F7Fu; o.rho = (ECC == 8) ? 127 : 32767; }
+    }
+  } else {
+    static_assert(ECC == 8, "fp16 supports an 8-bit ECC");
+    if (ab >= 0x38800000u) {                           // |x| >= 2^-14
+      o.h = ((ab + 0x1000u) >> 13) - (112u << 10);     // RNA, rebias 127 -> 15
+      const int32_t L = ((int32_t)(ab << 19)) >> 19;   // sext13
+      o.rho = min(rne_shift(L, 5), 127);
+      if (o.h >= 0x7C00u) {                            // overflow (|x| >= 65520), inf, nan
+        if (ab > 0x7F800000u)       { o.h = 0x7E00u; o.rho = 0; }
+        else if (ab == 0x7F800000u) { o.h = 0x7C00u; o.rho = 0; }
+        else                        { o.h = 0x7BFFu; o.rho = 127; }
+      }
+    } else {
+      // |x| < 2^-14: fp16 values are multiples of 2^-24.  |x| = M * 2^(E-23);
+      // in units of 2^-24, |x| = M / 2^s with s = -(E+1) >= 14.
+      const uint32_t e = ab >> 23;
+      const uint32_t M = e ? ((ab & 0x7FFFFFu) | 0x800000u) : ab;
+      const int s = e ? (126 - (int)e) : 125;
+      uint32_t k = 0;
+      int32_t diff = (int32_t)M;
+      if (s <= 24) {
+        k = (M + (1u << (s - 1))) >> s;               // RNA
+        diff = (int32_t)M - (int32_t)(k << s);
+      }
+      // delta = diff * 2^(E-23) * 2^8 / 2^-24 = diff / 2^(s-8)
+      const int r = s - 8;
+      int32_t rho = (r >= 25) ? 0 : rne_shift(diff, r);
+      o.rho = max(min(rho, 127), -128);
+      o.h = k;                                         // k = 1024 is the smallest normal
+    }
+  }
+  o.h |= (xb >> 16) & 0x8000u;
+  return o;
+}
+
+// ---------------------------------------------------------------------------
+// Block scales: smallest binary16 >= x (x >= 0), saturating at 65504
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t ru_fp16(float x) {
+  const uint32_t ux = f2u(x) & 0x7FFFFFFFu;            // callers pass |.| or sqrt: sign ignored
+  if (ux > 0x7F800000u) return 0x7E00u;                // NaN
+  if (ux >= 0x477FE000u) return 0x7BFFu;               // >= 65504 (and +inf)
+  const uint32_t e = ux >> 23;
+  if (e >= 113u)                                       // >= 2^-14: truncate, then bump if inexact
+    return ((ux >> 13) - (112u << 10)) + ((ux & 0x1FFFu) != 0u);
+  const uint32_t M = e ? ((ux & 0x7FFFFFu) | 0x800000u) : ux;
+  const int s = e ? (126 - (int)e) : 125;              // value = M / 2^s units of 2^-24
+  if (s >= 25) return M ? 1u : 0u;
+  return (M + (1u << s) - 1u) >> s;                    // ceil
+}
+
+// ---------------------------------------------------------------------------
+// Cross-lane helpers (DPP inside a quad of 4 lanes = one 32-element block)
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// quad_perm selectors
+constexpr int QP_SWAP1 = 0xB1;   // [1,0,3,2]
+constexpr int QP_SWAP2 = 0x4E;   // [2,3,0,1]
+template <int J> constexpr int qp_bcast() { return J * 0x55; }   // [J,J,J,J]
+
+__device__ __forceinline__ float quad_max(float x) {   // IEEE maxNum over the 4 lanes
+  x = fmaxf(x, dpp_f<QP_SWAP1>(x));
+  x = fmaxf(x, dpp_f<QP_SWAP2>(x));
+  return x;
+}
+template <int J>
+__device__ __forceinline__ float quad_bcast(float x) { return dpp_f<qp_bcast<J>()>(x); }
+
+// ---------------------------------------------------------------------------
+// State codecs
+// ---------------------------------------------------------------------------
+// LDS tables shared by a workgroup:
+//   lut[i]  = RN32((i-127) / (254 - |i-127|)), i in [0,254]: momentum levels
+//   thr[k]  = smallest f32 >= (2k+1)/(507-2k), k in [0,126]: the |z| at which
+//             round(127*phi(|z|)) steps from k to k+1; thr[127] = 2 (never reached)
+struct CodecTables { float lut[256]; float thr[128]; };
+
+__device__ __forceinline__ void init_tables(CodecTables& T, int tid, int nthreads) {
+  for (int i = tid; i < 255; i += nthreads) {
+    const int q = i - 127;
+    const int aq = q < 0 ? -q : q;
+    T.lut[i] = (float)q / (float)(254 - aq);           // IEEE division
+  }
+  for (int k = tid; k < 128; k += nthreads) {
+    if (k == 127) { T.thr[k] = 2.0f; continue; }
+    const float a = (float)(2 * k + 1), b = (float)(507 - 2 * k);
+    float t = a / b;                                   // nearest
+    // exact residual t*b - a (fma is exact here); below the true quotient -> step up
+    if (__builtin_fmaf(t, b, -a) < 0.0f) t = u2f(f2u(t) + 1u);
+    T.thr[k] = t;
+  }
+  if (tid == 0) T.lut[255] = 0.0f;
+}
+
+// momentum, companded: z = m*R (R = RN32(1/s)); q = sign(z)*round(127*phi(min(|z|,1)))
+// The code is exact: an estimate y with error << 1/2 gives k = floor(y), and the
+// exact rounding is k + (a >= thr[k]) (no ties exist for float32 a).
+__device__ __forceinline__ int32_t encode_m_companded(float m, float R, const float* thr) {
+  const float z = m * R;
+  const float a = fminf(fabsf(z), 1.0f);               // NaN -> 1
+  const float y = (254.0f * a) * __builtin_amdgcn_rcpf(1.0f + a);
+  const int32_t k = (int32_t)y;                        // y >= 0: truncation = floor
+  const int32_t q = k + (a >= thr[k] ? 1 : 0);
+  return (z < 0.0f) ? -q : q;
+}
+
+// Clamping happens in float with IEEE minNum/maxNum, which also sends NaN to
+// the upper bound, so the float->int conversions below always see in-range values.
+__device__ __forceinline__ int32_t encode_m_linear(float m, float C) {
+  const float y = fmaxf(fminf(m * C, 127.0f), -127.0f);   // C = RN32(127/s); NaN -> 127
+  return (int32_t)__builtin_rintf(y);
+}
+
+// variance: y = x*C, C = RN32(255/s) (companded, x = sqrt(v)) or RN32(255/s^2) (linear, x = v)
+__device__ __forceinline__ uint32_t encode_v(float x, float C) {
+  const float y = fminf(x * C, 255.0f);                   // x*C >= 0; NaN -> 255
+  return (uint32_t)__builtin_rintf(y);
+}
+
+constexpr float K127 = 1.0f / 127.0f;   // RN32(1/127), constant-folded
+constexpr float K255 = 1.0f / 255.0f;   // RN32(1/255)
+
+}  // namespace fo

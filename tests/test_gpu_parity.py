@@ -1,0 +1,317 @@
+"""GPU parity of the HIP path against the CPU oracle, through the C ABI.
+
+Sizes are ones the oracle finishes in seconds while spanning many wave tiles
+and ragged tails.  Full-size workloads are in test_gpu_configs.py.
+Runs are free-running from the same seeded inputs (no state is ever copied
+from the GPU into the oracle).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from oracle.numerics import FORMATS, bits_to_value, spacing_in, spacing_out
+from oracle.optim import fresh_adamw_state, fresh_sgdm_state
+from precision_optimizer_state_amd import binding as B
+from precision_optimizer_state_amd.state import alloc_adamw_state, alloc_sgdm_state
+from tests.gpu_helpers import (
+    adamw_state_to_host,
+    check_adamw_state,
+    check_codes,
+    check_sgdm_state,
+    check_weights,
+    sgdm_state_to_host,
+    to_dev,
+    to_host,
+)
+from workloads import host_grad_bits, host_grads, host_weights
+
+pytestmark = pytest.mark.gpu
+DT = {"bf16": torch.bfloat16, "fp16": torch.float16}
+ECC_DT = {8: torch.int8, 16: torch.int16}
+VARIANTS = [("bf16", 8), ("bf16", 16), ("fp16", 8)]
+
+
+def _split_inputs(fmt, seed=0):
+    """Edges and interiors of every 16-bit pattern's rounding interval, both
+    signs, plus N(0, 0.02) weights, random f32 bit patterns and specials."""
+    F = FORMATS[fmt]
+    pats = np.arange(0, 0x8000, dtype=np.uint16)
+    a = bits_to_value(pats, fmt)
+    ok = np.isfinite(a) & (a < F.max_finite)
+    a = a[ok]
+    uo = spacing_out(a, fmt)
+    ui = np.where(a > 0, spacing_in(np.where(a > 0, a, 1.0), fmt), 0.0)
+    lo = (a - ui / 2).astype(np.float32)
+    hi = (a + uo / 2).astype(np.float32)
+    rng = np.random.default_rng(seed)
+    t = rng.random((6, a.size))
+    inner = (lo[None].astype(np.float64) + t * (hi - lo)[None]).astype(np.float32)
+    pts = np.concatenate([lo, np.nextafter(lo, np.float32(np.inf)), a.astype(np.float32),
+                          np.nextafter(hi, np.float32(0)), hi, inner.ravel()])
+    pts = np.abs(pts)
+    x = np.concatenate([pts, -pts,
+                        (rng.standard_normal(1_000_000) * 0.02).astype(np.float32),
+                        rng.integers(0, 2 ** 32, 500_000, dtype=np.uint64).astype(np.uint32).view(np.float32),
+                        np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 3.4e38, -3.4e38, 70000.0, 1e-45, -1e-45,
+                                  65519.0, 65520.0, 6.1e-5, 5.96e-8], np.float32)])
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("fmt,ecc_bits", VARIANTS)
+def test_split_matches_oracle_bitwise(fmt, ecc_bits):
+    x = _split_inputs(fmt)
+    print(f"split {fmt}+{ecc_bits}: n={x.size}", flush=True)
+    w_ref, e_ref = O.split_weights(x, fmt, ecc_bits)
+    xd = torch.from_numpy(x).cuda()
+    w = torch.empty(x.size, dtype=DT[fmt], device="cuda")
+    e = torch.empty(x.size, dtype=ECC_DT[ecc_bits], device="cuda")
+    B.fo_split_weights(xd, w, e, fmt, ecc_bits)
+    torch.cuda.synchronize()
+    wg, eg = to_host(w), to_host(e)
+    nan = np.isnan(x)
+    assert np.array_equal(wg[~nan], w_ref[~nan]), f"theta' differs on {np.count_nonzero(wg[~nan] != w_ref[~nan])}"
+    assert np.array_equal(eg, e_ref), f"rho differs on {np.count_nonzero(eg != e_ref)}"
+    # NaN inputs: quiet NaN with the input's sign
+    assert np.array_equal(wg[nan], w_ref[nan])
+
+
+@pytest.mark.parametrize("fmt,ecc_bits", VARIANTS)
+def test_reconstruct_matches_oracle_bitwise(fmt, ecc_bits):
+    x = _split_inputs(fmt, seed=1)
+    w_ref, e_ref = O.split_weights(x, fmt, ecc_bits)
+    r_ref = O.reconstruct_weights(w_ref, e_ref, fmt, ecc_bits)
+    out = torch.empty(x.size, dtype=torch.float32, device="cuda")
+    B.fo_reconstruct_weights(to_dev(w_ref, DT[fmt]), to_dev(e_ref, ECC_DT[ecc_bits]), out, fmt, ecc_bits)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    nan = np.isnan(r_ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), r_ref[~nan].view(np.uint32))
+
+
+def test_bf16_ecc16_identity_all_f32_patterns_on_device():
+    """split -> reconstruct with bf16 + 16-bit ECC is the identity on every
+    finite f32 below the bf16 overflow tie: all 2^32 patterns, on the device."""
+    chunk = 1 << 28
+    w = torch.empty(chunk, dtype=torch.bfloat16, device="cuda")
+    e = torch.empty(chunk, dtype=torch.int16, device="cuda")
+    r = torch.empty(chunk, dtype=torch.float32, device="cuda")
+    bad = 0
+    for s in range(0, 1 << 32, chunk):
+        u = torch.arange(s, s + chunk, dtype=torch.int64, device="cuda").to(torch.int32)
+        x = u.view(torch.float32)
+        B.fo_split_weights(x, w, e, "bf16", 16)
+        B.fo_reconstruct_weights(w, e, r, "bf16", 16)
+        keep = (u & 0x7FFFFFFF) < 0x7F7F8000
+        bad += int(((r.view(torch.int32) != u) & keep).sum().item())
+        del u, x, keep
+    print(f"bf16+16 identity over 2^32 patterns: {bad} mismatches", flush=True)
+    assert bad == 0
+
+
+def _state_inputs(kind, n, seed):
+    rng = np.random.default_rng(seed)
+    nb = -(-n // 32)
+    block_scale = np.repeat(10.0 ** rng.uniform(-9, 4, nb), 32)[:n]
+    g = rng.standard_t(3, n)
+    if kind == "m":
+        x = g * block_scale
+    else:
+        x = (g * g) * block_scale
+    x = x.astype(np.float32)
+    x[: 32 * 3] = 0.0                          # all-zero blocks
+    x[200:232] = x[200:232] * 1e-30            # underflowing scale
+    if kind == "m":
+        x[300] = 1e6                           # saturating scale
+    return x
+
+
+@pytest.mark.parametrize("kind", ["m", "v"])
+@pytest.mark.parametrize("codec", ["companded", "linear"])
+@pytest.mark.parametrize("n", [1 << 20, 1000, 4095 * 7 + 3])
+def test_quantize_dequantize_match_oracle(kind, codec, n):
+    x = _state_inputs(kind, n, seed=n)
+    q_ref, s_ref = O.quantize_state(x, kind, codec)
+    nb = -(-n // 32)
+    codes = torch.empty(n, dtype=torch.int8 if kind == "m" else torch.uint8, device="cuda")
+    scales = torch.empty(nb, dtype=torch.float16, device="cuda")
+    B.fo_companded_quantize(torch.from_numpy(x).cuda(), codes, scales, kind, codec)
+    out = torch.empty(n, dtype=torch.float32, device="cuda")
+    B.fo_dequantize(to_dev(q_ref, codes.dtype), to_dev(s_ref, torch.float16), out, kind, codec)
+    torch.cuda.synchronize()
+    bq = check_codes(f"quantize {kind}/{codec} codes", to_host(codes), q_ref)
+    bs = check_codes(f"quantize {kind}/{codec} scales", to_host(scales), s_ref)
+    print(f"quantize {kind}/{codec} n={n}: code mismatches {bq}, scale mismatches {bs}", flush=True)
+    d_ref = O.dequantize_state(q_ref, s_ref, kind, codec)
+    assert np.array_equal(out.cpu().numpy().view(np.uint32), d_ref.view(np.uint32))
+
+
+def _run_adamw(sizes, steps, hp, fmt="bf16", ecc_bits=8, codec="companded", tag="t", inject=None):
+    """Free-running GPU vs oracle over `steps` steps on a list of tensors."""
+    xs = [host_weights(tag, i, n) for i, n in enumerate(sizes)]
+    dev = [alloc_adamw_state(n, fmt, ecc_bits) for n in sizes]
+    ref = [fresh_adamw_state(x, fmt, ecc_bits) for x in xs]
+    for st, x in zip(dev, xs):
+        B.fo_split_weights(torch.from_numpy(x).cuda(), st["w16"], st["ecc"], fmt, ecc_bits)
+    tl = B.AdamWList(dev)
+    total_bad = 0
+    for step in range(1, steps + 1):
+        gbs = []
+        for i, (st, n) in enumerate(zip(dev, sizes)):
+            g = host_grads(tag, i, step, n, "t3")
+            if inject is not None:
+                g = inject(i, step, g)
+            gb = host_grad_bits(g, fmt)
+            gbs.append(gb)
+            st["grad"].copy_(to_dev(gb, DT[fmt]))
+        B.fo_fused_adamw_step(tl, B.adamw_hparams(step=step, wfmt=fmt, ecc_bits=ecc_bits, codec=codec, **hp))
+        for i in range(len(sizes)):
+            ref[i] = O.adamw_step(ref[i], gbs[i], dict(hp, step=step), fmt, ecc_bits, codec)
+        torch.cuda.synchronize()
+        for i in range(len(sizes)):
+            got = adamw_state_to_host(dev[i])
+            if inject is not None:
+                nan = np.isnan(O.reconstruct_weights(ref[i]["w16"], ref[i]["ecc"], fmt, ecc_bits))
+                assert np.array_equal(nan, np.isnan(O.reconstruct_weights(got["w16"], got["ecc"], fmt, ecc_bits)))
+                got["w16"] = np.where(nan, ref[i]["w16"], got["w16"])
+            bad = check_adamw_state(f"step {step} tensor {i} (n={sizes[i]})", got, ref[i], fmt, ecc_bits)
+            total_bad += sum(bad.values())
+    return total_bad
+
+
+HP_C1 = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+HP_LM = dict(lr=6e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+
+
+def test_fused_adamw_flat_1m_10_steps():
+    bad = _run_adamw([1 << 20], 10, HP_C1, tag="c1_flat1m")
+    print(f"c1 flat 1M, 10 steps: {bad} mismatching elements", flush=True)
+
+
+TAIL_SIZES = list(range(1, 34)) + [63, 64, 65, 1000, 2047, 2048, 2049, 4095, 4096, 4097, 8191, 8193, 20000]
+
+
+def test_fused_adamw_ragged_tails_multi_tensor():
+    rng = np.random.default_rng(7)
+    sizes = TAIL_SIZES + [int(v) for v in rng.integers(1, 100_000, 6)]
+    bad = _run_adamw(sizes, 3, HP_LM, tag="tails")
+    print(f"{len(sizes)} ragged tensors, 3 steps: {bad} mismatching elements", flush=True)
+
+
+@pytest.mark.parametrize("fmt,ecc_bits,codec", [("fp16", 8, "companded"), ("bf16", 16, "companded"),
+                                                ("bf16", 8, "linear"), ("fp16", 8, "linear"),
+                                                ("bf16", 16, "linear")])
+def test_fused_adamw_variants(fmt, ecc_bits, codec):
+    sizes = [300_000, 4097, 33, 1]
+    bad = _run_adamw(sizes, 4, HP_C1, fmt, ecc_bits, codec, tag=f"var_{fmt}{ecc_bits}{codec}")
+    print(f"variant {fmt}+{ecc_bits}/{codec}: {bad} mismatching elements", flush=True)
+
+
+def test_fused_adamw_nan_inf_grads_propagate():
+    def inject(i, step, g):
+        g = g.copy()
+        g[5] = np.nan
+        g[77] = np.inf
+        g[4000] = -np.inf
+        return g
+    _run_adamw([8192 + 5], 2, HP_C1, tag="nan", inject=inject)
+
+
+def _run_sgdm(sizes, steps, hp, fmt="bf16", ecc_bits=8, codec="companded", tag="s"):
+    xs = [host_weights(tag, i, n) for i, n in enumerate(sizes)]
+    dev = [alloc_sgdm_state(n, fmt, ecc_bits) for n in sizes]
+    ref = [fresh_sgdm_state(x, fmt, ecc_bits) for x in xs]
+    for st, x in zip(dev, xs):
+        B.fo_split_weights(torch.from_numpy(x).cuda(), st["w16"], st["ecc"], fmt, ecc_bits)
+    tl = B.SGDMList(dev)
+    total = 0
+    for step in range(1, steps + 1):
+        gbs = []
+        for i, (st, n) in enumerate(zip(dev, sizes)):
+            gb = host_grad_bits(host_grads(tag, i, step, n, "normal_outliers"), fmt)
+            gbs.append(gb)
+            st["grad"].copy_(to_dev(gb, DT[fmt]))
+        B.fo_fused_sgdm_step(tl, B.sgdm_hparams(step=step, wfmt=fmt, ecc_bits=ecc_bits, codec=codec, **hp))
+        for i in range(len(sizes)):
+            ref[i] = O.sgdm_step(ref[i], gbs[i], hp, fmt, ecc_bits, codec)
+        torch.cuda.synchronize()
+        for i in range(len(sizes)):
+            bad = check_sgdm_state(f"sgdm step {step} tensor {i} (n={sizes[i]})", sgdm_state_to_host(dev[i]),
+                                   ref[i], fmt, ecc_bits)
+            total += sum(bad.values())
+    return total
+
+
+HP_C4 = dict(lr=0.1, momentum=0.9, weight_decay=1e-4)
+
+
+@pytest.mark.parametrize("fmt,ecc_bits,codec", [("bf16", 8, "companded"), ("bf16", 16, "companded"),
+                                                ("fp16", 8, "companded"), ("bf16", 8, "linear")])
+def test_fused_sgdm_matches_oracle(fmt, ecc_bits, codec):
+    sizes = [9408, 64, 64, 4096, 36864, 16384, 1000, 2_048_000 // 8, 33, 1]
+    bad = _run_sgdm(sizes, 5, HP_C4, fmt, ecc_bits, codec, tag=f"sgdm_{fmt}{ecc_bits}{codec}")
+    print(f"sgdm {fmt}+{ecc_bits}/{codec}: {bad} mismatching elements", flush=True)
+
+
+def test_gradient_release_chunks_equal_whole_tensor():
+    """Stepping 32-aligned chunks of a tensor in separate calls (as gradients
+    arrive) gives bitwise the same state as one call on the whole tensor."""
+    n = (1 << 20) + 4096
+    x = host_weights("release", 0, n)
+    a = alloc_adamw_state(n)
+    B.fo_split_weights(torch.from_numpy(x).cuda(), a["w16"], a["ecc"])
+    b = {k: (v.clone() if v is not None else None) for k, v in a.items()}
+    bounds = [0, 1 << 18, 1 << 19, (1 << 19) + 2048, 1 << 20, n]
+    for step in (1, 2, 3):
+        gb = host_grad_bits(host_grads("release", 0, step, n, "t3"), "bf16")
+        a["grad"].copy_(to_dev(gb, torch.bfloat16))
+        b["grad"].copy_(a["grad"])
+        hp = B.adamw_hparams(step=step, **HP_C1)
+        B.fo_fused_adamw_step([a], hp)
+        for lo, hi in zip(bounds[:-1], bounds[1:]):
+            chunk = {k: b[k][lo:hi] for k in ("w16", "ecc", "grad", "m_q", "v_q")}
+            chunk["m_s"] = b["m_s"][lo // 32: -(-hi // 32)]
+            chunk["v_s"] = b["v_s"][lo // 32: -(-hi // 32)]
+            B.fo_fused_adamw_step([chunk], hp)
+    torch.cuda.synchronize()
+    for k in ("w16", "ecc", "m_q", "m_s", "v_q", "v_s"):
+        assert torch.equal(a[k].view(torch.uint8), b[k].view(torch.uint8)), k
+
+
+def test_determinism_two_runs_bitwise_equal():
+    n = 3 * (1 << 18) + 17
+    x = torch.from_numpy(host_weights("det", 0, n)).cuda()
+    outs = []
+    for _ in range(2):
+        st = alloc_adamw_state(n)
+        B.fo_split_weights(x, st["w16"], st["ecc"])
+        for step in (1, 2):
+            st["grad"].copy_(to_dev(host_grad_bits(host_grads("det", 0, step, n, "t3"), "bf16"), torch.bfloat16))
+            B.fo_fused_adamw_step([st], B.adamw_hparams(step=step, **HP_LM))
+        outs.append({k: v.clone() for k, v in st.items()})
+    for k in ("w16", "ecc", "m_q", "m_s", "v_q", "v_s"):
+        assert torch.equal(outs[0][k].view(torch.uint8), outs[1][k].view(torch.uint8)), k
+
+
+def test_stream_probe_preserves_data_with_zero_key():
+    n = 100_003
+    st = alloc_adamw_state(n)
+    for k in ("w16", "ecc", "m_q", "v_q"):
+        st[k].view(torch.uint8).copy_(torch.randint(0, 256, (st[k].numel() * st[k].element_size(),),
+                                                    dtype=torch.uint8, device="cuda"))
+    before = {k: v.clone() for k, v in st.items()}
+    B.fo_stream_probe([st], "bf16", 8, 0)
+    torch.cuda.synchronize()
+    for k in before:
+        assert torch.equal(before[k].view(torch.uint8), st[k].view(torch.uint8)), k
+
+
+def test_aliasing_list_rejected():
+    st = alloc_adamw_state(4096)
+    bad = dict(st)
+    bad["v_q"] = st["m_q"].view(torch.uint8)
+    with pytest.raises(B.FoError) as ei:
+        B.fo_fused_adamw_step([bad], B.adamw_hparams(step=1, **HP_C1))
+    assert ei.value.code == B.FO_EALIAS
