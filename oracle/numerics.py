@@ -116,7 +116,8 @@ def rna_downcast(x32: np.ndarray, fmt) -> tuple[np.ndarray, np.ndarray]:
     happened.  Non-finite inputs return their own magnitude (inf or nan).
     """
     fmt = _fmt(fmt)
-    ax = np.abs(np.asarray(x32, dtype=np.float32).astype(np.float64))
+    with np.errstate(invalid="ignore"):
+        ax = np.abs(np.asarray(x32, dtype=np.float32).astype(np.float64))
     finite = np.isfinite(ax)
     axf = np.where(finite, ax, 0.0)
     q = spacing_out_from_value(axf, fmt)
@@ -175,7 +176,8 @@ def split_weights(x32: np.ndarray, fmt="bf16", ecc_bits: int = 8):
     x32 = np.ascontiguousarray(x32, dtype=np.float32)
     neg = np.signbit(x32)
     nan = np.isnan(x32)
-    ax = np.abs(x32.astype(np.float64))
+    with np.errstate(invalid="ignore"):
+        ax = np.abs(x32.astype(np.float64))
     finite = np.isfinite(ax)
     with np.errstate(invalid="ignore"):
         a, _ = rna_downcast(x32, fmt)

@@ -73,8 +73,10 @@ __device__ __forceinline__ float ecc_decode(float t, int32_t rho) {
     const uint32_t a = f2u(t) & 0x7FFFFFFFu;
     if (a > 0x38800000u)                         // |theta'| above the smallest fp16 normal
       return u2f(f2u(t) + ((uint32_t)rho << 5)); // one fp16 spacing = 2^13 f32 spacings
-    // zero, subnormal and the smallest normal: spacing 2^-24 on both sides
-    return t + copysignf((float)rho * 0x1p-32f, t);
+    // zero, subnormal and the smallest normal: spacing 2^-24 on both sides;
+    // the offset rho * 2^-32 (exact) is applied to the magnitude
+    const float off = (float)rho * 0x1p-32f;
+    return t + u2f(f2u(off) ^ (f2u(t) & 0x80000000u));
   }
 }
 
