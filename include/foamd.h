@@ -196,6 +196,20 @@ int fo_fused_sgdm_step(const fo_sgdm_tensor* list, int32_t count,
 int fo_stream_probe(const fo_adamw_tensor* list, int32_t count, int32_t wfmt,
                     int32_t ecc_bits, uint32_t key, void* stream);
 
+/*
+ * fo_selftest -- verification of the exact fast arithmetic the fused kernels
+ * use on this device.  Over the f32 bit patterns [lo, lo + count) it counts
+ * (synchronously, into *mismatches) where
+ *   what 0: the Newton-refined hardware reciprocal differs from IEEE 1/x
+ *           (the kernels use it for positive normal x < 2^126);
+ *   what 1: the neighbour-corrected hardware square root differs from the
+ *           IEEE square root (used for x = 0 and x >= 2^-96);
+ *   what 2: the hardware float-to-u8 conversion differs from
+ *           clamp(round_half_even(x), 0, 255) (NaN skipped).
+ * Errors: FO_EINVAL (bad `what`, NULL output, range past 2^32), FO_ENOMEM, FO_EHIP.
+ */
+int fo_selftest(int what, uint32_t lo, uint64_t count, uint64_t* mismatches, void* stream);
+
 /* Message of the last failing call on this thread ("" if none). */
 const char* fo_last_error(void);
 /* FO_ABI_VERSION of the loaded library. */

@@ -25,7 +25,10 @@ U3  Per-element float32 operation order, every operation rounded once (no
         v = b2*v + (1-b2)*(g*g)
         theta = theta*decay
         d = sqrt(v)*ibc2 + eps
-        theta = theta - step_size*(m/d)
+        r = 1/d
+        theta = theta - step_size*(m*r)
+    The quotient m/d is formed as m times the correctly rounded reciprocal of
+    d (one rounding more than a division; the same textbook update).
 U4  SGD-M = torch.optim.SGD defaults: coupled L2 weight decay, dampening 0,
     no Nesterov:  d = g + wd*theta;  b = mu*b + d;  theta = theta - lr*b.
     With a zero-initialised buffer the first step gives b = d, as torch does.
@@ -101,7 +104,8 @@ def adamw_update(theta, g, m, v, S: AdamWScalars):
         th = theta * S.decay
         w = np.sqrt(v1)
         d = w * S.ibc2 + S.eps
-        th = th - S.step_size * (m1 / d)
+        r = np.float32(1.0) / d
+        th = th - S.step_size * (m1 * r)
     return th.astype(F32), m1.astype(F32), v1.astype(F32), w.astype(F32)
 
 

@@ -22,7 +22,8 @@ FO_MOMENTUM, FO_VARIANCE = 0, 1
 
 EXPORTS = (
     "fo_split_weights", "fo_reconstruct_weights", "fo_companded_quantize", "fo_dequantize",
-    "fo_fused_adamw_step", "fo_fused_sgdm_step", "fo_stream_probe", "fo_last_error", "fo_abi_version",
+    "fo_fused_adamw_step", "fo_fused_sgdm_step", "fo_stream_probe", "fo_selftest", "fo_last_error",
+    "fo_abi_version",
 )
 
 WFMT = {"bf16": FO_BF16, "fp16": FO_FP16}
@@ -77,6 +78,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fo_fused_adamw_step.argtypes = [ctypes.POINTER(AdamWTensor), c_int32, ctypes.POINTER(AdamWHParams), P]
     lib.fo_fused_sgdm_step.argtypes = [ctypes.POINTER(SGDMTensor), c_int32, ctypes.POINTER(SGDMHParams), P]
     lib.fo_stream_probe.argtypes = [ctypes.POINTER(AdamWTensor), c_int32, c_int32, c_int32, c_uint32, P]
+    lib.fo_selftest.argtypes = [c_int, c_uint32, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64), P]
     for name in EXPORTS:
         getattr(lib, name).restype = c_int
     lib.fo_last_error.restype = ctypes.c_char_p
@@ -201,6 +203,14 @@ def fo_stream_probe(tlist, wfmt="bf16", ecc_bits=8, key=0, stream=None) -> None:
         tlist = AdamWList(tlist)
     _check(load().fo_stream_probe(tlist.array, len(tlist), _fmt(wfmt, WFMT), int(ecc_bits), int(key),
                                   _stream(stream)))
+
+
+def fo_selftest(what: int, lo: int, count: int, stream=None) -> int:
+    """Mismatch count of the device's fast exact arithmetic over f32 patterns
+    [lo, lo + count): 0 = reciprocal, 1 = square root, 2 = float-to-u8."""
+    out = ctypes.c_uint64(0)
+    _check(load().fo_selftest(int(what), int(lo), int(count), ctypes.byref(out), _stream(stream)))
+    return int(out.value)
 
 
 def fo_abi_version() -> int:

@@ -34,6 +34,15 @@ namespace fo {
 enum { BF16 = 0, FP16 = 1 };
 enum { COMPANDED = 0, LINEAR = 1 };
 
+// Pointers into device memory are declared in the global address space so the
+// compiler emits global_* (not flat_*) memory instructions: flat accesses share
+// the LDS wait counter and would make every LDS table lookup wait for all
+// in-flight HBM loads.
+#define FO_GLOBAL __attribute__((address_space(1)))
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 __device__ __forceinline__ uint32_t f2u(float x) { return __float_as_uint(x); }
 __device__ __forceinline__ float u2f(uint32_t x) { return __uint_as_float(x); }
 
@@ -142,6 +151,68 @@ __device__ __forceinline__ SplitOut ecc_encode(float x) {
   return o;
 }
 
+// byte/half selection helpers (v_perm_b32: bytes 0-3 = src1, 4-7 = src0)
+__device__ __forceinline__ uint32_t perm(uint32_t hi_src, uint32_t lo_src, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi_src, lo_src, sel);
+}
+// low bytes of four words -> one packed word
+__device__ __forceinline__ uint32_t pack4_byte0(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return perm(perm(d, c, 0x0C0C0400u), perm(b, a, 0x0C0C0400u), 0x05040100u);
+}
+// byte 1 of four words -> one packed word
+__device__ __forceinline__ uint32_t pack4_byte1(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
+  return perm(perm(d, c, 0x0C0C0501u), perm(b, a, 0x0C0C0501u), 0x05040100u);
+}
+
+// Split of 8 consecutive values into packed theta' (4 dwords) and ECC (ECC/4
+// dwords).  bf16 fast path, valid while every value of the wave is below the
+// bf16 overflow tie and not NaN: theta' = high half of (bits + 0x8000) (RNA on
+// the magnitude; the sign bit is untouched), ECC8 = byte 1 of
+// min(sext16(bits) + 127 + bit8, 32767) (round-half-even of the offset / 256,
+// clamped at 127), ECC16 = the low half of the pattern (the offset itself).
+// Otherwise every element goes through ecc_encode.
+template <int WFMT, int ECC>
+__device__ __forceinline__ void split8(const float (&x)[8], uint32_t (&wo)[4], uint32_t (&eo)[ECC / 4]) {
+  if constexpr (WFMT == BF16) {
+    uint64_t special = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) special |= __builtin_amdgcn_ballot_w64(!(fabsf(x[k]) < 0x1.ffp+127f));
+    if (special == 0) {
+      uint32_t t[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) t[k] = f2u(x[k]) + 0x8000u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wo[i] = perm(t[2 * i + 1], t[2 * i], 0x07060302u);
+      if constexpr (ECC == 8) {
+        uint32_t S[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const uint32_t xb = f2u(x[k]);
+          const int32_t L = ((int32_t)(xb << 16)) >> 16;
+          S[k] = (uint32_t)min(L + 127 + (int32_t)((xb >> 8) & 1u), 32767);
+        }
+        eo[0] = pack4_byte1(S[0], S[1], S[2], S[3]);
+        eo[1] = pack4_byte1(S[4], S[5], S[6], S[7]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) eo[i] = perm(f2u(x[2 * i + 1]), f2u(x[2 * i]), 0x05040100u);
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wo[i] = 0;
+#pragma unroll
+  for (int i = 0; i < ECC / 4; ++i) eo[i] = 0;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const SplitOut so = ecc_encode<WFMT, ECC>(x[k]);
+    wo[k >> 1] |= so.h << (16 * (k & 1));
+    if constexpr (ECC == 8) eo[k >> 2] |= ((uint32_t)so.rho & 0xFFu) << (8 * (k & 3));
+    else eo[k >> 1] |= ((uint32_t)so.rho & 0xFFFFu) << (16 * (k & 1));
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Block scales: smallest binary16 >= x (x >= 0), saturating at 65504
 // ---------------------------------------------------------------------------
@@ -179,40 +250,92 @@ template <int J>
 __device__ __forceinline__ float quad_bcast(float x) { return dpp_f<qp_bcast<J>()>(x); }
 
 // ---------------------------------------------------------------------------
+// Exact fast arithmetic (gfx950)
+// ---------------------------------------------------------------------------
+// Correctly rounded square root from the hardware estimate: v_sqrt_f32 is
+// within one ulp, and the residuals v - s'*s of the two neighbours decide the
+// rounding exactly (no float lies strictly between s_lo*s and the squared
+// midpoint).  The residuals are exact for v >= 2^-96; v = 0, inf and NaN pass
+// through unchanged.  Callers fall back to the IEEE expansion when any lane
+// has 0 < v < 2^-96 (sqrt_needs_scaling).
+__device__ __forceinline__ float sqrt_corrected(float v) {
+  float s = __builtin_amdgcn_sqrtf(v);
+  const float s_dn = u2f(f2u(s) - 1u), s_up = u2f(f2u(s) + 1u);
+  const float r_dn = __builtin_fmaf(-s_dn, s, v);
+  const float r_up = __builtin_fmaf(-s_up, s, v);
+  s = (r_dn <= 0.0f) ? s_dn : s;
+  s = (r_up > 0.0f) ? s_up : s;
+  return s;
+}
+__device__ __forceinline__ bool sqrt_needs_scaling(float v) {   // 0 < v < 2^-96
+  return (f2u(v) - 1u) < 0x0F7FFFFFu;
+}
+// Correctly rounded reciprocal for positive normal b < 2^126: one Newton step
+// on the hardware estimate.  Verified exhaustively on gfx950 (fo_selftest);
+// callers fall back to IEEE division outside that range.
+__device__ __forceinline__ float rcp_refined(float b) {
+  const float y0 = __builtin_amdgcn_rcpf(b);
+  const float e = __builtin_fmaf(-b, y0, 1.0f);
+  return __builtin_fmaf(e, y0, y0);
+}
+
+// ---------------------------------------------------------------------------
 // State codecs
 // ---------------------------------------------------------------------------
-// LDS tables shared by a workgroup:
+// Momentum encode by interval table: a in [0,1] is keyed by the top 16 bits of
+// its f32 pattern (from 2^-9 on; below 2^-9 every a has code 0).  A key interval
+// is narrower than the spacing of the code thresholds (2k+1)/(507-2k), so it
+// holds at most one threshold: code(a) = menc[key].code + (a >= menc[key].thr).
+struct MEnc { float thr; int32_t code; };
+constexpr uint32_t MENC_BASE = 0x3B00u;                  // bits(2^-9) >> 16
+constexpr int MENC_N = 0x3F80 - 0x3B00 + 1;              // keys up to a = 1
+constexpr int MENC_CAP = 1160;
+// Workgroup copy of the codec tables (built once per device by k_init_tables):
 //   lut[i]  = RN32((i-127) / (254 - |i-127|)), i in [0,254]: momentum levels
-//   thr[k]  = smallest f32 >= (2k+1)/(507-2k), k in [0,126]: the |z| at which
-//             round(127*phi(|z|)) steps from k to k+1; thr[127] = 2 (never reached)
-struct CodecTables { float lut[256]; float thr[128]; };
+//   menc[k] = interval table of the momentum code as above
+struct CodecTables { float lut[256]; MEnc menc[MENC_CAP]; };
+static_assert(sizeof(CodecTables) % 16 == 0, "table copy granularity");
 
-__device__ __forceinline__ void init_tables(CodecTables& T, int tid, int nthreads) {
-  for (int i = tid; i < 255; i += nthreads) {
+// Builds the tables (one workgroup).  thr[k] = smallest f32 >= (2k+1)/(507-2k),
+// the |z| at which round(127*phi(|z|)) steps from k to k+1.
+__device__ __forceinline__ void build_tables(FO_GLOBAL CodecTables* out, float* thr, int tid, int nthreads) {
+  for (int i = tid; i < 256; i += nthreads) {
     const int q = i - 127;
     const int aq = q < 0 ? -q : q;
-    T.lut[i] = (float)q / (float)(254 - aq);           // IEEE division
+    out->lut[i] = (i < 255) ? (float)q / (float)(254 - aq) : 0.0f;   // IEEE division
   }
-  for (int k = tid; k < 128; k += nthreads) {
-    if (k == 127) { T.thr[k] = 2.0f; continue; }
+  for (int k = tid; k < 127; k += nthreads) {
     const float a = (float)(2 * k + 1), b = (float)(507 - 2 * k);
-    float t = a / b;                                   // nearest
-    // exact residual t*b - a (fma is exact here); below the true quotient -> step up
-    if (__builtin_fmaf(t, b, -a) < 0.0f) t = u2f(f2u(t) + 1u);
-    T.thr[k] = t;
+    float t = a / b;                                    // nearest
+    if (__builtin_fmaf(t, b, -a) < 0.0f) t = u2f(f2u(t) + 1u);   // exact residual: step up
+    thr[k] = t;
   }
-  if (tid == 0) T.lut[255] = 0.0f;
+  __syncthreads();
+  for (int key = tid; key < MENC_CAP; key += nthreads) {
+    MEnc e;
+    if (key < MENC_N) {
+      const float lo = (key == 0) ? 0.0f : u2f((MENC_BASE + key) << 16);
+      const float hi = u2f((MENC_BASE + key + 1) << 16);
+      int code = 0;
+      for (int k = 0; k < 127; ++k) code += (thr[k] <= lo) ? 1 : 0;
+      e.code = code;
+      e.thr = (code < 127 && thr[code] < hi) ? thr[code] : 2.0f;
+    } else {
+      e.code = 127;
+      e.thr = 2.0f;
+    }
+    out->menc[key].thr = e.thr;
+    out->menc[key].code = e.code;
+  }
 }
 
 // momentum, companded: z = m*R (R = RN32(1/s)); q = sign(z)*round(127*phi(min(|z|,1)))
-// The code is exact: an estimate y with error << 1/2 gives k = floor(y), and the
-// exact rounding is k + (a >= thr[k]) (no ties exist for float32 a).
-__device__ __forceinline__ int32_t encode_m_companded(float m, float R, const float* thr) {
+__device__ __forceinline__ int32_t encode_m_companded(float m, float R, const CodecTables& T) {
   const float z = m * R;
-  const float a = fminf(fabsf(z), 1.0f);               // NaN -> 1
-  const float y = (254.0f * a) * __builtin_amdgcn_rcpf(1.0f + a);
-  const int32_t k = (int32_t)y;                        // y >= 0: truncation = floor
-  const int32_t q = k + (a >= thr[k] ? 1 : 0);
+  const float a = fminf(fabsf(z), 1.0f);                  // NaN -> 1
+  const uint32_t key = __builtin_elementwise_sub_sat(f2u(a) >> 16, MENC_BASE);
+  const MEnc e = T.menc[key];
+  const int32_t q = e.code + (a >= e.thr ? 1 : 0);
   return (z < 0.0f) ? -q : q;
 }
 
@@ -223,10 +346,13 @@ __device__ __forceinline__ int32_t encode_m_linear(float m, float C) {
   return (int32_t)__builtin_rintf(y);
 }
 
-// variance: y = x*C, C = RN32(255/s) (companded, x = sqrt(v)) or RN32(255/s^2) (linear, x = v)
-__device__ __forceinline__ uint32_t encode_v(float x, float C) {
-  const float y = fminf(x * C, 255.0f);                   // x*C >= 0; NaN -> 255
-  return (uint32_t)__builtin_rintf(y);
+// variance: y = x*C, C = RN32(255/s) (companded, x = sqrt(v)) or RN32(255/s^2)
+// (linear, x = v); code = clamp(round_half_even(y), 0, 255) written into byte
+// `k` of `acc` (v_cvt_pk_u8_f32 rounds half to even and saturates; verified
+// against rint+clamp over every f32 by fo_selftest).
+__device__ __forceinline__ uint32_t encode_v_into(float x, float C, uint32_t k, uint32_t acc) {
+  const float y = fminf(x * C, 255.0f);                    // x*C >= 0; NaN -> 255
+  return __builtin_amdgcn_cvt_pk_u8_f32(y, k, acc);
 }
 
 constexpr float K127 = 1.0f / 127.0f;   // RN32(1/127), constant-folded

@@ -11,9 +11,12 @@
 //   * Per-block arithmetic (scale rounding, reciprocals) is done once per
 //     block: lane 4Q+j owns block (sub-tile j, quad Q), and the results are
 //     broadcast back to the quad with one DPP quad permute per sub-tile.
-//   * Waves are persistent and stride over the global tile list of all
-//     tensors of the step; a tile never crosses a tensor, and the last tile of
-//     a tensor takes a masked path.
+//   * The grid has one wave per wave tile (flat launch; the tile loop below
+//     also serves smaller grids).  A tile never crosses a tensor, and the last
+//     tile of a tensor takes a masked path.
+//   * Rare inputs (NaN/Inf/overflowing weights, tiny variances, out-of-range
+//     denominators) leave the fast arithmetic through wave-uniform branches
+//     onto IEEE sequences; the results are identical either way.
 // Pages: FlashOptim thread (Davis Blalock) and the blog "FlashOptim: Breaking
 // the Memory Wall with 24-bit Weights and Companded States" (Methodology
 // sections 1 and 2) define what is computed; the launch structure is ours.
@@ -30,6 +33,9 @@ constexpr int NSUB = 4;
 constexpr int TILE = SUB * NSUB;           // 2048 elements per wave tile
 constexpr int WAVES_PER_WG = 4;
 constexpr int WG = WAVE * WAVES_PER_WG;    // 256 threads
+// Block ownership (lane 4Q+j owns block 16j+Q of the tile) needs exactly one
+// sub-tile per lane of a quad: 4 sub-tiles, 64 blocks, 64 lanes.
+static_assert(NSUB == 4 && TILE / 32 == WAVE, "one owned block per lane");
 
 // Device copy of one tensor of a step (built by the host launcher).
 struct alignas(16) TensorDesc {
@@ -39,8 +45,13 @@ struct alignas(16) TensorDesc {
 };
 static_assert(sizeof(TensorDesc) == 80, "descriptor layout");
 
-struct AdamWConsts { float b1, b2, omb1, omb2, decay, step_size, ibc2, eps; };
+struct AdamWConsts {
+  float b1, b2, omb1, omb2, decay, step_size, ibc2, eps;
+  int fast_rcp;   // eps >= 2^-126: every denominator is a positive normal >= eps
+};
 struct SGDMConsts { float lr, mu, wd; };
+
+template <typename T> using gp = FO_GLOBAL T*;
 
 // ---------------------------------------------------------------------------
 // masked vector access for the last (partial) tile of a tensor
@@ -48,16 +59,16 @@ struct SGDMConsts { float lr, mu, wd; };
 template <int NDW>
 struct DW { uint32_t w[NDW]; };
 
-// load 8 elements of ESZ bytes (NDW = 2*ESZ dwords) starting at element p[0]
+// load 8 elements of ESZ bytes (2*ESZ dwords)
 template <int ESZ, bool FULL>
-__device__ __forceinline__ DW<2 * ESZ> load8(const void* base, int cnt) {
+__device__ __forceinline__ DW<2 * ESZ> load8(gp<const uint8_t> base, int cnt) {
   DW<2 * ESZ> r;
   if (FULL || cnt >= 8) {
     if constexpr (ESZ == 2) {
-      const uint4 v = *(const uint4*)base;
+      const u32x4 v = *(gp<const u32x4>)base;
       r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
     } else {
-      const uint2 v = *(const uint2*)base;
+      const u32x2 v = *(gp<const u32x2>)base;
       r.w[0] = v.x; r.w[1] = v.y;
     }
     return r;
@@ -68,8 +79,8 @@ __device__ __forceinline__ DW<2 * ESZ> load8(const void* base, int cnt) {
   for (int k = 0; k < 8; ++k) {
     if (k < cnt) {
       uint32_t x;
-      if constexpr (ESZ == 2) x = ((const uint16_t*)base)[k];
-      else x = ((const uint8_t*)base)[k];
+      if constexpr (ESZ == 2) x = ((gp<const uint16_t>)base)[k];
+      else x = base[k];
       r.w[(k * ESZ) >> 2] |= x << (8 * ((k * ESZ) & 3));
     }
   }
@@ -77,24 +88,23 @@ __device__ __forceinline__ DW<2 * ESZ> load8(const void* base, int cnt) {
 }
 
 template <int ESZ, bool FULL>
-__device__ __forceinline__ void store8(void* base, const DW<2 * ESZ>& r, int cnt) {
+__device__ __forceinline__ void store8(gp<uint8_t> base, const uint32_t* w, int cnt) {
   if (FULL || cnt >= 8) {
-    if constexpr (ESZ == 2) *(uint4*)base = make_uint4(r.w[0], r.w[1], r.w[2], r.w[3]);
-    else *(uint2*)base = make_uint2(r.w[0], r.w[1]);
+    if constexpr (ESZ == 2) *(gp<u32x4>)base = u32x4{w[0], w[1], w[2], w[3]};
+    else *(gp<u32x2>)base = u32x2{w[0], w[1]};
     return;
   }
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     if (k < cnt) {
-      const uint32_t x = r.w[(k * ESZ) >> 2] >> (8 * ((k * ESZ) & 3));
-      if constexpr (ESZ == 2) ((uint16_t*)base)[k] = (uint16_t)x;
-      else ((uint8_t*)base)[k] = (uint8_t)x;
+      const uint32_t x = w[(k * ESZ) >> 2] >> (8 * ((k * ESZ) & 3));
+      if constexpr (ESZ == 2) ((gp<uint16_t>)base)[k] = (uint16_t)x;
+      else base[k] = (uint8_t)x;
     }
   }
 }
 
 // element k of a packed group
-__device__ __forceinline__ uint32_t h16(const DW<4>& v, int k) { return (v.w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu; }
 __device__ __forceinline__ int32_t s8(const DW<2>& v, int k) {
   return ((int32_t)(v.w[k >> 2] << (24 - 8 * (k & 3)))) >> 24;
 }
@@ -106,17 +116,47 @@ template <int WFMT>
 __device__ __forceinline__ float wid(const DW<4>& v, int k) {
   return widen<WFMT>(v.w[k >> 1], k & 1);
 }
+template <int ECC>
+__device__ __forceinline__ int32_t rho_at(const DW<ECC / 4>& e, int k) {
+  if constexpr (ECC == 8) return s8(e, k);
+  else return s16(e, k);
+}
+
+__device__ __forceinline__ float bcast_j(float x, int j) {   // j is a compile-time constant after unrolling
+  return j == 0 ? quad_bcast<0>(x) : j == 1 ? quad_bcast<1>(x) : j == 2 ? quad_bcast<2>(x) : quad_bcast<3>(x);
+}
 
 // ---------------------------------------------------------------------------
-// tile lookup
+// shared pieces of the fused update
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ int find_tensor(const TensorDesc* __restrict__ tab, int count, int64_t T) {
-  int lo = 0, hi = count - 1;              // largest t with tile_begin <= T
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (tab[mid].tile_begin <= T) lo = mid; else hi = mid - 1;
+// w = sqrt(v) correctly rounded for 8 values (IEEE expansion when any lane of
+// the wave needs scaling)
+__device__ __forceinline__ void sqrt8(const float (&v)[EPL], float (&w)[EPL]) {
+  uint64_t slow = 0;
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) {
+    w[k] = sqrt_corrected(v[k]);
+    slow |= __builtin_amdgcn_ballot_w64(sqrt_needs_scaling(v[k]));
   }
-  return lo;
+  if (slow) {
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) w[k] = __builtin_sqrtf(v[k]);
+  }
+}
+
+// r = RN(1/d) for 8 denominators (IEEE division when any lane is outside the
+// verified range, or when eps does not keep denominators normal)
+__device__ __forceinline__ void rcp8(const float (&d)[EPL], float (&r)[EPL], int fast) {
+  uint64_t slow = fast ? 0ull : ~0ull;
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) {
+    r[k] = rcp_refined(d[k]);
+    slow |= __builtin_amdgcn_ballot_w64(!(d[k] < 0x1p126f));
+  }
+  if (slow) {
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) r[k] = 1.0f / d[k];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -128,13 +168,13 @@ __device__ __forceinline__ void adamw_tile(const TensorDesc& d, int64_t e0, int 
   constexpr int EB = ECC / 8;                                  // ECC bytes per element
   const int Q = lane >> 2, p = lane & 3;
   const int64_t n = d.n;
-  const uint16_t* __restrict__ grad = (const uint16_t*)d.grad + e0;
-  uint16_t* __restrict__ w16 = (uint16_t*)d.w16 + e0;
-  uint8_t* __restrict__ ecc = (uint8_t*)d.ecc + e0 * EB;
-  int8_t* __restrict__ mq = (int8_t*)d.q1 + e0;
-  uint8_t* __restrict__ vq = (uint8_t*)d.q2 + e0;
-  uint16_t* __restrict__ ms = (uint16_t*)d.s1 + (e0 >> 5);
-  uint16_t* __restrict__ vs = (uint16_t*)d.s2 + (e0 >> 5);
+  const gp<const uint8_t> grad = (gp<const uint8_t>)d.grad + e0 * 2;
+  const gp<uint8_t> w16 = (gp<uint8_t>)d.w16 + e0 * 2;
+  const gp<uint8_t> ecc = (gp<uint8_t>)d.ecc + e0 * EB;
+  const gp<uint8_t> mq = (gp<uint8_t>)d.q1 + e0;
+  const gp<uint8_t> vq = (gp<uint8_t>)d.q2 + e0;
+  const gp<uint16_t> ms = (gp<uint16_t>)d.s1 + (e0 >> 5);
+  const gp<uint16_t> vs = (gp<uint16_t>)d.s2 + (e0 >> 5);
   const int64_t rem = n - e0;                                  // valid elements from e0 on
   const int own = p * 16 + Q;                                  // owned block within the tile
   const bool own_ok = FULL || (int64_t)own * 32 < rem;
@@ -148,8 +188,8 @@ __device__ __forceinline__ void adamw_tile(const TensorDesc& d, int64_t e0, int 
   for (int j = 0; j < NSUB; ++j) {
     const int off = j * SUB + lane * EPL;
     cnt[j] = FULL ? 8 : (int)max((int64_t)0, min((int64_t)8, rem - off));
-    G[j] = load8<2, FULL>(grad + off, cnt[j]);
-    W[j] = load8<2, FULL>(w16 + off, cnt[j]);
+    G[j] = load8<2, FULL>(grad + off * 2, cnt[j]);
+    W[j] = load8<2, FULL>(w16 + off * 2, cnt[j]);
     E[j] = load8<EB, FULL>(ecc + off * EB, cnt[j]);
     MQ[j] = load8<1, FULL>(mq + off, cnt[j]);
     VQ[j] = load8<1, FULL>(vq + off, cnt[j]);
@@ -157,7 +197,7 @@ __device__ __forceinline__ void adamw_tile(const TensorDesc& d, int64_t e0, int 
   const uint32_t sm_old = own_ok ? (uint32_t)ms[own] : 0u;
   const uint32_t sv_old = own_ok ? (uint32_t)vs[own] : 0u;
 
-  // ---- per-block decode constants (owned block), then per sub-tile -------
+  // ---- per-block decode constants (owned block) -------------------------
   const float smf = h2f(sm_old), svf = h2f(sv_old);
   const float dm_own = (CODEC == COMPANDED) ? smf : smf * K127;
   const float dv_own = (CODEC == COMPANDED) ? svf * K255 : (svf * svf) * K255;
@@ -167,49 +207,44 @@ __device__ __forceinline__ void adamw_tile(const TensorDesc& d, int64_t e0, int 
 
 #pragma unroll
   for (int j = 0; j < NSUB; ++j) {
-    float dm, dv;
-    if (j == 0) { dm = quad_bcast<0>(dm_own); dv = quad_bcast<0>(dv_own); }
-    if (j == 1) { dm = quad_bcast<1>(dm_own); dv = quad_bcast<1>(dv_own); }
-    if (j == 2) { dm = quad_bcast<2>(dm_own); dv = quad_bcast<2>(dv_own); }
-    if (j == 3) { dm = quad_bcast<3>(dm_own); dv = quad_bcast<3>(dv_own); }
-    DW<4> Wo;
-    DW<2 * EB> Eo;
-#pragma unroll
-    for (int i = 0; i < 2 * EB; ++i) Eo.w[i] = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Wo.w[i] = 0;
-    float mmax = 0.0f, xmax = 0.0f;
+    const float dm = bcast_j(dm_own, j), dv = bcast_j(dv_own, j);
+    float th[EPL], m[EPL], v[EPL], w[EPL], den[EPL], r[EPL];
 #pragma unroll
     for (int k = 0; k < EPL; ++k) {
       const float g = wid<WFMT>(G[j], k);
-      int32_t rho;
-      if constexpr (ECC == 8) rho = s8(E[j], k); else rho = s16(E[j], k);
-      float th = ecc_decode<WFMT, ECC>(wid<WFMT>(W[j], k), rho);
+      th[k] = ecc_decode<WFMT, ECC>(wid<WFMT>(W[j], k), rho_at<ECC>(E[j], k));
       const int32_t qm = s8(MQ[j], k);
-      float m = (CODEC == COMPANDED) ? dm * tabs.lut[qm + 127] : dm * (float)qm;
+      const float mh = (CODEC == COMPANDED) ? dm * tabs.lut[qm + 127] : dm * (float)qm;
       const float tv = dv * (float)u8(VQ[j], k);
-      float v = (CODEC == COMPANDED) ? tv * tv : tv;
+      const float vh = (CODEC == COMPANDED) ? tv * tv : tv;
       // update (fixed float32 order, one rounding per operation)
-      m = c.b1 * m + c.omb1 * g;
-      v = c.b2 * v + c.omb2 * (g * g);
-      th = th * c.decay;
-      const float w = __builtin_sqrtf(v);
-      const float den = w * c.ibc2 + c.eps;
-      th = th - c.step_size * (m / den);
-      // split the new master
-      const SplitOut so = ecc_encode<WFMT, ECC>(th);
-      Wo.w[k >> 1] |= so.h << (16 * (k & 1));
-      if constexpr (ECC == 8) Eo.w[k >> 2] |= ((uint32_t)so.rho & 0xFFu) << (8 * (k & 3));
-      else Eo.w[k >> 1] |= ((uint32_t)so.rho & 0xFFFFu) << (16 * (k & 1));
-      const float x = (CODEC == COMPANDED) ? w : v;
-      Mn[j][k] = m;
+      m[k] = c.b1 * mh + c.omb1 * g;
+      v[k] = c.b2 * vh + c.omb2 * (g * g);
+      th[k] = th[k] * c.decay;
+    }
+    sqrt8(v, w);
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) den[k] = w[k] * c.ibc2 + c.eps;
+    rcp8(den, r, c.fast_rcp);
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) th[k] = th[k] - c.step_size * (m[k] * r[k]);
+
+    // split the new master and store it
+    uint32_t wo[4], eo[ECC / 4];
+    split8<WFMT, ECC>(th, wo, eo);
+    const int off = j * SUB + lane * EPL;
+    store8<2, FULL>(w16 + off * 2, wo, cnt[j]);
+    store8<EB, FULL>(ecc + off * EB, eo, cnt[j]);
+
+    float mmax = 0.0f, xmax = 0.0f;
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) {
+      const float x = (CODEC == COMPANDED) ? w[k] : v[k];
+      Mn[j][k] = m[k];
       Xn[j][k] = x;
-      mmax = fmaxf(mmax, fabsf(m));
+      mmax = fmaxf(mmax, fabsf(m[k]));
       xmax = fmaxf(xmax, x);
     }
-    const int off = j * SUB + lane * EPL;
-    store8<2, FULL>(w16 + off, Wo, cnt[j]);
-    store8<EB, FULL>(ecc + off * EB, Eo, cnt[j]);
     mmax = quad_max(mmax);
     xmax = quad_max(xmax);
     own_mmax = (p == j) ? mmax : own_mmax;
@@ -233,24 +268,18 @@ __device__ __forceinline__ void adamw_tile(const TensorDesc& d, int64_t e0, int 
 
 #pragma unroll
   for (int j = 0; j < NSUB; ++j) {
-    float cm, cv;
-    if (j == 0) { cm = quad_bcast<0>(cm_own); cv = quad_bcast<0>(cv_own); }
-    if (j == 1) { cm = quad_bcast<1>(cm_own); cv = quad_bcast<1>(cv_own); }
-    if (j == 2) { cm = quad_bcast<2>(cm_own); cv = quad_bcast<2>(cv_own); }
-    if (j == 3) { cm = quad_bcast<3>(cm_own); cv = quad_bcast<3>(cv_own); }
-    DW<2> Mo, Vo;
-    Mo.w[0] = Mo.w[1] = Vo.w[0] = Vo.w[1] = 0;
+    const float cm = bcast_j(cm_own, j), cv = bcast_j(cv_own, j);
+    uint32_t qm[EPL], vo[2] = {0u, 0u};
 #pragma unroll
     for (int k = 0; k < EPL; ++k) {
-      const int32_t qm = (CODEC == COMPANDED) ? encode_m_companded(Mn[j][k], cm, tabs.thr)
-                                              : encode_m_linear(Mn[j][k], cm);
-      const uint32_t qv = encode_v(Xn[j][k], cv);
-      Mo.w[k >> 2] |= ((uint32_t)qm & 0xFFu) << (8 * (k & 3));
-      Vo.w[k >> 2] |= qv << (8 * (k & 3));
+      qm[k] = (uint32_t)((CODEC == COMPANDED) ? encode_m_companded(Mn[j][k], cm, tabs)
+                                              : encode_m_linear(Mn[j][k], cm));
+      vo[k >> 2] = encode_v_into(Xn[j][k], cv, k & 3, vo[k >> 2]);
     }
+    const uint32_t mo[2] = {pack4_byte0(qm[0], qm[1], qm[2], qm[3]), pack4_byte0(qm[4], qm[5], qm[6], qm[7])};
     const int off = j * SUB + lane * EPL;
-    store8<1, FULL>(mq + off, Mo, cnt[j]);
-    store8<1, FULL>(vq + off, Vo, cnt[j]);
+    store8<1, FULL>(mq + off, mo, cnt[j]);
+    store8<1, FULL>(vq + off, vo, cnt[j]);
   }
 }
 
@@ -263,11 +292,11 @@ __device__ __forceinline__ void sgdm_tile(const TensorDesc& d, int64_t e0, int l
   constexpr int EB = ECC / 8;
   const int Q = lane >> 2, p = lane & 3;
   const int64_t n = d.n;
-  const uint16_t* __restrict__ grad = (const uint16_t*)d.grad + e0;
-  uint16_t* __restrict__ w16 = (uint16_t*)d.w16 + e0;
-  uint8_t* __restrict__ ecc = (uint8_t*)d.ecc + e0 * EB;
-  int8_t* __restrict__ bq = (int8_t*)d.q1 + e0;
-  uint16_t* __restrict__ bs = (uint16_t*)d.s1 + (e0 >> 5);
+  const gp<const uint8_t> grad = (gp<const uint8_t>)d.grad + e0 * 2;
+  const gp<uint8_t> w16 = (gp<uint8_t>)d.w16 + e0 * 2;
+  const gp<uint8_t> ecc = (gp<uint8_t>)d.ecc + e0 * EB;
+  const gp<uint8_t> bq = (gp<uint8_t>)d.q1 + e0;
+  const gp<uint16_t> bs = (gp<uint16_t>)d.s1 + (e0 >> 5);
   const int64_t rem = n - e0;
   const int own = p * 16 + Q;
   const bool own_ok = FULL || (int64_t)own * 32 < rem;
@@ -280,8 +309,8 @@ __device__ __forceinline__ void sgdm_tile(const TensorDesc& d, int64_t e0, int l
   for (int j = 0; j < NSUB; ++j) {
     const int off = j * SUB + lane * EPL;
     cnt[j] = FULL ? 8 : (int)max((int64_t)0, min((int64_t)8, rem - off));
-    G[j] = load8<2, FULL>(grad + off, cnt[j]);
-    W[j] = load8<2, FULL>(w16 + off, cnt[j]);
+    G[j] = load8<2, FULL>(grad + off * 2, cnt[j]);
+    W[j] = load8<2, FULL>(w16 + off * 2, cnt[j]);
     E[j] = load8<EB, FULL>(ecc + off * EB, cnt[j]);
     BQ[j] = load8<1, FULL>(bq + off, cnt[j]);
   }
@@ -293,39 +322,26 @@ __device__ __forceinline__ void sgdm_tile(const TensorDesc& d, int64_t e0, int l
   float own_bmax = 0.0f;
 #pragma unroll
   for (int j = 0; j < NSUB; ++j) {
-    float db;
-    if (j == 0) db = quad_bcast<0>(db_own);
-    if (j == 1) db = quad_bcast<1>(db_own);
-    if (j == 2) db = quad_bcast<2>(db_own);
-    if (j == 3) db = quad_bcast<3>(db_own);
-    DW<4> Wo;
-    DW<2 * EB> Eo;
-#pragma unroll
-    for (int i = 0; i < 2 * EB; ++i) Eo.w[i] = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) Wo.w[i] = 0;
+    const float db = bcast_j(db_own, j);
+    float th[EPL], b[EPL];
     float bmax = 0.0f;
 #pragma unroll
     for (int k = 0; k < EPL; ++k) {
       const float g = wid<WFMT>(G[j], k);
-      int32_t rho;
-      if constexpr (ECC == 8) rho = s8(E[j], k); else rho = s16(E[j], k);
-      float th = ecc_decode<WFMT, ECC>(wid<WFMT>(W[j], k), rho);
+      const float t0 = ecc_decode<WFMT, ECC>(wid<WFMT>(W[j], k), rho_at<ECC>(E[j], k));
       const int32_t qb = s8(BQ[j], k);
-      float b = (CODEC == COMPANDED) ? db * tabs.lut[qb + 127] : db * (float)qb;
-      const float dd = g + c.wd * th;
-      b = c.mu * b + dd;
-      th = th - c.lr * b;
-      const SplitOut so = ecc_encode<WFMT, ECC>(th);
-      Wo.w[k >> 1] |= so.h << (16 * (k & 1));
-      if constexpr (ECC == 8) Eo.w[k >> 2] |= ((uint32_t)so.rho & 0xFFu) << (8 * (k & 3));
-      else Eo.w[k >> 1] |= ((uint32_t)so.rho & 0xFFFFu) << (16 * (k & 1));
-      Bn[j][k] = b;
-      bmax = fmaxf(bmax, fabsf(b));
+      const float bh = (CODEC == COMPANDED) ? db * tabs.lut[qb + 127] : db * (float)qb;
+      const float dd = g + c.wd * t0;
+      b[k] = c.mu * bh + dd;
+      th[k] = t0 - c.lr * b[k];
+      Bn[j][k] = b[k];
+      bmax = fmaxf(bmax, fabsf(b[k]));
     }
+    uint32_t wo[4], eo[ECC / 4];
+    split8<WFMT, ECC>(th, wo, eo);
     const int off = j * SUB + lane * EPL;
-    store8<2, FULL>(w16 + off, Wo, cnt[j]);
-    store8<EB, FULL>(ecc + off * EB, Eo, cnt[j]);
+    store8<2, FULL>(w16 + off * 2, wo, cnt[j]);
+    store8<EB, FULL>(ecc + off * EB, eo, cnt[j]);
     bmax = quad_max(bmax);
     own_bmax = (p == j) ? bmax : own_bmax;
   }
@@ -335,20 +351,14 @@ __device__ __forceinline__ void sgdm_tile(const TensorDesc& d, int64_t e0, int l
   const float cb_own = (sb > 0.0f) ? ((CODEC == COMPANDED) ? 1.0f : 127.0f) / sb : 0.0f;
 #pragma unroll
   for (int j = 0; j < NSUB; ++j) {
-    float cb;
-    if (j == 0) cb = quad_bcast<0>(cb_own);
-    if (j == 1) cb = quad_bcast<1>(cb_own);
-    if (j == 2) cb = quad_bcast<2>(cb_own);
-    if (j == 3) cb = quad_bcast<3>(cb_own);
-    DW<2> Bo;
-    Bo.w[0] = Bo.w[1] = 0;
+    const float cb = bcast_j(cb_own, j);
+    uint32_t q[EPL];
 #pragma unroll
-    for (int k = 0; k < EPL; ++k) {
-      const int32_t q = (CODEC == COMPANDED) ? encode_m_companded(Bn[j][k], cb, tabs.thr)
-                                             : encode_m_linear(Bn[j][k], cb);
-      Bo.w[k >> 2] |= ((uint32_t)q & 0xFFu) << (8 * (k & 3));
-    }
-    store8<1, FULL>(bq + j * SUB + lane * EPL, Bo, cnt[j]);
+    for (int k = 0; k < EPL; ++k)
+      q[k] = (uint32_t)((CODEC == COMPANDED) ? encode_m_companded(Bn[j][k], cb, tabs)
+                                             : encode_m_linear(Bn[j][k], cb));
+    const uint32_t bo[2] = {pack4_byte0(q[0], q[1], q[2], q[3]), pack4_byte0(q[4], q[5], q[6], q[7])};
+    store8<1, FULL>(bq + j * SUB + lane * EPL, bo, cnt[j]);
   }
 }
 
@@ -359,13 +369,13 @@ template <int ECC, bool FULL>
 __device__ __forceinline__ void probe_tile(const TensorDesc& d, int64_t e0, int lane, uint32_t key) {
   constexpr int EB = ECC / 8;
   const int Q = lane >> 2, p = lane & 3;
-  const uint16_t* __restrict__ grad = (const uint16_t*)d.grad + e0;
-  uint16_t* __restrict__ w16 = (uint16_t*)d.w16 + e0;
-  uint8_t* __restrict__ ecc = (uint8_t*)d.ecc + e0 * EB;
-  int8_t* __restrict__ mq = (int8_t*)d.q1 + e0;
-  uint8_t* __restrict__ vq = (uint8_t*)d.q2 + e0;
-  uint16_t* __restrict__ ms = (uint16_t*)d.s1 + (e0 >> 5);
-  uint16_t* __restrict__ vs = (uint16_t*)d.s2 + (e0 >> 5);
+  const gp<const uint8_t> grad = (gp<const uint8_t>)d.grad + e0 * 2;
+  const gp<uint8_t> w16 = (gp<uint8_t>)d.w16 + e0 * 2;
+  const gp<uint8_t> ecc = (gp<uint8_t>)d.ecc + e0 * EB;
+  const gp<uint8_t> mq = (gp<uint8_t>)d.q1 + e0;
+  const gp<uint8_t> vq = (gp<uint8_t>)d.q2 + e0;
+  const gp<uint16_t> ms = (gp<uint16_t>)d.s1 + (e0 >> 5);
+  const gp<uint16_t> vs = (gp<uint16_t>)d.s2 + (e0 >> 5);
   const int64_t rem = d.n - e0;
   const int own = p * 16 + Q;
   const bool own_ok = FULL || (int64_t)own * 32 < rem;
@@ -377,38 +387,47 @@ __device__ __forceinline__ void probe_tile(const TensorDesc& d, int64_t e0, int 
   for (int j = 0; j < NSUB; ++j) {
     const int off = j * SUB + lane * EPL;
     cnt[j] = FULL ? 8 : (int)max((int64_t)0, min((int64_t)8, rem - off));
-    G[j] = load8<2, FULL>(grad + off, cnt[j]);
-    W[j] = load8<2, FULL>(w16 + off, cnt[j]);
+    G[j] = load8<2, FULL>(grad + off * 2, cnt[j]);
+    W[j] = load8<2, FULL>(w16 + off * 2, cnt[j]);
     E[j] = load8<EB, FULL>(ecc + off * EB, cnt[j]);
     MQ[j] = load8<1, FULL>(mq + off, cnt[j]);
     VQ[j] = load8<1, FULL>(vq + off, cnt[j]);
   }
-  uint32_t sm = own_ok ? (uint32_t)ms[own] : 0u;
-  uint32_t sv = own_ok ? (uint32_t)vs[own] : 0u;
+  const uint32_t sm = own_ok ? (uint32_t)ms[own] : 0u;
+  const uint32_t sv = own_ok ? (uint32_t)vs[own] : 0u;
 #pragma unroll
   for (int j = 0; j < NSUB; ++j) {
     // fold the gradient into the key so it is really read
-    uint32_t k2 = key & (G[j].w[0] ^ G[j].w[1] ^ G[j].w[2] ^ G[j].w[3]);
+    const uint32_t k2 = key & (G[j].w[0] ^ G[j].w[1] ^ G[j].w[2] ^ G[j].w[3]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) W[j].w[i] ^= k2;
 #pragma unroll
     for (int i = 0; i < 2 * EB; ++i) E[j].w[i] ^= key;
     MQ[j].w[0] ^= key; MQ[j].w[1] ^= key; VQ[j].w[0] ^= key; VQ[j].w[1] ^= key;
     const int off = j * SUB + lane * EPL;
-    store8<2, FULL>(w16 + off, W[j], cnt[j]);
-    store8<EB, FULL>(ecc + off * EB, E[j], cnt[j]);
-    store8<1, FULL>(mq + off, MQ[j], cnt[j]);
-    store8<1, FULL>(vq + off, VQ[j], cnt[j]);
+    store8<2, FULL>(w16 + off * 2, W[j].w, cnt[j]);
+    store8<EB, FULL>(ecc + off * EB, E[j].w, cnt[j]);
+    store8<1, FULL>(mq + off, MQ[j].w, cnt[j]);
+    store8<1, FULL>(vq + off, VQ[j].w, cnt[j]);
   }
   if (own_ok) { ms[own] = (uint16_t)(sm ^ key); vs[own] = (uint16_t)(sv ^ key); }
 }
 
 // ---------------------------------------------------------------------------
-// persistent multi-tensor kernels
+// multi-tensor kernels
 // ---------------------------------------------------------------------------
-// Persistent waves stride over the global wave-tile list of the step.  The
-// tensor of a tile is found by binary search over the descriptors' first-tile
-// indices when a wave leaves its current tensor (tiles only move forward).
+__device__ __forceinline__ int find_tensor(const TensorDesc* __restrict__ tab, int count, int64_t T) {
+  int lo = 0, hi = count - 1;              // largest t with tile_begin <= T
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tab[mid].tile_begin <= T) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// Waves stride over the global wave-tile list of the step (one tile per wave
+// with the default flat grid).  The tensor of a tile is found by binary search
+// over the descriptors' first-tile indices when a wave leaves its tensor.
 template <typename F>
 __device__ __forceinline__ void tile_loop(const TensorDesc* __restrict__ tab, int count, int64_t total_tiles, F&& body) {
   const int lane = threadIdx.x & (WAVE - 1);
@@ -427,12 +446,26 @@ __device__ __forceinline__ void tile_loop(const TensorDesc* __restrict__ tab, in
   }
 }
 
+// copy the codec tables from global memory into the workgroup's LDS
+__device__ __forceinline__ void load_tables(CodecTables& dst, const CodecTables* __restrict__ src) {
+  constexpr int N16 = sizeof(CodecTables) / 16;
+  const gp<const u32x4> s = (gp<const u32x4>)src;
+  u32x4* d = (u32x4*)&dst;
+  for (int i = threadIdx.x; i < N16; i += blockDim.x) d[i] = s[i];
+  __syncthreads();
+}
+
+__global__ void __launch_bounds__(WG) k_init_tables(CodecTables* out) {
+  __shared__ float thr[128];
+  build_tables((gp<CodecTables>)out, thr, threadIdx.x, blockDim.x);
+}
+
 template <int WFMT, int ECC, int CODEC>
 __global__ void __launch_bounds__(WG) k_fused_adamw(const TensorDesc* __restrict__ tab, int count,
-                                                    int64_t total_tiles, AdamWConsts c) {
+                                                    int64_t total_tiles, const CodecTables* __restrict__ gtabs,
+                                                    AdamWConsts c) {
   __shared__ CodecTables tabs;
-  init_tables(tabs, threadIdx.x, blockDim.x);
-  __syncthreads();
+  load_tables(tabs, gtabs);
   tile_loop(tab, count, total_tiles, [&](const TensorDesc& d, int64_t e0, int lane) {
     if (e0 + TILE <= d.n) adamw_tile<WFMT, ECC, CODEC, true>(d, e0, lane, tabs, c);
     else adamw_tile<WFMT, ECC, CODEC, false>(d, e0, lane, tabs, c);
@@ -441,10 +474,10 @@ __global__ void __launch_bounds__(WG) k_fused_adamw(const TensorDesc* __restrict
 
 template <int WFMT, int ECC, int CODEC>
 __global__ void __launch_bounds__(WG) k_fused_sgdm(const TensorDesc* __restrict__ tab, int count,
-                                                   int64_t total_tiles, SGDMConsts c) {
+                                                   int64_t total_tiles, const CodecTables* __restrict__ gtabs,
+                                                   SGDMConsts c) {
   __shared__ CodecTables tabs;
-  init_tables(tabs, threadIdx.x, blockDim.x);
-  __syncthreads();
+  load_tables(tabs, gtabs);
   tile_loop(tab, count, total_tiles, [&](const TensorDesc& d, int64_t e0, int lane) {
     if (e0 + TILE <= d.n) sgdm_tile<WFMT, ECC, CODEC, true>(d, e0, lane, tabs, c);
     else sgdm_tile<WFMT, ECC, CODEC, false>(d, e0, lane, tabs, c);
@@ -467,36 +500,29 @@ template <int WFMT, int ECC>
 __global__ void __launch_bounds__(WG) k_split(const float* __restrict__ x, int64_t n,
                                               uint16_t* __restrict__ w16, uint8_t* __restrict__ ecc) {
   constexpr int EB = ECC / 8;
+  const gp<const float> xs = (gp<const float>)x;
   const int64_t stride = (int64_t)gridDim.x * WG * EPL;
-  for (int64_t i = ((int64_t)blockIdx.x * WG + threadIdx.x) * EPL; i < n; i += stride) {
-    const int cnt = (int)min((int64_t)8, n - i);
+  // every lane of a wave iterates together (the stride is a multiple of 512),
+  // so the wave-uniform branches inside split8 see whole waves
+  for (int64_t i0 = (int64_t)blockIdx.x * WG * EPL; i0 < n; i0 += stride) {
+    const int64_t i = i0 + threadIdx.x * EPL;
+    const int cnt = (int)max((int64_t)0, min((int64_t)8, n - i));
     float v[8];
     if (cnt == 8) {
-      const float4 a = *(const float4*)(x + i), b = *(const float4*)(x + i + 4);
+      const f32x4 a = *(gp<const f32x4>)(xs + i), b = *(gp<const f32x4>)(xs + i + 4);
       v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     } else {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = (k < cnt) ? x[i + k] : 0.0f;
+      for (int k = 0; k < 8; ++k) v[k] = (k < cnt) ? xs[i + k] : 0.0f;
     }
-    DW<4> Wo;
-    DW<2 * EB> Eo;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) Wo.w[q] = 0;
-#pragma unroll
-    for (int q = 0; q < 2 * EB; ++q) Eo.w[q] = 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const SplitOut so = ecc_encode<WFMT, ECC>(v[k]);
-      Wo.w[k >> 1] |= so.h << (16 * (k & 1));
-      if constexpr (ECC == 8) Eo.w[k >> 2] |= ((uint32_t)so.rho & 0xFFu) << (8 * (k & 3));
-      else Eo.w[k >> 1] |= ((uint32_t)so.rho & 0xFFFFu) << (16 * (k & 1));
-    }
+    uint32_t wo[4], eo[ECC / 4];
+    split8<WFMT, ECC>(v, wo, eo);
     if (cnt == 8) {
-      store8<2, true>(w16 + i, Wo, 8);
-      store8<EB, true>(ecc + i * EB, Eo, 8);
-    } else {
-      store8<2, false>(w16 + i, Wo, cnt);
-      store8<EB, false>(ecc + i * EB, Eo, cnt);
+      store8<2, true>((gp<uint8_t>)w16 + i * 2, wo, 8);
+      store8<EB, true>((gp<uint8_t>)ecc + i * EB, eo, 8);
+    } else if (cnt > 0) {
+      store8<2, false>((gp<uint8_t>)w16 + i * 2, wo, cnt);
+      store8<EB, false>((gp<uint8_t>)ecc + i * EB, eo, cnt);
     }
   }
 }
@@ -505,26 +531,25 @@ template <int WFMT, int ECC>
 __global__ void __launch_bounds__(WG) k_reconstruct(const uint16_t* __restrict__ w16, const uint8_t* __restrict__ ecc,
                                                     int64_t n, float* __restrict__ out) {
   constexpr int EB = ECC / 8;
+  const gp<float> o = (gp<float>)out;
   const int64_t stride = (int64_t)gridDim.x * WG * EPL;
   for (int64_t i = ((int64_t)blockIdx.x * WG + threadIdx.x) * EPL; i < n; i += stride) {
     const int cnt = (int)min((int64_t)8, n - i);
     DW<4> W;
     DW<2 * EB> E;
-    if (cnt == 8) { W = load8<2, true>(w16 + i, 8); E = load8<EB, true>(ecc + i * EB, 8); }
-    else { W = load8<2, false>(w16 + i, cnt); E = load8<EB, false>(ecc + i * EB, cnt); }
+    const gp<const uint8_t> wp = (gp<const uint8_t>)w16 + i * 2;
+    const gp<const uint8_t> ep = (gp<const uint8_t>)ecc + i * EB;
+    if (cnt == 8) { W = load8<2, true>(wp, 8); E = load8<EB, true>(ep, 8); }
+    else { W = load8<2, false>(wp, cnt); E = load8<EB, false>(ep, cnt); }
     float v[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      int32_t rho;
-      if constexpr (ECC == 8) rho = s8(E, k); else rho = s16(E, k);
-      v[k] = ecc_decode<WFMT, ECC>(wid<WFMT>(W, k), rho);
-    }
+    for (int k = 0; k < 8; ++k) v[k] = ecc_decode<WFMT, ECC>(wid<WFMT>(W, k), rho_at<ECC>(E, k));
     if (cnt == 8) {
-      *(float4*)(out + i) = make_float4(v[0], v[1], v[2], v[3]);
-      *(float4*)(out + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      *(gp<f32x4>)(o + i) = f32x4{v[0], v[1], v[2], v[3]};
+      *(gp<f32x4>)(o + i + 4) = f32x4{v[4], v[5], v[6], v[7]};
     } else {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) if (k < cnt) out[i + k] = v[k];
+      for (int k = 0; k < 8; ++k) if (k < cnt) o[i + k] = v[k];
     }
   }
 }
@@ -532,84 +557,119 @@ __global__ void __launch_bounds__(WG) k_reconstruct(const uint16_t* __restrict__
 // KIND 0 = momentum (int8), 1 = variance (uint8).  A quad of lanes = one block.
 template <int KIND, int CODEC>
 __global__ void __launch_bounds__(WG) k_quantize(const float* __restrict__ x, int64_t n,
-                                                 uint8_t* __restrict__ codes, uint16_t* __restrict__ scales) {
+                                                 uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
+                                                 const CodecTables* __restrict__ gtabs) {
   __shared__ CodecTables tabs;
-  init_tables(tabs, threadIdx.x, blockDim.x);
-  __syncthreads();
+  load_tables(tabs, gtabs);
+  const gp<const float> xs = (gp<const float>)x;
   const int64_t stride = (int64_t)gridDim.x * WG * EPL;
-  for (int64_t i = ((int64_t)blockIdx.x * WG + threadIdx.x) * EPL; i < n + 0; i += stride) {
-    // every lane of a wave iterates together (the stride is a multiple of 512),
-    // so the 4 lanes of a block are always active at the same time
-    const int cnt = (int)min((int64_t)8, n - i);
+  // all lanes iterate together (stride multiple of 512), so the 4 lanes of a
+  // block are active at the same time; lanes past n contribute zeros
+  for (int64_t i0 = (int64_t)blockIdx.x * WG * EPL; i0 < n; i0 += stride) {
+    const int64_t i = i0 + threadIdx.x * EPL;
+    const int cnt = (int)max((int64_t)0, min((int64_t)8, n - i));
     float v[8];
     if (cnt == 8) {
-      const float4 a = *(const float4*)(x + i), b = *(const float4*)(x + i + 4);
+      const f32x4 a = *(gp<const f32x4>)(xs + i), b = *(gp<const f32x4>)(xs + i + 4);
       v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     } else {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = (k < cnt) ? x[i + k] : 0.0f;
+      for (int k = 0; k < 8; ++k) v[k] = (k < cnt) ? xs[i + k] : 0.0f;
     }
     float e[8];
+    if (KIND == 1 && CODEC == COMPANDED) {
+      sqrt8(v, e);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) e[k] = v[k];
+    }
     float mx = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      e[k] = (KIND == 0) ? v[k] : ((CODEC == COMPANDED) ? __builtin_sqrtf(v[k]) : v[k]);
-      mx = fmaxf(mx, (KIND == 0) ? fabsf(e[k]) : e[k]);
-    }
+    for (int k = 0; k < 8; ++k) mx = fmaxf(mx, (KIND == 0) ? fabsf(e[k]) : e[k]);
     mx = quad_max(mx);
     const uint32_t sb = ru_fp16((KIND == 1 && CODEC == LINEAR) ? __builtin_sqrtf(mx) : mx);
-    if ((threadIdx.x & 3) == 0) scales[i >> 5] = (uint16_t)sb;
+    if ((threadIdx.x & 3) == 0 && cnt > 0) ((gp<uint16_t>)scales)[i >> 5] = (uint16_t)sb;
     const float s = h2f(sb);
     float C;
     if (KIND == 0) C = (s > 0.0f) ? ((CODEC == COMPANDED) ? 1.0f : 127.0f) / s : 0.0f;
     else if (CODEC == COMPANDED) C = (s > 0.0f) ? 255.0f / s : 0.0f;
     else { const float s2 = s * s; C = (s2 > 0.0f) ? 255.0f / s2 : 0.0f; }
-    DW<2> o;
-    o.w[0] = o.w[1] = 0;
+    uint32_t o[2];
+    if (KIND == 0) {
+      uint32_t q[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      uint32_t q;
-      if (KIND == 0) q = (uint32_t)((CODEC == COMPANDED) ? encode_m_companded(e[k], C, tabs.thr)
-                                                         : encode_m_linear(e[k], C)) & 0xFFu;
-      else q = encode_v(e[k], C);
-      o.w[k >> 2] |= q << (8 * (k & 3));
+      for (int k = 0; k < 8; ++k)
+        q[k] = (uint32_t)((CODEC == COMPANDED) ? encode_m_companded(e[k], C, tabs) : encode_m_linear(e[k], C));
+      o[0] = pack4_byte0(q[0], q[1], q[2], q[3]);
+      o[1] = pack4_byte0(q[4], q[5], q[6], q[7]);
+    } else {
+      o[0] = o[1] = 0u;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) o[k >> 2] = encode_v_into(e[k], C, k & 3, o[k >> 2]);
     }
-    if (cnt == 8) store8<1, true>(codes + i, o, 8);
-    else store8<1, false>(codes + i, o, cnt);
+    if (cnt == 8) store8<1, true>((gp<uint8_t>)codes + i, o, 8);
+    else if (cnt > 0) store8<1, false>((gp<uint8_t>)codes + i, o, cnt);
   }
 }
 
 template <int KIND, int CODEC>
 __global__ void __launch_bounds__(WG) k_dequantize(const uint8_t* __restrict__ codes, const uint16_t* __restrict__ scales,
-                                                   int64_t n, float* __restrict__ out) {
+                                                   int64_t n, float* __restrict__ out,
+                                                   const CodecTables* __restrict__ gtabs) {
   __shared__ CodecTables tabs;
-  init_tables(tabs, threadIdx.x, blockDim.x);
-  __syncthreads();
+  load_tables(tabs, gtabs);
+  const gp<float> o = (gp<float>)out;
   const int64_t stride = (int64_t)gridDim.x * WG * EPL;
   for (int64_t i = ((int64_t)blockIdx.x * WG + threadIdx.x) * EPL; i < n; i += stride) {
     const int cnt = (int)min((int64_t)8, n - i);
-    DW<2> q = (cnt == 8) ? load8<1, true>(codes + i, 8) : load8<1, false>(codes + i, cnt);
-    const float s = h2f(scales[i >> 5]);
+    const gp<const uint8_t> cp = (gp<const uint8_t>)codes + i;
+    const DW<2> q = (cnt == 8) ? load8<1, true>(cp, 8) : load8<1, false>(cp, cnt);
+    const float s = h2f(((gp<const uint16_t>)scales)[i >> 5]);
     float v[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
       if (KIND == 0) {
-        const int32_t c = s8(q, k);
-        v[k] = (CODEC == COMPANDED) ? s * tabs.lut[c + 127] : (s * K127) * (float)c;
+        const int32_t cq = s8(q, k);
+        v[k] = (CODEC == COMPANDED) ? s * tabs.lut[cq + 127] : (s * K127) * (float)cq;
       } else {
-        const float c = (float)u8(q, k);
-        if (CODEC == COMPANDED) { const float t = (s * K255) * c; v[k] = t * t; }
-        else v[k] = ((s * s) * K255) * c;
+        const float cq = (float)u8(q, k);
+        if (CODEC == COMPANDED) { const float t = (s * K255) * cq; v[k] = t * t; }
+        else v[k] = ((s * s) * K255) * cq;
       }
     }
     if (cnt == 8) {
-      *(float4*)(out + i) = make_float4(v[0], v[1], v[2], v[3]);
-      *(float4*)(out + i + 4) = make_float4(v[4], v[5], v[6], v[7]);
+      *(gp<f32x4>)(o + i) = f32x4{v[0], v[1], v[2], v[3]};
+      *(gp<f32x4>)(o + i + 4) = f32x4{v[4], v[5], v[6], v[7]};
     } else {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) if (k < cnt) out[i + k] = v[k];
+      for (int k = 0; k < 8; ++k) if (k < cnt) o[i + k] = v[k];
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// self-test of the exact fast arithmetic (mismatch counters; not a hot path)
+// ---------------------------------------------------------------------------
+// what 0: rcp_refined vs IEEE 1/b on the f32 patterns [lo, lo+count)
+// what 1: sqrt_corrected vs the IEEE square root
+// what 2: v_cvt_pk_u8_f32 vs clamp(round_half_even(x), 0, 255) (NaN skipped)
+__global__ void __launch_bounds__(WG) k_selftest(int what, uint32_t lo, uint64_t count,
+                                                 unsigned long long* __restrict__ bad) {
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  unsigned long long nb = 0;
+  for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
+    const float x = u2f(lo + (uint32_t)i);
+    bool ok;
+    if (what == 0) ok = f2u(rcp_refined(x)) == f2u(1.0f / x);
+    else if (what == 1) ok = f2u(sqrt_corrected(x)) == f2u(__builtin_sqrtf(x));
+    else {
+      const uint32_t got = __builtin_amdgcn_cvt_pk_u8_f32(x, 0, 0u) & 0xFFu;
+      const uint32_t ref = (uint32_t)__builtin_rintf(fmaxf(fminf(x, 255.0f), 0.0f));
+      ok = (x != x) || got == ref;
+    }
+    nb += ok ? 0 : 1;
+  }
+  if (nb) atomicAdd(bad, nb);
 }
 
 }  // namespace fo

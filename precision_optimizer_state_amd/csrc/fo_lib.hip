@@ -48,7 +48,7 @@ bool fmt_ok(int wfmt, int ecc_bits) {
 // ---------------------------------------------------------------------------
 // device properties and grid sizing
 // ---------------------------------------------------------------------------
-struct DevInfo { int cus = 0; };
+struct DevInfo { int cus = 0; CodecTables* tables = nullptr; };
 std::mutex g_dev_mu;
 std::vector<DevInfo> g_dev;
 
@@ -71,16 +71,33 @@ int device_cus(int dev, int* cus) {
   return FO_OK;
 }
 
-template <typename K>
-int persistent_grid(K kernel, int dev, int64_t total_tiles, int* grid) {
-  int cus = 0;
-  int rc = device_cus(dev, &cus);
-  if (rc) return rc;
-  int occ = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, kernel, WG, 0);
-  if (e != hipSuccess || occ < 1) occ = 1;
+// Codec tables of the device (momentum levels and the momentum-code interval
+// table), built once by k_init_tables on the stream of the first call that
+// needs them; later calls on any stream of the device are ordered after that
+// build by the synchronisation below.
+int device_tables(int dev, hipStream_t stream, const CodecTables** out) {
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  if ((int)g_dev.size() <= dev) g_dev.resize(dev + 1);
+  if (!g_dev[dev].tables) {
+    CodecTables* t = nullptr;
+    hipError_t e = hipMalloc((void**)&t, sizeof(CodecTables));
+    if (e != hipSuccess) return fail(FO_ENOMEM, "hipMalloc(codec tables): %s", hipGetErrorString(e));
+    hipLaunchKernelGGL(k_init_tables, 1, WG, 0, stream, t);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) { (void)hipFree(t); return hip_fail(e, "codec table build"); }
+    g_dev[dev].tables = t;
+  }
+  *out = g_dev[dev].tables;
+  return FO_OK;
+}
+
+// One wave per wave tile: the flat grid measured faster on MI355X than
+// persistent waves for this read/write mix (new workgroups keep the memory
+// pipeline full while finished ones retire).
+int tile_grid(int64_t total_tiles, int* grid) {
   const int64_t want = (total_tiles + WAVES_PER_WG - 1) / WAVES_PER_WG;
-  *grid = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)cus * occ));
+  *grid = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)INT32_MAX));
   return FO_OK;
 }
 
@@ -310,13 +327,14 @@ int fo_companded_quantize(const float* x, int64_t n, int kind, int codec, void* 
   int rc = check_alias(r);
   if (rc) return rc;
   int dev, grid;
-  if ((rc = current_device(&dev)) || (rc = elementwise_grid(dev, n, &grid))) return rc;
-  auto* c = (uint8_t*)codes_out;
   hipStream_t s = as_stream(stream);
-  if (kind == FO_MOMENTUM && codec == FO_COMPANDED) hipLaunchKernelGGL((k_quantize<0, COMPANDED>), grid, WG, 0, s, x, n, c, scales_out);
-  else if (kind == FO_MOMENTUM) hipLaunchKernelGGL((k_quantize<0, LINEAR>), grid, WG, 0, s, x, n, c, scales_out);
-  else if (codec == FO_COMPANDED) hipLaunchKernelGGL((k_quantize<1, COMPANDED>), grid, WG, 0, s, x, n, c, scales_out);
-  else hipLaunchKernelGGL((k_quantize<1, LINEAR>), grid, WG, 0, s, x, n, c, scales_out);
+  const CodecTables* tb = nullptr;
+  if ((rc = current_device(&dev)) || (rc = elementwise_grid(dev, n, &grid)) || (rc = device_tables(dev, s, &tb))) return rc;
+  auto* c = (uint8_t*)codes_out;
+  if (kind == FO_MOMENTUM && codec == FO_COMPANDED) hipLaunchKernelGGL((k_quantize<0, COMPANDED>), grid, WG, 0, s, x, n, c, scales_out, tb);
+  else if (kind == FO_MOMENTUM) hipLaunchKernelGGL((k_quantize<0, LINEAR>), grid, WG, 0, s, x, n, c, scales_out, tb);
+  else if (codec == FO_COMPANDED) hipLaunchKernelGGL((k_quantize<1, COMPANDED>), grid, WG, 0, s, x, n, c, scales_out, tb);
+  else hipLaunchKernelGGL((k_quantize<1, LINEAR>), grid, WG, 0, s, x, n, c, scales_out, tb);
   return launch_check("k_quantize launch");
 }
 
@@ -334,13 +352,14 @@ int fo_dequantize(const void* codes, const uint16_t* scales, int64_t n, int kind
   int rc = check_alias(r);
   if (rc) return rc;
   int dev, grid;
-  if ((rc = current_device(&dev)) || (rc = elementwise_grid(dev, n, &grid))) return rc;
-  auto* c = (const uint8_t*)codes;
   hipStream_t s = as_stream(stream);
-  if (kind == FO_MOMENTUM && codec == FO_COMPANDED) hipLaunchKernelGGL((k_dequantize<0, COMPANDED>), grid, WG, 0, s, c, scales, n, x_out);
-  else if (kind == FO_MOMENTUM) hipLaunchKernelGGL((k_dequantize<0, LINEAR>), grid, WG, 0, s, c, scales, n, x_out);
-  else if (codec == FO_COMPANDED) hipLaunchKernelGGL((k_dequantize<1, COMPANDED>), grid, WG, 0, s, c, scales, n, x_out);
-  else hipLaunchKernelGGL((k_dequantize<1, LINEAR>), grid, WG, 0, s, c, scales, n, x_out);
+  const CodecTables* tb = nullptr;
+  if ((rc = current_device(&dev)) || (rc = elementwise_grid(dev, n, &grid)) || (rc = device_tables(dev, s, &tb))) return rc;
+  auto* c = (const uint8_t*)codes;
+  if (kind == FO_MOMENTUM && codec == FO_COMPANDED) hipLaunchKernelGGL((k_dequantize<0, COMPANDED>), grid, WG, 0, s, c, scales, n, x_out, tb);
+  else if (kind == FO_MOMENTUM) hipLaunchKernelGGL((k_dequantize<0, LINEAR>), grid, WG, 0, s, c, scales, n, x_out, tb);
+  else if (codec == FO_COMPANDED) hipLaunchKernelGGL((k_dequantize<1, COMPANDED>), grid, WG, 0, s, c, scales, n, x_out, tb);
+  else hipLaunchKernelGGL((k_dequantize<1, LINEAR>), grid, WG, 0, s, c, scales, n, x_out, tb);
   return launch_check("k_dequantize launch");
 }
 
@@ -404,11 +423,13 @@ int fo_fused_adamw_step(const fo_adamw_tensor* list, int32_t count, const fo_ada
   c.step_size = (float)(hp->lr / (1.0 - std::pow(hp->beta1, t)));
   c.ibc2 = (float)(1.0 / std::sqrt(1.0 - std::pow(hp->beta2, t)));
   c.eps = (float)hp->eps;
-  void (*kern)(const TensorDesc*, int, int64_t, AdamWConsts) = nullptr;
+  c.fast_rcp = (c.eps >= 0x1p-126f) ? 1 : 0;
+  void (*kern)(const TensorDesc*, int, int64_t, const CodecTables*, AdamWConsts) = nullptr;
   FO_SELECT3(k_fused_adamw, hp->wfmt, hp->ecc_bits, hp->codec, kern);
   int dev, grid;
-  if ((rc = current_device(&dev)) || (rc = persistent_grid(kern, dev, e->total_tiles, &grid))) return rc;
-  hipLaunchKernelGGL(kern, grid, WG, 0, s, (const TensorDesc*)e->dptr, e->count, e->total_tiles, c);
+  const CodecTables* tb = nullptr;
+  if ((rc = current_device(&dev)) || (rc = tile_grid(e->total_tiles, &grid)) || (rc = device_tables(dev, s, &tb))) return rc;
+  hipLaunchKernelGGL(kern, grid, WG, 0, s, (const TensorDesc*)e->dptr, e->count, e->total_tiles, tb, c);
   rc = launch_check("k_fused_adamw launch");
   if (rc) return rc;
   return record_use(e, s);
@@ -428,8 +449,8 @@ int fo_stream_probe(const fo_adamw_tensor* list, int32_t count, int32_t wfmt, in
   if (rc) return rc;
   if (e->total_tiles == 0) return FO_OK;
   void (*kern)(const TensorDesc*, int, int64_t, uint32_t) = (ecc_bits == 8) ? k_stream_probe<8> : k_stream_probe<16>;
-  int dev, grid;
-  if ((rc = current_device(&dev)) || (rc = persistent_grid(kern, dev, e->total_tiles, &grid))) return rc;
+  int grid;
+  if ((rc = tile_grid(e->total_tiles, &grid))) return rc;
   hipLaunchKernelGGL(kern, grid, WG, 0, s, (const TensorDesc*)e->dptr, e->count, e->total_tiles, key);
   rc = launch_check("k_stream_probe launch");
   if (rc) return rc;
@@ -484,14 +505,38 @@ int fo_fused_sgdm_step(const fo_sgdm_tensor* list, int32_t count, const fo_sgdm_
   c.lr = (float)hp->lr;
   c.mu = (float)hp->momentum;
   c.wd = (float)hp->weight_decay;
-  void (*kern)(const TensorDesc*, int, int64_t, SGDMConsts) = nullptr;
+  void (*kern)(const TensorDesc*, int, int64_t, const CodecTables*, SGDMConsts) = nullptr;
   FO_SELECT3(k_fused_sgdm, hp->wfmt, hp->ecc_bits, hp->codec, kern);
   int grid;
-  if ((rc = persistent_grid(kern, dev, e->total_tiles, &grid))) return rc;
-  hipLaunchKernelGGL(kern, grid, WG, 0, s, (const TensorDesc*)e->dptr, e->count, e->total_tiles, c);
+  const CodecTables* tb = nullptr;
+  if ((rc = tile_grid(e->total_tiles, &grid)) || (rc = device_tables(dev, s, &tb))) return rc;
+  hipLaunchKernelGGL(kern, grid, WG, 0, s, (const TensorDesc*)e->dptr, e->count, e->total_tiles, tb, c);
   rc = launch_check("k_fused_sgdm launch");
   if (rc) return rc;
   return record_use(e, s);
+}
+
+int fo_selftest(int what, uint32_t lo, uint64_t count, uint64_t* mismatches, void* stream) {
+  g_err.clear();
+  if (what < 0 || what > 2) return fail(FO_EINVAL, "bad self-test %d", what);
+  if (!mismatches) return fail(FO_EINVAL, "mismatches is NULL");
+  if (count > (1ull << 32) - lo) return fail(FO_EINVAL, "range exceeds the f32 patterns");
+  hipStream_t s = as_stream(stream);
+  unsigned long long* d = nullptr;
+  hipError_t e = hipMalloc((void**)&d, sizeof(*d));
+  if (e != hipSuccess) return fail(FO_ENOMEM, "hipMalloc: %s", hipGetErrorString(e));
+  unsigned long long h = 0;
+  e = hipMemcpyAsync(d, &h, sizeof(h), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(k_selftest, 4096, WG, 0, s, what, lo, count, d);
+    e = hipGetLastError();
+  }
+  if (e == hipSuccess) e = hipMemcpyAsync(&h, d, sizeof(h), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  (void)hipFree(d);
+  if (e != hipSuccess) return hip_fail(e, "self-test");
+  *mismatches = h;
+  return FO_OK;
 }
 
 }  // extern "C"
