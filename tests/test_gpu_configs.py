@@ -1,0 +1,129 @@
+"""Full-size parity of every workload configuration, in the launch
+configuration bench.py times (one fused call over the whole parameter list;
+19 chunked calls per step in gradient-release mode).
+
+The oracle cannot run 8 billion elements, but 32-element blocks are
+independent: for a seeded sample of blocks of every tensor (always including
+the tensor's last, possibly partial, block) the test copies the f32 weights
+and each step's 16-bit gradients back from the device generators, runs the
+oracle on those blocks alone, and compares the final state of the same blocks
+element by element.  No value produced by the HIP path enters the oracle.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from oracle.optim import fresh_adamw_state, fresh_sgdm_state
+from precision_optimizer_state_amd import binding as B
+from precision_optimizer_state_amd.state import alloc_adamw_state, alloc_sgdm_state
+from tests.gpu_helpers import check_adamw_state, check_sgdm_state, to_host
+from workloads import config, device_grads, device_weights
+from workloads.configs import RELEASE_CHUNKS
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_blocks(n, k, rng):
+    nb = -(-n // 32)
+    pick = rng.choice(nb, size=min(nb, k), replace=False)
+    pick = np.unique(np.concatenate([pick, [nb - 1]]))
+    idx = (pick[:, None] * 32 + np.arange(32)[None, :]).ravel()
+    return pick, idx[idx < n]
+
+
+def _gather(t, idx_dev):
+    return to_host(t[idx_dev])
+
+
+def _run(cfg_name, steps, blocks_per_tensor, release=False):
+    cfg = config(cfg_name)
+    rng = np.random.default_rng(7)
+    adam = cfg.optimizer == "adamw"
+    states, samples, refs = [], [], []
+    print(f"{cfg_name}: {len(cfg.numels)} tensors, {cfg.params} params, {steps} steps", flush=True)
+    for i, n in enumerate(cfg.numels):
+        st = (alloc_adamw_state if adam else alloc_sgdm_state)(n, cfg.wfmt, cfg.ecc_bits)
+        w = device_weights(cfg.name, i, n)
+        blocks, idx = _sample_blocks(n, blocks_per_tensor, rng)
+        idx_dev = torch.from_numpy(idx).cuda()
+        x0 = w[idx_dev].cpu().numpy()
+        B.fo_split_weights(w, st["w16"], st["ecc"], cfg.wfmt, cfg.ecc_bits)
+        del w
+        states.append(st)
+        samples.append((torch.from_numpy(blocks).cuda(), idx_dev))
+        refs.append((fresh_adamw_state if adam else fresh_sgdm_state)(x0, cfg.wfmt, cfg.ecc_bits))
+    if adam and release:
+        st = states[0]
+        lists, lo = [], 0
+        for m in RELEASE_CHUNKS:
+            hi = lo + m
+            c = {k: st[k][lo:hi] for k in ("w16", "ecc", "grad", "m_q", "v_q")}
+            c["m_s"] = st["m_s"][lo // 32: -(-hi // 32)]
+            c["v_s"] = st["v_s"][lo // 32: -(-hi // 32)]
+            lists.append(B.AdamWList([c]))
+            lo = hi
+    else:
+        lists = [B.AdamWList(states) if adam else B.SGDMList(states)]
+    for step in range(1, steps + 1):
+        gsamp = []
+        for i, (st, n) in enumerate(zip(states, cfg.numels)):
+            device_grads(cfg.name, i, step, n, cfg.grad_kind, cfg.wfmt, out=st["grad"])
+            gsamp.append(_gather(st["grad"], samples[i][1]))
+        for tl in lists:
+            if adam:
+                B.fo_fused_adamw_step(tl, B.adamw_hparams(step=step, wfmt=cfg.wfmt, ecc_bits=cfg.ecc_bits,
+                                                          codec=cfg.codec, **cfg.hp))
+            else:
+                B.fo_fused_sgdm_step(tl, B.sgdm_hparams(step=step, wfmt=cfg.wfmt, ecc_bits=cfg.ecc_bits,
+                                                        codec=cfg.codec, **cfg.hp))
+        for i in range(len(states)):
+            if adam:
+                refs[i] = O.adamw_step(refs[i], gsamp[i], dict(cfg.hp, step=step), cfg.wfmt, cfg.ecc_bits, cfg.codec)
+            else:
+                refs[i] = O.sgdm_step(refs[i], gsamp[i], cfg.hp, cfg.wfmt, cfg.ecc_bits, cfg.codec)
+    torch.cuda.synchronize()
+    total, bad = 0, 0
+    for i, st in enumerate(states):
+        bdev, idev = samples[i]
+        if adam:
+            got = {"w16": _gather(st["w16"], idev), "ecc": _gather(st["ecc"], idev),
+                   "m_q": _gather(st["m_q"], idev), "v_q": _gather(st["v_q"], idev),
+                   "m_s": _gather(st["m_s"], bdev), "v_s": _gather(st["v_s"], bdev)}
+            b = check_adamw_state(f"{cfg_name} tensor {i}", got, refs[i], cfg.wfmt, cfg.ecc_bits)
+        else:
+            got = {"w16": _gather(st["w16"], idev), "ecc": _gather(st["ecc"], idev),
+                   "b_q": _gather(st["b_q"], idev), "b_s": _gather(st["b_s"], bdev)}
+            b = check_sgdm_state(f"{cfg_name} tensor {i}", got, refs[i], cfg.wfmt, cfg.ecc_bits)
+        bad += sum(b.values())
+        total += idev.numel()
+    print(f"{cfg_name}{' release' if release else ''}: {total} sampled elements after {steps} steps, "
+          f"{bad} mismatches", flush=True)
+    del states, lists
+    torch.cuda.empty_cache()
+
+
+def test_config_c1_flat_1m_full():
+    _run("c1_flat1m", 10, 1 << 15)          # every block of the 1M tensor
+
+
+def test_config_c2_gpt2_small_full():
+    _run("c2_gpt2", 20, 96)
+
+
+def test_config_c3_llama31_8b_full():
+    _run("c3_llama8b", 3, 64)
+
+
+def test_config_c4_resnet50_sgdm_full():
+    _run("c4_resnet50", 20, 128)
+
+
+@pytest.mark.parametrize("name", ["c5_flat1g_bf16e8", "c5_flat1g_fp16e8", "c5_flat1g_bf16e16", "c5_flat1g_linear"])
+def test_config_c5_flat_2_30_variants(name):
+    _run(name, 2, 20000)
+
+
+def test_config_c5_gradient_release_chunks():
+    _run("c5_flat1g_bf16e8", 2, 20000, release=True)
