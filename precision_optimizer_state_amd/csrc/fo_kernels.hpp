@@ -54,8 +54,12 @@ struct SGDMConsts { float lr, mu, wd; };
 template <typename T> using gp = FO_GLOBAL T*;
 
 // ---------------------------------------------------------------------------
-// masked vector access for the last (partial) tile of a tensor
+// vector access (masked for the last, partial tile of a tensor)
 // ---------------------------------------------------------------------------
+// Every stream is touched once per step, so full-group loads and stores (and
+// the block-scale accesses of the fused steps) carry the nontemporal hint.
+// Measured on MI355X (Llama-8B list): 19.1 -> 17.8 ms; the hint on loads only
+// or on stores only changes nothing.
 template <int NDW>
 struct DW { uint32_t w[NDW]; };
 
@@ -65,10 +69,10 @@ __device__ __forceinline__ DW<2 * ESZ> load8(gp<const uint8_t> base, int cnt) {
   DW<2 * ESZ> r;
   if (FULL || cnt >= 8) {
     if constexpr (ESZ == 2) {
-      const u32x4 v = *(gp<const u32x4>)base;
+      const u32x4 v = __builtin_nontemporal_load((gp<const u32x4>)base);
       r.w[0] = v.x; r.w[1] = v.y; r.w[2] = v.z; r.w[3] = v.w;
     } else {
-      const u32x2 v = *(gp<const u32x2>)base;
+      const u32x2 v = __builtin_nontemporal_load((gp<const u32x2>)base);
       r.w[0] = v.x; r.w[1] = v.y;
     }
     return r;
@@ -90,8 +94,8 @@ __device__ __forceinline__ DW<2 * ESZ> load8(gp<const uint8_t> base, int cnt) {
 template <int ESZ, bool FULL>
 __device__ __forceinline__ void store8(gp<uint8_t> base, const uint32_t* w, int cnt) {
   if (FULL || cnt >= 8) {
-    if constexpr (ESZ == 2) *(gp<u32x4>)base = u32x4{w[0], w[1], w[2], w[3]};
-    else *(gp<u32x2>)base = u32x2{w[0], w[1]};
+    if constexpr (ESZ == 2) __builtin_nontemporal_store(u32x4{w[0], w[1], w[2], w[3]}, (gp<u32x4>)base);
+    else __builtin_nontemporal_store(u32x2{w[0], w[1]}, (gp<u32x2>)base);
     return;
   }
 #pragma unroll
@@ -194,8 +198,8 @@ __device__ __forceinline__ void adamw_tile(const TensorDesc& d, int64_t e0, int 
     MQ[j] = load8<1, FULL>(mq + off, cnt[j]);
     VQ[j] = load8<1, FULL>(vq + off, cnt[j]);
   }
-  const uint32_t sm_old = own_ok ? (uint32_t)ms[own] : 0u;
-  const uint32_t sv_old = own_ok ? (uint32_t)vs[own] : 0u;
+  const uint32_t sm_old = own_ok ? (uint32_t)__builtin_nontemporal_load(ms + own) : 0u;
+  const uint32_t sv_old = own_ok ? (uint32_t)__builtin_nontemporal_load(vs + own) : 0u;
 
   // ---- per-block decode constants (owned block) -------------------------
   const float smf = h2f(sm_old), svf = h2f(sv_old);
@@ -254,7 +258,10 @@ __device__ __forceinline__ void adamw_tile(const TensorDesc& d, int64_t e0, int 
   // ---- new block scales and encode constants (owned block) ---------------
   const uint32_t smb = ru_fp16(own_mmax);
   const uint32_t svb = ru_fp16((CODEC == COMPANDED) ? own_xmax : __builtin_sqrtf(own_xmax));
-  if (own_ok) { ms[own] = (uint16_t)smb; vs[own] = (uint16_t)svb; }
+  if (own_ok) {
+    __builtin_nontemporal_store((uint16_t)smb, ms + own);
+    __builtin_nontemporal_store((uint16_t)svb, vs + own);
+  }
   const float sm = h2f(smb), sv = h2f(svb);
   float cm_own, cv_own;
   if constexpr (CODEC == COMPANDED) {
@@ -314,7 +321,7 @@ __device__ __forceinline__ void sgdm_tile(const TensorDesc& d, int64_t e0, int l
     E[j] = load8<EB, FULL>(ecc + off * EB, cnt[j]);
     BQ[j] = load8<1, FULL>(bq + off, cnt[j]);
   }
-  const uint32_t sb_old = own_ok ? (uint32_t)bs[own] : 0u;
+  const uint32_t sb_old = own_ok ? (uint32_t)__builtin_nontemporal_load(bs + own) : 0u;
   const float sbf = h2f(sb_old);
   const float db_own = (CODEC == COMPANDED) ? sbf : sbf * K127;
 
@@ -346,7 +353,7 @@ __device__ __forceinline__ void sgdm_tile(const TensorDesc& d, int64_t e0, int l
     own_bmax = (p == j) ? bmax : own_bmax;
   }
   const uint32_t sbb = ru_fp16(own_bmax);
-  if (own_ok) bs[own] = (uint16_t)sbb;
+  if (own_ok) __builtin_nontemporal_store((uint16_t)sbb, bs + own);
   const float sb = h2f(sbb);
   const float cb_own = (sb > 0.0f) ? ((CODEC == COMPANDED) ? 1.0f : 127.0f) / sb : 0.0f;
 #pragma unroll
