@@ -21,3 +21,4 @@ from .binding import (  # noqa: F401
     fo_stream_probe,
 )
 from .state import AdamWState, SGDMState, alloc_adamw_state, alloc_sgdm_state  # noqa: F401
+from .optim import FlashAdamW, FlashSGD  # noqa: F401

@@ -1,0 +1,208 @@
+"""Drop-in torch.optim optimizers over split weights and 8-bit states.
+
+FlashOptim's optimizers are drop-in replacements for torch.optim that compute
+the same updates with less memory ([BLOG] "FlashOptim: Breaking the Memory
+Wall ...", Conclusion & Perspective; Davis Blalock's FlashOptim thread, the
+launch post).  Here the model parameter itself becomes the 16-bit theta' (the
+thread's post on avoiding the redundant f32 + low-precision copies); the
+optimizer keeps the ECC and the 8-bit states.  Gradients therefore arrive in
+16 bits (the post on keeping gradients in backward precision).  Optional
+gradient release steps each parameter as soon as its gradient is
+accumulated and frees the gradient (the post on gradient release).
+
+All arithmetic runs in the HIP library (fo_fused_adamw_step /
+fo_fused_sgdm_step); this module only groups tensors and keeps step counts.
+"""
+
+from __future__ import annotations
+
+from typing import Iterable
+
+import torch
+
+from . import binding as B
+
+_W16 = {"bf16": torch.bfloat16, "fp16": torch.float16}
+_ECC = {8: torch.int8, 16: torch.int16}
+
+
+def _nb(n: int) -> int:
+    return (n + 31) // 32
+
+
+class _FlashBase(torch.optim.Optimizer):
+    _state_keys: tuple = ()
+
+    def __init__(self, params, defaults, wfmt, ecc_bits, codec, grad_release):
+        if (wfmt, ecc_bits) not in (("bf16", 8), ("bf16", 16), ("fp16", 8)):
+            raise ValueError(f"unsupported weight format {wfmt}+ECC{ecc_bits}")
+        if codec not in ("companded", "linear"):
+            raise ValueError(f"unknown codec {codec}")
+        self.wfmt, self.ecc_bits, self.codec = wfmt, ecc_bits, codec
+        self.grad_release = grad_release
+        self._hooks = []
+        super().__init__(params, defaults)
+        for group in self.param_groups:
+            for p in group["params"]:
+                self._adopt(p)
+                if grad_release:
+                    self._hooks.append(p.register_post_accumulate_grad_hook(self._release_hook))
+
+    # -- conversion of a parameter into theta' + ECC ------------------------
+    def _adopt(self, p: torch.nn.Parameter) -> None:
+        if not p.is_cuda:
+            raise ValueError("parameters must live on the GPU")
+        st = self.state[p]
+        if "ecc" in st:
+            return
+        n = p.numel()
+        w16 = torch.empty(p.shape, dtype=_W16[self.wfmt], device=p.device)
+        ecc = torch.empty(p.shape, dtype=_ECC[self.ecc_bits], device=p.device)
+        master = p.detach().to(torch.float32).contiguous()
+        B.fo_split_weights(master.view(-1), w16.view(-1), ecc.view(-1), self.wfmt, self.ecc_bits)
+        p.data = w16
+        st["step"] = 0
+        st["ecc"] = ecc
+        for key, dt, per_block in self._state_keys:
+            st[key] = torch.zeros(_nb(n) if per_block else n, dtype=dt, device=p.device)
+
+    # -- master weights -------------------------------------------------------
+    @torch.no_grad()
+    def master_weights(self, p: torch.nn.Parameter) -> torch.Tensor:
+        """The reconstructed f32 master weight of `p` (theta' + ECC)."""
+        out = torch.empty(p.shape, dtype=torch.float32, device=p.device)
+        B.fo_reconstruct_weights(p.detach().view(-1), self.state[p]["ecc"].view(-1), out.view(-1),
+                                 self.wfmt, self.ecc_bits)
+        return out
+
+    @torch.no_grad()
+    def load_master_weights(self, p: torch.nn.Parameter, w32: torch.Tensor) -> None:
+        """Re-split an f32 master weight into `p` (theta') and its ECC."""
+        w32 = w32.to(device=p.device, dtype=torch.float32).contiguous().view(-1)
+        B.fo_split_weights(w32, p.data.view(-1), self.state[p]["ecc"].view(-1), self.wfmt, self.ecc_bits)
+
+    # -- stepping ---------------------------------------------------------------
+    def _entry(self, p):
+        raise NotImplementedError
+
+    def _launch(self, entries, group, step):
+        raise NotImplementedError
+
+    def _step_params(self, group, params):
+        # parameters of one group that share a step count go into one launch
+        by_step = {}
+        for p in params:
+            st = self.state[p]
+            st["step"] += 1
+            by_step.setdefault(st["step"], []).append(p)
+        for step, ps in by_step.items():
+            # a fresh marshalled list per call holds no reference to the
+            # gradients afterwards (the library caches device tables itself)
+            self._launch(self._make_list([self._entry(p) for p in ps]), group, step)
+
+    @torch.no_grad()
+    def step(self, closure=None):
+        loss = None
+        if closure is not None:
+            with torch.enable_grad():
+                loss = closure()
+        for group in self.param_groups:
+            ps = [p for p in group["params"] if p.grad is not None]
+            for p in ps:
+                if p.grad.dtype != p.dtype or not p.grad.is_contiguous():
+                    p.grad = p.grad.to(p.dtype).contiguous()
+            if ps:
+                self._step_params(group, ps)
+        return loss
+
+    @torch.no_grad()
+    def _release_hook(self, p):
+        group = next(g for g in self.param_groups if any(q is p for q in g["params"]))
+        if p.grad.dtype != p.dtype or not p.grad.is_contiguous():
+            p.grad = p.grad.to(p.dtype).contiguous()
+        self._step_params(group, [p])
+        p.grad = None          # freed in stream order by torch's caching allocator
+
+    def load_state_dict(self, state_dict):
+        """torch's loader casts every tensor of a floating-point parameter's
+        state to the parameter dtype; the ECC, codes and scale patterns are raw
+        integers, so they are re-installed unchanged after the base loader."""
+        saved_ids = [i for g in state_dict["param_groups"] for i in g["params"]]
+        raw = {k: {kk: vv for kk, vv in v.items() if torch.is_tensor(vv)}
+               for k, v in state_dict["state"].items()}
+        super().load_state_dict(state_dict)
+        params = [p for g in self.param_groups for p in g["params"]]
+        for pid, p in zip(saved_ids, params):
+            for key, val in raw.get(pid, {}).items():
+                self.state[p][key] = val.to(device=p.device).clone()
+            if "step" in self.state[p]:
+                self.state[p]["step"] = int(self.state[p]["step"])
+
+    def remove_hooks(self):
+        for h in self._hooks:
+            h.remove()
+        self._hooks = []
+
+
+class FlashAdamW(_FlashBase):
+    """AdamW (decoupled weight decay, bias correction) with bf16/fp16 theta' +
+    8/16-bit ECC master weights and companded 8-bit m, v."""
+
+    # scales are kept as int16 bit patterns of fp16 values: torch's
+    # load_state_dict would cast floating-point state to the parameter dtype
+    _state_keys = (("m_q", torch.int8, False), ("m_s", torch.int16, True),
+                   ("v_q", torch.uint8, False), ("v_s", torch.int16, True))
+
+    def __init__(self, params: Iterable, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=1e-2, *,
+                 wfmt="bf16", ecc_bits=8, codec="companded", grad_release=False):
+        defaults = dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay)
+        super().__init__(params, defaults, wfmt, ecc_bits, codec, grad_release)
+
+    def _entry(self, p):
+        st = self.state[p]
+        return {"w16": p.data.view(-1), "ecc": st["ecc"].view(-1), "grad": p.grad.view(-1),
+                "m_q": st["m_q"], "m_s": st["m_s"], "v_q": st["v_q"], "v_s": st["v_s"]}
+
+    @staticmethod
+    def _make_list(entries):
+        return B.AdamWList(entries)
+
+    def _launch(self, tl, group, step):
+        b1, b2 = group["betas"]
+        B.fo_fused_adamw_step(tl, B.adamw_hparams(group["lr"], b1, b2, group["eps"], group["weight_decay"], step,
+                                                  self.wfmt, self.ecc_bits, self.codec))
+
+    @torch.no_grad()
+    def export_torch_state(self, p):
+        """f32 (exp_avg, exp_avg_sq) of `p`, decoded from the 8-bit states."""
+        st = self.state[p]
+        m = torch.empty(p.numel(), dtype=torch.float32, device=p.device)
+        v = torch.empty_like(m)
+        B.fo_dequantize(st["m_q"], st["m_s"], m, "m", self.codec)
+        B.fo_dequantize(st["v_q"], st["v_s"], v, "v", self.codec)   # scale patterns read as fp16 bits
+        return m.view(p.shape), v.view(p.shape)
+
+
+class FlashSGD(_FlashBase):
+    """SGD with momentum (coupled weight decay, dampening 0, no Nesterov) with
+    split master weights and a companded 8-bit momentum buffer."""
+
+    _state_keys = (("b_q", torch.int8, False), ("b_s", torch.int16, True))
+
+    def __init__(self, params: Iterable, lr=1e-2, momentum=0.9, weight_decay=0.0, *,
+                 wfmt="bf16", ecc_bits=8, codec="companded", grad_release=False):
+        defaults = dict(lr=lr, momentum=momentum, weight_decay=weight_decay)
+        super().__init__(params, defaults, wfmt, ecc_bits, codec, grad_release)
+
+    def _entry(self, p):
+        st = self.state[p]
+        return {"w16": p.data.view(-1), "ecc": st["ecc"].view(-1), "grad": p.grad.view(-1),
+                "b_q": st["b_q"], "b_s": st["b_s"]}
+
+    @staticmethod
+    def _make_list(entries):
+        return B.SGDMList(entries)
+
+    def _launch(self, tl, group, step):
+        B.fo_fused_sgdm_step(tl, B.sgdm_hparams(group["lr"], group["momentum"], group["weight_decay"], step,
+                                                self.wfmt, self.ecc_bits, self.codec))

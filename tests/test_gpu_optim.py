@@ -1,0 +1,151 @@
+"""The drop-in optimizers (FlashAdamW, FlashSGD) on a small model: every step
+matches the oracle bit for bit, gradient release matches the plain step,
+state_dict save/load resumes bit for bit, and training tracks
+torch.optim.AdamW in float32."""
+
+import copy
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from oracle.optim import fresh_adamw_state, fresh_sgdm_state
+from precision_optimizer_state_amd import FlashAdamW, FlashSGD
+from tests.gpu_helpers import check_adamw_state, check_sgdm_state, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _model(seed=0):
+    torch.manual_seed(seed)
+    m = torch.nn.Sequential(torch.nn.Linear(64, 96), torch.nn.GELU(), torch.nn.Linear(96, 33))
+    return m.cuda()
+
+
+def _batch(i, dtype=torch.bfloat16):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1000 + i)
+    x = torch.randn(128, 64, generator=g, device="cuda").to(dtype)
+    y = torch.randn(128, 33, generator=g, device="cuda").to(dtype)
+    return x, y
+
+
+def _loss(model, i):
+    x, y = _batch(i)
+    return torch.nn.functional.mse_loss(model(x).float(), y.float())
+
+
+HP = dict(lr=3e-3, betas=(0.9, 0.95), eps=1e-8, weight_decay=0.1)
+
+
+def test_flash_adamw_matches_oracle_every_step():
+    model = _model()
+    x0 = [p.detach().float().cpu().numpy().ravel().copy() for p in model.parameters()]
+    opt = FlashAdamW(model.parameters(), **HP)
+    refs = [fresh_adamw_state(x) for x in x0]
+    for step in range(1, 6):
+        opt.zero_grad(set_to_none=True)
+        _loss(model, step).backward()
+        grads = [to_host(p.grad.view(-1)) for p in model.parameters()]
+        opt.step()
+        hp = dict(lr=HP["lr"], beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=step)
+        for i, p in enumerate(model.parameters()):
+            refs[i] = O.adamw_step(refs[i], grads[i], hp)
+            st = opt.state[p]
+            got = {"w16": to_host(p.data.view(-1)), "ecc": to_host(st["ecc"].view(-1)),
+                   "m_q": to_host(st["m_q"]), "v_q": to_host(st["v_q"]),
+                   "m_s": to_host(st["m_s"]).view(np.uint16), "v_s": to_host(st["v_s"]).view(np.uint16)}
+            bad = check_adamw_state(f"FlashAdamW step {step} param {i}", got, refs[i])
+            assert sum(bad.values()) == 0
+    # master weights are the oracle's reconstruction
+    for i, p in enumerate(model.parameters()):
+        mw = opt.master_weights(p).view(-1).cpu().numpy()
+        assert np.array_equal(mw.view(np.uint32), O.reconstruct_weights(refs[i]["w16"], refs[i]["ecc"]).view(np.uint32))
+
+
+def test_flash_sgd_matches_oracle_every_step():
+    model = _model(1)
+    x0 = [p.detach().float().cpu().numpy().ravel().copy() for p in model.parameters()]
+    opt = FlashSGD(model.parameters(), lr=0.05, momentum=0.9, weight_decay=1e-4)
+    refs = [fresh_sgdm_state(x) for x in x0]
+    for step in range(1, 6):
+        opt.zero_grad(set_to_none=True)
+        _loss(model, step).backward()
+        grads = [to_host(p.grad.view(-1)) for p in model.parameters()]
+        opt.step()
+        for i, p in enumerate(model.parameters()):
+            refs[i] = O.sgdm_step(refs[i], grads[i], dict(lr=0.05, momentum=0.9, weight_decay=1e-4))
+            st = opt.state[p]
+            got = {"w16": to_host(p.data.view(-1)), "ecc": to_host(st["ecc"].view(-1)),
+                   "b_q": to_host(st["b_q"]), "b_s": to_host(st["b_s"]).view(np.uint16)}
+            assert sum(check_sgdm_state(f"FlashSGD step {step} param {i}", got, refs[i]).values()) == 0
+
+
+def _train(model, opt, steps, start=1):
+    for step in range(start, start + steps):
+        opt.zero_grad(set_to_none=True)
+        _loss(model, step).backward()
+        opt.step()
+
+
+def _snapshot(model, opt):
+    out = [p.detach().clone() for p in model.parameters()]
+    for p in model.parameters():
+        out += [v.clone() for k, v in opt.state[p].items() if torch.is_tensor(v)]
+    return out
+
+
+def test_gradient_release_equals_plain_step():
+    a, b = _model(2), _model(2)
+    oa = FlashAdamW(a.parameters(), **HP)
+    ob = FlashAdamW(b.parameters(), **HP, grad_release=True)
+    _train(a, oa, 4)
+    _train(b, ob, 4)
+    for p in b.parameters():
+        assert p.grad is None                 # released
+    for x, y in zip(_snapshot(a, oa), _snapshot(b, ob)):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+
+
+def test_state_dict_resume_is_bitwise():
+    a = _model(3)
+    oa = FlashAdamW(a.parameters(), **HP)
+    _train(a, oa, 4)
+    ref = _snapshot(a, oa)
+
+    b = _model(3)
+    ob = FlashAdamW(b.parameters(), **HP)
+    _train(b, ob, 2)
+    msd, osd = copy.deepcopy(b.state_dict()), copy.deepcopy(ob.state_dict())
+    c = _model(99)                            # different init, then restored
+    oc = FlashAdamW(c.parameters(), **HP)
+    c.load_state_dict(msd)
+    oc.load_state_dict(osd)
+    _train(c, oc, 2, start=3)
+    for x, y in zip(ref, _snapshot(c, oc)):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+
+
+def test_training_tracks_fp32_adamw():
+    torch.manual_seed(5)
+    w_true = torch.randn(64, 33, device="cuda") / 8
+    ref = torch.nn.Linear(64, 33, bias=False).cuda()
+    fl = copy.deepcopy(ref)
+    o_ref = torch.optim.AdamW(ref.parameters(), lr=1e-2, weight_decay=0.0)
+    o_fl = FlashAdamW(fl.parameters(), lr=1e-2, weight_decay=0.0)
+    for i in range(200):
+        x, _ = _batch(i, torch.float32)
+        y = x @ w_true
+        for m, o, dt in ((ref, o_ref, torch.float32), (fl, o_fl, torch.bfloat16)):
+            o.zero_grad(set_to_none=True)
+            loss = torch.nn.functional.mse_loss(m(x.to(dt)).float(), y)
+            loss.backward()
+            o.step()
+    # compare the optimizers, not the bf16 forward pass: evaluate both in f32,
+    # FlashAdamW through its reconstructed master weights
+    w_fl = o_fl.master_weights(fl.weight)
+    err_ref = (ref.weight.detach().T - w_true).norm() / w_true.norm()
+    err_fl = (w_fl.T - w_true).norm() / w_true.norm()
+    print(f"relative weight error after 200 steps: fp32 AdamW {err_ref:.3e}, FlashAdamW {err_fl:.3e}", flush=True)
+    assert err_fl < 2e-2 and err_ref < 2e-2
