@@ -138,7 +138,7 @@ def _oracle_task(args):
     else:
         st = fresh_sgdm_state(x, cfg.wfmt, cfg.ecc_bits)
         t0 = time.perf_counter()
-        O.sgdm_step(st, gb, cfg.hp, cfg.wfmt, cfg.ecc_bits, cfg.codec)
+        O.sgdm_step(st, gb, dict(cfg.hp, step=2), cfg.wfmt, cfg.ecc_bits, cfg.codec)
     return m, time.perf_counter() - t0
 
 

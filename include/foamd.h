@@ -141,12 +141,15 @@ typedef struct fo_adamw_hparams {
   int32_t wfmt;      /* fo_wfmt */
   int32_t ecc_bits;  /* 8 or 16 */
   int32_t codec;     /* fo_codec */
+  int32_t l2_decay;  /* 0: AdamW (decoupled decay, theta *= 1 - lr*wd);
+                        1: Adam (wd*theta added to the gradient, no decoupled decay) */
 } fo_adamw_hparams;
 
 /*
  * fo_fused_adamw_step -- [UPDATE] with [SPLIT] and [STATE]
  * One AdamW step (decoupled weight decay, bias correction, step >= 1) over a
- * list of `count` tensors in one launch.  Per element: widen the gradient,
+ * list of `count` tensors in one launch; with hp->l2_decay = 1 the step is
+ * Adam with the weight decay added to the gradient (torch.optim.Adam).  Per element: widen the gradient,
  * reconstruct the f32 master, decode m and v, update in float32 with a fixed
  * operation order, split the new master into theta' + ECC, recompute the
  * block scales of the new m and v and re-encode them.  Blocks never cross
@@ -170,18 +173,22 @@ typedef struct fo_sgdm_tensor {
 } fo_sgdm_tensor;
 
 typedef struct fo_sgdm_hparams {
-  double  lr, momentum, weight_decay;
-  int64_t step;      /* informational (no bias correction); must be >= 1 */
+  double  lr, momentum, weight_decay, dampening;
+  int64_t step;      /* 1-based; at step 1 the buffer is set to the decayed gradient */
   int32_t wfmt;
   int32_t ecc_bits;
   int32_t codec;
+  int32_t nesterov;  /* 1: Nesterov momentum (needs momentum > 0, dampening 0) */
 } fo_sgdm_hparams;
 
 /*
  * fo_fused_sgdm_step -- [UPDATE] with [SPLIT] and [STATE]
- * One SGD-with-momentum step (coupled L2 weight decay, dampening 0, no
- * Nesterov) over a list of tensors; the momentum buffer uses the momentum
- * codec.  Same layout, ownership and error rules as fo_fused_adamw_step.
+ * One SGD-with-momentum step over a list of tensors, as torch.optim.SGD:
+ * d = g + wd*theta; buffer = d at step 1, else momentum*buffer + (1-dampening)*d;
+ * theta -= lr * (Nesterov ? d + momentum*buffer : buffer).  The momentum
+ * buffer uses the momentum codec.  Same layout, ownership and error rules as
+ * fo_fused_adamw_step (FO_EINVAL also for dampening outside [0,1] and for
+ * Nesterov without momentum or with dampening).
  */
 int fo_fused_sgdm_step(const fo_sgdm_tensor* list, int32_t count,
                        const fo_sgdm_hparams* hp, void* stream);

@@ -29,10 +29,14 @@ U3  Per-element float32 operation order, every operation rounded once (no
         theta = theta - step_size*(m*r)
     The quotient m/d is formed as m times the correctly rounded reciprocal of
     d (one rounding more than a division; the same textbook update).
-U4  SGD-M = torch.optim.SGD defaults: coupled L2 weight decay, dampening 0,
-    no Nesterov:  d = g + wd*theta;  b = mu*b + d;  theta = theta - lr*b.
-    With a zero-initialised buffer the first step gives b = d, as torch does.
+U4  SGD-M = torch.optim.SGD: coupled L2 weight decay, optional dampening and
+    Nesterov:  d = g + wd*theta;  b = d at step 1, else b = mu*b + (1-damp)*d;
+    u = d + mu*b (Nesterov) or u = b;  theta = theta - lr*u.  With dampening 0
+    (1 - damp = 1 exactly) the buffer update is mu*b + d.
 U5  The momentum buffer of SGD-M uses the momentum codec.
+U6  Adam with coupled L2 weight decay (torch.optim.Adam): g = g + wd*theta
+    (theta = the reconstructed master) before the moments; no decoupled
+    decay (decay = 1); otherwise as U3.
 
 Parity status: pinned (unquantised update against torch.optim.AdamW / SGD in
 float64 and a float64 textbook loop; bf16+16 ECC reproduces a plain float32
@@ -68,6 +72,8 @@ class AdamWScalars:
     step_size: np.float32
     ibc2: np.float32
     eps: np.float32
+    wd: np.float32 = F32(0.0)      # coupled decay (U6); 0 for AdamW
+    l2: bool = False
 
 
 @dataclass(frozen=True)
@@ -75,23 +81,28 @@ class SGDMScalars:
     lr: np.float32
     mu: np.float32
     wd: np.float32
+    damp1: np.float32 = F32(1.0)   # 1 - dampening
+    nesterov: bool = False
 
 
-def adamw_scalars(lr: float, beta1: float, beta2: float, eps: float, weight_decay: float, step: int) -> AdamWScalars:
-    """U2: float64 -> one float32 rounding each."""
+def adamw_scalars(lr: float, beta1: float, beta2: float, eps: float, weight_decay: float, step: int,
+                  l2: bool = False) -> AdamWScalars:
+    """U2: float64 -> one float32 rounding each.  l2 selects U6 (Adam)."""
     if step < 1:
         raise ValueError("step counts from 1")
     bc1 = 1.0 - beta1 ** step
     bc2 = 1.0 - beta2 ** step
     return AdamWScalars(
         b1=F32(beta1), b2=F32(beta2), omb1=F32(1.0 - beta1), omb2=F32(1.0 - beta2),
-        decay=F32(1.0 - lr * weight_decay), step_size=F32(lr / bc1),
-        ibc2=F32(1.0 / math.sqrt(bc2)), eps=F32(eps),
+        decay=F32(1.0) if l2 else F32(1.0 - lr * weight_decay), step_size=F32(lr / bc1),
+        ibc2=F32(1.0 / math.sqrt(bc2)), eps=F32(eps), wd=F32(weight_decay) if l2 else F32(0.0), l2=l2,
     )
 
 
-def sgdm_scalars(lr: float, momentum: float, weight_decay: float) -> SGDMScalars:
-    return SGDMScalars(lr=F32(lr), mu=F32(momentum), wd=F32(weight_decay))
+def sgdm_scalars(lr: float, momentum: float, weight_decay: float, dampening: float = 0.0,
+                 nesterov: bool = False) -> SGDMScalars:
+    return SGDMScalars(lr=F32(lr), mu=F32(momentum), wd=F32(weight_decay), damp1=F32(1.0 - dampening),
+                       nesterov=bool(nesterov))
 
 
 def adamw_update(theta, g, m, v, S: AdamWScalars):
@@ -99,6 +110,8 @@ def adamw_update(theta, g, m, v, S: AdamWScalars):
     theta = np.asarray(theta, F32); g = np.asarray(g, F32)
     m = np.asarray(m, F32); v = np.asarray(v, F32)
     with np.errstate(all="ignore"):
+        if S.l2:
+            g = g + S.wd * theta
         m1 = S.b1 * m + S.omb1 * g
         v1 = S.b2 * v + S.omb2 * (g * g)
         th = theta * S.decay
@@ -109,13 +122,14 @@ def adamw_update(theta, g, m, v, S: AdamWScalars):
     return th.astype(F32), m1.astype(F32), v1.astype(F32), w.astype(F32)
 
 
-def sgdm_update(theta, g, b, S: SGDMScalars):
+def sgdm_update(theta, g, b, S: SGDMScalars, first: bool = False):
     """U4 on float32 arrays.  Returns (theta, b)."""
     theta = np.asarray(theta, F32); g = np.asarray(g, F32); b = np.asarray(b, F32)
     with np.errstate(all="ignore"):
         d = g + S.wd * theta
-        b1 = S.mu * b + d
-        th = theta - S.lr * b1
+        b1 = d if first else S.mu * b + S.damp1 * d
+        u = d + S.mu * b1 if S.nesterov else b1
+        th = theta - S.lr * u
     return th.astype(F32), b1.astype(F32)
 
 
@@ -133,7 +147,8 @@ def adamw_step(state: dict, grad_bits: np.ndarray, hp: dict, fmt: str = "bf16",
     Returns the new state (same keys).  Steps: widen grad, reconstruct master,
     decode states, update (U3), split, block scales, encode.
     """
-    S = adamw_scalars(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"], hp["step"])
+    S = adamw_scalars(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"], hp["step"],
+                      l2=hp.get("l2_decay", False))
     theta = reconstruct_weights(state["w16"], state["ecc"], fmt, ecc_bits)
     g = widen_grad(grad_bits, fmt)
     m = decode_momentum(state["m_q"], state["m_s"], codec)
@@ -153,13 +168,15 @@ def sgdm_step(state: dict, grad_bits: np.ndarray, hp: dict, fmt: str = "bf16",
               ecc_bits: int = 8, codec: str = "companded") -> dict:
     """One fused SGD-with-momentum step on one tensor.
 
-    state: {"w16", "ecc", "b_q": int8, "b_s": uint16}; hp: lr, momentum, weight_decay.
+    state: {"w16", "ecc", "b_q": int8, "b_s": uint16}; hp: lr, momentum, weight_decay,
+    optional dampening, nesterov and step (step 1 sets the buffer to d).
     """
-    S = sgdm_scalars(hp["lr"], hp["momentum"], hp["weight_decay"])
+    S = sgdm_scalars(hp["lr"], hp["momentum"], hp["weight_decay"], hp.get("dampening", 0.0),
+                     hp.get("nesterov", False))
     theta = reconstruct_weights(state["w16"], state["ecc"], fmt, ecc_bits)
     g = widen_grad(grad_bits, fmt)
     b = decode_momentum(state["b_q"], state["b_s"], codec)
-    th, b1 = sgdm_update(theta, g, b, S)
+    th, b1 = sgdm_update(theta, g, b, S, first=hp["step"] == 1)
     w16, ecc = split_weights(th, fmt, ecc_bits)
     b_s = block_scales(b1, "m")
     return {"w16": w16, "ecc": ecc, "b_q": encode_momentum(b1, b_s, codec), "b_s": b_s}

@@ -1,6 +1,6 @@
 """MI355X (gfx950) fused low-precision optimizer step: 16-bit weights with an
 ULP-normalised error-correction code, companded 8-bit optimizer states, fused
-AdamW and momentum SGD over tensor lists.  The compute lives in the HIP
+AdamW / Adam and momentum SGD over tensor lists.  The compute lives in the HIP
 library csrc/ -> lib/libfoamd.so; binding.py marshals torch tensors into its
 C ABI (include/foamd.h)."""
 
@@ -21,4 +21,4 @@ from .binding import (  # noqa: F401
     fo_stream_probe,
 )
 from .state import AdamWState, SGDMState, alloc_adamw_state, alloc_sgdm_state  # noqa: F401
-from .optim import FlashAdamW, FlashSGD  # noqa: F401
+from .optim import FlashAdam, FlashAdamW, FlashSGD  # noqa: F401

@@ -45,7 +45,7 @@ class AdamWTensor(ctypes.Structure):
 class AdamWHParams(ctypes.Structure):
     _fields_ = [("lr", c_double), ("beta1", c_double), ("beta2", c_double), ("eps", c_double),
                 ("weight_decay", c_double), ("step", c_int64), ("wfmt", c_int32), ("ecc_bits", c_int32),
-                ("codec", c_int32)]
+                ("codec", c_int32), ("l2_decay", c_int32)]
 
 
 class SGDMTensor(ctypes.Structure):
@@ -54,8 +54,9 @@ class SGDMTensor(ctypes.Structure):
 
 
 class SGDMHParams(ctypes.Structure):
-    _fields_ = [("lr", c_double), ("momentum", c_double), ("weight_decay", c_double), ("step", c_int64),
-                ("wfmt", c_int32), ("ecc_bits", c_int32), ("codec", c_int32)]
+    _fields_ = [("lr", c_double), ("momentum", c_double), ("weight_decay", c_double), ("dampening", c_double),
+                ("step", c_int64), ("wfmt", c_int32), ("ecc_bits", c_int32), ("codec", c_int32),
+                ("nesterov", c_int32)]
 
 
 _lib = None
@@ -171,13 +172,16 @@ class SGDMList:
         return len(self.tensors)
 
 
-def adamw_hparams(lr, beta1, beta2, eps, weight_decay, step, wfmt="bf16", ecc_bits=8, codec="companded"):
+def adamw_hparams(lr, beta1, beta2, eps, weight_decay, step, wfmt="bf16", ecc_bits=8, codec="companded",
+                  l2_decay=False):
     return AdamWHParams(lr, beta1, beta2, eps, weight_decay, int(step), _fmt(wfmt, WFMT), int(ecc_bits),
-                        _fmt(codec, CODEC))
+                        _fmt(codec, CODEC), int(bool(l2_decay)))
 
 
-def sgdm_hparams(lr, momentum, weight_decay, step, wfmt="bf16", ecc_bits=8, codec="companded"):
-    return SGDMHParams(lr, momentum, weight_decay, int(step), _fmt(wfmt, WFMT), int(ecc_bits), _fmt(codec, CODEC))
+def sgdm_hparams(lr, momentum, weight_decay, step, wfmt="bf16", ecc_bits=8, codec="companded",
+                 dampening=0.0, nesterov=False):
+    return SGDMHParams(lr, momentum, weight_decay, dampening, int(step), _fmt(wfmt, WFMT), int(ecc_bits),
+                       _fmt(codec, CODEC), int(bool(nesterov)))
 
 
 def fo_fused_adamw_step(tlist, hp, stream=None) -> None:

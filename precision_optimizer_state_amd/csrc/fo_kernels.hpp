@@ -47,9 +47,15 @@ static_assert(sizeof(TensorDesc) == 80, "descriptor layout");
 
 struct AdamWConsts {
   float b1, b2, omb1, omb2, decay, step_size, ibc2, eps;
+  float wd;       // coupled (L2) weight decay of Adam; unused by AdamW
   int fast_rcp;   // eps >= 2^-126: every denominator is a positive normal >= eps
 };
-struct SGDMConsts { float lr, mu, wd; };
+struct SGDMConsts {
+  float lr, mu, wd;
+  float damp1;    // 1 - dampening
+  int nesterov;
+  int first;      // step 1: the buffer is set to the (decayed) gradient
+};
 
 template <typename T> using gp = FO_GLOBAL T*;
 
@@ -166,7 +172,7 @@ __device__ __forceinline__ void rcp8(const float (&d)[EPL], float (&r)[EPL], int
 // ---------------------------------------------------------------------------
 // fused AdamW: one wave tile
 // ---------------------------------------------------------------------------
-template <int WFMT, int ECC, int CODEC, bool FULL>
+template <int WFMT, int ECC, int CODEC, bool L2, bool FULL>
 __device__ __forceinline__ void adamw_tile(const TensorDesc& d, int64_t e0, int lane,
                                            const CodecTables& tabs, const AdamWConsts& c) {
   constexpr int EB = ECC / 8;                                  // ECC bytes per element
@@ -215,8 +221,9 @@ __device__ __forceinline__ void adamw_tile(const TensorDesc& d, int64_t e0, int 
     float th[EPL], m[EPL], v[EPL], w[EPL], den[EPL], r[EPL];
 #pragma unroll
     for (int k = 0; k < EPL; ++k) {
-      const float g = wid<WFMT>(G[j], k);
+      float g = wid<WFMT>(G[j], k);
       th[k] = ecc_decode<WFMT, ECC>(wid<WFMT>(W[j], k), rho_at<ECC>(E[j], k));
+      if constexpr (L2) g = g + c.wd * th[k];                  // Adam: decay folded into the gradient
       const int32_t qm = s8(MQ[j], k);
       const float mh = (CODEC == COMPANDED) ? dm * tabs.lut[qm + 127] : dm * (float)qm;
       const float tv = dv * (float)u8(VQ[j], k);
@@ -339,8 +346,9 @@ __device__ __forceinline__ void sgdm_tile(const TensorDesc& d, int64_t e0, int l
       const int32_t qb = s8(BQ[j], k);
       const float bh = (CODEC == COMPANDED) ? db * tabs.lut[qb + 127] : db * (float)qb;
       const float dd = g + c.wd * t0;
-      b[k] = c.mu * bh + dd;
-      th[k] = t0 - c.lr * b[k];
+      b[k] = c.first ? dd : c.mu * bh + c.damp1 * dd;
+      const float u = c.nesterov ? dd + c.mu * b[k] : b[k];
+      th[k] = t0 - c.lr * u;
       Bn[j][k] = b[k];
       bmax = fmaxf(bmax, fabsf(b[k]));
     }
@@ -467,15 +475,15 @@ __global__ void __launch_bounds__(WG) k_init_tables(CodecTables* out) {
   build_tables((gp<CodecTables>)out, thr, threadIdx.x, blockDim.x);
 }
 
-template <int WFMT, int ECC, int CODEC>
+template <int WFMT, int ECC, int CODEC, bool L2>
 __global__ void __launch_bounds__(WG) k_fused_adamw(const TensorDesc* __restrict__ tab, int count,
                                                     int64_t total_tiles, const CodecTables* __restrict__ gtabs,
                                                     AdamWConsts c) {
   __shared__ CodecTables tabs;
   load_tables(tabs, gtabs);
   tile_loop(tab, count, total_tiles, [&](const TensorDesc& d, int64_t e0, int lane) {
-    if (e0 + TILE <= d.n) adamw_tile<WFMT, ECC, CODEC, true>(d, e0, lane, tabs, c);
-    else adamw_tile<WFMT, ECC, CODEC, false>(d, e0, lane, tabs, c);
+    if (e0 + TILE <= d.n) adamw_tile<WFMT, ECC, CODEC, L2, true>(d, e0, lane, tabs, c);
+    else adamw_tile<WFMT, ECC, CODEC, L2, false>(d, e0, lane, tabs, c);
   });
 }
 

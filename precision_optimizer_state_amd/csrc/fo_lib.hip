@@ -254,6 +254,12 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
     else if (wfmt == FO_FP16 && ecc == 8 && codec == FO_LINEAR) OUT = KERNEL<FP16, 8, LINEAR>;  \
   } while (0)
 
+// AdamW (decoupled decay) and Adam (L2 decay folded into the gradient)
+template <int W, int E, int C>
+constexpr auto k_fused_adamw_dec = k_fused_adamw<W, E, C, false>;
+template <int W, int E, int C>
+constexpr auto k_fused_adamw_l2 = k_fused_adamw<W, E, C, true>;
+
 int launch_check(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, what);
@@ -401,6 +407,7 @@ int fo_fused_adamw_step(const fo_adamw_tensor* list, int32_t count, const fo_ada
   if (!fmt_ok(hp->wfmt, hp->ecc_bits)) return fail(FO_EINVAL, "unsupported format/ECC combination (%d, %d)", hp->wfmt, hp->ecc_bits);
   if (hp->codec != FO_COMPANDED && hp->codec != FO_LINEAR) return fail(FO_EINVAL, "bad codec %d", hp->codec);
   if (hp->step < 1) return fail(FO_EINVAL, "step must be >= 1");
+  if (hp->l2_decay != 0 && hp->l2_decay != 1) return fail(FO_EINVAL, "l2_decay must be 0 or 1");
   if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0 && hp->beta2 >= 0.0 && hp->beta2 < 1.0))
     return fail(FO_EINVAL, "betas must lie in [0, 1)");
   if (!(hp->lr >= 0.0) || !(hp->eps >= 0.0) || !(hp->weight_decay >= 0.0))
@@ -423,9 +430,12 @@ int fo_fused_adamw_step(const fo_adamw_tensor* list, int32_t count, const fo_ada
   c.step_size = (float)(hp->lr / (1.0 - std::pow(hp->beta1, t)));
   c.ibc2 = (float)(1.0 / std::sqrt(1.0 - std::pow(hp->beta2, t)));
   c.eps = (float)hp->eps;
+  c.wd = hp->l2_decay ? (float)hp->weight_decay : 0.0f;
+  if (hp->l2_decay) c.decay = 1.0f;                 // Adam: no decoupled decay
   c.fast_rcp = (c.eps >= 0x1p-126f) ? 1 : 0;
   void (*kern)(const TensorDesc*, int, int64_t, const CodecTables*, AdamWConsts) = nullptr;
-  FO_SELECT3(k_fused_adamw, hp->wfmt, hp->ecc_bits, hp->codec, kern);
+  if (hp->l2_decay) FO_SELECT3(k_fused_adamw_l2, hp->wfmt, hp->ecc_bits, hp->codec, kern);
+  else FO_SELECT3(k_fused_adamw_dec, hp->wfmt, hp->ecc_bits, hp->codec, kern);
   int dev, grid;
   const CodecTables* tb = nullptr;
   if ((rc = current_device(&dev)) || (rc = tile_grid(e->total_tiles, &grid)) || (rc = device_tables(dev, s, &tb))) return rc;
@@ -467,6 +477,10 @@ int fo_fused_sgdm_step(const fo_sgdm_tensor* list, int32_t count, const fo_sgdm_
   if (hp->step < 1) return fail(FO_EINVAL, "step must be >= 1");
   if (!(hp->lr >= 0.0) || !(hp->momentum >= 0.0) || !(hp->weight_decay >= 0.0))
     return fail(FO_EINVAL, "lr, momentum and weight_decay must be >= 0");
+  if (!(hp->dampening >= 0.0 && hp->dampening <= 1.0)) return fail(FO_EINVAL, "dampening must lie in [0, 1]");
+  if (hp->nesterov != 0 && hp->nesterov != 1) return fail(FO_EINVAL, "nesterov must be 0 or 1");
+  if (hp->nesterov && (hp->momentum <= 0.0 || hp->dampening != 0.0))
+    return fail(FO_EINVAL, "Nesterov momentum needs momentum > 0 and dampening 0");
   if (count == 0) return FO_OK;
   hipStream_t s = as_stream(stream);
   std::vector<uint8_t> key(1 + 8 + (size_t)count * sizeof(fo_sgdm_tensor));
@@ -505,6 +519,9 @@ int fo_fused_sgdm_step(const fo_sgdm_tensor* list, int32_t count, const fo_sgdm_
   c.lr = (float)hp->lr;
   c.mu = (float)hp->momentum;
   c.wd = (float)hp->weight_decay;
+  c.damp1 = (float)(1.0 - hp->dampening);
+  c.nesterov = hp->nesterov;
+  c.first = (hp->step == 1) ? 1 : 0;
   void (*kern)(const TensorDesc*, int, int64_t, const CodecTables*, SGDMConsts) = nullptr;
   FO_SELECT3(k_fused_sgdm, hp->wfmt, hp->ecc_bits, hp->codec, kern);
   int grid;

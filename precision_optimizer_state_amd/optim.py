@@ -12,6 +12,7 @@ accumulated and frees the gradient (the post on gradient release).
 
 All arithmetic runs in the HIP library (fo_fused_adamw_step /
 fo_fused_sgdm_step); this module only groups tensors and keeps step counts.
+FlashAdamW, FlashAdam and FlashSGD follow torch.optim.AdamW, Adam and SGD.
 """
 
 from __future__ import annotations
@@ -167,10 +168,12 @@ class FlashAdamW(_FlashBase):
     def _make_list(entries):
         return B.AdamWList(entries)
 
+    _l2_decay = False
+
     def _launch(self, tl, group, step):
         b1, b2 = group["betas"]
         B.fo_fused_adamw_step(tl, B.adamw_hparams(group["lr"], b1, b2, group["eps"], group["weight_decay"], step,
-                                                  self.wfmt, self.ecc_bits, self.codec))
+                                                  self.wfmt, self.ecc_bits, self.codec, self._l2_decay))
 
     @torch.no_grad()
     def export_torch_state(self, p):
@@ -183,15 +186,28 @@ class FlashAdamW(_FlashBase):
         return m.view(p.shape), v.view(p.shape)
 
 
+class FlashAdam(FlashAdamW):
+    """Adam as torch.optim.Adam: the weight decay is added to the gradient
+    (L2 regularisation) instead of being applied to the weights."""
+
+    _l2_decay = True
+
+    def __init__(self, params: Iterable, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.0, **kw):
+        super().__init__(params, lr=lr, betas=betas, eps=eps, weight_decay=weight_decay, **kw)
+
+
 class FlashSGD(_FlashBase):
-    """SGD with momentum (coupled weight decay, dampening 0, no Nesterov) with
-    split master weights and a companded 8-bit momentum buffer."""
+    """SGD with momentum as torch.optim.SGD (coupled weight decay, optional
+    dampening and Nesterov momentum) with split master weights and a companded
+    8-bit momentum buffer."""
 
     _state_keys = (("b_q", torch.int8, False), ("b_s", torch.int16, True))
 
-    def __init__(self, params: Iterable, lr=1e-2, momentum=0.9, weight_decay=0.0, *,
+    def __init__(self, params: Iterable, lr=1e-2, momentum=0.9, dampening=0.0, weight_decay=0.0, nesterov=False, *,
                  wfmt="bf16", ecc_bits=8, codec="companded", grad_release=False):
-        defaults = dict(lr=lr, momentum=momentum, weight_decay=weight_decay)
+        if nesterov and (momentum <= 0.0 or dampening != 0.0):
+            raise ValueError("Nesterov momentum requires a momentum and zero dampening")
+        defaults = dict(lr=lr, momentum=momentum, dampening=dampening, weight_decay=weight_decay, nesterov=nesterov)
         super().__init__(params, defaults, wfmt, ecc_bits, codec, grad_release)
 
     def _entry(self, p):
@@ -205,4 +221,7 @@ class FlashSGD(_FlashBase):
 
     def _launch(self, tl, group, step):
         B.fo_fused_sgdm_step(tl, B.sgdm_hparams(group["lr"], group["momentum"], group["weight_decay"], step,
-                                                self.wfmt, self.ecc_bits, self.codec))
+                                                self.wfmt, self.ecc_bits, self.codec,
+                                                # with momentum 0 torch ignores dampening (no buffer)
+                                                group["dampening"] if group["momentum"] else 0.0,
+                                                group["nesterov"]))

@@ -32,7 +32,7 @@ def test_struct_layouts_match_header():
     assert ctypes.sizeof(B.AdamWTensor) == 64
     assert ctypes.sizeof(B.AdamWHParams) == 64
     assert ctypes.sizeof(B.SGDMTensor) == 48
-    assert ctypes.sizeof(B.SGDMHParams) == 48
+    assert ctypes.sizeof(B.SGDMHParams) == 56
 
 
 def _rc(fn, *args):

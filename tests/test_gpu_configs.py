@@ -82,7 +82,8 @@ def _run(cfg_name, steps, blocks_per_tensor, release=False):
             if adam:
                 refs[i] = O.adamw_step(refs[i], gsamp[i], dict(cfg.hp, step=step), cfg.wfmt, cfg.ecc_bits, cfg.codec)
             else:
-                refs[i] = O.sgdm_step(refs[i], gsamp[i], cfg.hp, cfg.wfmt, cfg.ecc_bits, cfg.codec)
+                refs[i] = O.sgdm_step(refs[i], gsamp[i], dict(cfg.hp, step=step), cfg.wfmt, cfg.ecc_bits,
+                                       cfg.codec)
     torch.cuda.synchronize()
     total, bad = 0, 0
     for i, st in enumerate(states):

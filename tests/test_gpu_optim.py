@@ -1,4 +1,4 @@
-"""The drop-in optimizers (FlashAdamW, FlashSGD) on a small model: every step
+"""The drop-in optimizers (FlashAdamW, FlashAdam, FlashSGD) on a small model: every step
 matches the oracle bit for bit, gradient release matches the plain step,
 state_dict save/load resumes bit for bit, and training tracks
 torch.optim.AdamW in float32."""
@@ -11,7 +11,7 @@ import torch
 
 import oracle as O
 from oracle.optim import fresh_adamw_state, fresh_sgdm_state
-from precision_optimizer_state_amd import FlashAdamW, FlashSGD
+from precision_optimizer_state_amd import FlashAdam, FlashAdamW, FlashSGD
 from tests.gpu_helpers import check_adamw_state, check_sgdm_state, to_host
 
 pytestmark = pytest.mark.gpu
@@ -39,24 +39,26 @@ def _loss(model, i):
 HP = dict(lr=3e-3, betas=(0.9, 0.95), eps=1e-8, weight_decay=0.1)
 
 
-def test_flash_adamw_matches_oracle_every_step():
+@pytest.mark.parametrize("cls", [FlashAdamW, FlashAdam])
+def test_flash_adamw_matches_oracle_every_step(cls):
     model = _model()
     x0 = [p.detach().float().cpu().numpy().ravel().copy() for p in model.parameters()]
-    opt = FlashAdamW(model.parameters(), **HP)
+    opt = cls(model.parameters(), **HP)
     refs = [fresh_adamw_state(x) for x in x0]
     for step in range(1, 6):
         opt.zero_grad(set_to_none=True)
         _loss(model, step).backward()
         grads = [to_host(p.grad.view(-1)) for p in model.parameters()]
         opt.step()
-        hp = dict(lr=HP["lr"], beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=step)
+        hp = dict(lr=HP["lr"], beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=step,
+                  l2_decay=cls is FlashAdam)
         for i, p in enumerate(model.parameters()):
             refs[i] = O.adamw_step(refs[i], grads[i], hp)
             st = opt.state[p]
             got = {"w16": to_host(p.data.view(-1)), "ecc": to_host(st["ecc"].view(-1)),
                    "m_q": to_host(st["m_q"]), "v_q": to_host(st["v_q"]),
                    "m_s": to_host(st["m_s"]).view(np.uint16), "v_s": to_host(st["v_s"]).view(np.uint16)}
-            bad = check_adamw_state(f"FlashAdamW step {step} param {i}", got, refs[i])
+            bad = check_adamw_state(f"{cls.__name__} step {step} param {i}", got, refs[i])
             assert sum(bad.values()) == 0
     # master weights are the oracle's reconstruction
     for i, p in enumerate(model.parameters()):
@@ -64,10 +66,11 @@ def test_flash_adamw_matches_oracle_every_step():
         assert np.array_equal(mw.view(np.uint32), O.reconstruct_weights(refs[i]["w16"], refs[i]["ecc"]).view(np.uint32))
 
 
-def test_flash_sgd_matches_oracle_every_step():
+@pytest.mark.parametrize("extra", [{}, {"nesterov": True}, {"dampening": 0.3}])
+def test_flash_sgd_matches_oracle_every_step(extra):
     model = _model(1)
     x0 = [p.detach().float().cpu().numpy().ravel().copy() for p in model.parameters()]
-    opt = FlashSGD(model.parameters(), lr=0.05, momentum=0.9, weight_decay=1e-4)
+    opt = FlashSGD(model.parameters(), lr=0.05, momentum=0.9, weight_decay=1e-4, **extra)
     refs = [fresh_sgdm_state(x) for x in x0]
     for step in range(1, 6):
         opt.zero_grad(set_to_none=True)
@@ -75,7 +78,7 @@ def test_flash_sgd_matches_oracle_every_step():
         grads = [to_host(p.grad.view(-1)) for p in model.parameters()]
         opt.step()
         for i, p in enumerate(model.parameters()):
-            refs[i] = O.sgdm_step(refs[i], grads[i], dict(lr=0.05, momentum=0.9, weight_decay=1e-4))
+            refs[i] = O.sgdm_step(refs[i], grads[i], dict(lr=0.05, momentum=0.9, weight_decay=1e-4, step=step, **extra))
             st = opt.state[p]
             got = {"w16": to_host(p.data.view(-1)), "ecc": to_host(st["ecc"].view(-1)),
                    "b_q": to_host(st["b_q"]), "b_s": to_host(st["b_s"]).view(np.uint16)}

@@ -235,7 +235,7 @@ def _run_sgdm(sizes, steps, hp, fmt="bf16", ecc_bits=8, codec="companded", tag="
             st["grad"].copy_(to_dev(gb, DT[fmt]))
         B.fo_fused_sgdm_step(tl, B.sgdm_hparams(step=step, wfmt=fmt, ecc_bits=ecc_bits, codec=codec, **hp))
         for i in range(len(sizes)):
-            ref[i] = O.sgdm_step(ref[i], gbs[i], hp, fmt, ecc_bits, codec)
+            ref[i] = O.sgdm_step(ref[i], gbs[i], dict(hp, step=step), fmt, ecc_bits, codec)
         torch.cuda.synchronize()
         for i in range(len(sizes)):
             bad = check_sgdm_state(f"sgdm step {step} tensor {i} (n={sizes[i]})", sgdm_state_to_host(dev[i]),
@@ -253,6 +253,23 @@ def test_fused_sgdm_matches_oracle(fmt, ecc_bits, codec):
     sizes = [9408, 64, 64, 4096, 36864, 16384, 1000, 2_048_000 // 8, 33, 1]
     bad = _run_sgdm(sizes, 5, HP_C4, fmt, ecc_bits, codec, tag=f"sgdm_{fmt}{ecc_bits}{codec}")
     print(f"sgdm {fmt}+{ecc_bits}/{codec}: {bad} mismatching elements", flush=True)
+
+
+@pytest.mark.parametrize("nesterov,dampening", [(True, 0.0), (False, 0.5), (False, 1.0)])
+def test_fused_sgd_nesterov_and_dampening_match_oracle(nesterov, dampening):
+    sizes = [9408, 4096, 2049, 33, 1, 100_000]
+    hp = dict(HP_C4, nesterov=nesterov, dampening=dampening)
+    bad = _run_sgdm(sizes, 4, hp, tag=f"sgd_n{int(nesterov)}_d{dampening}")
+    print(f"sgd nesterov={nesterov} dampening={dampening}: {bad} mismatching elements", flush=True)
+
+
+@pytest.mark.parametrize("fmt,ecc_bits,codec", [("bf16", 8, "companded"), ("fp16", 8, "companded"),
+                                                ("bf16", 16, "linear")])
+def test_fused_adam_l2_decay_matches_oracle(fmt, ecc_bits, codec):
+    sizes = [300_000, 4097, 33, 1]
+    hp = dict(HP_C1, weight_decay=0.05, l2_decay=True)
+    bad = _run_adamw(sizes, 4, hp, fmt, ecc_bits, codec, tag=f"adam_l2_{fmt}{ecc_bits}{codec}")
+    print(f"Adam (L2) {fmt}+{ecc_bits}/{codec}: {bad} mismatching elements", flush=True)
 
 
 def test_gradient_release_chunks_equal_whole_tensor():

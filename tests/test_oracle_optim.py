@@ -158,7 +158,7 @@ def test_sgdm_full_step_first_step_equals_torch_buffer():
     g = (rng.standard_normal(64) * 1e-2).astype(np.float32)
     gb = (g.view(np.uint32) + 0x8000 >> 16).astype(np.uint16)
     gw = (gb.astype(np.uint32) << 16).view(np.float32)
-    st2 = O.sgdm_step(st, gb, dict(lr=0.1, momentum=0.9, weight_decay=1e-4))
+    st2 = O.sgdm_step(st, gb, dict(lr=0.1, momentum=0.9, weight_decay=1e-4, step=1))
     th0 = O.reconstruct_weights(st["w16"], st["ecc"])
     d = gw + np.float32(1e-4) * th0
     want = th0 - np.float32(0.1) * d
@@ -176,3 +176,44 @@ def test_bytes_per_param():
     assert total / n == 7.125
     # the fp32 mixed-precision baseline: 4 master + 4 grad + 8 Adam = 16
     assert (4 + 4 + 8) == 16
+
+
+def test_adam_l2_matches_torch_adam():
+    # U6: coupled L2 decay added to the gradient (torch.optim.Adam weight_decay)
+    rng = np.random.default_rng(30)
+    x0 = (rng.standard_normal((7, 5)) * 0.02).astype(np.float32)
+    grads = [(rng.standard_t(3, (7, 5)) * 1e-3).astype(np.float32) for _ in range(10)]
+    p = torch.nn.Parameter(torch.tensor(x0, dtype=torch.float64))
+    opt = torch.optim.Adam([p], lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=0.1, foreach=False)
+    th = x0.copy(); m = np.zeros_like(th); v = np.zeros_like(th)
+    for t, g in enumerate(grads, start=1):
+        p.grad = torch.tensor(g, dtype=torch.float64)
+        opt.step()
+        th, m, v, _ = O.adamw_update(th, g, m, v, O.adamw_scalars(1e-3, 0.9, 0.999, 1e-8, 0.1, t, l2=True))
+        ref = p.detach().numpy()
+        assert np.max(np.abs(th - ref)) <= 1e-6 * np.max(np.abs(ref))
+        assert np.max(np.abs((th - x0) - (ref - x0))) <= 1e-4 * np.max(np.abs(ref - x0))
+    # and it differs from AdamW by far more than that (the decay is not decoupled)
+    th2 = x0.copy(); m2 = np.zeros_like(th2); v2 = np.zeros_like(th2)
+    for t, g in enumerate(grads, start=1):
+        th2, m2, v2, _ = O.adamw_update(th2, g, m2, v2, O.adamw_scalars(1e-3, 0.9, 0.999, 1e-8, 0.1, t))
+    assert np.max(np.abs(th2 - th)) > 1e-3 * np.max(np.abs(th - x0))
+
+
+@pytest.mark.parametrize("nesterov,dampening", [(True, 0.0), (False, 0.5), (False, 0.0)])
+def test_sgd_variants_match_torch(nesterov, dampening):
+    rng = np.random.default_rng(31)
+    x0 = (rng.standard_normal((7, 5)) * 0.02).astype(np.float32)
+    grads = [(rng.standard_normal((7, 5)) * 1e-2).astype(np.float32) for _ in range(10)]
+    p = torch.nn.Parameter(torch.tensor(x0, dtype=torch.float64))
+    opt = torch.optim.SGD([p], lr=0.1, momentum=0.9, weight_decay=1e-4, dampening=dampening,
+                          nesterov=nesterov, foreach=False)
+    S = O.sgdm_scalars(0.1, 0.9, 1e-4, dampening, nesterov)
+    th = x0.copy(); b = np.zeros_like(th)
+    for t, g in enumerate(grads, start=1):
+        p.grad = torch.tensor(g, dtype=torch.float64)
+        opt.step()
+        th, b = O.sgdm_update(th, g, b, S, first=(t == 1))
+        ref = p.detach().numpy()
+        assert np.max(np.abs(th - ref)) <= 1e-6 * np.max(np.abs(ref))
+        assert np.max(np.abs((th - x0) - (ref - x0))) <= 1e-4 * np.max(np.abs(ref - x0))
