@@ -170,7 +170,7 @@ __device__ __forceinline__ uint32_t pack4_byte1(uint32_t a, uint32_t b, uint32_t
 // the magnitude; the sign bit is untouched), ECC8 = byte 1 of
 // min(sext16(bits) + 127 + bit8, 32767) (round-half-even of the offset / 256,
 // clamped at 127), ECC16 = the low half of the pattern (the offset itself).
-// Otherwise every element goes through ecc_encode.
+// fp16 fast path below.  Otherwise every element goes through ecc_encode.
 template <int WFMT, int ECC>
 __device__ __forceinline__ void split8(const float (&x)[8], uint32_t (&wo)[4], uint32_t (&eo)[ECC / 4]) {
   if constexpr (WFMT == BF16) {
@@ -197,6 +197,44 @@ __device__ __forceinline__ void split8(const float (&x)[8], uint32_t (&wo)[4], u
 #pragma unroll
         for (int i = 0; i < 4; ++i) eo[i] = perm(f2u(x[2 * i + 1]), f2u(x[2 * i]), 0x05040100u);
       }
+      return;
+    }
+  } else {
+    // fp16 + ECC8, valid while every value of the wave is finite and below
+    // the RNA overflow threshold 65520.  Both ranges are computed on every
+    // lane and selected per lane (about 0.24% of N(0, 0.02) weights fall
+    // below 2^-14, so most waves hold at least one):
+    //  |x| >= 2^-14: integer RNA of the pattern with the exponent rebiased,
+    //               rho = round-half-even(sext13(bits) / 32), clamped at 127;
+    //  |x| <  2^-14: theta' = k * 2^-24 with k = RNA(|x| * 2^24) (k = 1024 is
+    //               the smallest normal), rho = rint((|x| - k 2^-24) * 2^32).
+    //               Both products are exact power-of-two scalings and the
+    //               difference is exact (Sterbenz, or k = 0).
+    uint64_t special = 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) special |= __builtin_amdgcn_ballot_w64(!(fabsf(x[k]) < 65520.0f));
+    if (special == 0) {
+      uint32_t H[8], R[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const uint32_t xb = f2u(x[k]);
+        const uint32_t ab = xb & 0x7FFFFFFFu;
+        const bool nrm = ab >= 0x38800000u;
+        const uint32_t hn = ((ab + 0x1000u) >> 13) - (112u << 10);
+        const int32_t rn = min(rne_shift(((int32_t)(ab << 19)) >> 19, 5), 127);
+        const float a = nrm ? 0.0f : u2f(ab);
+        const float y = a * 0x1p24f;
+        const float ty = __builtin_truncf(y);
+        const float kf = ty + ((y - ty >= 0.5f) ? 1.0f : 0.0f);
+        const float d = a - kf * 0x1p-24f;
+        const int32_t rs = (int32_t)__builtin_fminf(__builtin_rintf(d * 0x1p32f), 127.0f);
+        H[k] = (nrm ? hn : (uint32_t)kf) | ((xb >> 16) & 0x8000u);
+        R[k] = (uint32_t)(nrm ? rn : rs);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wo[i] = perm(H[2 * i + 1], H[2 * i], 0x05040100u);
+      eo[0] = pack4_byte0(R[0], R[1], R[2], R[3]);
+      eo[1] = pack4_byte0(R[4], R[5], R[6], R[7]);
       return;
     }
   }

@@ -185,6 +185,27 @@ class FlashAdamW(_FlashBase):
         B.fo_dequantize(st["v_q"], st["v_s"], v, "v", self.codec)   # scale patterns read as fp16 bits
         return m.view(p.shape), v.view(p.shape)
 
+    @torch.no_grad()
+    def import_torch_state(self, p, exp_avg, exp_avg_sq, step):
+        """Quantise an f32 (exp_avg, exp_avg_sq) pair, e.g. from torch.optim.AdamW,
+        into the 8-bit states of `p` and set its step count."""
+        st = self.state[p]
+        for key, x, kind in (("m", exp_avg, "m"), ("v", exp_avg_sq, "v")):
+            x = x.detach().to(device=p.device, dtype=torch.float32).contiguous().view(-1)
+            if x.numel() != p.numel():
+                raise ValueError(f"state of {x.numel()} elements for a parameter of {p.numel()}")
+            B.fo_companded_quantize(x, st[key + "_q"], st[key + "_s"], kind, self.codec)
+        st["step"] = int(step)
+
+    def import_torch_optimizer(self, torch_opt):
+        """Take over the moments and step counts of a torch.optim.Adam/AdamW that
+        was stepping the same parameters (its state is keyed by them)."""
+        for group in self.param_groups:
+            for p in group["params"]:
+                s = torch_opt.state.get(p)
+                if s and "exp_avg" in s:
+                    self.import_torch_state(p, s["exp_avg"], s["exp_avg_sq"], int(s["step"]))
+
 
 class FlashAdam(FlashAdamW):
     """Adam as torch.optim.Adam: the weight decay is added to the gradient
@@ -218,6 +239,24 @@ class FlashSGD(_FlashBase):
     @staticmethod
     def _make_list(entries):
         return B.SGDMList(entries)
+
+    @torch.no_grad()
+    def export_torch_state(self, p):
+        """f32 momentum_buffer of `p`, decoded from the 8-bit state."""
+        st = self.state[p]
+        b = torch.empty(p.numel(), dtype=torch.float32, device=p.device)
+        B.fo_dequantize(st["b_q"], st["b_s"], b, "m", self.codec)
+        return b.view(p.shape)
+
+    @torch.no_grad()
+    def import_torch_state(self, p, momentum_buffer, step):
+        """Quantise an f32 momentum buffer (torch.optim.SGD) into `p`'s state."""
+        st = self.state[p]
+        x = momentum_buffer.detach().to(device=p.device, dtype=torch.float32).contiguous().view(-1)
+        if x.numel() != p.numel():
+            raise ValueError(f"state of {x.numel()} elements for a parameter of {p.numel()}")
+        B.fo_companded_quantize(x, st["b_q"], st["b_s"], "m", self.codec)
+        st["step"] = int(step)
 
     def _launch(self, tl, group, step):
         B.fo_fused_sgdm_step(tl, B.sgdm_hparams(group["lr"], group["momentum"], group["weight_decay"], step,

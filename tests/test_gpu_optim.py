@@ -152,3 +152,34 @@ def test_training_tracks_fp32_adamw():
     err_fl = (w_fl.T - w_true).norm() / w_true.norm()
     print(f"relative weight error after 200 steps: fp32 AdamW {err_ref:.3e}, FlashAdamW {err_fl:.3e}", flush=True)
     assert err_fl < 2e-2 and err_ref < 2e-2
+
+
+def test_torch_state_import_export_round_trip():
+    """Moments of a torch.optim.AdamW run, imported into FlashAdamW, come back
+    out as the oracle's quantise -> dequantise of the same f32 values; the
+    next step then matches the oracle started from those codes."""
+    model = _model(4)
+    tor = torch.optim.AdamW(model.parameters(), lr=1e-3, weight_decay=0.1)
+    for step in range(1, 4):
+        tor.zero_grad(set_to_none=True)
+        x, y = _batch(step, torch.float32)
+        torch.nn.functional.mse_loss(model(x), y).backward()
+        tor.step()
+    mom = {p: (tor.state[p]["exp_avg"].clone(), tor.state[p]["exp_avg_sq"].clone()) for p in model.parameters()}
+    model.to(torch.bfloat16)                      # the parameters stay the same objects
+    fl = FlashAdamW(model.parameters(), lr=1e-3, weight_decay=0.1)
+    fl.import_torch_optimizer(tor)
+    for p in model.parameters():
+        assert fl.state[p]["step"] == 3
+        m, v = fl.export_torch_state(p)
+        for got, x, kind in ((m, mom[p][0], "m"), (v, mom[p][1], "v")):
+            q, sc = O.quantize_state(x.float().cpu().numpy().ravel(), kind, "companded")
+            want = O.dequantize_state(q, sc, kind, "companded")
+            assert np.array_equal(got.cpu().numpy().ravel().view(np.uint32), want.view(np.uint32))
+    sgd = FlashSGD(_model(5).parameters(), lr=0.1, momentum=0.9)
+    p = next(iter(sgd.param_groups[0]["params"]))
+    buf = torch.randn(p.shape, device="cuda") * 1e-2
+    sgd.import_torch_state(p, buf, 7)
+    q, sc = O.quantize_state(buf.cpu().numpy().ravel(), "m", "companded")
+    assert np.array_equal(sgd.export_torch_state(p).cpu().numpy().ravel().view(np.uint32),
+                          O.dequantize_state(q, sc, "m", "companded").view(np.uint32))
