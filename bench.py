@@ -14,6 +14,7 @@ the timed region.  The same gradient buffer is used by every timed step.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -174,6 +175,14 @@ def cpu_baseline(cfg, segments=64, seg=1 << 20, log=print):
 
 
 # ---------------------------------------------------------------------------
+# optimizer variants on the same byte streams (hyperparameter additions)
+VARIANTS = {
+    "adam_l2": ("adamw", {"l2_decay": True}),
+    "sgd_nesterov": ("sgdm", {"nesterov": True}),
+    "sgd_dampening": ("sgdm", {"dampening": 0.1}),
+}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -184,6 +193,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
     ap.add_argument("--copy-calib", action="store_true", help="also run a plain device copy of 4 GiB (counter calibration)")
+    ap.add_argument("--variant", default=None, choices=sorted(VARIANTS),
+                    help="optimizer variant: Adam with L2 decay (AdamW lists) or SGD with "
+                         "Nesterov momentum / dampening (SGD-M lists)")
     ap.add_argument("--quiet", action="store_true")
     args = ap.parse_args(argv)
 
@@ -203,6 +215,12 @@ def main(argv=None):
     from workloads.configs import FLAT_1G, RELEASE_CHUNKS
 
     cfg = config(args.config)
+    if args.variant:
+        opt, extra = VARIANTS[args.variant]
+        if cfg.optimizer != opt:
+            print(f"--variant {args.variant} needs a {opt} workload", file=sys.stderr)
+            return 2
+        cfg = dataclasses.replace(cfg, hp=dict(cfg.hp, **extra))
     torch.cuda.set_device(0)
     B.load()
     states = build_states(cfg, log)
@@ -292,6 +310,7 @@ def main(argv=None):
             "codec": cfg.codec,
             "bytes_per_param_moved": bpp,
             "release_chunks": len(release) if release else None,
+            "variant": args.variant,
         },
         "roofline": {
             "bound": "hbm",
@@ -299,7 +318,8 @@ def main(argv=None):
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBS,
-            "traffic": read_traffic(cfg.name + ("_release" if release else "")),
+            "traffic": read_traffic(cfg.name + ("_release" if release else "")
+                                    + (f"_{args.variant}" if args.variant else "")),
         },
         "kernel_ms_avg": avg_ms,
         "stream_probe_gbs": probe_gbs,

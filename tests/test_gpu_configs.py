@@ -20,15 +20,19 @@ from precision_optimizer_state_amd import binding as B
 from precision_optimizer_state_amd.state import alloc_adamw_state, alloc_sgdm_state
 from tests.gpu_helpers import check_adamw_state, check_sgdm_state, to_host
 from workloads import config, device_grads, device_weights
+from workloads.configs import Config
 from workloads.configs import RELEASE_CHUNKS
 
 pytestmark = pytest.mark.gpu
 
 
-def _sample_blocks(n, k, rng):
+def _sample_blocks(n, k, rng, forced=()):
     nb = -(-n // 32)
+    if nb == 0:
+        return np.zeros(0, np.int64), np.zeros(0, np.int64)
     pick = rng.choice(nb, size=min(nb, k), replace=False)
-    pick = np.unique(np.concatenate([pick, [nb - 1]]))
+    extra = [b for b in forced if 0 <= b < nb]
+    pick = np.unique(np.concatenate([pick, [nb - 1], np.asarray(extra, dtype=np.int64)])).astype(np.int64)
     idx = (pick[:, None] * 32 + np.arange(32)[None, :]).ravel()
     return pick, idx[idx < n]
 
@@ -37,8 +41,8 @@ def _gather(t, idx_dev):
     return to_host(t[idx_dev])
 
 
-def _run(cfg_name, steps, blocks_per_tensor, release=False):
-    cfg = config(cfg_name)
+def _run(cfg_name, steps, blocks_per_tensor, release=False, cfg=None, forced=()):
+    cfg = cfg or config(cfg_name)
     rng = np.random.default_rng(7)
     adam = cfg.optimizer == "adamw"
     states, samples, refs = [], [], []
@@ -46,7 +50,7 @@ def _run(cfg_name, steps, blocks_per_tensor, release=False):
     for i, n in enumerate(cfg.numels):
         st = (alloc_adamw_state if adam else alloc_sgdm_state)(n, cfg.wfmt, cfg.ecc_bits)
         w = device_weights(cfg.name, i, n)
-        blocks, idx = _sample_blocks(n, blocks_per_tensor, rng)
+        blocks, idx = _sample_blocks(n, blocks_per_tensor, rng, forced)
         idx_dev = torch.from_numpy(idx).cuda()
         x0 = w[idx_dev].cpu().numpy()
         B.fo_split_weights(w, st["w16"], st["ecc"], cfg.wfmt, cfg.ecc_bits)
@@ -79,6 +83,8 @@ def _run(cfg_name, steps, blocks_per_tensor, release=False):
                 B.fo_fused_sgdm_step(tl, B.sgdm_hparams(step=step, wfmt=cfg.wfmt, ecc_bits=cfg.ecc_bits,
                                                         codec=cfg.codec, **cfg.hp))
         for i in range(len(states)):
+            if cfg.numels[i] == 0:
+                continue
             if adam:
                 refs[i] = O.adamw_step(refs[i], gsamp[i], dict(cfg.hp, step=step), cfg.wfmt, cfg.ecc_bits, cfg.codec)
             else:
@@ -88,6 +94,8 @@ def _run(cfg_name, steps, blocks_per_tensor, release=False):
     total, bad = 0, 0
     for i, st in enumerate(states):
         bdev, idev = samples[i]
+        if cfg.numels[i] == 0:
+            continue
         if adam:
             got = {"w16": _gather(st["w16"], idev), "ecc": _gather(st["ecc"], idev),
                    "m_q": _gather(st["m_q"], idev), "v_q": _gather(st["v_q"], idev),
@@ -128,3 +136,17 @@ def test_config_c5_flat_2_30_variants(name):
 
 def test_config_c5_gradient_release_chunks():
     _run("c5_flat1g_bf16e8", 2, 20000, release=True)
+
+
+def test_tensor_beyond_2_31_elements_next_to_empty_and_tiny_tensors():
+    """64-bit indexing at the largest sizes: one AdamW tensor of
+    2^31 + 2^11 + 45 elements (its theta' byte offsets pass 2^31 at element
+    2^30 and 2^32 at element 2^31; its ECC and code offsets pass 2^31 at
+    element 2^31), listed after a 33-element and an empty tensor, 2 steps.
+    Sampled blocks include those around both boundaries and the ragged tail."""
+    big = (1 << 31) + (1 << 11) + 45
+    base = config("c5_flat1g_bf16e8")
+    cfg = Config("huge_2_31", "adamw", (("tiny", (33,)), ("empty", (0,)), ("huge", (big,))), base.hp,
+                 steps=2, grad_kind="t3")
+    forced = [b + d for b in ((1 << 30) // 32, (1 << 31) // 32) for d in range(-3, 3)]
+    _run("huge_2_31", 2, 4000, cfg=cfg, forced=forced)
