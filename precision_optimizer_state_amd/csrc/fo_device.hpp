@@ -201,15 +201,15 @@ __device__ __forceinline__ void split8(const float (&x)[8], uint32_t (&wo)[4], u
     }
   } else {
     // fp16 + ECC8, valid while every value of the wave is finite and below
-    // the RNA overflow threshold 65520.  Both ranges are computed on every
-    // lane and selected per lane (about 0.24% of N(0, 0.02) weights fall
-    // below 2^-14, so most waves hold at least one):
-    //  |x| >= 2^-14: integer RNA of the pattern with the exponent rebiased,
-    //               rho = round-half-even(sext13(bits) / 32), clamped at 127;
-    //  |x| <  2^-14: theta' = k * 2^-24 with k = RNA(|x| * 2^24) (k = 1024 is
-    //               the smallest normal), rho = rint((|x| - k 2^-24) * 2^32).
-    //               Both products are exact power-of-two scalings and the
-    //               difference is exact (Sterbenz, or k = 0).
+    // the RNA overflow threshold 65520.  theta' starts as the hardware
+    // round-to-nearest-even conversion t; d = |x| - |t| is exact (Sterbenz,
+    // or t = 0), and rho = rint(d * 2^8 / ulp_side(t)) = rint(ldexp(d, k))
+    // with k = 145 - max(biased exponent of t, 113) (113: the fp16 subnormal
+    // spacing 2^-24), plus one on the inner side of a power of two above
+    // 2^-14.  RNE and RNA differ only on an exact tie that RNE rounded
+    // towards zero, which shows as d * 2^k == +128 exactly: then theta' moves
+    // one pattern away from zero and rho = -128.  Any other value rounding
+    // to 128 clamps to 127.
     uint64_t special = 0;
 #pragma unroll
     for (int k = 0; k < 8; ++k) special |= __builtin_amdgcn_ballot_w64(!(fabsf(x[k]) < 65520.0f));
@@ -217,19 +217,18 @@ __device__ __forceinline__ void split8(const float (&x)[8], uint32_t (&wo)[4], u
       uint32_t H[8], R[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const uint32_t xb = f2u(x[k]);
-        const uint32_t ab = xb & 0x7FFFFFFFu;
-        const bool nrm = ab >= 0x38800000u;
-        const uint32_t hn = ((ab + 0x1000u) >> 13) - (112u << 10);
-        const int32_t rn = min(rne_shift(((int32_t)(ab << 19)) >> 19, 5), 127);
-        const float a = nrm ? 0.0f : u2f(ab);
-        const float y = a * 0x1p24f;
-        const float ty = __builtin_truncf(y);
-        const float kf = ty + ((y - ty >= 0.5f) ? 1.0f : 0.0f);
-        const float d = a - kf * 0x1p-24f;
-        const int32_t rs = (int32_t)__builtin_fminf(__builtin_rintf(d * 0x1p32f), 127.0f);
-        H[k] = (nrm ? hn : (uint32_t)kf) | ((xb >> 16) & 0x8000u);
-        R[k] = (uint32_t)(nrm ? rn : rs);
+        const _Float16 hh = (_Float16)x[k];
+        const float t = (float)hh;
+        const float d = fabsf(x[k]) - fabsf(t);
+        const uint32_t tb = f2u(t);
+        const int eb = (int)((tb >> 23) & 0xFFu);
+        const bool inner = (d < 0.0f) && ((tb & 0x7FFFFFu) == 0u) && (eb > 113);
+        const int sh = 145 - max(eb, 113) + (inner ? 1 : 0);
+        const float rf = __builtin_ldexpf(d, sh);
+        const bool tie = (rf == 128.0f);
+        const int32_t r = min((int32_t)__builtin_rintf(rf), 127);
+        H[k] = (uint32_t)__builtin_bit_cast(uint16_t, hh) + (tie ? 1u : 0u);
+        R[k] = (uint32_t)(tie ? -128 : r);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) wo[i] = perm(H[2 * i + 1], H[2 * i], 0x05040100u);

@@ -475,8 +475,11 @@ __global__ void __launch_bounds__(WG) k_init_tables(CodecTables* out) {
   build_tables((gp<CodecTables>)out, thr, threadIdx.x, blockDim.x);
 }
 
+// ECC8: three waves per SIMD (at most 168 VGPRs), the occupancy the stream
+// needs.  ECC16 holds more registers; forcing three waves there spills, and
+// two waves without spills run faster.
 template <int WFMT, int ECC, int CODEC, bool L2>
-__global__ void __launch_bounds__(WG) k_fused_adamw(const TensorDesc* __restrict__ tab, int count,
+__global__ void __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(ECC == 8 ? 3 : 1))) k_fused_adamw(const TensorDesc* __restrict__ tab, int count,
                                                     int64_t total_tiles, const CodecTables* __restrict__ gtabs,
                                                     AdamWConsts c) {
   __shared__ CodecTables tabs;
