@@ -12,6 +12,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <functional>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -202,6 +203,10 @@ int record_use(TableEntry* e, hipStream_t stream) {
 // ---------------------------------------------------------------------------
 struct ArraySpec { const void* p; size_t elem_bytes; bool per_block; const char* name; };
 
+// Element counts above 2^56 cannot describe device memory; rejecting them
+// keeps every byte-range computation below within int64 / uintptr_t.
+constexpr int64_t kMaxElems = int64_t(1) << 56;
+
 int build_descs(int ntens, const std::vector<std::vector<ArraySpec>>& arrays, const std::vector<int64_t>& ns,
                 std::vector<TensorDesc>* descs, int64_t* total_tiles) {
   std::vector<Range> ranges;
@@ -209,7 +214,7 @@ int build_descs(int ntens, const std::vector<std::vector<ArraySpec>>& arrays, co
   int64_t tiles = 0;
   for (int i = 0; i < ntens; ++i) {
     const int64_t n = ns[i];
-    if (n < 0) return fail(FO_EINVAL, "tensor %d: n < 0", i);
+    if (n < 0 || n > kMaxElems) return fail(FO_EINVAL, "tensor %d: n out of range (%lld)", i, (long long)n);
     if (n == 0) continue;
     const int64_t nb = (n + 31) / 32;
     uint64_t ptr[7] = {0, 0, 0, 0, 0, 0, 0};
@@ -278,7 +283,7 @@ int fo_split_weights(const float* w32, int64_t n, int wfmt, int ecc_bits, void* 
                      void* stream) {
   g_err.clear();
   if (!fmt_ok(wfmt, ecc_bits)) return fail(FO_EINVAL, "unsupported format/ECC combination (%d, %d)", wfmt, ecc_bits);
-  if (n < 0) return fail(FO_EINVAL, "n < 0");
+  if (n < 0 || n > kMaxElems) return fail(FO_EINVAL, "n out of range (%lld)", (long long)n);
   if (n == 0) return FO_OK;
   if (!w32 || !w16_out || !ecc_out) return fail(FO_EINVAL, "NULL pointer");
   if (!aligned(w32, 16) || !aligned(w16_out, 16) || !aligned(ecc_out, 16)) return fail(FO_EINVAL, "pointer not 16-byte aligned");
@@ -300,7 +305,7 @@ int fo_reconstruct_weights(const void* w16, const void* ecc, int64_t n, int wfmt
                            void* stream) {
   g_err.clear();
   if (!fmt_ok(wfmt, ecc_bits)) return fail(FO_EINVAL, "unsupported format/ECC combination (%d, %d)", wfmt, ecc_bits);
-  if (n < 0) return fail(FO_EINVAL, "n < 0");
+  if (n < 0 || n > kMaxElems) return fail(FO_EINVAL, "n out of range (%lld)", (long long)n);
   if (n == 0) return FO_OK;
   if (!w16 || !ecc || !w32_out) return fail(FO_EINVAL, "NULL pointer");
   if (!aligned(w16, 16) || !aligned(ecc, 16) || !aligned(w32_out, 16)) return fail(FO_EINVAL, "pointer not 16-byte aligned");
@@ -323,7 +328,7 @@ int fo_companded_quantize(const float* x, int64_t n, int kind, int codec, void* 
   g_err.clear();
   if (kind != FO_MOMENTUM && kind != FO_VARIANCE) return fail(FO_EINVAL, "bad kind %d", kind);
   if (codec != FO_COMPANDED && codec != FO_LINEAR) return fail(FO_EINVAL, "bad codec %d", codec);
-  if (n < 0) return fail(FO_EINVAL, "n < 0");
+  if (n < 0 || n > kMaxElems) return fail(FO_EINVAL, "n out of range (%lld)", (long long)n);
   if (n == 0) return FO_OK;
   if (!x || !codes_out || !scales_out) return fail(FO_EINVAL, "NULL pointer");
   if (!aligned(x, 16) || !aligned(codes_out, 16) || !aligned(scales_out, 2)) return fail(FO_EINVAL, "misaligned pointer");
@@ -348,7 +353,7 @@ int fo_dequantize(const void* codes, const uint16_t* scales, int64_t n, int kind
   g_err.clear();
   if (kind != FO_MOMENTUM && kind != FO_VARIANCE) return fail(FO_EINVAL, "bad kind %d", kind);
   if (codec != FO_COMPANDED && codec != FO_LINEAR) return fail(FO_EINVAL, "bad codec %d", codec);
-  if (n < 0) return fail(FO_EINVAL, "n < 0");
+  if (n < 0 || n > kMaxElems) return fail(FO_EINVAL, "n out of range (%lld)", (long long)n);
   if (n == 0) return FO_OK;
   if (!codes || !scales || !x_out) return fail(FO_EINVAL, "NULL pointer");
   if (!aligned(codes, 16) || !aligned(scales, 2) || !aligned(x_out, 16)) return fail(FO_EINVAL, "misaligned pointer");
@@ -369,6 +374,32 @@ int fo_dequantize(const void* codes, const uint16_t* scales, int64_t n, int kind
   return launch_check("k_dequantize launch");
 }
 
+// Device table of a tensor list.  The cache is consulted first: an identical
+// list was validated when it was stored.  On a miss the list is validated
+// before any device error is returned, so argument errors are reported even
+// where no device is usable.  `fill` describes each tensor's arrays.  The
+// caller holds g_tab_mu; the entry stays the caller's until its use is
+// recorded.
+using FillArrays = std::function<void(std::vector<std::vector<ArraySpec>>&, std::vector<int64_t>&)>;
+static int list_table(const std::vector<uint8_t>& key, int32_t count, const FillArrays& fill, hipStream_t stream,
+                      TableEntry** entry) {
+  int dev = -1;
+  const int dev_rc = current_device(&dev);
+  if (dev_rc == FO_OK)
+    for (auto& e : g_tab)
+      if (e.dev == dev && e.key == key) { e.stamp = ++g_stamp; *entry = &e; return FO_OK; }
+  std::vector<std::vector<ArraySpec>> arrays(count);
+  std::vector<int64_t> ns(count);
+  fill(arrays, ns);
+  std::vector<TensorDesc> descs;
+  int64_t tiles = 0;
+  const int rc = build_descs(count, arrays, ns, &descs, &tiles);
+  if (rc) return rc;
+  if (tiles == 0) { *entry = nullptr; g_err.clear(); return FO_OK; }   // only empty tensors: nothing to do
+  if (dev_rc) return dev_rc;                  // its message is still the current one
+  return get_table(dev, key, descs, tiles, stream, entry);
+}
+
 static int adamw_like_table(const fo_adamw_tensor* list, int32_t count, int wfmt, int ecc_bits, uint8_t tag,
                             hipStream_t stream, TableEntry** entry) {
   std::vector<uint8_t> key(1 + sizeof(int32_t) * 2 + (size_t)count * sizeof(fo_adamw_tensor));
@@ -376,27 +407,16 @@ static int adamw_like_table(const fo_adamw_tensor* list, int32_t count, int wfmt
   std::memcpy(&key[1], &wfmt, 4);
   std::memcpy(&key[5], &ecc_bits, 4);
   if (count) std::memcpy(&key[9], list, (size_t)count * sizeof(fo_adamw_tensor));
-  int dev;
-  int rc = current_device(&dev);
-  if (rc) return rc;
-  // caller holds g_tab_mu
-  for (auto& e : g_tab)
-    if (e.dev == dev && e.key == key) { e.stamp = ++g_stamp; *entry = &e; return FO_OK; }
-  std::vector<std::vector<ArraySpec>> arrays(count);
-  std::vector<int64_t> ns(count);
   const size_t eb = (size_t)ecc_bits / 8;
-  for (int i = 0; i < count; ++i) {
-    const fo_adamw_tensor& t = list[i];
-    ns[i] = t.n;
-    arrays[i] = {{t.w16, 2, false, "w16"}, {t.ecc, eb, false, "ecc"}, {t.grad, 2, false, "grad"},
-                 {t.m_q, 1, false, "m_q"}, {t.m_s, 2, true, "m_s"}, {t.v_q, 1, false, "v_q"},
-                 {t.v_s, 2, true, "v_s"}};
-  }
-  std::vector<TensorDesc> descs;
-  int64_t tiles = 0;
-  rc = build_descs(count, arrays, ns, &descs, &tiles);
-  if (rc) return rc;
-  return get_table(dev, key, descs, tiles, stream, entry);
+  return list_table(key, count, [&](std::vector<std::vector<ArraySpec>>& arrays, std::vector<int64_t>& ns) {
+    for (int i = 0; i < count; ++i) {
+      const fo_adamw_tensor& t = list[i];
+      ns[i] = t.n;
+      arrays[i] = {{t.w16, 2, false, "w16"}, {t.ecc, eb, false, "ecc"}, {t.grad, 2, false, "grad"},
+                   {t.m_q, 1, false, "m_q"}, {t.m_s, 2, true, "m_s"}, {t.v_q, 1, false, "v_q"},
+                   {t.v_s, 2, true, "v_s"}};
+    }
+  }, stream, entry);
 }
 
 int fo_fused_adamw_step(const fo_adamw_tensor* list, int32_t count, const fo_adamw_hparams* hp, void* stream) {
@@ -418,7 +438,7 @@ int fo_fused_adamw_step(const fo_adamw_tensor* list, int32_t count, const fo_ada
   TableEntry* e = nullptr;
   int rc = adamw_like_table(list, count, hp->wfmt, hp->ecc_bits, 'A', s, &e);
   if (rc) return rc;
-  if (e->total_tiles == 0) return FO_OK;
+  if (!e || e->total_tiles == 0) return FO_OK;
   // per-step float32 constants: double arithmetic, one rounding each
   const double t = (double)hp->step;
   AdamWConsts c;
@@ -457,7 +477,7 @@ int fo_stream_probe(const fo_adamw_tensor* list, int32_t count, int32_t wfmt, in
   TableEntry* e = nullptr;
   int rc = adamw_like_table(list, count, wfmt, ecc_bits, 'A', s, &e);
   if (rc) return rc;
-  if (e->total_tiles == 0) return FO_OK;
+  if (!e || e->total_tiles == 0) return FO_OK;
   void (*kern)(const TensorDesc*, int, int64_t, uint32_t) = (ecc_bits == 8) ? k_stream_probe<8> : k_stream_probe<16>;
   int grid;
   if ((rc = tile_grid(e->total_tiles, &grid))) return rc;
@@ -488,33 +508,19 @@ int fo_fused_sgdm_step(const fo_sgdm_tensor* list, int32_t count, const fo_sgdm_
   std::memcpy(&key[1], &hp->wfmt, 4);
   std::memcpy(&key[5], &hp->ecc_bits, 4);
   std::memcpy(&key[9], list, (size_t)count * sizeof(fo_sgdm_tensor));
-  int dev;
-  int rc = current_device(&dev);
-  if (rc) return rc;
   TableEntry* e = nullptr;
   std::lock_guard<std::mutex> lk(g_tab_mu);
-  {
-    for (auto& x : g_tab)
-      if (x.dev == dev && x.key == key) { x.stamp = ++g_stamp; e = &x; break; }
-    if (!e) {
-      std::vector<std::vector<ArraySpec>> arrays(count);
-      std::vector<int64_t> ns(count);
-      const size_t eb = (size_t)hp->ecc_bits / 8;
-      for (int i = 0; i < count; ++i) {
-        const fo_sgdm_tensor& t = list[i];
-        ns[i] = t.n;
-        arrays[i] = {{t.w16, 2, false, "w16"}, {t.ecc, eb, false, "ecc"}, {t.grad, 2, false, "grad"},
-                     {t.b_q, 1, false, "b_q"}, {t.b_s, 2, true, "b_s"}};
-      }
-      std::vector<TensorDesc> descs;
-      int64_t tiles = 0;
-      rc = build_descs(count, arrays, ns, &descs, &tiles);
-      if (rc) return rc;
-      rc = get_table(dev, key, descs, tiles, s, &e);
-      if (rc) return rc;
+  const size_t eb = (size_t)hp->ecc_bits / 8;
+  int rc = list_table(key, count, [&](std::vector<std::vector<ArraySpec>>& arrays, std::vector<int64_t>& ns) {
+    for (int i = 0; i < count; ++i) {
+      const fo_sgdm_tensor& t = list[i];
+      ns[i] = t.n;
+      arrays[i] = {{t.w16, 2, false, "w16"}, {t.ecc, eb, false, "ecc"}, {t.grad, 2, false, "grad"},
+                   {t.b_q, 1, false, "b_q"}, {t.b_s, 2, true, "b_s"}};
     }
-  }
-  if (e->total_tiles == 0) return FO_OK;
+  }, s, &e);
+  if (rc) return rc;
+  if (!e || e->total_tiles == 0) return FO_OK;
   SGDMConsts c;
   c.lr = (float)hp->lr;
   c.mu = (float)hp->momentum;
@@ -526,7 +532,7 @@ int fo_fused_sgdm_step(const fo_sgdm_tensor* list, int32_t count, const fo_sgdm_
   FO_SELECT3(k_fused_sgdm, hp->wfmt, hp->ecc_bits, hp->codec, kern);
   int grid;
   const CodecTables* tb = nullptr;
-  if ((rc = tile_grid(e->total_tiles, &grid)) || (rc = device_tables(dev, s, &tb))) return rc;
+  if ((rc = tile_grid(e->total_tiles, &grid)) || (rc = device_tables(e->dev, s, &tb))) return rc;
   hipLaunchKernelGGL(kern, grid, WG, 0, s, (const TensorDesc*)e->dptr, e->count, e->total_tiles, tb, c);
   rc = launch_check("k_fused_sgdm launch");
   if (rc) return rc;
