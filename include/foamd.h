@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define FO_ABI_VERSION 1
+#define FO_ABI_VERSION 2   /* 2: l2_decay in fo_adamw_hparams; dampening, nesterov in fo_sgdm_hparams */
 
 enum fo_status {
   FO_OK = 0,

@@ -60,6 +60,7 @@ class SGDMHParams(ctypes.Structure):
 
 
 _lib = None
+ABI_VERSION = 2          # FO_ABI_VERSION of include/foamd.h (struct layouts below)
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -85,6 +86,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fo_last_error.restype = ctypes.c_char_p
     lib.fo_last_error.argtypes = []
     lib.fo_abi_version.argtypes = []
+    if lib.fo_abi_version() != ABI_VERSION:
+        raise ImportError(f"{path} implements C ABI version {lib.fo_abi_version()}, this binding needs "
+                          f"{ABI_VERSION}: rebuild it with __graft_entry__.build()")
     _lib = lib
     return lib
 

@@ -183,3 +183,31 @@ def test_torch_state_import_export_round_trip():
     q, sc = O.quantize_state(buf.cpu().numpy().ravel(), "m", "companded")
     assert np.array_equal(sgd.export_torch_state(p).cpu().numpy().ravel().view(np.uint32),
                           O.dequantize_state(q, sc, "m", "companded").view(np.uint32))
+
+
+def test_param_groups_use_their_own_hyperparameters():
+    """Weights and biases in separate groups (different lr, decay only on
+    weights), as training scripts set them up: each group matches the oracle
+    with its own hyperparameters at every step."""
+    model = _model(6)
+    params = list(model.parameters())
+    x0 = [p.detach().float().cpu().numpy().ravel().copy() for p in params]
+    groups = [{"params": [p for p in params if p.dim() > 1], "lr": 2e-3, "weight_decay": 0.1},
+              {"params": [p for p in params if p.dim() == 1], "lr": 5e-3, "weight_decay": 0.0}]
+    opt = FlashAdamW(groups, betas=(0.9, 0.95), eps=1e-8)
+    hp_of = {id(p): g for g in opt.param_groups for p in g["params"]}
+    refs = [fresh_adamw_state(x) for x in x0]
+    for step in range(1, 4):
+        opt.zero_grad(set_to_none=True)
+        _loss(model, step).backward()
+        grads = [to_host(p.grad.view(-1)) for p in params]
+        opt.step()
+        for i, p in enumerate(params):
+            g = hp_of[id(p)]
+            hp = dict(lr=g["lr"], beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=g["weight_decay"], step=step)
+            refs[i] = O.adamw_step(refs[i], grads[i], hp)
+            st = opt.state[p]
+            got = {"w16": to_host(p.data.view(-1)), "ecc": to_host(st["ecc"].view(-1)),
+                   "m_q": to_host(st["m_q"]), "v_q": to_host(st["v_q"]),
+                   "m_s": to_host(st["m_s"]).view(np.uint16), "v_s": to_host(st["v_s"]).view(np.uint16)}
+            assert sum(check_adamw_state(f"group step {step} param {i}", got, refs[i]).values()) == 0
