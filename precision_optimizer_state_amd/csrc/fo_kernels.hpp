@@ -37,7 +37,11 @@ constexpr int WG = WAVE * WAVES_PER_WG;    // 256 threads
 // sub-tile per lane of a quad: 4 sub-tiles, 64 blocks, 64 lanes.
 static_assert(NSUB == 4 && TILE / 32 == WAVE, "one owned block per lane");
 
-// Device copy of one tensor of a step (built by the host launcher).
+// Device copy of one tensor of a step (built by the host launcher).  The
+// launch table is the non-empty tensors' descriptors, a sentinel (tile_begin =
+// total tiles, n = the bucket shift) and an int32 tile-bucket index: entry b
+// is the tensor holding tile b << shift.
+constexpr int TILE_BUCKET_SHIFT_MIN = 8;
 struct alignas(16) TensorDesc {
   uint64_t w16, ecc, grad, q1, s1, q2, s2;  // q2/s2 unused by SGD-M
   int64_t n;
@@ -432,7 +436,11 @@ __device__ __forceinline__ void probe_tile(const TensorDesc& d, int64_t e0, int 
 // multi-tensor kernels
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int find_tensor(const TensorDesc* __restrict__ tab, int count, int64_t T) {
-  int lo = 0, hi = count - 1;              // largest t with tile_begin <= T
+  // the tensor of tile T lies between the entries of T's bucket and the next
+  const int shift = (int)tab[count].n;
+  const int32_t* bk = reinterpret_cast<const int32_t*>(tab + count + 1);
+  const int64_t b = T >> shift;
+  int lo = bk[b], hi = bk[b + 1];          // largest t in [lo, hi] with tile_begin <= T
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
     if (tab[mid].tile_begin <= T) lo = mid; else hi = mid - 1;
@@ -441,8 +449,9 @@ __device__ __forceinline__ int find_tensor(const TensorDesc* __restrict__ tab, i
 }
 
 // Waves stride over the global wave-tile list of the step (one tile per wave
-// with the default flat grid).  The tensor of a tile is found by binary search
-// over the descriptors' first-tile indices when a wave leaves its tensor.
+// with the default flat grid).  When a wave leaves its tensor, the tensor of
+// its tile is found through the tile-bucket index (a short binary search over
+// the first-tile indices of one bucket's tensors).
 template <typename F>
 __device__ __forceinline__ void tile_loop(const TensorDesc* __restrict__ tab, int count, int64_t total_tiles, F&& body) {
   const int lane = threadIdx.x & (WAVE - 1);
@@ -456,6 +465,7 @@ __device__ __forceinline__ void tile_loop(const TensorDesc* __restrict__ tab, in
       t_begin = tab[t].tile_begin;
       t_end = tab[t + 1].tile_begin;
     }
+    if (T < t_begin) continue;              // cannot happen with a well-formed table
     const TensorDesc d = tab[t];
     body(d, (T - t_begin) * TILE, lane);
   }

@@ -119,7 +119,7 @@ struct TableEntry {
   std::vector<uint8_t> key;
   TensorDesc* dptr = nullptr;
   TensorDesc* hptr = nullptr;   // pinned staging copy
-  size_t cap = 0;               // entries
+  size_t cap = 0;               // bytes
   hipEvent_t ev = nullptr;      // last stream-ordered use of dptr/hptr
   bool ev_recorded = false;
   uint64_t stamp = 0;
@@ -145,7 +145,7 @@ int check_alias(std::vector<Range>& r) {
 // Build (or fetch) the device table for `descs` (already validated, n > 0 only).
 // On success *entry_out is locked by the caller's mutex scope.
 int get_table(int dev, const std::vector<uint8_t>& key, const std::vector<TensorDesc>& descs,
-              int64_t total_tiles, hipStream_t stream, TableEntry** out) {
+              const std::vector<int32_t>& buckets, int64_t total_tiles, hipStream_t stream, TableEntry** out) {
   for (auto& e : g_tab) {
     if (e.dev == dev && e.key == key) {
       e.stamp = ++g_stamp;
@@ -163,28 +163,31 @@ int get_table(int dev, const std::vector<uint8_t>& key, const std::vector<Tensor
     if (he != hipSuccess) return hip_fail(he, "hipEventSynchronize");
     e.ev_recorded = false;
   }
-  const size_t need = descs.size();
+  // device layout: descriptors (with the sentinel), then the tile-bucket index
+  const size_t desc_bytes = descs.size() * sizeof(TensorDesc);
+  const size_t need = desc_bytes + buckets.size() * sizeof(int32_t);
   if (e.dev != dev || e.cap < need) {
     if (e.dptr) { (void)hipFree(e.dptr); e.dptr = nullptr; }
     if (e.hptr) { (void)hipHostFree(e.hptr); e.hptr = nullptr; }
     if (e.ev) { (void)hipEventDestroy(e.ev); e.ev = nullptr; }
     e.cap = 0;
     e.dev = -1;
-    const size_t cap = std::max<size_t>(need, 64);
-    he = hipMalloc((void**)&e.dptr, cap * sizeof(TensorDesc));
+    const size_t cap = std::max<size_t>(need, 64 * sizeof(TensorDesc));
+    he = hipMalloc((void**)&e.dptr, cap);
     if (he != hipSuccess) { e.dptr = nullptr; return fail(FO_ENOMEM, "hipMalloc(launch table): %s", hipGetErrorString(he)); }
-    he = hipHostMalloc((void**)&e.hptr, cap * sizeof(TensorDesc), hipHostMallocDefault);
+    he = hipHostMalloc((void**)&e.hptr, cap, hipHostMallocDefault);
     if (he != hipSuccess) { e.hptr = nullptr; return fail(FO_ENOMEM, "hipHostMalloc(launch table): %s", hipGetErrorString(he)); }
     he = hipEventCreateWithFlags(&e.ev, hipEventDisableTiming);
     if (he != hipSuccess) { e.ev = nullptr; return hip_fail(he, "hipEventCreate"); }
     e.cap = cap;
     e.dev = dev;
   }
-  std::memcpy(e.hptr, descs.data(), need * sizeof(TensorDesc));
-  he = hipMemcpyAsync(e.dptr, e.hptr, need * sizeof(TensorDesc), hipMemcpyHostToDevice, stream);
+  std::memcpy(e.hptr, descs.data(), desc_bytes);
+  std::memcpy(reinterpret_cast<uint8_t*>(e.hptr) + desc_bytes, buckets.data(), buckets.size() * sizeof(int32_t));
+  he = hipMemcpyAsync(e.dptr, e.hptr, need, hipMemcpyHostToDevice, stream);
   if (he != hipSuccess) { e.key.clear(); return hip_fail(he, "hipMemcpyAsync(launch table)"); }
   e.key = key;
-  e.count = (int)need - 1;
+  e.count = (int)descs.size() - 1;
   e.total_tiles = total_tiles;
   e.stamp = ++g_stamp;
   *out = &e;
@@ -208,7 +211,7 @@ struct ArraySpec { const void* p; size_t elem_bytes; bool per_block; const char*
 constexpr int64_t kMaxElems = int64_t(1) << 56;
 
 int build_descs(int ntens, const std::vector<std::vector<ArraySpec>>& arrays, const std::vector<int64_t>& ns,
-                std::vector<TensorDesc>* descs, int64_t* total_tiles) {
+                std::vector<TensorDesc>* descs, std::vector<int32_t>* buckets, int64_t* total_tiles) {
   std::vector<Range> ranges;
   descs->clear();
   int64_t tiles = 0;
@@ -236,9 +239,27 @@ int build_descs(int ntens, const std::vector<std::vector<ArraySpec>>& arrays, co
   }
   int rc = check_alias(ranges);
   if (rc) return rc;
+  // Tile-bucket index: bucket b (tiles [b << shift, (b + 1) << shift)) records
+  // the tensor holding its first tile, so a wave searches only between two
+  // adjacent entries.  At most 65536 buckets; the shift rides in the sentinel.
+  int shift = TILE_BUCKET_SHIFT_MIN;
+  while ((tiles >> shift) > 65535) ++shift;
+  buckets->clear();
+  if (tiles > 0) {
+    const int64_t nbk = (tiles >> shift) + 1;
+    buckets->resize((size_t)nbk + 1);
+    int t = 0;
+    const int ndesc = (int)descs->size();
+    for (int64_t b = 0; b <= nbk; ++b) {
+      const int64_t first = std::min<int64_t>(b << shift, tiles - 1);
+      while (t + 1 < ndesc && (*descs)[t + 1].tile_begin <= first) ++t;
+      (*buckets)[(size_t)b] = t;
+    }
+  }
   TensorDesc sentinel;
   std::memset(&sentinel, 0, sizeof(sentinel));
   sentinel.tile_begin = tiles;
+  sentinel.n = shift;
   descs->push_back(sentinel);
   *total_tiles = tiles;
   return FO_OK;
@@ -392,12 +413,13 @@ static int list_table(const std::vector<uint8_t>& key, int32_t count, const Fill
   std::vector<int64_t> ns(count);
   fill(arrays, ns);
   std::vector<TensorDesc> descs;
+  std::vector<int32_t> buckets;
   int64_t tiles = 0;
-  const int rc = build_descs(count, arrays, ns, &descs, &tiles);
+  const int rc = build_descs(count, arrays, ns, &descs, &buckets, &tiles);
   if (rc) return rc;
   if (tiles == 0) { *entry = nullptr; g_err.clear(); return FO_OK; }   // only empty tensors: nothing to do
   if (dev_rc) return dev_rc;                  // its message is still the current one
-  return get_table(dev, key, descs, tiles, stream, entry);
+  return get_table(dev, key, descs, buckets, tiles, stream, entry);
 }
 
 static int adamw_like_table(const fo_adamw_tensor* list, int32_t count, int wfmt, int ecc_bits, uint8_t tag,
