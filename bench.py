@@ -323,6 +323,8 @@ def main(argv=None):
         },
         "kernel_ms_avg": avg_ms,
         "stream_probe_gbs": probe_gbs,
+        # the fused kernel against the same byte streams moved with no arithmetic
+        "vs_stream_probe": (achieved / probe_gbs) if probe_gbs else None,
         "kernel_src_sha": kernel_source_hash(),
     }
     if not args.no_cpu_baseline:
