@@ -219,6 +219,51 @@ def test_fused_adamw_nan_inf_grads_propagate():
     _run_adamw([8192 + 5], 2, HP_C1, tag="nan", inject=inject)
 
 
+@pytest.mark.parametrize("name,hp", [
+    ("beta1_0", dict(lr=1e-3, beta1=0.0, beta2=0.5, eps=1e-8, weight_decay=0.01)),
+    ("lr_0", dict(lr=0.0, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1)),
+    ("large_lr_no_decay", dict(lr=0.5, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.0)),
+    ("tiny_eps", dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-30, weight_decay=0.01)),
+    ("eps_below_normal", dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-40, weight_decay=0.01)),
+])
+def test_fused_adamw_degenerate_hyperparameters(name, hp):
+    """Hyperparameters at the edges of their ranges take the same path through
+    the oracle and the kernel (eps below the smallest normal switches the
+    kernel to its IEEE reciprocal)."""
+    bad = _run_adamw([20000, 33], 3, hp, tag=f"hp_{name}")
+    print(f"degenerate hp {name}: {bad} mismatching elements", flush=True)
+
+
+def test_fused_adamw_late_step_and_zero_eps():
+    """Bias correction near 1 at step 10^6, and eps = 0, where blocks whose
+    variance decodes to zero divide by zero: NaN and Inf must appear at the
+    same elements on both sides (NaN payloads are compared as NaN)."""
+    sizes = [4096 + 7]
+    xs = [host_weights("late", 0, sizes[0])]
+    for hp, step0 in ((dict(HP_C1), 10 ** 6), (dict(HP_C1, eps=0.0), 1)):
+        dev = [alloc_adamw_state(n) for n in sizes]
+        ref = [fresh_adamw_state(x) for x in xs]
+        B.fo_split_weights(torch.from_numpy(xs[0]).cuda(), dev[0]["w16"], dev[0]["ecc"], "bf16", 8)
+        tl = B.AdamWList(dev)
+        for step in range(step0, step0 + 3):
+            g = host_grads("late", 0, step, sizes[0], "t3")
+            g[:64] = 0.0                                    # whole zero blocks: v stays 0
+            gb = host_grad_bits(g, "bf16")
+            dev[0]["grad"].copy_(to_dev(gb, DT["bf16"]))
+            B.fo_fused_adamw_step(tl, B.adamw_hparams(step=step, **hp))
+            ref[0] = O.adamw_step(ref[0], gb, dict(hp, step=step))
+        torch.cuda.synchronize()
+        got = adamw_state_to_host(dev[0])
+        r_ref = O.reconstruct_weights(ref[0]["w16"], ref[0]["ecc"])
+        r_got = O.reconstruct_weights(got["w16"], got["ecc"])
+        nan = np.isnan(r_ref)
+        assert np.array_equal(nan, np.isnan(r_got))
+        got["w16"] = np.where(nan, ref[0]["w16"], got["w16"])
+        bad = check_adamw_state(f"step0={step0} eps={hp['eps']}", got, ref[0])
+        print(f"late/zero-eps case step0={step0} eps={hp['eps']}: {sum(bad.values())} mismatches, "
+              f"{int(nan.sum())} NaN weights", flush=True)
+
+
 def _run_sgdm(sizes, steps, hp, fmt="bf16", ecc_bits=8, codec="companded", tag="s"):
     xs = [host_weights(tag, i, n) for i, n in enumerate(sizes)]
     dev = [alloc_sgdm_state(n, fmt, ecc_bits) for n in sizes]
@@ -270,6 +315,16 @@ def test_fused_adam_l2_decay_matches_oracle(fmt, ecc_bits, codec):
     hp = dict(HP_C1, weight_decay=0.05, l2_decay=True)
     bad = _run_adamw(sizes, 4, hp, fmt, ecc_bits, codec, tag=f"adam_l2_{fmt}{ecc_bits}{codec}")
     print(f"Adam (L2) {fmt}+{ecc_bits}/{codec}: {bad} mismatching elements", flush=True)
+
+
+@pytest.mark.parametrize("name,hp", [
+    ("momentum_0", dict(lr=0.1, momentum=0.0, weight_decay=1e-4)),
+    ("lr_0", dict(lr=0.0, momentum=0.9, weight_decay=1e-4)),
+    ("no_decay", dict(lr=0.1, momentum=0.99, weight_decay=0.0)),
+])
+def test_fused_sgd_degenerate_hyperparameters(name, hp):
+    bad = _run_sgdm([20000, 33], 3, hp, tag=f"sgd_hp_{name}")
+    print(f"sgd degenerate hp {name}: {bad} mismatching elements", flush=True)
 
 
 def test_gradient_release_chunks_equal_whole_tensor():
