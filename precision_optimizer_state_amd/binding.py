@@ -158,9 +158,21 @@ class AdamWList:
             arr[i] = AdamWTensor(_ptr(t["w16"]), _ptr(t["ecc"]), _ptr(t["grad"]), _ptr(t["m_q"]),
                                  _ptr(t["m_s"]), _ptr(t["v_q"]), _ptr(t["v_s"]), t["w16"].numel())
         self.array = arr
+        self.count = len(self.tensors)
+
+    @classmethod
+    def from_rows(cls, rows):
+        """A list from raw rows (w16, ecc, grad, m_q, m_s, v_q, v_s, n) of device
+        addresses and sizes.  It keeps no tensor alive: the caller guarantees
+        the memory outlives every call that uses the list."""
+        self = cls.__new__(cls)
+        self.tensors = ()
+        self.array = (AdamWTensor * max(1, len(rows)))(*[AdamWTensor(*r) for r in rows])
+        self.count = len(rows)
+        return self
 
     def __len__(self):
-        return len(self.tensors)
+        return self.count
 
 
 class SGDMList:
@@ -171,9 +183,19 @@ class SGDMList:
             arr[i] = SGDMTensor(_ptr(t["w16"]), _ptr(t["ecc"]), _ptr(t["grad"]), _ptr(t["b_q"]),
                                 _ptr(t["b_s"]), t["w16"].numel())
         self.array = arr
+        self.count = len(self.tensors)
+
+    @classmethod
+    def from_rows(cls, rows):
+        """As AdamWList.from_rows with rows (w16, ecc, grad, b_q, b_s, n)."""
+        self = cls.__new__(cls)
+        self.tensors = ()
+        self.array = (SGDMTensor * max(1, len(rows)))(*[SGDMTensor(*r) for r in rows])
+        self.count = len(rows)
+        return self
 
     def __len__(self):
-        return len(self.tensors)
+        return self.count
 
 
 def adamw_hparams(lr, beta1, beta2, eps, weight_decay, step, wfmt="bf16", ecc_bits=8, codec="companded",

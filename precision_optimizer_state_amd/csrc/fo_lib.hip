@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <cstring>
 #include <functional>
+#include <unordered_map>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -127,10 +128,30 @@ struct TableEntry {
   int64_t total_tiles = 0;
 };
 
-constexpr size_t kCacheEntries = 64;
+// Enough slots for one list per parameter of a large model (gradient release
+// steps every parameter separately), so per-parameter lists do not evict each
+// other; the index makes a lookup O(1) in the number of slots.
+constexpr size_t kCacheEntries = 1024;
 std::mutex g_tab_mu;
 std::vector<TableEntry> g_tab(kCacheEntries);
+std::unordered_map<std::string, size_t> g_index;   // (device, key) -> slot
 uint64_t g_stamp = 0;
+
+std::string index_key(int dev, const std::vector<uint8_t>& key) {
+  std::string k(sizeof(int) + key.size(), '\0');
+  std::memcpy(&k[0], &dev, sizeof(int));
+  if (!key.empty()) std::memcpy(&k[sizeof(int)], key.data(), key.size());
+  return k;
+}
+
+// caller holds g_tab_mu
+TableEntry* find_entry(int dev, const std::vector<uint8_t>& key) {
+  auto it = g_index.find(index_key(dev, key));
+  if (it == g_index.end()) return nullptr;
+  TableEntry& e = g_tab[it->second];
+  e.stamp = ++g_stamp;
+  return &e;
+}
 
 struct Range { uintptr_t lo, hi; };
 
@@ -146,17 +167,13 @@ int check_alias(std::vector<Range>& r) {
 // On success *entry_out is locked by the caller's mutex scope.
 int get_table(int dev, const std::vector<uint8_t>& key, const std::vector<TensorDesc>& descs,
               const std::vector<int32_t>& buckets, int64_t total_tiles, hipStream_t stream, TableEntry** out) {
-  for (auto& e : g_tab) {
-    if (e.dev == dev && e.key == key) {
-      e.stamp = ++g_stamp;
-      *out = &e;
-      return FO_OK;
-    }
-  }
+  if ((*out = find_entry(dev, key))) return FO_OK;
   // miss: evict the least recently used entry of the cache
-  TableEntry* victim = &g_tab[0];
-  for (auto& e : g_tab) if (e.stamp < victim->stamp) victim = &e;
-  TableEntry& e = *victim;
+  size_t vi = 0;
+  for (size_t i = 1; i < g_tab.size(); ++i) if (g_tab[i].stamp < g_tab[vi].stamp) vi = i;
+  TableEntry& e = g_tab[vi];
+  if (!e.key.empty()) g_index.erase(index_key(e.dev, e.key));
+  e.key.clear();
   hipError_t he;
   if (e.ev_recorded) {
     he = hipEventSynchronize(e.ev);           // previous users of this slot are done
@@ -186,7 +203,13 @@ int get_table(int dev, const std::vector<uint8_t>& key, const std::vector<Tensor
   std::memcpy(reinterpret_cast<uint8_t*>(e.hptr) + desc_bytes, buckets.data(), buckets.size() * sizeof(int32_t));
   he = hipMemcpyAsync(e.dptr, e.hptr, need, hipMemcpyHostToDevice, stream);
   if (he != hipSuccess) { e.key.clear(); return hip_fail(he, "hipMemcpyAsync(launch table)"); }
+  // the staging copy is in flight: mark the slot used now, so that a later
+  // eviction waits for it even if the launch that follows fails
+  he = hipEventRecord(e.ev, stream);
+  if (he != hipSuccess) { e.key.clear(); return hip_fail(he, "hipEventRecord(launch table)"); }
+  e.ev_recorded = true;
   e.key = key;
+  g_index[index_key(dev, key)] = vi;
   e.count = (int)descs.size() - 1;
   e.total_tiles = total_tiles;
   e.stamp = ++g_stamp;
@@ -406,9 +429,7 @@ static int list_table(const std::vector<uint8_t>& key, int32_t count, const Fill
                       TableEntry** entry) {
   int dev = -1;
   const int dev_rc = current_device(&dev);
-  if (dev_rc == FO_OK)
-    for (auto& e : g_tab)
-      if (e.dev == dev && e.key == key) { e.stamp = ++g_stamp; *entry = &e; return FO_OK; }
+  if (dev_rc == FO_OK && (*entry = find_entry(dev, key))) return FO_OK;
   std::vector<std::vector<ArraySpec>> arrays(count);
   std::vector<int64_t> ns(count);
   fill(arrays, ns);

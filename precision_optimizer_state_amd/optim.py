@@ -42,6 +42,10 @@ class _FlashBase(torch.optim.Optimizer):
         self.wfmt, self.ecc_bits, self.codec = wfmt, ecc_bits, codec
         self.grad_release = grad_release
         self._hooks = []
+        # marshalled launch lists keyed by their raw device addresses (ints
+        # only: nothing here keeps a gradient or a state tensor alive)
+        self._lists = {}
+        self._group_of = {}
         super().__init__(params, defaults)
         for group in self.param_groups:
             for p in group["params"]:
@@ -86,6 +90,9 @@ class _FlashBase(torch.optim.Optimizer):
     def _entry(self, p):
         raise NotImplementedError
 
+    def _row(self, p):
+        raise NotImplementedError
+
     def _launch(self, entries, group, step):
         raise NotImplementedError
 
@@ -97,9 +104,15 @@ class _FlashBase(torch.optim.Optimizer):
             st["step"] += 1
             by_step.setdefault(st["step"], []).append(p)
         for step, ps in by_step.items():
-            # a fresh marshalled list per call holds no reference to the
-            # gradients afterwards (the library caches device tables itself)
-            self._launch(self._make_list([self._entry(p) for p in ps]), group, step)
+            # rows of raw addresses: no tensor views, no reference kept; the
+            # ctypes array is rebuilt only when an address changes
+            rows = tuple(self._row(p) for p in ps)
+            tl = self._lists.get(rows)
+            if tl is None:
+                if len(self._lists) >= 4096:
+                    self._lists.clear()
+                tl = self._lists[rows] = self._list_from_rows(rows)
+            self._launch(tl, group, step)
 
     @torch.no_grad()
     def step(self, closure=None):
@@ -116,9 +129,18 @@ class _FlashBase(torch.optim.Optimizer):
                 self._step_params(group, ps)
         return loss
 
+    def _group(self, p):
+        # id -> (group, parameter); the stored parameter guards against a
+        # reused id, and a miss (e.g. after add_param_group) rebuilds the map
+        e = self._group_of.get(id(p))
+        if e is None or e[1] is not p:
+            self._group_of = {id(q): (grp, q) for grp in self.param_groups for q in grp["params"]}
+            e = self._group_of[id(p)]
+        return e[0]
+
     @torch.no_grad()
     def _release_hook(self, p):
-        group = next(g for g in self.param_groups if any(q is p for q in g["params"]))
+        group = self._group(p)
         if p.grad.dtype != p.dtype or not p.grad.is_contiguous():
             p.grad = p.grad.to(p.dtype).contiguous()
         self._step_params(group, [p])
@@ -132,6 +154,8 @@ class _FlashBase(torch.optim.Optimizer):
         raw = {k: {kk: vv for kk, vv in v.items() if torch.is_tensor(vv)}
                for k, v in state_dict["state"].items()}
         super().load_state_dict(state_dict)
+        self._lists.clear()
+        self._group_of = {}
         params = [p for g in self.param_groups for p in g["params"]]
         for pid, p in zip(saved_ids, params):
             for key, val in raw.get(pid, {}).items():
@@ -164,9 +188,18 @@ class FlashAdamW(_FlashBase):
         return {"w16": p.data.view(-1), "ecc": st["ecc"].view(-1), "grad": p.grad.view(-1),
                 "m_q": st["m_q"], "m_s": st["m_s"], "v_q": st["v_q"], "v_s": st["v_s"]}
 
+    def _row(self, p):
+        st = self.state[p]
+        return (p.data_ptr(), st["ecc"].data_ptr(), p.grad.data_ptr(), st["m_q"].data_ptr(), st["m_s"].data_ptr(),
+                st["v_q"].data_ptr(), st["v_s"].data_ptr(), p.numel())
+
     @staticmethod
     def _make_list(entries):
         return B.AdamWList(entries)
+
+    @staticmethod
+    def _list_from_rows(rows):
+        return B.AdamWList.from_rows(rows)
 
     _l2_decay = False
 
@@ -236,9 +269,18 @@ class FlashSGD(_FlashBase):
         return {"w16": p.data.view(-1), "ecc": st["ecc"].view(-1), "grad": p.grad.view(-1),
                 "b_q": st["b_q"], "b_s": st["b_s"]}
 
+    def _row(self, p):
+        st = self.state[p]
+        return (p.data_ptr(), st["ecc"].data_ptr(), p.grad.data_ptr(), st["b_q"].data_ptr(), st["b_s"].data_ptr(),
+                p.numel())
+
     @staticmethod
     def _make_list(entries):
         return B.SGDMList(entries)
+
+    @staticmethod
+    def _list_from_rows(rows):
+        return B.SGDMList.from_rows(rows)
 
     @torch.no_grad()
     def export_torch_state(self, p):
