@@ -448,18 +448,19 @@ __device__ __forceinline__ int find_tensor(const TensorDesc* __restrict__ tab, i
   return lo;
 }
 
-// Waves stride over the global wave-tile list of the step (one tile per wave
-// with the default flat grid).  When a wave leaves its tensor, the tensor of
+// Waves stride over the tiles [tile0, tile_end) of the step's global wave-tile
+// list (one tile per wave with the default flat grid).  When a wave leaves its tensor, the tensor of
 // its tile is found through the tile-bucket index (a short binary search over
 // the first-tile indices of one bucket's tensors).
 template <typename F>
-__device__ __forceinline__ void tile_loop(const TensorDesc* __restrict__ tab, int count, int64_t total_tiles, F&& body) {
+__device__ __forceinline__ void tile_loop(const TensorDesc* __restrict__ tab, int count, int64_t tile0,
+                                          int64_t tile_end, F&& body) {
   const int lane = threadIdx.x & (WAVE - 1);
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
   int t = 0;
   int64_t t_begin = 0, t_end = -1;
-  for (int64_t T = (int64_t)blockIdx.x * WAVES_PER_WG + wid; T < total_tiles; T += nwaves) {
+  for (int64_t T = tile0 + (int64_t)blockIdx.x * WAVES_PER_WG + wid; T < tile_end; T += nwaves) {
     if (T >= t_end) {
       t = find_tensor(tab, count, T);
       t_begin = tab[t].tile_begin;
@@ -490,11 +491,11 @@ __global__ void __launch_bounds__(WG) k_init_tables(CodecTables* out) {
 // two waves without spills run faster.
 template <int WFMT, int ECC, int CODEC, bool L2>
 __global__ void __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(ECC == 8 ? 3 : 1))) k_fused_adamw(const TensorDesc* __restrict__ tab, int count,
-                                                    int64_t total_tiles, const CodecTables* __restrict__ gtabs,
+                                                    int64_t tile0, int64_t tile_end, const CodecTables* __restrict__ gtabs,
                                                     AdamWConsts c) {
   __shared__ CodecTables tabs;
   load_tables(tabs, gtabs);
-  tile_loop(tab, count, total_tiles, [&](const TensorDesc& d, int64_t e0, int lane) {
+  tile_loop(tab, count, tile0, tile_end, [&](const TensorDesc& d, int64_t e0, int lane) {
     if (e0 + TILE <= d.n) adamw_tile<WFMT, ECC, CODEC, L2, true>(d, e0, lane, tabs, c);
     else adamw_tile<WFMT, ECC, CODEC, L2, false>(d, e0, lane, tabs, c);
   });
@@ -502,11 +503,11 @@ __global__ void __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(ECC == 
 
 template <int WFMT, int ECC, int CODEC>
 __global__ void __launch_bounds__(WG) k_fused_sgdm(const TensorDesc* __restrict__ tab, int count,
-                                                   int64_t total_tiles, const CodecTables* __restrict__ gtabs,
+                                                   int64_t tile0, int64_t tile_end, const CodecTables* __restrict__ gtabs,
                                                    SGDMConsts c) {
   __shared__ CodecTables tabs;
   load_tables(tabs, gtabs);
-  tile_loop(tab, count, total_tiles, [&](const TensorDesc& d, int64_t e0, int lane) {
+  tile_loop(tab, count, tile0, tile_end, [&](const TensorDesc& d, int64_t e0, int lane) {
     if (e0 + TILE <= d.n) sgdm_tile<WFMT, ECC, CODEC, true>(d, e0, lane, tabs, c);
     else sgdm_tile<WFMT, ECC, CODEC, false>(d, e0, lane, tabs, c);
   });
@@ -514,8 +515,8 @@ __global__ void __launch_bounds__(WG) k_fused_sgdm(const TensorDesc* __restrict_
 
 template <int ECC>
 __global__ void __launch_bounds__(WG) k_stream_probe(const TensorDesc* __restrict__ tab, int count,
-                                                     int64_t total_tiles, uint32_t key) {
-  tile_loop(tab, count, total_tiles, [&](const TensorDesc& d, int64_t e0, int lane) {
+                                                     int64_t tile0, int64_t tile_end, uint32_t key) {
+  tile_loop(tab, count, tile0, tile_end, [&](const TensorDesc& d, int64_t e0, int lane) {
     if (e0 + TILE <= d.n) probe_tile<ECC, true>(d, e0, lane, key);
     else probe_tile<ECC, false>(d, e0, lane, key);
   });

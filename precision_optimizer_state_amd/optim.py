@@ -7,8 +7,10 @@ launch post).  Here the model parameter itself becomes the 16-bit theta' (the
 thread's post on avoiding the redundant f32 + low-precision copies); the
 optimizer keeps the ECC and the 8-bit states.  Gradients therefore arrive in
 16 bits (the post on keeping gradients in backward precision).  Optional
-gradient release steps each parameter as soon as its gradient is
-accumulated and frees the gradient (the post on gradient release).
+gradient release steps parameters while backward runs, as their gradients
+are accumulated, and frees those gradients (the post on gradient release);
+parameters are stepped in buckets of at least `release_bucket` elements so
+that many small tensors share one fused call.
 
 All arithmetic runs in the HIP library (fo_fused_adamw_step /
 fo_fused_sgdm_step); this module only groups tensors and keeps step counts.
@@ -34,13 +36,19 @@ def _nb(n: int) -> int:
 class _FlashBase(torch.optim.Optimizer):
     _state_keys: tuple = ()
 
-    def __init__(self, params, defaults, wfmt, ecc_bits, codec, grad_release):
+    def __init__(self, params, defaults, wfmt, ecc_bits, codec, grad_release, release_bucket=1 << 26):
         if (wfmt, ecc_bits) not in (("bf16", 8), ("bf16", 16), ("fp16", 8)):
             raise ValueError(f"unsupported weight format {wfmt}+ECC{ecc_bits}")
         if codec not in ("companded", "linear"):
             raise ValueError(f"unknown codec {codec}")
         self.wfmt, self.ecc_bits, self.codec = wfmt, ecc_bits, codec
         self.grad_release = grad_release
+        # gradient release steps parameters in buckets of at least this many
+        # elements (one fused call each); the rest is stepped when backward ends
+        self.release_bucket = int(release_bucket)
+        self._pending = []
+        self._pending_elems = 0
+        self._flush_queued = False
         self._hooks = []
         # marshalled launch lists keyed by their raw device addresses (ints
         # only: nothing here keeps a gradient or a state tensor alive)
@@ -140,11 +148,44 @@ class _FlashBase(torch.optim.Optimizer):
 
     @torch.no_grad()
     def _release_hook(self, p):
-        group = self._group(p)
+        """Runs when p's gradient is complete during backward.  Parameters are
+        queued; a bucket of at least `release_bucket` elements is stepped in one
+        fused call and its gradients freed at once, and whatever is still queued
+        when backward finishes is stepped then (the end-of-backward callback)."""
         if p.grad.dtype != p.dtype or not p.grad.is_contiguous():
             p.grad = p.grad.to(p.dtype).contiguous()
-        self._step_params(group, [p])
-        p.grad = None          # freed in stream order by torch's caching allocator
+        self._pending.append(p)
+        self._pending_elems += p.numel()
+        if not self._flush_queued:
+            try:
+                torch.autograd.Variable._execution_engine.queue_callback(self.flush_released)
+            except RuntimeError:        # not inside a backward pass: the caller flushes
+                pass
+            self._flush_queued = True   # either way, until the next flush
+        if self._pending_elems >= self.release_bucket:
+            self._step_pending()
+
+    @torch.no_grad()
+    def _step_pending(self):
+        by_group = {}
+        for q in self._pending:
+            g = self._group(q)
+            by_group.setdefault(id(g), (g, []))[1].append(q)
+        for g, ps in by_group.values():
+            self._step_params(g, ps)
+        for q in self._pending:
+            q.grad = None       # freed in stream order by torch's caching allocator
+        self._pending = []
+        self._pending_elems = 0
+
+    @torch.no_grad()
+    def flush_released(self):
+        """Step every parameter still queued by gradient release.  Called by
+        autograd at the end of each backward pass; call it directly when the
+        hooks were driven outside a backward pass."""
+        self._flush_queued = False
+        if self._pending:
+            self._step_pending()
 
     def load_state_dict(self, state_dict):
         """torch's loader casts every tensor of a floating-point parameter's
@@ -179,9 +220,9 @@ class FlashAdamW(_FlashBase):
                    ("v_q", torch.uint8, False), ("v_s", torch.int16, True))
 
     def __init__(self, params: Iterable, lr=1e-3, betas=(0.9, 0.999), eps=1e-8, weight_decay=1e-2, *,
-                 wfmt="bf16", ecc_bits=8, codec="companded", grad_release=False):
+                 wfmt="bf16", ecc_bits=8, codec="companded", grad_release=False, release_bucket=1 << 26):
         defaults = dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay)
-        super().__init__(params, defaults, wfmt, ecc_bits, codec, grad_release)
+        super().__init__(params, defaults, wfmt, ecc_bits, codec, grad_release, release_bucket)
 
     def _entry(self, p):
         st = self.state[p]
@@ -258,11 +299,11 @@ class FlashSGD(_FlashBase):
     _state_keys = (("b_q", torch.int8, False), ("b_s", torch.int16, True))
 
     def __init__(self, params: Iterable, lr=1e-2, momentum=0.9, dampening=0.0, weight_decay=0.0, nesterov=False, *,
-                 wfmt="bf16", ecc_bits=8, codec="companded", grad_release=False):
+                 wfmt="bf16", ecc_bits=8, codec="companded", grad_release=False, release_bucket=1 << 26):
         if nesterov and (momentum <= 0.0 or dampening != 0.0):
             raise ValueError("Nesterov momentum requires a momentum and zero dampening")
         defaults = dict(lr=lr, momentum=momentum, dampening=dampening, weight_decay=weight_decay, nesterov=nesterov)
-        super().__init__(params, defaults, wfmt, ecc_bits, codec, grad_release)
+        super().__init__(params, defaults, wfmt, ecc_bits, codec, grad_release, release_bucket)
 
     def _entry(self, p):
         st = self.state[p]

@@ -99,10 +99,14 @@ def _snapshot(model, opt):
     return out
 
 
-def test_gradient_release_equals_plain_step():
+@pytest.mark.parametrize("bucket", [1, 5000, 1 << 30])
+def test_gradient_release_equals_plain_step(bucket):
+    """Release in buckets (every parameter alone, flushes in the middle of
+    backward, everything at the end-of-backward flush) is bitwise the plain
+    step, and no gradient survives the backward pass."""
     a, b = _model(2), _model(2)
     oa = FlashAdamW(a.parameters(), **HP)
-    ob = FlashAdamW(b.parameters(), **HP, grad_release=True)
+    ob = FlashAdamW(b.parameters(), **HP, grad_release=True, release_bucket=bucket)
     _train(a, oa, 4)
     _train(b, ob, 4)
     for p in b.parameters():
