@@ -4,7 +4,7 @@
 // Host responsibilities: argument validation (before anything is launched),
 // the per-step float32 constants (computed in double, rounded once), the
 // multi-tensor launch table (cached per distinct tensor list and device), and
-// grid sizing for persistent waves.
+// the launches themselves (one wave per tile; long lists in tile ranges).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -135,8 +135,8 @@ struct TableEntry {
 };
 
 // Enough slots for one list per parameter of a large model (gradient release
-// steps every parameter separately), so per-parameter lists do not evict each
-// other; the index makes a lookup O(1) in the number of slots.
+// can step parameters one by one or in small buckets), so such lists do not
+// evict each other; the index makes a lookup O(1) in the number of slots.
 constexpr size_t kCacheEntries = 1024;
 std::mutex g_tab_mu;
 std::vector<TableEntry> g_tab(kCacheEntries);
@@ -170,7 +170,7 @@ int check_alias(std::vector<Range>& r) {
 }
 
 // Build (or fetch) the device table for `descs` (already validated, n > 0 only).
-// On success *entry_out is locked by the caller's mutex scope.
+// On success *out stays the caller's while it holds g_tab_mu.
 int get_table(int dev, const std::vector<uint8_t>& key, const std::vector<TensorDesc>& descs,
               const std::vector<int32_t>& buckets, int64_t total_tiles, hipStream_t stream, TableEntry** out) {
   if ((*out = find_entry(dev, key))) return FO_OK;

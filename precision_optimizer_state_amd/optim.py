@@ -95,9 +95,6 @@ class _FlashBase(torch.optim.Optimizer):
         B.fo_split_weights(w32, p.data.view(-1), self.state[p]["ecc"].view(-1), self.wfmt, self.ecc_bits)
 
     # -- stepping ---------------------------------------------------------------
-    def _entry(self, p):
-        raise NotImplementedError
-
     def _row(self, p):
         raise NotImplementedError
 
@@ -224,19 +221,10 @@ class FlashAdamW(_FlashBase):
         defaults = dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay)
         super().__init__(params, defaults, wfmt, ecc_bits, codec, grad_release, release_bucket)
 
-    def _entry(self, p):
-        st = self.state[p]
-        return {"w16": p.data.view(-1), "ecc": st["ecc"].view(-1), "grad": p.grad.view(-1),
-                "m_q": st["m_q"], "m_s": st["m_s"], "v_q": st["v_q"], "v_s": st["v_s"]}
-
     def _row(self, p):
         st = self.state[p]
         return (p.data_ptr(), st["ecc"].data_ptr(), p.grad.data_ptr(), st["m_q"].data_ptr(), st["m_s"].data_ptr(),
                 st["v_q"].data_ptr(), st["v_s"].data_ptr(), p.numel())
-
-    @staticmethod
-    def _make_list(entries):
-        return B.AdamWList(entries)
 
     @staticmethod
     def _list_from_rows(rows):
@@ -305,19 +293,10 @@ class FlashSGD(_FlashBase):
         defaults = dict(lr=lr, momentum=momentum, dampening=dampening, weight_decay=weight_decay, nesterov=nesterov)
         super().__init__(params, defaults, wfmt, ecc_bits, codec, grad_release, release_bucket)
 
-    def _entry(self, p):
-        st = self.state[p]
-        return {"w16": p.data.view(-1), "ecc": st["ecc"].view(-1), "grad": p.grad.view(-1),
-                "b_q": st["b_q"], "b_s": st["b_s"]}
-
     def _row(self, p):
         st = self.state[p]
         return (p.data_ptr(), st["ecc"].data_ptr(), p.grad.data_ptr(), st["b_q"].data_ptr(), st["b_s"].data_ptr(),
                 p.numel())
-
-    @staticmethod
-    def _make_list(entries):
-        return B.SGDMList(entries)
 
     @staticmethod
     def _list_from_rows(rows):
