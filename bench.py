@@ -153,7 +153,7 @@ def _oracle_task(args):
     return m, time.perf_counter() - t0
 
 
-def cpu_baseline(cfg, segments=64, seg=1 << 20, log=print):
+def cpu_baseline(cfg, segments=96, seg=1 << 20, log=print):
     import multiprocessing as mp
 
     import numpy as np
