@@ -148,8 +148,10 @@ typedef struct fo_adamw_hparams {
 /*
  * fo_fused_adamw_step -- [UPDATE] with [SPLIT] and [STATE]
  * One AdamW step (decoupled weight decay, bias correction, step >= 1) over a
- * list of `count` tensors in one launch; with hp->l2_decay = 1 the step is
- * Adam with the weight decay added to the gradient (torch.optim.Adam).  Per element: widen the gradient,
+ * list of `count` tensors, enqueued on `stream` as one kernel per range of
+ * 2^17 wave tiles (2^28 elements; one kernel for most lists); with
+ * hp->l2_decay = 1 the step is Adam with the weight decay added to the
+ * gradient (torch.optim.Adam).  Per element: widen the gradient,
  * reconstruct the f32 master, decode m and v, update in float32 with a fixed
  * operation order, split the new master into theta' + ECC, recompute the
  * block scales of the new m and v and re-encode them.  Blocks never cross
