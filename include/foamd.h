@@ -31,7 +31,15 @@
  *     16-byte aligned; scale arrays must be 2-byte aligned.
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls are
  *     asynchronous with respect to the host; kernel faults surface at the
- *     caller's next synchronisation.
+ *     caller's next synchronisation.  Two exceptions block the host: the
+ *     first call on a device that needs the codec tables builds them and
+ *     synchronises `stream` once, and a launch-table cache miss that evicts
+ *     a slot waits for that slot's last use.  Make one call per tensor list
+ *     before capturing a HIP graph; later calls with the same list are
+ *     capture-safe (no allocation, no synchronisation, no memset).
+ *   - The library keeps, per device, one codec-table buffer and up to 1024
+ *     cached launch tables (device + pinned host memory, a few KB each for
+ *     ordinary lists), held until the process ends.
  *   - n == 0 is a no-op returning FO_OK.
  *   - Return value: FO_OK (0) or a negative FO_E* code; fo_last_error()
  *     returns a per-thread message for the last failing call.  Argument
