@@ -18,6 +18,7 @@ import dataclasses
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -30,11 +31,19 @@ KERNEL_SOURCES = ("precision_optimizer_state_amd/csrc/fo_device.hpp",
                   "precision_optimizer_state_amd/csrc/fo_kernels.hpp")
 
 
+def _code_only(text: str) -> str:
+    """C++ source with comments removed and whitespace collapsed, so that an
+    edit of comments alone keeps the hash (the kernels it names are the same)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

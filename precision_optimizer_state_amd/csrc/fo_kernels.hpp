@@ -11,9 +11,11 @@
 //   * Per-block arithmetic (scale rounding, reciprocals) is done once per
 //     block: lane 4Q+j owns block (sub-tile j, quad Q), and the results are
 //     broadcast back to the quad with one DPP quad permute per sub-tile.
-//   * The grid has one wave per wave tile (flat launch; the tile loop below
-//     also serves smaller grids).  A tile never crosses a tensor, and the last
-//     tile of a tensor takes a masked path.
+//   * A launch covers a range of the step's wave tiles with one wave per tile
+//     (the host issues one launch per 2^17 tiles; the tile loop below also
+//     serves smaller grids).  A tile never crosses a tensor, and the last tile
+//     of a tensor takes a masked path; the tensor of a tile is found through a
+//     tile-bucket index built by the host.
 //   * Rare inputs (NaN/Inf/overflowing weights, tiny variances, out-of-range
 //     denominators) leave the fast arithmetic through wave-uniform branches
 //     onto IEEE sequences; the results are identical either way.
