@@ -311,8 +311,8 @@ def main(argv=None):
             print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported by this build "
-              "(the step needs no communication; see DESIGN.md for how it would shard)", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported (the step needs no "
+              "communication; on several GPUs each would step its own shard of the parameter list)", file=sys.stderr)
         return 2
 
     import torch

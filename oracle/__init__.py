@@ -21,8 +21,8 @@ method computes, written from the pages that describe FlashOptim:
 It shares no code with the HIP path: the HIP kernels use integer bit tricks on
 IEEE encodings, the oracle uses float64 arithmetic on values (spacings,
 floors, exact rationals).  Where the pages leave a step open the oracle takes
-the reading listed at the top of each module; every reading is also listed in
-the design doc.  Parity status of each function is stated in its module header.
+the reading listed at the top of each module.  Parity status of each function
+is stated in its module header.
 """
 
 from .numerics import (  # noqa: F401

@@ -17,7 +17,7 @@ What the pages fix:
   "8-bit Optimizers via Block-wise Quantization", Block-wise Dynamic
   Quantization) -- prior art for the block structure.
 
-Readings (listed in DESIGN.md):
+Readings:
 
 C1  Block = 32 consecutive elements of the flattened tensor; the last block
     holds n mod 32 elements.  The absmax ignores NaN (IEEE maxNum) and, for a

@@ -15,7 +15,7 @@ Memory Wall with 24-bit Weights and Companded States", Methodology section 1
   quantised to an N-bit integer; N = 8 with B = 16 gives "24-bit" master
   weights, N = 32 - B is meant to be lossless.
 
-Readings taken where the pages are silent (also listed in the design doc):
+Readings taken where the pages are silent:
 
 R1  The downcast rounds to nearest with ties AWAY from zero (RNA).  Under RNA
     every finite theta' owns exactly 2^(24-p) f32 values on each side

@@ -11,7 +11,7 @@ for torch.optim).  Gradients stay in the backward pass's 16-bit precision
 (thread, the post on gradients).  The pages print no update equations, so the
 textbook AdamW / SGD-with-momentum definitions are used.
 
-Readings (listed in DESIGN.md):
+Readings:
 
 U1  AdamW = torch.optim.AdamW defaults: decoupled weight decay, bias
     correction, step t counted from 1, amsgrad off.  The update uses the fresh
@@ -38,9 +38,10 @@ U6  Adam with coupled L2 weight decay (torch.optim.Adam): g = g + wd*theta
     (theta = the reconstructed master) before the moments; no decoupled
     decay (decay = 1); otherwise as U3.
 
-Parity status: pinned (unquantised update against torch.optim.AdamW / SGD in
-float64 and a float64 textbook loop; bf16+16 ECC reproduces a plain float32
-master bit for bit; first-step closed form; tests/test_oracle_optim.py).
+Parity status: pinned (unquantised update against torch.optim.AdamW, Adam
+with weight decay (U6) and SGD (plain, Nesterov, dampening) in float64 and a
+float64 textbook loop; bf16+16 ECC reproduces a plain float32 master bit for
+bit; first-step closed form; tests/test_oracle_optim.py).
 """
 
 from __future__ import annotations
