@@ -134,6 +134,31 @@ def test_state_dict_resume_is_bitwise():
         assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
 
 
+def test_checkpoint_through_torch_save_and_safe_load_resumes_bitwise():
+    """state_dict() written with torch.save and read back with
+    torch.load(weights_only=True) (no unpickling of code) resumes bit for bit."""
+    import io
+    a = _model(7)
+    oa = FlashAdamW(a.parameters(), **HP)
+    _train(a, oa, 4)
+    ref = _snapshot(a, oa)
+
+    b = _model(7)
+    ob = FlashAdamW(b.parameters(), **HP)
+    _train(b, ob, 2)
+    buf = io.BytesIO()
+    torch.save({"model": b.state_dict(), "opt": ob.state_dict()}, buf)
+    buf.seek(0)
+    ck = torch.load(buf, weights_only=True, map_location="cuda")
+    c = _model(98)
+    oc = FlashAdamW(c.parameters(), **HP)
+    c.load_state_dict(ck["model"])
+    oc.load_state_dict(ck["opt"])
+    _train(c, oc, 2, start=3)
+    for x, y in zip(ref, _snapshot(c, oc)):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+
+
 def test_training_tracks_fp32_adamw():
     torch.manual_seed(5)
     w_true = torch.randn(64, 33, device="cuda") / 8
