@@ -138,15 +138,17 @@ def test_config_c5_gradient_release_chunks():
     _run("c5_flat1g_bf16e8", 2, 20000, release=True)
 
 
-def test_tensor_beyond_2_31_elements_next_to_empty_and_tiny_tensors():
-    """64-bit indexing at the largest sizes: one AdamW tensor of
-    2^31 + 2^11 + 45 elements (its theta' byte offsets pass 2^31 at element
-    2^30 and 2^32 at element 2^31; its ECC and code offsets pass 2^31 at
-    element 2^31), listed after a 33-element and an empty tensor, 2 steps.
-    Sampled blocks include those around both boundaries and the ragged tail."""
+@pytest.mark.parametrize("opt,wfmt,ecc", [("adamw", "bf16", 8), ("adamw", "bf16", 16), ("sgdm", "fp16", 8)])
+def test_tensor_beyond_2_31_elements_next_to_empty_and_tiny_tensors(opt, wfmt, ecc):
+    """64-bit indexing at the largest sizes: one tensor of 2^31 + 2^11 + 45
+    elements (its 16-bit byte offsets pass 2^31 at element 2^30 and 2^32 at
+    element 2^31; its byte-stream offsets pass 2^31 at element 2^31), listed
+    after a 33-element and an empty tensor, 2 steps; AdamW with 8- and 16-bit
+    ECC and SGD-M on fp16.  Sampled blocks include those around both
+    boundaries and the ragged tail."""
     big = (1 << 31) + (1 << 11) + 45
-    base = config("c5_flat1g_bf16e8")
-    cfg = Config("huge_2_31", "adamw", (("tiny", (33,)), ("empty", (0,)), ("huge", (big,))), base.hp,
-                 steps=2, grad_kind="t3")
+    hp = config("c5_flat1g_bf16e8").hp if opt == "adamw" else config("c4_resnet50").hp
+    cfg = Config(f"huge_2_31_{opt}_{wfmt}{ecc}", opt, (("tiny", (33,)), ("empty", (0,)), ("huge", (big,))), hp,
+                 steps=2, grad_kind="t3", wfmt=wfmt, ecc_bits=ecc)
     forced = [b + d for b in ((1 << 30) // 32, (1 << 31) // 32) for d in range(-3, 3)]
-    _run("huge_2_31", 2, 4000, cfg=cfg, forced=forced)
+    _run(cfg.name, 2, 4000, cfg=cfg, forced=forced)
