@@ -46,6 +46,10 @@ C5  Linear ablation (no companding), same scales as C2:
 C6  Codes are clamped to range before rounding (IEEE minNum/maxNum, which
     send NaN to the upper bound): a NaN momentum element gets +127 and a NaN
     variance element 255, under either codec.
+C7  The one int8 pattern outside the momentum code range, -128, is never
+    written by the encoder.  Stored states may still hold it, so decode
+    defines it: the companded LUT saturates it to -127 (so every code decodes
+    into [-s, s]); the linear decode is the plain product for every int8.
 
 RN32(.) is one IEEE float32 rounding; numpy float32 arithmetic provides it.
 Where floating point decides a code, the decision is taken in float32 (the
@@ -153,7 +157,7 @@ def decode_momentum(q: np.ndarray, scale_bits: np.ndarray, codec: str = "compand
     s = _per_elem(scale_bits, q.size)
     if codec == "companded":
         lut = momentum_lut("companded")
-        return (s * lut[q.astype(np.int64) + 127]).astype(np.float32)
+        return (s * lut[np.maximum(q.astype(np.int64), -127) + 127]).astype(np.float32)   # C7
     if codec == "linear":
         step = (s * K127).astype(np.float32)
         return (step * q.astype(np.float32)).astype(np.float32)

@@ -193,3 +193,15 @@ def test_variance_decode_definition():
     v = O.decode_variance(q, sb)
     t255 = np.float32(K255) * np.float32(255)
     assert v[0] == 0 and v[1] == np.float32(K255) * np.float32(K255) and v[2] == t255 * t255
+
+
+def test_momentum_decode_of_minus_128():
+    # -128 is never written by the encoder; the companded decode saturates it to
+    # -127 (so every int8 decodes into [-s, s]), the linear decode is -128 * step
+    sb = np.array([0x4400], np.uint16)                      # s = 4
+    q = np.array([-128, -127, 127] + [0] * 29, np.int8)
+    m = O.decode_momentum(q, sb)
+    assert m[0] == m[1] == np.float32(-4.0) and m[2] == np.float32(4.0)
+    ml = O.decode_momentum(q, sb, "linear")
+    step = np.float32(4.0) * np.float32(1.0 / 127.0)
+    assert ml[0] == step * np.float32(-128.0) and ml[1] == step * np.float32(-127.0)
