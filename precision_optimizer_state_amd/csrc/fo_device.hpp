@@ -319,27 +319,33 @@ __device__ __forceinline__ float rcp_refined(float b) {
 // ---------------------------------------------------------------------------
 // State codecs
 // ---------------------------------------------------------------------------
-// Momentum encode by interval table: a in [0,1] is keyed by the top 16 bits of
-// its f32 pattern (from 2^-9 on; below 2^-9 every a has code 0).  A key interval
-// is narrower than the spacing of the code thresholds (2k+1)/(507-2k), so it
-// holds at most one threshold: code(a) = menc[key].code + (a >= menc[key].thr).
+// Momentum encode by interval table: a in [0,1] is keyed by the top 15 bits of
+// its f32 pattern (sign, exponent and 6 mantissa bits), counted from 2^-9 (every
+// a below 2^-9 shares key 0).  Every key interval holds at most one of the code
+// thresholds (2k+1)/(507-2k) (checked exactly for all 577 keys; one mantissa bit
+// fewer would put two thresholds into some intervals just below 1), so
+// code(a) = menc[key].code + (a >= menc[key].thr).
 struct MEnc { float thr; int32_t code; };
-constexpr uint32_t MENC_BASE = 0x3B00u;                  // bits(2^-9) >> 16
-constexpr int MENC_N = 0x3F80 - 0x3B00 + 1;              // keys up to a = 1
-constexpr int MENC_CAP = 1160;
-// Workgroup copy of the codec tables (built once per device by k_init_tables):
-//   lut[i]  = RN32((i-127) / (254 - |i-127|)), i in [0,254]: momentum levels
-//   menc[k] = interval table of the momentum code as above
+constexpr int MENC_SHIFT = 17;
+constexpr uint32_t MENC_BASE = 0x3B000000u >> MENC_SHIFT;                 // 2^-9
+constexpr int MENC_N = (int)((0x3F800000u >> MENC_SHIFT) - MENC_BASE) + 1;  // keys up to a = 1
+constexpr int MENC_CAP = 640;                            // pads the tables to 6 KiB
+static_assert(MENC_CAP >= MENC_N, "interval table capacity");
+// Codec tables (built once per device by k_init_tables, copied into LDS):
+//   lut[q + 128] = RN32(q / (254 - |q|)) for q in [-127, 127]: momentum levels;
+//                  lut[0] (code -128, never written by the encoder) = lut[1]
+//   menc[k]      = interval table of the momentum code as above
 struct CodecTables { float lut[256]; MEnc menc[MENC_CAP]; };
-static_assert(sizeof(CodecTables) % 16 == 0, "table copy granularity");
+constexpr int LUT_BIAS = 128;
+static_assert(sizeof(CodecTables) == 6 * 1024, "six 1-KiB chunks: one 64-lane x 16-B load each");
 
 // Builds the tables (one workgroup).  thr[k] = smallest f32 >= (2k+1)/(507-2k),
 // the |z| at which round(127*phi(|z|)) steps from k to k+1.
 __device__ __forceinline__ void build_tables(FO_GLOBAL CodecTables* out, float* thr, int tid, int nthreads) {
   for (int i = tid; i < 256; i += nthreads) {
-    const int q = i - 127;
+    const int q = max(i - LUT_BIAS, -127);
     const int aq = q < 0 ? -q : q;
-    out->lut[i] = (i < 255) ? (float)q / (float)(254 - aq) : 0.0f;   // IEEE division
+    out->lut[i] = (float)q / (float)(254 - aq);         // IEEE division
   }
   for (int k = tid; k < 127; k += nthreads) {
     const float a = (float)(2 * k + 1), b = (float)(507 - 2 * k);
@@ -351,8 +357,8 @@ __device__ __forceinline__ void build_tables(FO_GLOBAL CodecTables* out, float* 
   for (int key = tid; key < MENC_CAP; key += nthreads) {
     MEnc e;
     if (key < MENC_N) {
-      const float lo = (key == 0) ? 0.0f : u2f((MENC_BASE + key) << 16);
-      const float hi = u2f((MENC_BASE + key + 1) << 16);
+      const float lo = (key == 0) ? 0.0f : u2f((MENC_BASE + key) << MENC_SHIFT);
+      const float hi = u2f((MENC_BASE + key + 1) << MENC_SHIFT);
       int code = 0;
       for (int k = 0; k < 127; ++k) code += (thr[k] <= lo) ? 1 : 0;
       e.code = code;
@@ -370,7 +376,7 @@ __device__ __forceinline__ void build_tables(FO_GLOBAL CodecTables* out, float* 
 __device__ __forceinline__ int32_t encode_m_companded(float m, float R, const CodecTables& T) {
   const float z = m * R;
   const float a = fminf(fabsf(z), 1.0f);                  // NaN -> 1
-  const uint32_t key = __builtin_elementwise_sub_sat(f2u(a) >> 16, MENC_BASE);
+  const uint32_t key = __builtin_elementwise_sub_sat(f2u(a) >> MENC_SHIFT, MENC_BASE);
   const MEnc e = T.menc[key];
   const int32_t q = e.code + (a >= e.thr ? 1 : 0);
   return (z < 0.0f) ? -q : q;

@@ -231,7 +231,7 @@ __device__ __forceinline__ void adamw_tile(const TensorDesc& d, int64_t e0, int 
       th[k] = ecc_decode<WFMT, ECC>(wid<WFMT>(W[j], k), rho_at<ECC>(E[j], k));
       if constexpr (L2) g = g + c.wd * th[k];                  // Adam: decay folded into the gradient
       const int32_t qm = s8(MQ[j], k);
-      const float mh = (CODEC == COMPANDED) ? dm * tabs.lut[qm + 127] : dm * (float)qm;
+      const float mh = (CODEC == COMPANDED) ? dm * tabs.lut[qm + LUT_BIAS] : dm * (float)qm;
       const float tv = dv * (float)u8(VQ[j], k);
       const float vh = (CODEC == COMPANDED) ? tv * tv : tv;
       // update (fixed float32 order, one rounding per operation)
@@ -350,7 +350,7 @@ __device__ __forceinline__ void sgdm_tile(const TensorDesc& d, int64_t e0, int l
       const float g = wid<WFMT>(G[j], k);
       const float t0 = ecc_decode<WFMT, ECC>(wid<WFMT>(W[j], k), rho_at<ECC>(E[j], k));
       const int32_t qb = s8(BQ[j], k);
-      const float bh = (CODEC == COMPANDED) ? db * tabs.lut[qb + 127] : db * (float)qb;
+      const float bh = (CODEC == COMPANDED) ? db * tabs.lut[qb + LUT_BIAS] : db * (float)qb;
       const float dd = g + c.wd * t0;
       b[k] = c.first ? dd : c.mu * bh + c.damp1 * dd;
       const float u = c.nesterov ? dd + c.mu * b[k] : b[k];
@@ -483,6 +483,30 @@ __device__ __forceinline__ void load_tables(CodecTables& dst, const CodecTables*
   __syncthreads();
 }
 
+// Each wave of a fused step keeps its own LDS copy of the codec tables, filled
+// by six asynchronous buffer->LDS loads (64 lanes x 16 B each) issued before
+// the tile's own loads: the copy's latency overlaps the tile's instead of
+// preceding it, and no workgroup barrier is needed, because a wave reads only
+// the copy it filled.  The buffer form (not the global one) keeps the vector
+// memory counter in order, so the first table read waits for these six loads
+// only and the tile's loads still retire progressively.  The scheduling
+// barrier keeps them ahead of the tile's loads.
+typedef __attribute__((address_space(3))) void lds_void;
+constexpr int BUFFER_RSRC_WORD3 = 0x00020000;   // raw buffer, 32-bit data format
+__device__ __forceinline__ const CodecTables& wave_tables(CodecTables* lds, const CodecTables* __restrict__ src) {
+  constexpr int CHUNKS = sizeof(CodecTables) / (16 * WAVE);
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & (WAVE - 1);
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, (int)sizeof(CodecTables), BUFFER_RSRC_WORD3);
+  u32x4* d = (u32x4*)(lds + wid);
+#pragma unroll
+  for (int i = 0; i < CHUNKS; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(d + i * WAVE), 16, lane * 16 + i * 16 * WAVE, 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  return lds[wid];
+}
+
 __global__ void __launch_bounds__(WG) k_init_tables(CodecTables* out) {
   __shared__ float thr[128];
   build_tables((gp<CodecTables>)out, thr, threadIdx.x, blockDim.x);
@@ -495,8 +519,8 @@ template <int WFMT, int ECC, int CODEC, bool L2>
 __global__ void __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(ECC == 8 ? 3 : 1))) k_fused_adamw(const TensorDesc* __restrict__ tab, int count,
                                                     int64_t tile0, int64_t tile_end, const CodecTables* __restrict__ gtabs,
                                                     AdamWConsts c) {
-  __shared__ CodecTables tabs;
-  load_tables(tabs, gtabs);
+  __shared__ CodecTables wtabs[WAVES_PER_WG];
+  const CodecTables& tabs = wave_tables(wtabs, gtabs);
   tile_loop(tab, count, tile0, tile_end, [&](const TensorDesc& d, int64_t e0, int lane) {
     if (e0 + TILE <= d.n) adamw_tile<WFMT, ECC, CODEC, L2, true>(d, e0, lane, tabs, c);
     else adamw_tile<WFMT, ECC, CODEC, L2, false>(d, e0, lane, tabs, c);
@@ -507,8 +531,8 @@ template <int WFMT, int ECC, int CODEC>
 __global__ void __launch_bounds__(WG) k_fused_sgdm(const TensorDesc* __restrict__ tab, int count,
                                                    int64_t tile0, int64_t tile_end, const CodecTables* __restrict__ gtabs,
                                                    SGDMConsts c) {
-  __shared__ CodecTables tabs;
-  load_tables(tabs, gtabs);
+  __shared__ CodecTables wtabs[WAVES_PER_WG];
+  const CodecTables& tabs = wave_tables(wtabs, gtabs);
   tile_loop(tab, count, tile0, tile_end, [&](const TensorDesc& d, int64_t e0, int lane) {
     if (e0 + TILE <= d.n) sgdm_tile<WFMT, ECC, CODEC, true>(d, e0, lane, tabs, c);
     else sgdm_tile<WFMT, ECC, CODEC, false>(d, e0, lane, tabs, c);
@@ -661,7 +685,7 @@ __global__ void __launch_bounds__(WG) k_dequantize(const uint8_t* __restrict__ c
     for (int k = 0; k < 8; ++k) {
       if (KIND == 0) {
         const int32_t cq = s8(q, k);
-        v[k] = (CODEC == COMPANDED) ? s * tabs.lut[cq + 127] : (s * K127) * (float)cq;
+        v[k] = (CODEC == COMPANDED) ? s * tabs.lut[cq + LUT_BIAS] : (s * K127) * (float)cq;
       } else {
         const float cq = (float)u8(q, k);
         if (CODEC == COMPANDED) { const float t = (s * K255) * cq; v[k] = t * t; }

@@ -148,6 +148,56 @@ def test_quantize_dequantize_match_oracle(kind, codec, n):
     assert np.array_equal(out.cpu().numpy().view(np.uint32), d_ref.view(np.uint32))
 
 
+def _oracle_code_steps():
+    """Smallest f32 pattern in [0, 1] whose oracle momentum code (scale 1) is
+    at least k + 1, for k = 0..126, by bisection over the patterns (the code
+    is non-decreasing in the value)."""
+    one = np.full(4, 0x3C00, np.uint16)                  # fp16 1.0 for every block
+    code = lambda p: O.encode_momentum(p.astype(np.uint32).view(np.float32), one, "companded").astype(np.int64)
+    want = np.arange(1, 128)
+    lo = np.zeros(127, np.int64)
+    hi = np.full(127, 0x3F800000, np.int64)
+    assert np.all(code(lo) < want) and np.all(code(hi) >= want)
+    while np.any(hi - lo > 1):
+        mid = (lo + hi) // 2
+        up = code(mid) >= want
+        hi = np.where(up, mid, hi)
+        lo = np.where(up, lo, mid)
+    return hi
+
+
+def test_momentum_encode_every_f32_in_unit_interval():
+    """The companded momentum code of every f32 value in [0, 1] (and its
+    negative) at block scale 1.  Each 32-block is [1.0, 31 consecutive
+    patterns], so the scale is fp16 1.0, the reciprocal is exactly 1 and the
+    kernel codes z = a itself.  The codes must rise from 0 in 127 unit steps
+    placed exactly at the oracle's thresholds, which is the oracle's code on
+    all 1,065,353,217 values; negated inputs must give negated codes."""
+    N = 0x3F800000 + 1
+    nblk = -(-N // 31)
+    x = torch.empty(nblk, 32, dtype=torch.int32, device="cuda")
+    x[:, 0] = 0x3F800000
+    x[:, 1:] = torch.arange(nblk * 31, dtype=torch.int32, device="cuda").view(nblk, 31).clamp_(max=0x3F800000)
+    xf = x.view(torch.float32).view(-1)
+    codes = torch.empty(nblk * 32, dtype=torch.int8, device="cuda")
+    scales = torch.empty(nblk, dtype=torch.float16, device="cuda")
+    B.fo_companded_quantize(xf, codes, scales, "m", "companded")
+    assert bool((scales.view(torch.int16) == 0x3C00).all())
+    cv = codes.view(nblk, 32)[:, 1:].reshape(-1)[:N]
+    assert int(cv[0]) == 0
+    steps = torch.nonzero(cv[1:] != cv[:-1]).flatten() + 1
+    assert steps.numel() == 127, f"{steps.numel()} code changes over [0, 1]"
+    assert bool(((cv[steps].to(torch.int32) - cv[steps - 1].to(torch.int32)) == 1).all())
+    ref = _oracle_code_steps()
+    got = steps.cpu().numpy().astype(np.int64)
+    print(f"momentum code steps: {int(np.sum(got != ref))} of 127 misplaced", flush=True)
+    assert np.array_equal(got, ref)
+    xf.neg_()
+    neg = torch.empty_like(codes)
+    B.fo_companded_quantize(xf, neg, scales, "m", "companded")
+    assert bool((neg == codes.neg()).all())
+
+
 def _run_adamw(sizes, steps, hp, fmt="bf16", ecc_bits=8, codec="companded", tag="t", inject=None):
     """Free-running GPU vs oracle over `steps` steps on a list of tensors."""
     xs = [host_weights(tag, i, n) for i, n in enumerate(sizes)]
