@@ -33,8 +33,16 @@ constexpr int EPL = 8;                     // elements per lane per sub-tile
 constexpr int SUB = WAVE * EPL;            // 512
 constexpr int NSUB = 4;
 constexpr int TILE = SUB * NSUB;           // 2048 elements per wave tile
-constexpr int WAVES_PER_WG = 4;
+constexpr int WAVES_PER_WG = 4;           // element-wise kernels
 constexpr int WG = WAVE * WAVES_PER_WG;    // 256 threads
+// Waves per workgroup of the tile kernels (fused steps, stream probe).  A wave
+// needs nothing from its neighbours (private LDS tables, no barrier), and a
+// one-wave group releases its slot and LDS as soon as its tile is done: on the
+// Llama-8B list that measured 16.74-16.76 -> 16.58 ms against 4-wave groups.
+// The AdamW kernels with a 16-bit ECC (176 VGPRs, two waves per SIMD) ran
+// 1.6% slower that way and keep 4-wave groups.
+template <int ECC> constexpr int adamw_tile_waves = (ECC == 16) ? 4 : 1;
+constexpr int SGDM_TILE_WAVES = 1;
 // Block ownership (lane 4Q+j owns block 16j+Q of the tile) needs exactly one
 // sub-tile per lane of a quad: 4 sub-tiles, 64 blocks, 64 lanes.
 static_assert(NSUB == 4 && TILE / 32 == WAVE, "one owned block per lane");
@@ -454,15 +462,15 @@ __device__ __forceinline__ int find_tensor(const TensorDesc* __restrict__ tab, i
 // list (one tile per wave with the default flat grid).  When a wave leaves its tensor, the tensor of
 // its tile is found through the tile-bucket index (a short binary search over
 // the first-tile indices of one bucket's tensors).
-template <typename F>
+template <int WPG, typename F>
 __device__ __forceinline__ void tile_loop(const TensorDesc* __restrict__ tab, int count, int64_t tile0,
                                           int64_t tile_end, F&& body) {
   const int lane = threadIdx.x & (WAVE - 1);
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int64_t nwaves = (int64_t)gridDim.x * WAVES_PER_WG;
+  const int64_t nwaves = (int64_t)gridDim.x * WPG;
   int t = 0;
   int64_t t_begin = 0, t_end = -1;
-  for (int64_t T = tile0 + (int64_t)blockIdx.x * WAVES_PER_WG + wid; T < tile_end; T += nwaves) {
+  for (int64_t T = tile0 + (int64_t)blockIdx.x * WPG + wid; T < tile_end; T += nwaves) {
     if (T >= t_end) {
       t = find_tensor(tab, count, T);
       t_begin = tab[t].tile_begin;
@@ -516,33 +524,34 @@ __global__ void __launch_bounds__(WG) k_init_tables(CodecTables* out) {
 // needs.  ECC16 holds more registers; forcing three waves there spills, and
 // two waves without spills run faster.
 template <int WFMT, int ECC, int CODEC, bool L2>
-__global__ void __launch_bounds__(WG) __attribute__((amdgpu_waves_per_eu(ECC == 8 ? 3 : 1))) k_fused_adamw(const TensorDesc* __restrict__ tab, int count,
-                                                    int64_t tile0, int64_t tile_end, const CodecTables* __restrict__ gtabs,
-                                                    AdamWConsts c) {
-  __shared__ CodecTables wtabs[WAVES_PER_WG];
+__global__ void __launch_bounds__(WAVE * adamw_tile_waves<ECC>) __attribute__((amdgpu_waves_per_eu(ECC == 8 ? 3 : 1)))
+k_fused_adamw(const TensorDesc* __restrict__ tab, int count, int64_t tile0, int64_t tile_end,
+              const CodecTables* __restrict__ gtabs, AdamWConsts c) {
+  __shared__ CodecTables wtabs[adamw_tile_waves<ECC>];
   const CodecTables& tabs = wave_tables(wtabs, gtabs);
-  tile_loop(tab, count, tile0, tile_end, [&](const TensorDesc& d, int64_t e0, int lane) {
+  tile_loop<adamw_tile_waves<ECC>>(tab, count, tile0, tile_end, [&](const TensorDesc& d, int64_t e0, int lane) {
     if (e0 + TILE <= d.n) adamw_tile<WFMT, ECC, CODEC, L2, true>(d, e0, lane, tabs, c);
     else adamw_tile<WFMT, ECC, CODEC, L2, false>(d, e0, lane, tabs, c);
   });
 }
 
 template <int WFMT, int ECC, int CODEC>
-__global__ void __launch_bounds__(WG) k_fused_sgdm(const TensorDesc* __restrict__ tab, int count,
-                                                   int64_t tile0, int64_t tile_end, const CodecTables* __restrict__ gtabs,
-                                                   SGDMConsts c) {
-  __shared__ CodecTables wtabs[WAVES_PER_WG];
+__global__ void __launch_bounds__(WAVE * SGDM_TILE_WAVES) k_fused_sgdm(const TensorDesc* __restrict__ tab, int count,
+                                                                 int64_t tile0, int64_t tile_end,
+                                                                 const CodecTables* __restrict__ gtabs, SGDMConsts c) {
+  __shared__ CodecTables wtabs[SGDM_TILE_WAVES];
   const CodecTables& tabs = wave_tables(wtabs, gtabs);
-  tile_loop(tab, count, tile0, tile_end, [&](const TensorDesc& d, int64_t e0, int lane) {
+  tile_loop<SGDM_TILE_WAVES>(tab, count, tile0, tile_end, [&](const TensorDesc& d, int64_t e0, int lane) {
     if (e0 + TILE <= d.n) sgdm_tile<WFMT, ECC, CODEC, true>(d, e0, lane, tabs, c);
     else sgdm_tile<WFMT, ECC, CODEC, false>(d, e0, lane, tabs, c);
   });
 }
 
+// same launch shape as the AdamW step it is compared with
 template <int ECC>
-__global__ void __launch_bounds__(WG) k_stream_probe(const TensorDesc* __restrict__ tab, int count,
-                                                     int64_t tile0, int64_t tile_end, uint32_t key) {
-  tile_loop(tab, count, tile0, tile_end, [&](const TensorDesc& d, int64_t e0, int lane) {
+__global__ void __launch_bounds__(WAVE * adamw_tile_waves<ECC>) k_stream_probe(const TensorDesc* __restrict__ tab, int count,
+                                                                        int64_t tile0, int64_t tile_end, uint32_t key) {
+  tile_loop<adamw_tile_waves<ECC>>(tab, count, tile0, tile_end, [&](const TensorDesc& d, int64_t e0, int lane) {
     if (e0 + TILE <= d.n) probe_tile<ECC, true>(d, e0, lane, key);
     else probe_tile<ECC, false>(d, e0, lane, key);
   });

@@ -103,8 +103,11 @@ int device_tables(int dev, hipStream_t stream, const CodecTables** out) {
 // one launch over every tile; lists up to that size are one launch.
 constexpr int64_t kLaunchTiles = int64_t(1) << 17;
 
-int tile_grid(int64_t total_tiles, int* grid) {
-  const int64_t want = (total_tiles + WAVES_PER_WG - 1) / WAVES_PER_WG;
+// waves per workgroup of the AdamW step and probe kernels (their launch bounds)
+int adamw_waves(int ecc_bits) { return ecc_bits == 16 ? adamw_tile_waves<16> : adamw_tile_waves<8>; }
+
+int tile_grid(int64_t total_tiles, int waves_per_wg, int* grid) {
+  const int64_t want = (total_tiles + waves_per_wg - 1) / waves_per_wg;
   *grid = (int)std::max<int64_t>(1, std::min<int64_t>(want, (int64_t)INT32_MAX));
   return FO_OK;
 }
@@ -506,12 +509,13 @@ int fo_fused_adamw_step(const fo_adamw_tensor* list, int32_t count, const fo_ada
   if (hp->l2_decay) FO_SELECT3(k_fused_adamw_l2, hp->wfmt, hp->ecc_bits, hp->codec, kern);
   else FO_SELECT3(k_fused_adamw_dec, hp->wfmt, hp->ecc_bits, hp->codec, kern);
   int dev, grid;
+  const int waves = adamw_waves(hp->ecc_bits);
   const CodecTables* tb = nullptr;
   if ((rc = current_device(&dev)) || (rc = device_tables(dev, s, &tb))) return rc;
   for (int64_t t0 = 0; t0 < e->total_tiles; t0 += kLaunchTiles) {
     const int64_t t1 = std::min<int64_t>(t0 + kLaunchTiles, e->total_tiles);
-    if ((rc = tile_grid(t1 - t0, &grid))) return rc;
-    hipLaunchKernelGGL(kern, grid, WG, 0, s, (const TensorDesc*)e->dptr, e->count, t0, t1, tb, c);
+    if ((rc = tile_grid(t1 - t0, waves, &grid))) return rc;
+    hipLaunchKernelGGL(kern, grid, WAVE * waves, 0, s, (const TensorDesc*)e->dptr, e->count, t0, t1, tb, c);
   }
   rc = launch_check("k_fused_adamw launch");
   if (rc) return rc;
@@ -533,10 +537,11 @@ int fo_stream_probe(const fo_adamw_tensor* list, int32_t count, int32_t wfmt, in
   if (!e || e->total_tiles == 0) return FO_OK;
   void (*kern)(const TensorDesc*, int, int64_t, int64_t, uint32_t) = (ecc_bits == 8) ? k_stream_probe<8> : k_stream_probe<16>;
   int grid;
+  const int waves = adamw_waves(ecc_bits);
   for (int64_t t0 = 0; t0 < e->total_tiles; t0 += kLaunchTiles) {
     const int64_t t1 = std::min<int64_t>(t0 + kLaunchTiles, e->total_tiles);
-    if ((rc = tile_grid(t1 - t0, &grid))) return rc;
-    hipLaunchKernelGGL(kern, grid, WG, 0, s, (const TensorDesc*)e->dptr, e->count, t0, t1, key);
+    if ((rc = tile_grid(t1 - t0, waves, &grid))) return rc;
+    hipLaunchKernelGGL(kern, grid, WAVE * waves, 0, s, (const TensorDesc*)e->dptr, e->count, t0, t1, key);
   }
   rc = launch_check("k_stream_probe launch");
   if (rc) return rc;
@@ -591,8 +596,8 @@ int fo_fused_sgdm_step(const fo_sgdm_tensor* list, int32_t count, const fo_sgdm_
   if ((rc = device_tables(e->dev, s, &tb))) return rc;
   for (int64_t t0 = 0; t0 < e->total_tiles; t0 += kLaunchTiles) {
     const int64_t t1 = std::min<int64_t>(t0 + kLaunchTiles, e->total_tiles);
-    if ((rc = tile_grid(t1 - t0, &grid))) return rc;
-    hipLaunchKernelGGL(kern, grid, WG, 0, s, (const TensorDesc*)e->dptr, e->count, t0, t1, tb, c);
+    if ((rc = tile_grid(t1 - t0, SGDM_TILE_WAVES, &grid))) return rc;
+    hipLaunchKernelGGL(kern, grid, WAVE * SGDM_TILE_WAVES, 0, s, (const TensorDesc*)e->dptr, e->count, t0, t1, tb, c);
   }
   rc = launch_check("k_fused_sgdm launch");
   if (rc) return rc;
