@@ -19,6 +19,8 @@ FlashAdamW, FlashAdam and FlashSGD follow torch.optim.AdamW, Adam and SGD.
 
 from __future__ import annotations
 
+import itertools
+import operator
 from typing import Iterable
 
 import torch
@@ -31,6 +33,20 @@ _ECC = {8: torch.int8, 16: torch.int16}
 
 def _nb(n: int) -> int:
     return (n + 31) // 32
+
+
+class _Plan:
+    """What a parameter list needs at every step, built once per list: the
+    parameters (held, so their ids stay theirs), their state dicts and the
+    address-independent part of each launch row.  `gen` is unique per plan
+    and keys the marshalled lists built from it."""
+
+    __slots__ = ("params", "states", "static", "gen")
+    _gens = itertools.count()
+
+    def __init__(self, params, states, static):
+        self.params, self.states, self.static = params, states, static
+        self.gen = next(_Plan._gens)
 
 
 class _FlashBase(torch.optim.Optimizer):
@@ -50,8 +66,10 @@ class _FlashBase(torch.optim.Optimizer):
         self._pending_elems = 0
         self._flush_queued = False
         self._hooks = []
-        # marshalled launch lists keyed by their raw device addresses (ints
-        # only: nothing here keeps a gradient or a state tensor alive)
+        # per parameter list: a _Plan, and the marshalled launch lists keyed by
+        # (plan, theta' addresses, gradient addresses) -- ints only, so nothing
+        # here keeps a gradient alive
+        self._plans = {}
         self._lists = {}
         self._group_of = {}
         super().__init__(params, defaults)
@@ -95,29 +113,56 @@ class _FlashBase(torch.optim.Optimizer):
         B.fo_split_weights(w32, p.data.view(-1), self.state[p]["ecc"].view(-1), self.wfmt, self.ecc_bits)
 
     # -- stepping ---------------------------------------------------------------
-    def _row(self, p):
+    def _static(self, p):
+        """(ecc address, state addresses..., numel): the part of p's launch row
+        that does not change between steps."""
         raise NotImplementedError
 
     def _launch(self, entries, group, step):
         raise NotImplementedError
 
+    def _plan(self, params):
+        ids = tuple(map(id, params))
+        plan = self._plans.get(ids)
+        if plan is None or not all(map(operator.is_, plan.params, params)):
+            if len(self._plans) >= 4096:
+                self._plans.clear()
+                self._lists.clear()
+            plan = self._plans[ids] = _Plan(list(params), [self.state[p] for p in params],
+                                            [self._static(p) for p in params])
+        return plan
+
+    def _list_for(self, plan, params, static):
+        # rows of raw addresses (w16, ecc, grad, states..., n); the ctypes array
+        # is rebuilt only when a theta' or gradient address changes
+        w = tuple([p.data_ptr() for p in params])
+        g = tuple([p.grad.data_ptr() for p in params])
+        key = (plan.gen, w, g)
+        tl = self._lists.get(key)
+        if tl is None:
+            if len(self._lists) >= 4096:
+                self._lists.clear()
+            rows = tuple((wp, st[0], gp) + st[1:] for wp, gp, st in zip(w, g, static))
+            tl = self._lists[key] = self._list_from_rows(rows)
+        return tl
+
     def _step_params(self, group, params):
-        # parameters of one group that share a step count go into one launch
-        by_step = {}
-        for p in params:
-            st = self.state[p]
+        plan = self._plan(params)
+        steps = []
+        for st in plan.states:
             st["step"] += 1
-            by_step.setdefault(st["step"], []).append(p)
-        for step, ps in by_step.items():
-            # rows of raw addresses: no tensor views, no reference kept; the
-            # ctypes array is rebuilt only when an address changes
-            rows = tuple(self._row(p) for p in ps)
-            tl = self._lists.get(rows)
-            if tl is None:
-                if len(self._lists) >= 4096:
-                    self._lists.clear()
-                tl = self._lists[rows] = self._list_from_rows(rows)
-            self._launch(tl, group, step)
+            steps.append(st["step"])
+        if steps.count(steps[0]) == len(steps):
+            self._launch(self._list_for(plan, params, plan.static), group, steps[0])
+            return
+        # parameters with different step counts (imported or reloaded states):
+        # one launch per count
+        by_step = {}
+        for i, s in enumerate(steps):
+            by_step.setdefault(s, []).append(i)
+        for s, idx in by_step.items():
+            sub = self._plan([params[i] for i in idx])
+            self._launch(self._list_for(sub, sub.params, sub.static), group, s)
 
     @torch.no_grad()
     def step(self, closure=None):
@@ -125,11 +170,16 @@ class _FlashBase(torch.optim.Optimizer):
         if closure is not None:
             with torch.enable_grad():
                 loss = closure()
+        wdt = _W16[self.wfmt]
         for group in self.param_groups:
-            ps = [p for p in group["params"] if p.grad is not None]
-            for p in ps:
-                if p.grad.dtype != p.dtype or not p.grad.is_contiguous():
-                    p.grad = p.grad.to(p.dtype).contiguous()
+            ps = []
+            for p in group["params"]:
+                g = p.grad
+                if g is None:
+                    continue
+                if g.dtype is not wdt or not g.is_contiguous():
+                    p.grad = g.to(wdt).contiguous()
+                ps.append(p)
             if ps:
                 self._step_params(group, ps)
         return loss
@@ -192,6 +242,7 @@ class _FlashBase(torch.optim.Optimizer):
         raw = {k: {kk: vv for kk, vv in v.items() if torch.is_tensor(vv)}
                for k, v in state_dict["state"].items()}
         super().load_state_dict(state_dict)
+        self._plans.clear()
         self._lists.clear()
         self._group_of = {}
         params = [p for g in self.param_groups for p in g["params"]]
@@ -221,10 +272,10 @@ class FlashAdamW(_FlashBase):
         defaults = dict(lr=lr, betas=betas, eps=eps, weight_decay=weight_decay)
         super().__init__(params, defaults, wfmt, ecc_bits, codec, grad_release, release_bucket)
 
-    def _row(self, p):
+    def _static(self, p):
         st = self.state[p]
-        return (p.data_ptr(), st["ecc"].data_ptr(), p.grad.data_ptr(), st["m_q"].data_ptr(), st["m_s"].data_ptr(),
-                st["v_q"].data_ptr(), st["v_s"].data_ptr(), p.numel())
+        return (st["ecc"].data_ptr(), st["m_q"].data_ptr(), st["m_s"].data_ptr(), st["v_q"].data_ptr(),
+                st["v_s"].data_ptr(), p.numel())
 
     @staticmethod
     def _list_from_rows(rows):
@@ -293,10 +344,9 @@ class FlashSGD(_FlashBase):
         defaults = dict(lr=lr, momentum=momentum, dampening=dampening, weight_decay=weight_decay, nesterov=nesterov)
         super().__init__(params, defaults, wfmt, ecc_bits, codec, grad_release, release_bucket)
 
-    def _row(self, p):
+    def _static(self, p):
         st = self.state[p]
-        return (p.data_ptr(), st["ecc"].data_ptr(), p.grad.data_ptr(), st["b_q"].data_ptr(), st["b_s"].data_ptr(),
-                p.numel())
+        return (st["ecc"].data_ptr(), st["b_q"].data_ptr(), st["b_s"].data_ptr(), p.numel())
 
     @staticmethod
     def _list_from_rows(rows):
