@@ -79,13 +79,11 @@ __device__ __forceinline__ float ecc_decode(float t, int32_t rho) {
     return u2f(f2u(t) + ((uint32_t)rho << SH));
   } else {
     static_assert(ECC == 8, "fp16 supports an 8-bit ECC");
-    const uint32_t a = f2u(t) & 0x7FFFFFFFu;
-    if (a > 0x38800000u)                         // |theta'| above the smallest fp16 normal
+    if (fabsf(t) > 0x1p-14f)                     // |theta'| above the smallest fp16 normal (or inf)
       return u2f(f2u(t) + ((uint32_t)rho << 5)); // one fp16 spacing = 2^13 f32 spacings
-    // zero, subnormal and the smallest normal: spacing 2^-24 on both sides;
-    // the offset rho * 2^-32 (exact) is applied to the magnitude
-    const float off = (float)rho * 0x1p-32f;
-    return t + u2f(f2u(off) ^ (f2u(t) & 0x80000000u));
+    // zero, subnormal and the smallest normal (and NaN, which stays NaN): spacing
+    // 2^-24 on both sides; the offset rho * 2^-32 (exact) is applied to the magnitude
+    return t + (float)rho * __builtin_copysignf(0x1p-32f, t);
   }
 }
 
@@ -204,12 +202,14 @@ __device__ __forceinline__ void split8(const float (&x)[8], uint32_t (&wo)[4], u
     // the RNA overflow threshold 65520.  theta' starts as the hardware
     // round-to-nearest-even conversion t; d = |x| - |t| is exact (Sterbenz,
     // or t = 0), and rho = rint(d * 2^8 / ulp_side(t)) = rint(ldexp(d, k))
-    // with k = 145 - max(biased exponent of t, 113) (113: the fp16 subnormal
-    // spacing 2^-24), plus one on the inner side of a power of two above
-    // 2^-14.  RNE and RNA differ only on an exact tie that RNE rounded
-    // towards zero, which shows as d * 2^k == +128 exactly: then theta' moves
-    // one pattern away from zero and rho = -128.  Any other value rounding
-    // to 128 clamps to 127.
+    // with k = 145 - max(biased exponent of x, 113) (113: the fp16 subnormal
+    // spacing 2^-24).  The exponent of x itself gives the spacing on x's side
+    // of t: above t, and below a t that is not a power of two, x shares t's
+    // binade; below a power of two t (the inner side, half spacing) x lies in
+    // the binade under it.  RNE and RNA differ only on an exact tie that RNE
+    // rounded towards zero, which shows as d * 2^k == +128 exactly: then
+    // theta' moves one pattern away from zero and rho = -128.  Any other value
+    // rounding to 128 clamps to 127.
     uint64_t special = 0;
 #pragma unroll
     for (int k = 0; k < 8; ++k) special |= __builtin_amdgcn_ballot_w64(!(fabsf(x[k]) < 65520.0f));
@@ -220,10 +220,8 @@ __device__ __forceinline__ void split8(const float (&x)[8], uint32_t (&wo)[4], u
         const _Float16 hh = (_Float16)x[k];
         const float t = (float)hh;
         const float d = fabsf(x[k]) - fabsf(t);
-        const uint32_t tb = f2u(t);
-        const int eb = (int)((tb >> 23) & 0xFFu);
-        const bool inner = (d < 0.0f) && ((tb & 0x7FFFFFu) == 0u) && (eb > 113);
-        const int sh = 145 - max(eb, 113) + (inner ? 1 : 0);
+        const int eb = (int)((f2u(x[k]) >> 23) & 0xFFu);
+        const int sh = 145 - max(eb, 113);
         const float rf = __builtin_ldexpf(d, sh);
         const bool tie = (rf == 128.0f);
         const int32_t r = min((int32_t)__builtin_rintf(rf), 127);
