@@ -24,6 +24,8 @@
 // sections 1 and 2) define what is computed; the launch structure is ours.
 #pragma once
 
+#include <type_traits>
+
 #include "fo_device.hpp"
 
 namespace fo {
@@ -169,8 +171,9 @@ __device__ __forceinline__ void sqrt8(const float (&v)[EPL], float (&w)[EPL]) {
 }
 
 // r = RN(1/d) for 8 denominators (IEEE division when any lane is outside the
-// verified range, or when eps does not keep denominators normal)
-__device__ __forceinline__ void rcp8(const float (&d)[EPL], float (&r)[EPL], int fast) {
+// verified range, or when eps does not keep denominators normal).  Returns
+// whether the wave took the IEEE path; a NaN or infinite d always does.
+__device__ __forceinline__ bool rcp8(const float (&d)[EPL], float (&r)[EPL], int fast) {
   uint64_t slow = fast ? 0ull : ~0ull;
 #pragma unroll
   for (int k = 0; k < EPL; ++k) {
@@ -181,6 +184,7 @@ __device__ __forceinline__ void rcp8(const float (&d)[EPL], float (&r)[EPL], int
 #pragma unroll
     for (int k = 0; k < EPL; ++k) r[k] = 1.0f / d[k];
   }
+  return slow != 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -227,7 +231,13 @@ __device__ __forceinline__ void adamw_tile(const TensorDesc& d, int64_t e0, int 
   const float dv_own = (CODEC == COMPANDED) ? svf * K255 : (svf * svf) * K255;
 
   float Mn[NSUB][EPL], Xn[NSUB][EPL];       // fresh m and (sqrt(v) | v) for re-encoding
+  // block maxima start at NaN: IEEE maxNum returns any non-NaN element (the
+  // zeros of a partial block included), so only an all-NaN block keeps NaN
+  // and gets a NaN scale, which carries the NaN into the decoded state
   float own_mmax = 0.0f, own_xmax = 0.0f;
+  // some lane's denominator was NaN, infinite or beyond the fast reciprocal's
+  // range (wave-uniform); without that, no fresh v is NaN
+  bool any_wide = false;
 
 #pragma unroll
   for (int j = 0; j < NSUB; ++j) {
@@ -250,7 +260,7 @@ __device__ __forceinline__ void adamw_tile(const TensorDesc& d, int64_t e0, int 
     sqrt8(v, w);
 #pragma unroll
     for (int k = 0; k < EPL; ++k) den[k] = w[k] * c.ibc2 + c.eps;
-    rcp8(den, r, c.fast_rcp);
+    any_wide |= rcp8(den, r, c.fast_rcp);
 #pragma unroll
     for (int k = 0; k < EPL; ++k) th[k] = th[k] - c.step_size * (m[k] * r[k]);
 
@@ -261,7 +271,7 @@ __device__ __forceinline__ void adamw_tile(const TensorDesc& d, int64_t e0, int 
     store8<2, FULL>(w16 + off * 2, wo, cnt[j]);
     store8<EB, FULL>(ecc + off * EB, eo, cnt[j]);
 
-    float mmax = 0.0f, xmax = 0.0f;
+    float mmax = __builtin_nanf(""), xmax = __builtin_nanf("");
 #pragma unroll
     for (int k = 0; k < EPL; ++k) {
       const float x = (CODEC == COMPANDED) ? w[k] : v[k];
@@ -294,21 +304,25 @@ __device__ __forceinline__ void adamw_tile(const TensorDesc& d, int64_t e0, int 
     cv_own = (sv2 > 0.0f) ? 255.0f / sv2 : 0.0f;
   }
 
+  auto encode = [&](auto maybe_nan) {
 #pragma unroll
-  for (int j = 0; j < NSUB; ++j) {
-    const float cm = bcast_j(cm_own, j), cv = bcast_j(cv_own, j);
-    uint32_t qm[EPL], vo[2] = {0u, 0u};
+    for (int j = 0; j < NSUB; ++j) {
+      const float cm = bcast_j(cm_own, j), cv = bcast_j(cv_own, j);
+      uint32_t qm[EPL], vo[2] = {0u, 0u};
 #pragma unroll
-    for (int k = 0; k < EPL; ++k) {
-      qm[k] = (uint32_t)((CODEC == COMPANDED) ? encode_m_companded(Mn[j][k], cm, tabs)
-                                              : encode_m_linear(Mn[j][k], cm));
-      vo[k >> 2] = encode_v_into(Xn[j][k], cv, k & 3, vo[k >> 2]);
+      for (int k = 0; k < EPL; ++k) {
+        qm[k] = (uint32_t)((CODEC == COMPANDED) ? encode_m_companded(Mn[j][k], cm, tabs)
+                                                : encode_m_linear(Mn[j][k], cm));
+        vo[k >> 2] = encode_v_into<decltype(maybe_nan)::value>(Xn[j][k], cv, k & 3, vo[k >> 2]);
+      }
+      const uint32_t mo[2] = {pack4_byte0(qm[0], qm[1], qm[2], qm[3]), pack4_byte0(qm[4], qm[5], qm[6], qm[7])};
+      const int off = j * SUB + lane * EPL;
+      store8<1, FULL>(mq + off, mo, cnt[j]);
+      store8<1, FULL>(vq + off, vo, cnt[j]);
     }
-    const uint32_t mo[2] = {pack4_byte0(qm[0], qm[1], qm[2], qm[3]), pack4_byte0(qm[4], qm[5], qm[6], qm[7])};
-    const int off = j * SUB + lane * EPL;
-    store8<1, FULL>(mq + off, mo, cnt[j]);
-    store8<1, FULL>(vq + off, vo, cnt[j]);
-  }
+  };
+  if (any_wide) encode(std::true_type{});
+  else encode(std::false_type{});
 }
 
 // ---------------------------------------------------------------------------
@@ -352,7 +366,7 @@ __device__ __forceinline__ void sgdm_tile(const TensorDesc& d, int64_t e0, int l
   for (int j = 0; j < NSUB; ++j) {
     const float db = bcast_j(db_own, j);
     float th[EPL], b[EPL];
-    float bmax = 0.0f;
+    float bmax = __builtin_nanf("");          // all-NaN block -> NaN scale
 #pragma unroll
     for (int k = 0; k < EPL; ++k) {
       const float g = wid<WFMT>(G[j], k);
@@ -647,7 +661,7 @@ __global__ void __launch_bounds__(WG) k_quantize(const float* __restrict__ x, in
 #pragma unroll
       for (int k = 0; k < 8; ++k) e[k] = v[k];
     }
-    float mx = 0.0f;
+    float mx = __builtin_nanf("");            // all-NaN block -> NaN scale
 #pragma unroll
     for (int k = 0; k < 8; ++k) mx = fmaxf(mx, (KIND == 0) ? fabsf(e[k]) : e[k]);
     mx = quad_max(mx);

@@ -148,6 +148,34 @@ def test_quantize_dequantize_match_oracle(kind, codec, n):
     assert np.array_equal(out.cpu().numpy().view(np.uint32), d_ref.view(np.uint32))
 
 
+@pytest.mark.parametrize("kind", ["m", "v"])
+@pytest.mark.parametrize("codec", ["companded", "linear"])
+def test_quantize_special_values(kind, codec):
+    """NaN, infinities, values that saturate the fp16 scale, signed zeros and
+    subnormals, alone and mixed with ordinary values in a block."""
+    rng = np.random.default_rng(41)
+    sp = np.array([np.nan, np.inf, -np.inf, 3.0e38, -3.0e38, 1.0e6, -1.0e6, 65504.0, 65520.0, -0.0, 0.0,
+                   1e-45, -1e-45, 1e-30, 6.0e-8, 1.0], np.float32)
+    if kind == "v":
+        sp = np.where(np.isnan(sp), sp, np.abs(sp)).astype(np.float32)
+    blocks = [np.full(32, v, np.float32) for v in sp]
+    for v in sp:
+        b = (rng.standard_normal(32) * 0.01).astype(np.float32)
+        if kind == "v":
+            b = b * b
+        b[rng.integers(0, 32)] = v
+        blocks.append(b)
+    x = np.concatenate(blocks + [sp[:7]])
+    q_ref, s_ref = O.quantize_state(x, kind, codec)
+    n = x.size
+    codes = torch.empty(n, dtype=torch.int8 if kind == "m" else torch.uint8, device="cuda")
+    scales = torch.empty(-(-n // 32), dtype=torch.float16, device="cuda")
+    B.fo_companded_quantize(torch.from_numpy(x).cuda(), codes, scales, kind, codec)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(scales), s_ref)
+    assert np.array_equal(to_host(codes), q_ref)
+
+
 def _oracle_code_steps():
     """Smallest f32 pattern in [0, 1] whose oracle momentum code (scale 1) is
     at least k + 1, for k = 0..126, by bisection over the patterns (the code
@@ -259,14 +287,22 @@ def test_fused_adamw_variants(fmt, ecc_bits, codec):
     print(f"variant {fmt}+{ecc_bits}/{codec}: {bad} mismatching elements", flush=True)
 
 
-def test_fused_adamw_nan_inf_grads_propagate():
-    def inject(i, step, g):
-        g = g.copy()
-        g[5] = np.nan
-        g[77] = np.inf
-        g[4000] = -np.inf
-        return g
-    _run_adamw([8192 + 5], 2, HP_C1, tag="nan", inject=inject)
+def _inject_specials(i, step, g):
+    """Isolated NaN/inf gradients, and whole 32-element blocks of NaN and of
+    inf: an all-NaN block gets a NaN scale, which keeps the state NaN."""
+    g = g.copy()
+    g[5] = np.nan
+    g[77] = np.inf
+    g[4000] = -np.inf
+    g[2048 + 64: 2048 + 96] = np.nan
+    g[6144 + 32: 6144 + 64] = np.inf
+    return g
+
+
+@pytest.mark.parametrize("fmt,ecc_bits,codec", [("bf16", 8, "companded"), ("fp16", 8, "companded"),
+                                                ("bf16", 16, "companded"), ("bf16", 8, "linear")])
+def test_fused_adamw_nan_inf_grads_propagate(fmt, ecc_bits, codec):
+    _run_adamw([8192 + 5], 3, HP_C1, fmt, ecc_bits, codec, tag="nan", inject=_inject_specials)
 
 
 @pytest.mark.parametrize("name,hp", [
@@ -314,7 +350,7 @@ def test_fused_adamw_late_step_and_zero_eps():
               f"{int(nan.sum())} NaN weights", flush=True)
 
 
-def _run_sgdm(sizes, steps, hp, fmt="bf16", ecc_bits=8, codec="companded", tag="s"):
+def _run_sgdm(sizes, steps, hp, fmt="bf16", ecc_bits=8, codec="companded", tag="s", inject=None):
     xs = [host_weights(tag, i, n) for i, n in enumerate(sizes)]
     dev = [alloc_sgdm_state(n, fmt, ecc_bits) for n in sizes]
     ref = [fresh_sgdm_state(x, fmt, ecc_bits) for x in xs]
@@ -325,7 +361,10 @@ def _run_sgdm(sizes, steps, hp, fmt="bf16", ecc_bits=8, codec="companded", tag="
     for step in range(1, steps + 1):
         gbs = []
         for i, (st, n) in enumerate(zip(dev, sizes)):
-            gb = host_grad_bits(host_grads(tag, i, step, n, "normal_outliers"), fmt)
+            g = host_grads(tag, i, step, n, "normal_outliers")
+            if inject is not None:
+                g = inject(i, step, g)
+            gb = host_grad_bits(g, fmt)
             gbs.append(gb)
             st["grad"].copy_(to_dev(gb, DT[fmt]))
         B.fo_fused_sgdm_step(tl, B.sgdm_hparams(step=step, wfmt=fmt, ecc_bits=ecc_bits, codec=codec, **hp))
@@ -333,13 +372,22 @@ def _run_sgdm(sizes, steps, hp, fmt="bf16", ecc_bits=8, codec="companded", tag="
             ref[i] = O.sgdm_step(ref[i], gbs[i], dict(hp, step=step), fmt, ecc_bits, codec)
         torch.cuda.synchronize()
         for i in range(len(sizes)):
-            bad = check_sgdm_state(f"sgdm step {step} tensor {i} (n={sizes[i]})", sgdm_state_to_host(dev[i]),
-                                   ref[i], fmt, ecc_bits)
+            got = sgdm_state_to_host(dev[i])
+            if inject is not None:
+                nan = np.isnan(O.reconstruct_weights(ref[i]["w16"], ref[i]["ecc"], fmt, ecc_bits))
+                assert np.array_equal(nan, np.isnan(O.reconstruct_weights(got["w16"], got["ecc"], fmt, ecc_bits)))
+                got["w16"] = np.where(nan, ref[i]["w16"], got["w16"])
+            bad = check_sgdm_state(f"sgdm step {step} tensor {i} (n={sizes[i]})", got, ref[i], fmt, ecc_bits)
             total += sum(bad.values())
     return total
 
 
 HP_C4 = dict(lr=0.1, momentum=0.9, weight_decay=1e-4)
+
+
+@pytest.mark.parametrize("fmt,codec", [("bf16", "companded"), ("fp16", "companded"), ("bf16", "linear")])
+def test_fused_sgdm_nan_inf_grads_propagate(fmt, codec):
+    _run_sgdm([8192 + 5], 3, HP_C4, fmt, 8, codec, tag="snan", inject=_inject_specials)
 
 
 @pytest.mark.parametrize("fmt,ecc_bits,codec", [("bf16", 8, "companded"), ("bf16", 16, "companded"),
