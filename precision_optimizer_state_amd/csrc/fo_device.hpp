@@ -317,14 +317,12 @@ __device__ __forceinline__ float rcp_refined(float b) {
 // ---------------------------------------------------------------------------
 // State codecs
 // ---------------------------------------------------------------------------
-// Momentum encode by interval table: a = |z| is keyed by bits 17..30 of its f32
-// pattern (exponent and 6 mantissa bits), clamped to [2^-9, 1]: every a below
-// 2^-9 shares the first key, and every a from 1 on (also inf and NaN) the last.
-// Every key interval holds at most one of the code thresholds (2k+1)/(507-2k)
-// (checked exactly for all 577 keys; one mantissa bit fewer would put two
-// thresholds into some intervals just below 1), so
-// code(a) = menc[key].code + (a >= menc[key].thr), where an interval without a
-// threshold stores thr = NaN (the comparison is false: a >= 1 gives 127).
+// Momentum encode by interval table: a in [0,1] is keyed by the top 15 bits of
+// its f32 pattern (sign, exponent and 6 mantissa bits), counted from 2^-9 (every
+// a below 2^-9 shares key 0).  Every key interval holds at most one of the code
+// thresholds (2k+1)/(507-2k) (checked exactly for all 577 keys; one mantissa bit
+// fewer would put two thresholds into some intervals just below 1), so
+// code(a) = menc[key].code + (a >= menc[key].thr).
 struct MEnc { float thr; int32_t code; };
 constexpr int MENC_SHIFT = 17;
 constexpr uint32_t MENC_BASE = 0x3B000000u >> MENC_SHIFT;                 // 2^-9
@@ -362,10 +360,10 @@ __device__ __forceinline__ void build_tables(FO_GLOBAL CodecTables* out, float* 
       int code = 0;
       for (int k = 0; k < 127; ++k) code += (thr[k] <= lo) ? 1 : 0;
       e.code = code;
-      e.thr = (code < 127 && thr[code] < hi) ? thr[code] : __builtin_nanf("");
+      e.thr = (code < 127 && thr[code] < hi) ? thr[code] : 2.0f;
     } else {
       e.code = 127;
-      e.thr = __builtin_nanf("");
+      e.thr = 2.0f;
     }
     out->menc[key].thr = e.thr;
     out->menc[key].code = e.code;
@@ -373,13 +371,12 @@ __device__ __forceinline__ void build_tables(FO_GLOBAL CodecTables* out, float* 
 }
 
 // momentum, companded: z = m*R (R = RN32(1/s)); q = sign(z)*round(127*phi(min(|z|,1)))
-// (|z| > 1, inf and NaN take the last key: 127, with NaN -> +127)
 __device__ __forceinline__ int32_t encode_m_companded(float m, float R, const CodecTables& T) {
   const float z = m * R;
-  const uint32_t bits = __builtin_amdgcn_ubfe(f2u(z), MENC_SHIFT, 31 - MENC_SHIFT);   // of |z|
-  const uint32_t key = min(max(bits, MENC_BASE), MENC_BASE + (uint32_t)MENC_N - 1u);
-  const MEnc e = T.menc[key - MENC_BASE];
-  const int32_t q = e.code + (fabsf(z) >= e.thr ? 1 : 0);
+  const float a = fminf(fabsf(z), 1.0f);                  // NaN -> 1
+  const uint32_t key = __builtin_elementwise_sub_sat(f2u(a) >> MENC_SHIFT, MENC_BASE);
+  const MEnc e = T.menc[key];
+  const int32_t q = e.code + (a >= e.thr ? 1 : 0);
   return (z < 0.0f) ? -q : q;
 }
 
@@ -393,12 +390,10 @@ __device__ __forceinline__ int32_t encode_m_linear(float m, float C) {
 // variance: y = x*C, C = RN32(255/s) (companded, x = sqrt(v)) or RN32(255/s^2)
 // (linear, x = v); code = clamp(round_half_even(y), 0, 255) written into byte
 // `k` of `acc` (v_cvt_pk_u8_f32 rounds half to even and saturates; verified
-// against rint+clamp over every non-NaN f32 by fo_selftest).  It turns NaN into
-// 0, so NaN goes through fminf first (NaN -> 255); callers that know no
-// element of the wave is NaN pass MAYBE_NAN = false and skip it.
-template <bool MAYBE_NAN = true>
+// against rint+clamp over every non-NaN f32 by fo_selftest; it turns NaN into
+// 0, hence the fminf first).
 __device__ __forceinline__ uint32_t encode_v_into(float x, float C, uint32_t k, uint32_t acc) {
-  const float y = MAYBE_NAN ? fminf(x * C, 255.0f) : x * C;   // x*C >= 0
+  const float y = fminf(x * C, 255.0f);                    // x*C >= 0; NaN -> 255
   return __builtin_amdgcn_cvt_pk_u8_f32(y, k, acc);
 }
 

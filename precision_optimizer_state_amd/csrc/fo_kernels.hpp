@@ -24,8 +24,6 @@
 // sections 1 and 2) define what is computed; the launch structure is ours.
 #pragma once
 
-#include <type_traits>
-
 #include "fo_device.hpp"
 
 namespace fo {
@@ -171,9 +169,8 @@ __device__ __forceinline__ void sqrt8(const float (&v)[EPL], float (&w)[EPL]) {
 }
 
 // r = RN(1/d) for 8 denominators (IEEE division when any lane is outside the
-// verified range, or when eps does not keep denominators normal).  Returns
-// whether the wave took the IEEE path; a NaN or infinite d always does.
-__device__ __forceinline__ bool rcp8(const float (&d)[EPL], float (&r)[EPL], int fast) {
+// verified range, or when eps does not keep denominators normal)
+__device__ __forceinline__ void rcp8(const float (&d)[EPL], float (&r)[EPL], int fast) {
   uint64_t slow = fast ? 0ull : ~0ull;
 #pragma unroll
   for (int k = 0; k < EPL; ++k) {
@@ -184,7 +181,6 @@ __device__ __forceinline__ bool rcp8(const float (&d)[EPL], float (&r)[EPL], int
 #pragma unroll
     for (int k = 0; k < EPL; ++k) r[k] = 1.0f / d[k];
   }
-  return slow != 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -235,9 +231,6 @@ __device__ __forceinline__ void adamw_tile(const TensorDesc& d, int64_t e0, int 
   // zeros of a partial block included), so only an all-NaN block keeps NaN
   // and gets a NaN scale, which carries the NaN into the decoded state
   float own_mmax = 0.0f, own_xmax = 0.0f;
-  // some lane's denominator was NaN, infinite or beyond the fast reciprocal's
-  // range (wave-uniform); without that, no fresh v is NaN
-  bool any_wide = false;
 
 #pragma unroll
   for (int j = 0; j < NSUB; ++j) {
@@ -260,7 +253,7 @@ __device__ __forceinline__ void adamw_tile(const TensorDesc& d, int64_t e0, int 
     sqrt8(v, w);
 #pragma unroll
     for (int k = 0; k < EPL; ++k) den[k] = w[k] * c.ibc2 + c.eps;
-    any_wide |= rcp8(den, r, c.fast_rcp);
+    rcp8(den, r, c.fast_rcp);
 #pragma unroll
     for (int k = 0; k < EPL; ++k) th[k] = th[k] - c.step_size * (m[k] * r[k]);
 
@@ -304,25 +297,21 @@ __device__ __forceinline__ void adamw_tile(const TensorDesc& d, int64_t e0, int 
     cv_own = (sv2 > 0.0f) ? 255.0f / sv2 : 0.0f;
   }
 
-  auto encode = [&](auto maybe_nan) {
 #pragma unroll
-    for (int j = 0; j < NSUB; ++j) {
-      const float cm = bcast_j(cm_own, j), cv = bcast_j(cv_own, j);
-      uint32_t qm[EPL], vo[2] = {0u, 0u};
+  for (int j = 0; j < NSUB; ++j) {
+    const float cm = bcast_j(cm_own, j), cv = bcast_j(cv_own, j);
+    uint32_t qm[EPL], vo[2] = {0u, 0u};
 #pragma unroll
-      for (int k = 0; k < EPL; ++k) {
-        qm[k] = (uint32_t)((CODEC == COMPANDED) ? encode_m_companded(Mn[j][k], cm, tabs)
-                                                : encode_m_linear(Mn[j][k], cm));
-        vo[k >> 2] = encode_v_into<decltype(maybe_nan)::value>(Xn[j][k], cv, k & 3, vo[k >> 2]);
-      }
-      const uint32_t mo[2] = {pack4_byte0(qm[0], qm[1], qm[2], qm[3]), pack4_byte0(qm[4], qm[5], qm[6], qm[7])};
-      const int off = j * SUB + lane * EPL;
-      store8<1, FULL>(mq + off, mo, cnt[j]);
-      store8<1, FULL>(vq + off, vo, cnt[j]);
+    for (int k = 0; k < EPL; ++k) {
+      qm[k] = (uint32_t)((CODEC == COMPANDED) ? encode_m_companded(Mn[j][k], cm, tabs)
+                                              : encode_m_linear(Mn[j][k], cm));
+      vo[k >> 2] = encode_v_into(Xn[j][k], cv, k & 3, vo[k >> 2]);
     }
-  };
-  if (any_wide) encode(std::true_type{});
-  else encode(std::false_type{});
+    const uint32_t mo[2] = {pack4_byte0(qm[0], qm[1], qm[2], qm[3]), pack4_byte0(qm[4], qm[5], qm[6], qm[7])};
+    const int off = j * SUB + lane * EPL;
+    store8<1, FULL>(mq + off, mo, cnt[j]);
+    store8<1, FULL>(vq + off, vo, cnt[j]);
+  }
 }
 
 // ---------------------------------------------------------------------------
