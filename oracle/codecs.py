@@ -20,8 +20,9 @@ What the pages fix:
 Readings:
 
 C1  Block = 32 consecutive elements of the flattened tensor; the last block
-    holds n mod 32 elements.  The absmax ignores NaN (IEEE maxNum) and, for a
-    short last block, covers only the valid elements (zero padding is
+    holds n mod 32 elements.  The absmax ignores NaN (IEEE maxNum), so only a
+    block that is NaN throughout has a NaN absmax (and a NaN scale); for a
+    short last block it covers only the valid elements (zero padding is
     equivalent because every candidate is >= 0).
 C2  Scale format: IEEE binary16.  Momentum: s = RU16(max |m|).  Variance:
     s = RU16(sqrt_rn(max v)) -- the scale lives in the square-root domain, so

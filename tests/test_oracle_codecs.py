@@ -205,3 +205,20 @@ def test_momentum_decode_of_minus_128():
     ml = O.decode_momentum(q, sb, "linear")
     step = np.float32(4.0) * np.float32(1.0 / 127.0)
     assert ml[0] == step * np.float32(-128.0) and ml[1] == step * np.float32(-127.0)
+
+
+def test_block_absmax_ignores_nan_unless_all_nan():
+    # maxNum: a NaN element is skipped; a block with nothing but NaN keeps NaN
+    x = np.zeros(96, np.float32)
+    x[:32] = np.nan
+    x[32:64] = np.linspace(-2.0, 1.0, 32, dtype=np.float32)
+    x[40] = np.nan
+    x[64:96] = np.nan
+    x[95] = 0.25
+    for kind in ("m", "v"):
+        s = O.block_scales(np.abs(x) if kind == "v" else x, kind)
+        assert s[0] == 0x7E00
+        want1 = 0x4000 if kind == "m" else O.ru_fp16_bits(np.sqrt(np.array([2.0], np.float32)))[0]
+        assert s[1] == want1
+        want2 = 0x3400 if kind == "m" else 0x3800          # 0.25, and sqrt(0.25) = 0.5
+        assert s[2] == want2
