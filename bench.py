@@ -49,7 +49,7 @@ def kernel_source_hash() -> str:
 
 # the library launches a list as consecutive ranges of at most this many
 # 2048-element wave tiles (one kernel each)
-LAUNCH_TILES = 1 << 17
+LAUNCH_TILES = 1 << 18
 
 
 def launches_per_call(numels) -> int:
@@ -433,7 +433,7 @@ def main(argv=None):
         },
         "kernel_ms_avg": avg_ms,
         # dispatches of the fused kernel per step (the list is launched in
-        # ranges of 2^17 tiles); kernel_ms_avg and roofline cover all of them
+        # ranges of 2^18 tiles); kernel_ms_avg and roofline cover all of them
         "launches_per_step": (sum(launches_per_call([m]) for m in release) if release
                               else launches_per_call(cfg.numels)),
         "stream_probe_gbs": probe_gbs,

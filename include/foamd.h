@@ -157,7 +157,7 @@ typedef struct fo_adamw_hparams {
  * fo_fused_adamw_step -- [UPDATE] with [SPLIT] and [STATE]
  * One AdamW step (decoupled weight decay, bias correction, step >= 1) over a
  * list of `count` tensors, enqueued on `stream` as one kernel per range of
- * 2^17 wave tiles (2^28 elements; one kernel for most lists); with
+ * 2^18 wave tiles (2^29 elements; one kernel for most lists); with
  * hp->l2_decay = 1 the step is Adam with the weight decay added to the
  * gradient (torch.optim.Adam).  Per element: widen the gradient,
  * reconstruct the f32 master, decode m and v, update in float32 with a fixed

@@ -12,7 +12,7 @@
 //     block: lane 4Q+j owns block (sub-tile j, quad Q), and the results are
 //     broadcast back to the quad with one DPP quad permute per sub-tile.
 //   * A launch covers a range of the step's wave tiles with one wave per tile
-//     (the host issues one launch per 2^17 tiles; the tile loop below also
+//     (the host issues one launch per 2^18 tiles; the tile loop below also
 //     serves smaller grids).  A tile never crosses a tensor, and the last tile
 //     of a tensor takes a masked path; the tensor of a tile is found through a
 //     tile-bucket index built by the host.

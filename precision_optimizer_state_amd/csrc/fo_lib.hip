@@ -98,10 +98,12 @@ int device_tables(int dev, hipStream_t stream, const CodecTables** out) {
 // persistent waves for this read/write mix (new workgroups keep the memory
 // pipeline full while finished ones retire).
 // A list is launched as consecutive ranges of at most kLaunchTiles wave
-// tiles (2^28 elements), one kernel each, all reading the same table.  On the
-// Llama-3.1-8B list (291 tensors, 3.9M tiles) this measured 2-4% faster than
-// one launch over every tile; lists up to that size are one launch.
-constexpr int64_t kLaunchTiles = int64_t(1) << 17;
+// tiles (2^29 elements), one kernel each, all reading the same table.  On the
+// Llama-3.1-8B list (291 tensors, 3.9M tiles) one launch over every tile ran
+// 7-9% slower than ranges; of the range sizes 2^16..2^20, 2^18 measured best
+// (0.3-0.6% ahead of 2^17, 1-2% of 2^19, 3-4% of 2^20).  Lists up to that
+// size are one launch.
+constexpr int64_t kLaunchTiles = int64_t(1) << 18;
 
 // waves per workgroup of the AdamW step and probe kernels (their launch bounds)
 int adamw_waves(int ecc_bits) { return ecc_bits == 16 ? adamw_tile_waves<16> : adamw_tile_waves<8>; }

@@ -1,6 +1,6 @@
 """bench.py's command-line contract that needs no GPU: more than one GPU is
 refused with a message, and the launch count it reports matches the
-library's 2^17-tile launch ranges."""
+library's 2^18-tile launch ranges."""
 
 import os
 import subprocess
@@ -23,8 +23,8 @@ def test_launch_count_follows_the_tile_ranges():
     from workloads import config
     from workloads.configs import RELEASE_CHUNKS
     assert bench.launches_per_call([1]) == 1
-    assert bench.launches_per_call([2048 << 17]) == 1
-    assert bench.launches_per_call([(2048 << 17) + 1]) == 2
-    assert bench.launches_per_call(config("c3_llama8b").numels) == 30
-    assert bench.launches_per_call(config("c5_flat1g_bf16e8").numels) == 4
+    assert bench.launches_per_call([2048 << 18]) == 1
+    assert bench.launches_per_call([(2048 << 18) + 1]) == 2
+    assert bench.launches_per_call(config("c3_llama8b").numels) == 15
+    assert bench.launches_per_call(config("c5_flat1g_bf16e8").numels) == 2
     assert sum(bench.launches_per_call([m]) for m in RELEASE_CHUNKS) == len(RELEASE_CHUNKS)
