@@ -16,6 +16,10 @@
 //     serves smaller grids).  A tile never crosses a tensor, and the last tile
 //     of a tensor takes a masked path; the tensor of a tile is found through a
 //     tile-bucket index built by the host.
+//   * Each wave of a fused step copies the 6-KiB codec tables into its own
+//     LDS with asynchronous buffer-to-LDS loads issued ahead of its tile's
+//     loads; no wave waits for another, so these kernels run one wave per
+//     workgroup (four for AdamW with a 16-bit ECC, see adamw_tile_waves).
 //   * Rare inputs (NaN/Inf/overflowing weights, tiny variances, out-of-range
 //     denominators) leave the fast arithmetic through wave-uniform branches
 //     onto IEEE sequences; the results are identical either way.
