@@ -82,8 +82,10 @@ __device__ __forceinline__ float ecc_decode(float t, int32_t rho) {
     if (fabsf(t) > 0x1p-14f)                     // |theta'| above the smallest fp16 normal (or inf)
       return u2f(f2u(t) + ((uint32_t)rho << 5)); // one fp16 spacing = 2^13 f32 spacings
     // zero, subnormal and the smallest normal (and NaN, which stays NaN): spacing
-    // 2^-24 on both sides; the offset rho * 2^-32 (exact) is applied to the magnitude
-    return t + (float)rho * __builtin_copysignf(0x1p-32f, t);
+    // 2^-24 on both sides; the offset rho * 2^-32 (exact) is applied to the magnitude.
+    // Product and sum are both exact here, so one fused multiply-add gives the
+    // same value as the separate operations.
+    return __builtin_fmaf((float)rho, __builtin_copysignf(0x1p-32f, t), t);
   }
 }
 
@@ -209,7 +211,9 @@ __device__ __forceinline__ void split8(const float (&x)[8], uint32_t (&wo)[4], u
     // the binade under it.  RNE and RNA differ only on an exact tie that RNE
     // rounded towards zero, which shows as d * 2^k == +128 exactly: then
     // theta' moves one pattern away from zero and rho = -128.  Any other value
-    // rounding to 128 clamps to 127.
+    // rounding to 128 clamps to 127.  rho is rounded half to even by adding
+    // 1.5 * 2^23 (|d * 2^k| <= 128): the sum's pattern is 0x4B400000 + rho,
+    // whose low byte is rho's two's-complement byte.
     uint64_t special = 0;
 #pragma unroll
     for (int k = 0; k < 8; ++k) special |= __builtin_amdgcn_ballot_w64(!(fabsf(x[k]) < 65520.0f));
@@ -224,9 +228,9 @@ __device__ __forceinline__ void split8(const float (&x)[8], uint32_t (&wo)[4], u
         const int sh = 145 - max(eb, 113);
         const float rf = __builtin_ldexpf(d, sh);
         const bool tie = (rf == 128.0f);
-        const int32_t r = min((int32_t)__builtin_rintf(rf), 127);
+        const uint32_t rb = min(f2u(rf + 0x1.8p23f), 0x4B40007Fu);   // rho <= 127
         H[k] = (uint32_t)__builtin_bit_cast(uint16_t, hh) + (tie ? 1u : 0u);
-        R[k] = (uint32_t)(tie ? -128 : r);
+        R[k] = tie ? 0x4B3FFF80u : rb;                               // low byte: rho (tie: -128)
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) wo[i] = perm(H[2 * i + 1], H[2 * i], 0x05040100u);
