@@ -159,17 +159,13 @@ __device__ __forceinline__ uint32_t perm(uint32_t hi_src, uint32_t lo_src, uint3
 __device__ __forceinline__ uint32_t pack4_byte0(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
   return perm(perm(d, c, 0x0C0C0400u), perm(b, a, 0x0C0C0400u), 0x05040100u);
 }
-// byte 1 of four words -> one packed word
-__device__ __forceinline__ uint32_t pack4_byte1(uint32_t a, uint32_t b, uint32_t c, uint32_t d) {
-  return perm(perm(d, c, 0x0C0C0501u), perm(b, a, 0x0C0C0501u), 0x05040100u);
-}
 
 // Split of 8 consecutive values into packed theta' (4 dwords) and ECC (ECC/4
 // dwords).  bf16 fast path, valid while every value of the wave is below the
 // bf16 overflow tie and not NaN: theta' = high half of (bits + 0x8000) (RNA on
-// the magnitude; the sign bit is untouched), ECC8 = byte 1 of
-// min(sext16(bits) + 127 + bit8, 32767) (round-half-even of the offset / 256,
-// clamped at 127), ECC16 = the low half of the pattern (the offset itself).
+// the magnitude; the sign bit is untouched), ECC8 = round-half-even of
+// sext16(low half) / 256 clamped at 127, ECC16 = the low half of the pattern
+// (the offset itself).
 // fp16 fast path below.  Otherwise every element goes through ecc_encode.
 template <int WFMT, int ECC>
 __device__ __forceinline__ void split8(const float (&x)[8], uint32_t (&wo)[4], uint32_t (&eo)[ECC / 4]) {
@@ -184,15 +180,20 @@ __device__ __forceinline__ void split8(const float (&x)[8], uint32_t (&wo)[4], u
 #pragma unroll
       for (int i = 0; i < 4; ++i) wo[i] = perm(t[2 * i + 1], t[2 * i], 0x07060302u);
       if constexpr (ECC == 8) {
-        uint32_t S[8];
+        // rho = round_half_even(L / 256) clamped to 127, L = sext16(low half):
+        // 128 + L/256 is exact in one FMA, v_cvt_pk_u8_f32 rounds it half to
+        // even, saturates at 255 (rho = 127) and writes it into its byte, and
+        // the XOR with 0x80 turns offset binary into two's complement (checked
+        // against the integer form on all 2^16 low halves)
+        uint32_t e0 = 0u, e1 = 0u;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const uint32_t xb = f2u(x[k]);
-          const int32_t L = ((int32_t)(xb << 16)) >> 16;
-          S[k] = (uint32_t)min(L + 127 + (int32_t)((xb >> 8) & 1u), 32767);
+          const float y = __builtin_fmaf((float)(int16_t)f2u(x[k]), 0x1p-8f, 128.0f);
+          if (k < 4) e0 = __builtin_amdgcn_cvt_pk_u8_f32(y, k, e0);
+          else e1 = __builtin_amdgcn_cvt_pk_u8_f32(y, k - 4, e1);
         }
-        eo[0] = pack4_byte1(S[0], S[1], S[2], S[3]);
-        eo[1] = pack4_byte1(S[4], S[5], S[6], S[7]);
+        eo[0] = e0 ^ 0x80808080u;
+        eo[1] = e1 ^ 0x80808080u;
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) eo[i] = perm(f2u(x[2 * i + 1]), f2u(x[2 * i]), 0x05040100u);
