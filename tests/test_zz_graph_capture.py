@@ -23,19 +23,23 @@ def _state(n, tag):
     return st
 
 
-def test_captured_step_replays_match_eager_calls():
-    n = 300_000 + 77
+@pytest.mark.parametrize("sizes", [[300_000 + 77],
+                                   # two tensors over more than 2^18 wave tiles: the step is
+                                   # two launches (two kernel nodes in the graph)
+                                   [(1 << 29) - 5000, 3 * (1 << 20) + 77]],
+                         ids=["one_launch", "two_launches"])
+def test_captured_step_replays_match_eager_calls(sizes):
     hp = B.adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 5)
-    a = _state(n, "graph")
-    tl_a = B.AdamWList([a])
+    al = [_state(n, f"graph{i}") for i, n in enumerate(sizes)]
+    tl_a = B.AdamWList(al)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
         B.fo_fused_adamw_step(tl_a, hp)              # warm-up: codec tables and launch table exist
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
-    b = {k: v.clone() for k, v in a.items()}         # eager twin of the state
-    tl_b = B.AdamWList([b])
+    bl = [{k: v.clone() for k, v in a.items()} for a in al]   # eager twins of the states
+    tl_b = B.AdamWList(bl)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         B.fo_fused_adamw_step(tl_a, hp)
@@ -45,6 +49,7 @@ def test_captured_step_replays_match_eager_calls():
         junk = torch.randn(1 << 20, device="cuda").sum()    # unrelated eager work between replays
         torch.cuda.synchronize()
         assert torch.isfinite(junk)
-        for k in KEYS:
-            assert torch.equal(a[k].view(torch.uint8), b[k].view(torch.uint8)), f"replay {r}: {k} differs"
-    print("graph replays: 4 replays bitwise equal to eager calls", flush=True)
+        for i, (a, b) in enumerate(zip(al, bl)):
+            for k in KEYS:
+                assert torch.equal(a[k].view(torch.uint8), b[k].view(torch.uint8)), f"replay {r}: tensor {i} {k} differs"
+    print(f"graph replays ({len(sizes)} tensors): 4 replays bitwise equal to eager calls", flush=True)
