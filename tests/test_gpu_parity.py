@@ -91,6 +91,28 @@ def test_reconstruct_matches_oracle_bitwise(fmt, ecc_bits):
     assert np.array_equal(got[~nan].view(np.uint32), r_ref[~nan].view(np.uint32))
 
 
+@pytest.mark.parametrize("fmt", ["bf16", "fp16"])
+def test_reconstruct_every_pattern_and_offset(fmt):
+    """ECC decode (the device function the fused steps use) on every finite
+    16-bit pattern with every 8-bit offset, against the oracle.  The domain is
+    the one reconstruction is defined on: rho >= 0 when theta' is +-0."""
+    h = np.arange(0, 0x10000, dtype=np.uint32).astype(np.uint16)
+    h = h[np.isfinite(bits_to_value(h, fmt))]
+    rho = np.arange(-128, 128, dtype=np.int64)
+    H = np.repeat(h, rho.size)
+    R = np.tile(rho, h.size)
+    keep = ~(((H & 0x7FFF) == 0) & (R < 0))
+    H, R = H[keep], R[keep].astype(np.int8)
+    want = O.reconstruct_weights(H, R, fmt, 8)
+    out = torch.empty(H.size, dtype=torch.float32, device="cuda")
+    B.fo_reconstruct_weights(to_dev(H, DT[fmt]), to_dev(R, torch.int8), out, fmt, 8)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    bad = int(np.count_nonzero(got.view(np.uint32) != want.view(np.uint32)))
+    print(f"decode {fmt}+8 over {H.size} (pattern, offset) pairs: {bad} mismatches", flush=True)
+    assert bad == 0
+
+
 def test_bf16_ecc16_identity_all_f32_patterns_on_device():
     """split -> reconstruct with bf16 + 16-bit ECC is the identity on every
     finite f32 below the bf16 overflow tie: all 2^32 patterns, on the device."""
