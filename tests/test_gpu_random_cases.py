@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 DT = {"bf16": torch.bfloat16, "fp16": torch.float16}
 FORMATS = [("bf16", 8), ("bf16", 16), ("fp16", 8)]
-N_CASES = 40
+N_CASES = 120
 
 
 def _case(i):
