@@ -15,6 +15,14 @@ that many small tensors share one fused call.
 All arithmetic runs in the HIP library (fo_fused_adamw_step /
 fo_fused_sgdm_step); this module only groups tensors and keeps step counts.
 FlashAdamW, FlashAdam and FlashSGD follow torch.optim.AdamW, Adam and SGD.
+
+Between steps the optimizers keep the device addresses of each parameter's
+state tensors (ECC, codes, scales); only theta' and gradient addresses are
+read at every step.  State changes through load_state_dict(),
+import_torch_state(), import_torch_optimizer() and load_master_weights() are
+safe (they write in place or drop the kept addresses).  Code that replaces a
+state tensor in `optimizer.state` by other means must call
+invalidate_launch_cache() before the next step.
 """
 
 from __future__ import annotations
@@ -242,8 +250,7 @@ class _FlashBase(torch.optim.Optimizer):
         raw = {k: {kk: vv for kk, vv in v.items() if torch.is_tensor(vv)}
                for k, v in state_dict["state"].items()}
         super().load_state_dict(state_dict)
-        self._plans.clear()
-        self._lists.clear()
+        self.invalidate_launch_cache()
         self._group_of = {}
         params = [p for g in self.param_groups for p in g["params"]]
         for pid, p in zip(saved_ids, params):
@@ -251,6 +258,12 @@ class _FlashBase(torch.optim.Optimizer):
                 self.state[p][key] = val.to(device=p.device).clone()
             if "step" in self.state[p]:
                 self.state[p]["step"] = int(self.state[p]["step"])
+
+    def invalidate_launch_cache(self):
+        """Forget the kept state addresses and marshalled launch lists (after
+        state tensors were replaced outside this class's methods)."""
+        self._plans.clear()
+        self._lists.clear()
 
     def remove_hooks(self):
         for h in self._hooks:

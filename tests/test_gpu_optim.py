@@ -134,6 +134,26 @@ def test_state_dict_resume_is_bitwise():
         assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
 
 
+def test_replaced_state_tensors_after_invalidate_launch_cache():
+    """State tensors swapped by hand (clones at new addresses, the old ones
+    freed) are picked up after invalidate_launch_cache(): the run stays bitwise
+    equal to an untouched twin."""
+    a, b = _model(5), _model(5)
+    oa, ob = FlashAdamW(a.parameters(), **HP), FlashAdamW(b.parameters(), **HP)
+    _train(a, oa, 2)
+    _train(b, ob, 2)
+    for p in b.parameters():
+        st = ob.state[p]
+        for k in ("ecc", "m_q", "m_s", "v_q", "v_s"):
+            st[k] = st[k].clone()
+    ob.invalidate_launch_cache()
+    torch.cuda.synchronize()
+    _train(a, oa, 2, start=3)
+    _train(b, ob, 2, start=3)
+    for x, y in zip(_snapshot(a, oa), _snapshot(b, ob)):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+
+
 def test_checkpoint_through_torch_save_and_safe_load_resumes_bitwise():
     """state_dict() written with torch.save and read back with
     torch.load(weights_only=True) (no unpickling of code) resumes bit for bit."""
