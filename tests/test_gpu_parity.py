@@ -6,6 +6,8 @@ Runs are free-running from the same seeded inputs (no state is ever copied
 from the GPU into the oracle).
 """
 
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -110,6 +112,31 @@ def test_reconstruct_every_pattern_and_offset(fmt):
     got = out.cpu().numpy()
     bad = int(np.count_nonzero(got.view(np.uint32) != want.view(np.uint32)))
     print(f"decode {fmt}+8 over {H.size} (pattern, offset) pairs: {bad} mismatches", flush=True)
+    assert bad == 0
+
+
+@pytest.mark.skipif(os.environ.get("FO_EXHAUSTIVE") != "1",
+                    reason="every f32 pattern through the oracle takes ~3 min per format; set FO_EXHAUSTIVE=1")
+@pytest.mark.parametrize("fmt", ["bf16", "fp16"])
+def test_split_ecc8_every_f32_pattern(fmt):
+    """The 8-bit-ECC split of all 2^32 f32 patterns against the oracle: theta'
+    for every non-NaN input and rho for every input (NaN theta' is checked in
+    test_split_matches_oracle_bitwise)."""
+    bad = 0
+    for c0 in range(0, 1 << 32, 1 << 28):
+        x = np.arange(c0, c0 + (1 << 28), dtype=np.uint64).astype(np.uint32).view(np.float32)
+        w = torch.empty(x.size, dtype=DT[fmt], device="cuda")
+        e = torch.empty(x.size, dtype=torch.int8, device="cuda")
+        B.fo_split_weights(torch.from_numpy(x).cuda(), w, e, fmt, 8)
+        torch.cuda.synchronize()
+        wg, eg = to_host(w), to_host(e)
+        for s0 in range(0, x.size, 1 << 23):
+            xs = x[s0:s0 + (1 << 23)]
+            wr, er = O.split_weights(xs, fmt, 8)
+            bw = (wg[s0:s0 + (1 << 23)] != wr) & ~np.isnan(xs)
+            bad += int(np.count_nonzero(bw | (eg[s0:s0 + (1 << 23)] != er)))
+        print(f"split {fmt}+8: patterns below {c0 + (1 << 28):#x}: {bad} mismatches", flush=True)
+        del w, e
     assert bad == 0
 
 
