@@ -43,6 +43,7 @@ from .codecs import (  # noqa: F401
     quantize_state,
     dequantize_state,
     momentum_lut,
+    level_spacing,
 )
 from .optim import (  # noqa: F401
     adamw_scalars,
@@ -51,4 +52,5 @@ from .optim import (  # noqa: F401
     sgdm_update,
     adamw_step,
     sgdm_step,
+    sgdm_first,
 )

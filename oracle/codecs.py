@@ -20,49 +20,59 @@ What the pages fix:
 Readings:
 
 C1  Block = 32 consecutive elements of the flattened tensor; the last block
-    holds n mod 32 elements.  The absmax ignores NaN (IEEE maxNum), so only a
-    block that is NaN throughout has a NaN absmax (and a NaN scale); for a
-    short last block it covers only the valid elements (zero padding is
-    equivalent because every candidate is >= 0).
+    holds n mod 32 elements and only those count.  The absmax ignores NaN
+    (IEEE maxNum), so a block whose valid elements are all NaN -- a short last
+    block included -- has a NaN absmax and a NaN scale.  (Padding the short
+    block with NaN, which maxNum skips, gives exactly that.)
 C2  Scale format: IEEE binary16.  Momentum: s = RU16(max |m|).  Variance:
     s = RU16(sqrt_rn(max v)) -- the scale lives in the square-root domain, so
     it never underflows where max v would.  RU16 = smallest binary16 >= the
     value; above 65504 it saturates at 65504; NaN -> NaN.
-C3  Momentum compander (softsign-like): z = m * R with R = RN32(1/s) per
-    block (0 when s = 0); q = sign(z) * round_half_even(127 * phi(min(|z|,1)))
-    with phi(a) = 2a / (1 + a), phi(0) = 0, phi(1) = 1.  The rounding is the
-    exact one of the real number 127*phi(a) for the float32 a; no ties exist
-    (each threshold (2k+1)/(507-2k) has an odd denominator > 1).
-    Decode: m = RN32(s * LUT[q]) with LUT[q] = RN32(q / (254 - |q|)), the
+C3  Momentum compander (softsign-like).  Normalise, then compand: z = m / s,
+    one IEEE float32 division; q = sign(z) * round_half_even(127 * phi(a)),
+    a = min(|z|, 1), phi(a) = 2a / (1 + a), phi(0) = 0, phi(1) = 1.  The
+    rounding is the exact one of the real number 127*phi(a) for the float32
+    a; no ties exist (each threshold (2k+1)/(507-2k) has an odd denominator
+    > 1).  Decode: m = RN32(s * LUT[q]), LUT[q] = RN32(q / (254 - |q|)), the
     inverse of phi at q/127.  Codes in [-127, 127].
-C4  Variance compander (square root): C = RN32(255/s) per block (0 when
-    s = 0); q = clamp(round_half_even(RN32(sqrt_rn(v) * C)), 0, 255).
-    Decode: t = RN32(RN32(s * K255) * q) with K255 = RN32(1/255); v = RN32(t*t).
-    The decoded levels are (k/255)^2 * s^2: a linear-square grid.
-C5  Linear ablation (no companding), same scales as C2:
-    momentum q = clamp(rint(RN32(m * RN32(127/s))), -127, 127),
-             decode RN32(RN32(s * K127) * q), K127 = RN32(1/127);
-    variance q = clamp(rint(RN32(v * RN32(255/(s*s)))), 0, 255),
-             decode RN32(RN32(RN32(s*s) * K255) * q).
-C6  Codes are clamped to range before rounding (IEEE minNum/maxNum, which
-    send NaN to the upper bound): a NaN momentum element gets +127 and a NaN
-    variance element 255, under either codec.
+C4  Variance compander (square root).  Compand, normalise, scale to the code
+    range, each step one float32 operation: w = sqrt_rn(v), z = w / s,
+    y = 255 * z, q = clamp(round_half_even(y), 0, 255).  Decode with the
+    block's level spacing D = RN32(s / 255): t = RN32(D * q), v = RN32(t * t).
+    The decoded levels are (k * s/255)^2: a linear-square grid.
+C5  Linear ablation (no companding), same scales as C2.  Momentum:
+    z = m / s, y = 127 * z, q = clamp(round_half_even(y), -127, 127); decode
+    m = RN32(D * q), D = RN32(s / 127).  Variance: s2 = s * s (exact),
+    z = v / s2, y = 255 * z, q = clamp(round_half_even(y), 0, 255); decode
+    v = RN32(D * q), D = RN32(s2 / 255).
+C6  A NaN element has no nearest level: it gets code 0, and values beyond the
+    code range (+-Inf, or finite values past a saturated scale) clamp to the
+    end codes.  That is the rule of a saturating float-to-integer conversion
+    (Java's and Rust's casts, WebAssembly's trunc_sat: out-of-range values
+    clamp, NaN gives 0).  A NaN element therefore decodes to 0 on the next
+    step, the value of a fresh state; the NaN survives in the state only when
+    it fills its block (C1), whose NaN scale decodes every code to NaN.  An
+    all-zero block has s = 0, and 0/0 = NaN codes its elements 0 as well.
 C7  The one int8 pattern outside the momentum code range, -128, is never
     written by the encoder.  Stored states may still hold it, so decode
     defines it: the companded LUT saturates it to -127 (so every code decodes
     into [-s, s]); the linear decode is the plain product for every int8.
 
-RN32(.) is one IEEE float32 rounding; numpy float32 arithmetic provides it.
-Where floating point decides a code, the decision is taken in float32 (the
-kernel's precision) except the companded momentum rounding, which is the exact
-rounding of 127*phi(a) (float64 evaluation is exact for that decision:
+RN32(.) is one IEEE float32 rounding; numpy float32 arithmetic provides it
+(its division and square root are the correctly rounded IEEE operations).
+Every quotient above is such a division: there is no reciprocal-multiply
+anywhere.  Where floating point decides a code, the decision is taken on
+float32 values; the companded momentum rounding alone is evaluated exactly
+for its float32 argument (float64 is exact for that decision:
 |127*phi(a) - (k+1/2)| >= 2^-35 for every float32 a near a threshold, far
 above float64's error).
 
 Parity status: pinned (invertibility, monotone decode, phi(0)=0 and
 phi(+-1)=+-1, exhaustive half-step bound over float32 z in [-1, 1] sampled
-densely, hand-computed golden codes, RU16 against numpy's binary16 cast,
-companded-vs-linear error on heavy-tailed data; tests/test_oracle_codecs.py).
+densely, hand-computed golden codes, exact-rational codes for inputs where a
+reciprocal-multiply would differ from the division, RU16 against numpy's
+binary16 cast, companded-vs-linear error on heavy-tailed data, NaN and
+infinity codes, NaN-filled short last blocks; tests/test_oracle_codecs.py).
 """
 
 from __future__ import annotations
@@ -74,8 +84,7 @@ from .numerics import FORMATS, _exponent, f16_bits_to_f32
 BLOCK = 32
 F16 = FORMATS["fp16"]
 F16_MAX = 65504.0
-K127 = np.float32(1.0) / np.float32(127.0)
-K255 = np.float32(1.0) / np.float32(255.0)
+F32 = np.float32
 
 
 def ru_fp16_bits(x32: np.ndarray) -> np.ndarray:
@@ -92,10 +101,11 @@ def ru_fp16_bits(x32: np.ndarray) -> np.ndarray:
 
 
 def _blocks(x: np.ndarray) -> np.ndarray:
-    """(n,) -> (ceil(n/32), 32), zero padded (C1)."""
+    """(n,) -> (ceil(n/32), 32); the short last block is padded with NaN, which
+    the maxNum reductions skip, so only its valid elements count (C1)."""
     x = np.asarray(x, dtype=np.float32).ravel()
     nb = -(-x.size // BLOCK)
-    pad = np.zeros(nb * BLOCK, dtype=np.float32)
+    pad = np.full(nb * BLOCK, np.nan, dtype=np.float32)
     pad[: x.size] = x
     return pad.reshape(nb, BLOCK)
 
@@ -106,12 +116,13 @@ def block_scales(x: np.ndarray, kind: str) -> np.ndarray:
     b = _blocks(x)
     if b.shape[0] == 0:
         return np.zeros(0, dtype=np.uint16)
-    if kind == "m":
-        amax = np.fmax.reduce(np.abs(b), axis=1)
-    elif kind == "v":
-        amax = np.sqrt(np.fmax.reduce(b, axis=1))          # float32 sqrt: correctly rounded
-    else:
-        raise ValueError(kind)
+    with np.errstate(invalid="ignore"):
+        if kind == "m":
+            amax = np.fmax.reduce(np.abs(b), axis=1)
+        elif kind == "v":
+            amax = np.sqrt(np.fmax.reduce(b, axis=1))      # float32 sqrt: correctly rounded
+        else:
+            raise ValueError(kind)
     return ru_fp16_bits(amax.astype(np.float32))
 
 
@@ -125,7 +136,22 @@ def momentum_lut(codec: str = "companded") -> np.ndarray:
     q = np.arange(-127, 128, dtype=np.float32)
     if codec != "companded":
         raise ValueError("the momentum LUT exists for the companded codec only")
-    return q / (np.float32(254.0) - np.abs(q))
+    return q / (F32(254.0) - np.abs(q))
+
+
+def level_spacing(scale_bits: np.ndarray, kind: str, codec: str) -> np.ndarray:
+    """The block's level spacing D of the decodes in C4/C5 (float32 per block):
+    RN32(s/255) (variance, companded), RN32(s/127) (momentum, linear),
+    RN32(RN32(s*s)/255) (variance, linear)."""
+    s = f16_bits_to_f32(scale_bits)
+    with np.errstate(all="ignore"):
+        if kind == "v" and codec == "companded":
+            return (s / F32(255.0)).astype(F32)
+        if kind == "m" and codec == "linear":
+            return (s / F32(127.0)).astype(F32)
+        if kind == "v" and codec == "linear":
+            return ((s * s).astype(F32) / F32(255.0)).astype(F32)
+    raise ValueError((kind, codec))
 
 
 def _phi_code(a64: np.ndarray) -> np.ndarray:
@@ -133,35 +159,40 @@ def _phi_code(a64: np.ndarray) -> np.ndarray:
     return np.rint(254.0 * a64 / (1.0 + a64))
 
 
+def _saturating_code(y: np.ndarray, lo: int, hi: int) -> np.ndarray:
+    """round_half_even(y) clamped to [lo, hi]; NaN -> 0 (C6)."""
+    nan = np.isnan(y)
+    q = np.clip(np.rint(np.where(nan, F32(0), y)), lo, hi)
+    return np.where(nan, 0, q)
+
+
 def encode_momentum(m: np.ndarray, scale_bits: np.ndarray, codec: str = "companded") -> np.ndarray:
     m = np.asarray(m, dtype=np.float32).ravel()
     s = _per_elem(scale_bits, m.size)
     with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        z = (m / s).astype(F32)                                   # one float32 division (C3, C5)
         if codec == "companded":
-            r = np.where(s > 0, np.float32(1.0) / np.where(s > 0, s, np.float32(1)), np.float32(0))
-            z = (m * r).astype(np.float32)
-            a = np.fmin(np.abs(z), np.float32(1.0)).astype(np.float64)   # NaN -> 1 (C6)
+            nan = np.isnan(z)
+            a = np.fmin(np.abs(np.where(nan, F32(0), z)), F32(1.0)).astype(np.float64)
             q = _phi_code(a)
             q = np.where(z < 0, -q, q)
+            q = np.where(nan, 0, q)                               # C6
         elif codec == "linear":
-            c = np.where(s > 0, np.float32(127.0) / np.where(s > 0, s, np.float32(1)), np.float32(0))
-            y = (m * c).astype(np.float32)
-            y = np.fmax(np.fmin(y, np.float32(127)), np.float32(-127))     # NaN -> 127 (C6)
-            q = np.rint(y)
+            q = _saturating_code((F32(127.0) * z).astype(F32), -127, 127)
         else:
             raise ValueError(codec)
-    return np.clip(q, -127, 127).astype(np.int8)
+    return q.astype(np.int8)
 
 
 def decode_momentum(q: np.ndarray, scale_bits: np.ndarray, codec: str = "companded") -> np.ndarray:
     q = np.asarray(q, dtype=np.int8).ravel()
-    s = _per_elem(scale_bits, q.size)
     if codec == "companded":
+        s = _per_elem(scale_bits, q.size)
         lut = momentum_lut("companded")
-        return (s * lut[np.maximum(q.astype(np.int64), -127) + 127]).astype(np.float32)   # C7
+        return (s * lut[np.maximum(q.astype(np.int64), -127) + 127]).astype(F32)   # C7
     if codec == "linear":
-        step = (s * K127).astype(np.float32)
-        return (step * q.astype(np.float32)).astype(np.float32)
+        d = np.repeat(level_spacing(scale_bits, "m", "linear"), BLOCK)[: q.size]
+        return (d * q.astype(F32)).astype(F32)
     raise ValueError(codec)
 
 
@@ -170,30 +201,27 @@ def encode_variance(v: np.ndarray, scale_bits: np.ndarray, codec: str = "compand
     s = _per_elem(scale_bits, v.size)
     with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
         if codec == "companded":
-            c = np.where(s > 0, np.float32(255.0) / np.where(s > 0, s, np.float32(1)), np.float32(0))
-            y = (np.sqrt(v) * c).astype(np.float32)
+            w = np.sqrt(v).astype(F32)                            # correctly rounded (C4)
+            z = (w / s).astype(F32)
         elif codec == "linear":
-            s2 = (s * s).astype(np.float32)
-            c = np.where(s2 > 0, np.float32(255.0) / np.where(s2 > 0, s2, np.float32(1)), np.float32(0))
-            y = (v * c).astype(np.float32)
+            s2 = (s * s).astype(F32)                              # exact: 11-bit significands
+            z = (v / s2).astype(F32)
         else:
             raise ValueError(codec)
-        y = np.fmin(y, np.float32(255))                                    # NaN -> 255 (C6)
-        q = np.clip(np.rint(y), 0, 255)
+        y = (F32(255.0) * z).astype(F32)
+        q = _saturating_code(y, 0, 255)
     return q.astype(np.uint8)
 
 
 def decode_variance(q: np.ndarray, scale_bits: np.ndarray, codec: str = "companded") -> np.ndarray:
     q = np.asarray(q, dtype=np.uint8).ravel()
-    s = _per_elem(scale_bits, q.size)
-    qf = q.astype(np.float32)
+    d = np.repeat(level_spacing(scale_bits, "v", codec), BLOCK)[: q.size]
+    qf = q.astype(F32)
     if codec == "companded":
-        step = (s * K255).astype(np.float32)
-        t = (step * qf).astype(np.float32)
-        return (t * t).astype(np.float32)
+        t = (d * qf).astype(F32)
+        return (t * t).astype(F32)
     if codec == "linear":
-        step = ((s * s).astype(np.float32) * K255).astype(np.float32)
-        return (step * qf).astype(np.float32)
+        return (d * qf).astype(F32)
     raise ValueError(codec)
 
 

@@ -20,28 +20,34 @@ U2  Host scalars are computed in float64 and rounded once to float32:
     b1, b2, 1-b1, 1-b2, decay = 1 - lr*wd, step_size = lr / (1 - b1^t),
     ibc2 = 1 / sqrt(1 - b2^t), eps.
 U3  Per-element float32 operation order, every operation rounded once (no
-    fused multiply-add):
+    fused multiply-add; the division and the square root are the correctly
+    rounded IEEE operations):
         m = b1*m + (1-b1)*g
         v = b2*v + (1-b2)*(g*g)
         theta = theta*decay
         d = sqrt(v)*ibc2 + eps
-        r = 1/d
-        theta = theta - step_size*(m*r)
-    The quotient m/d is formed as m times the correctly rounded reciprocal of
-    d (one rounding more than a division; the same textbook update).
+        theta = theta - step_size*(m/d)
+    The quotient m/d of the textbook update is one IEEE division (rounded
+    once), then scaled by the bias-corrected step size and subtracted.
 U4  SGD-M = torch.optim.SGD: coupled L2 weight decay, optional dampening and
     Nesterov:  d = g + wd*theta;  b = d at step 1, else b = mu*b + (1-damp)*d;
     u = d + mu*b (Nesterov) or u = b;  theta = theta - lr*u.  With dampening 0
-    (1 - damp = 1 exactly) the buffer update is mu*b + d.
+    (1 - damp = 1 exactly) the buffer update is mu*b + d.  With momentum 0
+    torch keeps no buffer and steps theta -= lr*d at every step, dampening
+    unused; here every step then takes the step-1 rule b = d (so u = d), and
+    the stored buffer holds d, which the next step ignores.
 U5  The momentum buffer of SGD-M uses the momentum codec.
 U6  Adam with coupled L2 weight decay (torch.optim.Adam): g = g + wd*theta
     (theta = the reconstructed master) before the moments; no decoupled
     decay (decay = 1); otherwise as U3.
 
 Parity status: pinned (unquantised update against torch.optim.AdamW, Adam
-with weight decay (U6) and SGD (plain, Nesterov, dampening) in float64 and a
-float64 textbook loop; bf16+16 ECC reproduces a plain float32 master bit for
-bit; first-step closed form; tests/test_oracle_optim.py).
+with weight decay (U6) and SGD (plain, Nesterov, dampening, momentum 0 with
+dampening) in float64 and a float64 textbook loop; the update's quotient
+against the exact rational m/d rounded once, on inputs where a
+reciprocal-multiply rounds differently; bf16+16 ECC reproduces a plain
+float32 master bit for bit; first-step closed form;
+tests/test_oracle_optim.py).
 """
 
 from __future__ import annotations
@@ -118,9 +124,13 @@ def adamw_update(theta, g, m, v, S: AdamWScalars):
         th = theta * S.decay
         w = np.sqrt(v1)
         d = w * S.ibc2 + S.eps
-        r = np.float32(1.0) / d
-        th = th - S.step_size * (m1 * r)
+        th = th - S.step_size * (m1 / d)
     return th.astype(F32), m1.astype(F32), v1.astype(F32), w.astype(F32)
+
+
+def sgdm_first(step: int, momentum: float) -> bool:
+    """U4: the buffer is set to d at step 1 and, with momentum 0, at every step."""
+    return step == 1 or momentum == 0.0
 
 
 def sgdm_update(theta, g, b, S: SGDMScalars, first: bool = False):
@@ -177,7 +187,7 @@ def sgdm_step(state: dict, grad_bits: np.ndarray, hp: dict, fmt: str = "bf16",
     theta = reconstruct_weights(state["w16"], state["ecc"], fmt, ecc_bits)
     g = widen_grad(grad_bits, fmt)
     b = decode_momentum(state["b_q"], state["b_s"], codec)
-    th, b1 = sgdm_update(theta, g, b, S, first=hp["step"] == 1)
+    th, b1 = sgdm_update(theta, g, b, S, first=sgdm_first(hp["step"], hp["momentum"]))
     w16, ecc = split_weights(th, fmt, ecc_bits)
     b_s = block_scales(b1, "m")
     return {"w16": w16, "ecc": ecc, "b_q": encode_momentum(b1, b_s, codec), "b_s": b_s}

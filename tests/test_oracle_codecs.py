@@ -1,9 +1,12 @@
 """Pins for the oracle's blockwise state codecs (CPU only).
 
 Anchors: hand-derived golden codes, exact rational arithmetic near every code
-threshold, numpy's binary16 cast for the round-up scale, invertibility and
-monotonicity of the companders, the half-step bound, and the pages' claim
-that companding cuts quantisation error on heavy-tailed states.
+threshold and for the normalising divisions (on inputs where multiplying by a
+rounded reciprocal would give another code), numpy's binary16 cast for the
+round-up scale, invertibility and monotonicity of the companders, the
+half-step bound, the NaN / infinity codes, NaN-filled short last blocks, and
+the pages' claim that companding cuts quantisation error on heavy-tailed
+states.
 """
 
 import os
@@ -13,7 +16,9 @@ import numpy as np
 import pytest
 
 import oracle as O
-from oracle.codecs import K255, momentum_lut
+from oracle.codecs import momentum_lut
+
+from exact_fp import f32, rn32, rn32_sqrt, round_half_even
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "codec_cases.txt")
 
@@ -186,13 +191,33 @@ def test_tail_block_covers_valid_elements_only():
     assert q[33] == 127
 
 
-def test_variance_decode_definition():
-    # decode = (RN32(RN32(s * RN32(1/255)) * q))^2, pinned by hand for s = 1
-    sb = np.array([0x3C00], np.uint16)
-    q = np.array([0, 1, 255] + [0] * 29, np.uint8)
+def test_decode_level_spacing_is_one_division():
+    # D = RN32(s/255) (variance), RN32(s/127) (linear momentum),
+    # RN32(RN32(s*s)/255) (linear variance), each one correctly rounded
+    # division of the block's scale; decode = RN32(D*q) (squared for the
+    # companded variance).  Scales where s*RN32(1/255) rounds differently are
+    # included, so a reciprocal-multiply fails here.
+    pats = np.arange(0x0001, 0x7C00, 7, dtype=np.uint16)
+    s = pats.view(np.float16).astype(np.float32)
+    d = O.level_spacing(pats, "v", "companded")
+    want = np.array([f32(rn32(Fraction(float(x)) / 255)) for x in s], np.float32)
+    assert np.array_equal(d.view(np.uint32), want.view(np.uint32))
+    recip = (s * (np.float32(1) / np.float32(255))).astype(np.float32)
+    assert np.count_nonzero(recip != want) > 100
+    dl = O.level_spacing(pats, "m", "linear")
+    want = np.array([f32(rn32(Fraction(float(x)) / 127)) for x in s], np.float32)
+    assert np.array_equal(dl.view(np.uint32), want.view(np.uint32))
+    dv = O.level_spacing(pats, "v", "linear")
+    want = np.array([f32(rn32(Fraction(float(x)) ** 2 / 255)) for x in s], np.float32)
+    assert np.array_equal(dv.view(np.uint32), want.view(np.uint32))
+    # decode by hand for s = 3 (0x4200): t = RN32(D*q), v = RN32(t*t)
+    sb = np.array([0x4200], np.uint16)
+    q = np.array([0, 1, 200, 255] + [0] * 28, np.uint8)
     v = O.decode_variance(q, sb)
-    t255 = np.float32(K255) * np.float32(255)
-    assert v[0] == 0 and v[1] == np.float32(K255) * np.float32(K255) and v[2] == t255 * t255
+    D = rn32(Fraction(3, 255))
+    for qi, vi in zip(q[:4], v[:4]):
+        t = rn32(D * int(qi))
+        assert vi == f32(rn32(t * t))
 
 
 def test_momentum_decode_of_minus_128():
@@ -203,8 +228,127 @@ def test_momentum_decode_of_minus_128():
     m = O.decode_momentum(q, sb)
     assert m[0] == m[1] == np.float32(-4.0) and m[2] == np.float32(4.0)
     ml = O.decode_momentum(q, sb, "linear")
-    step = np.float32(4.0) * np.float32(1.0 / 127.0)
+    step = np.float32(4.0) / np.float32(127.0)
     assert ml[0] == step * np.float32(-128.0) and ml[1] == step * np.float32(-127.0)
+
+
+def _fp16_scales(rng, k):
+    return rng.integers(0x0400, 0x7BFF, k).astype(np.uint16)
+
+
+def _momentum_code_exact(z: Fraction, codec: str) -> int:
+    if codec == "companded":
+        a = min(abs(z), Fraction(1))
+        q = round_half_even(254 * a / (1 + a))
+        return -q if z < 0 else q
+    return max(-127, min(127, round_half_even(rn32(127 * z))))
+
+
+def test_momentum_codes_exact_rational():
+    # C3/C5: z = m/s is one float32 division, then the code of z.  Written out
+    # with exact rationals; the inputs sit a few float32 ulps from a code
+    # threshold and are kept where m * RN32(1/s) gives another code, so a
+    # reciprocal-multiply in the oracle fails here.
+    rng = np.random.default_rng(40)
+    k = rng.integers(0, 127, 40000)
+    sb = _fp16_scales(rng, k.size)
+    s = sb.view(np.float16).astype(np.float32)
+    sign = rng.choice([-1.0, 1.0], k.size)
+    for codec in ("companded", "linear"):
+        thr = (2 * k + 1) / (507.0 - 2 * k) if codec == "companded" else (k + 0.5) / 127.0
+        m0 = (sign * thr * s.astype(np.float64)).astype(np.float32)
+        m = (m0.view(np.int32) + rng.integers(-4, 5, k.size).astype(np.int32)).view(np.float32)
+        m = np.where(np.abs(m) <= s, m, m0).astype(np.float32)
+        recip = (m * (np.float32(1) / s)).astype(np.float32)
+        div = (m / s).astype(np.float32)
+        code_r = np.array([_momentum_code_exact(Fraction(float(z)), codec) for z in recip])
+        code_d = np.array([_momentum_code_exact(Fraction(float(z)), codec) for z in div])
+        pick = np.nonzero(code_r != code_d)[0][:80]
+        assert pick.size >= 20, codec
+        blocks = np.zeros((pick.size, 32), np.float32)
+        blocks[:, 0] = m[pick]
+        got = O.encode_momentum(blocks.ravel(), sb[pick], codec).reshape(-1, 32)[:, 0]
+        for i, gi in zip(pick, got):
+            want = _momentum_code_exact(rn32(Fraction(float(m[i])) / Fraction(float(s[i]))), codec)
+            assert int(gi) == want, (codec, float(m[i]), float(s[i]), int(gi), want)
+
+
+def test_variance_codes_exact_rational():
+    # C4: w = sqrt_rn(v), z = w/s, y = 255*z, code = round_half_even(y), each a
+    # float32 operation; C5 linear: z = v/(s*s), y = 255*z.  Inputs chosen where
+    # w * RN32(255/s) (or v * RN32(255/s^2)) gives another code.
+    rng = np.random.default_rng(41)
+    k = rng.integers(0, 255, 20000)
+    sb = _fp16_scales(rng, k.size)
+    s = sb.view(np.float16).astype(np.float32)
+    s64 = s.astype(np.float64)
+    for codec in ("companded", "linear"):
+        # inputs a few float32 ulps from a code's rounding boundary k + 1/2
+        if codec == "companded":
+            v0 = (((k + 0.5) / 255 * s64) ** 2).astype(np.float32)
+        else:
+            v0 = ((k + 0.5) / 255 * s64 * s64).astype(np.float32)
+        v = (v0.view(np.int32) + rng.integers(-6, 7, k.size).astype(np.int32)).view(np.float32)
+        if codec == "companded":
+            wr = np.sqrt(v).astype(np.float32)
+            recip = np.rint((wr * (np.float32(255) / s)).astype(np.float32))
+            plain = np.rint((np.float32(255) * (wr / s).astype(np.float32)).astype(np.float32))
+        else:
+            s2 = (s * s).astype(np.float32)
+            recip = np.rint((v * (np.float32(255) / s2)).astype(np.float32))
+            plain = np.rint((np.float32(255) * (v / s2).astype(np.float32)).astype(np.float32))
+        pick = np.nonzero(recip != plain)[0][:60]
+        assert pick.size >= 20, codec
+        blocks = np.zeros((pick.size, 32), np.float32)
+        blocks[:, 0] = v[pick]
+        got = O.encode_variance(blocks.ravel(), sb[pick], codec).reshape(-1, 32)[:, 0]
+        for i, gi in zip(pick, got):
+            fs = Fraction(float(s[i]))
+            if codec == "companded":
+                z = rn32(rn32_sqrt(Fraction(float(v[i]))) / fs)
+            else:
+                z = rn32(Fraction(float(v[i])) / (fs * fs))
+            want = max(0, min(255, round_half_even(rn32(255 * z))))
+            assert int(gi) == want, (codec, float(v[i]), float(s[i]), int(gi), want)
+
+
+def test_nan_and_infinity_codes():
+    # C6: NaN -> code 0 under every codec; +-Inf (scale saturated at 65504)
+    # -> the end codes; an all-zero block has s = 0 and codes 0
+    x = np.zeros(96, np.float32)
+    x[0:4] = [np.nan, 1.0, -0.5, np.nan]
+    x[32:35] = [np.inf, 1.0, -np.inf]
+    for codec in ("companded", "linear"):
+        q, s = O.quantize_state(x, "m", codec)
+        assert list(s) == [0x3C00, 0x7BFF, 0x0000]
+        assert q[0] == 0 and q[3] == 0 and q[1] == 127
+        assert q[32] == 127 and q[34] == -127 and q[33] == 0
+        assert np.all(q[64:] == 0)
+        v = np.abs(x)
+        qv, sv = O.quantize_state(v, "v", codec)
+        assert qv[0] == 0 and qv[3] == 0 and qv[1] == 255 and qv[32] == 255 and qv[34] == 255
+        assert sv[1] == 0x7BFF and sv[2] == 0 and np.all(qv[64:] == 0)
+    # a negative "variance" has no square root: NaN -> 0
+    qn, _ = O.quantize_state(np.array([-1.0, 4.0] + [0.0] * 30, np.float32), "v")
+    assert qn[0] == 0 and qn[1] == 255
+
+
+def test_short_last_block_all_nan_keeps_nan_scale():
+    # C1: the valid elements of a short last block are all NaN -> NaN scale,
+    # under both kinds; one finite element among them sets the scale alone
+    x = np.zeros(40, np.float32)
+    x[32:] = np.nan
+    for kind in ("m", "v"):
+        s = O.block_scales(x, kind)
+        assert list(s) == [0x0000, 0x7E00]
+    x[39] = 0.25
+    assert list(O.block_scales(x, "m")) == [0x0000, 0x3400]
+    assert list(O.block_scales(x, "v")) == [0x0000, 0x3800]        # sqrt(0.25) = 0.5
+    # a NaN scale decodes every code of the block to NaN
+    q = np.zeros(40, np.int8)
+    s = np.array([0x0000, 0x7E00], np.uint16)
+    assert np.all(np.isnan(O.decode_momentum(q, s)[32:]))
+    assert np.all(np.isnan(O.decode_variance(q.view(np.uint8), s)[32:]))
 
 
 def test_block_absmax_ignores_nan_unless_all_nan():

@@ -2,9 +2,14 @@
 
 Anchors: torch.optim.AdamW / torch.optim.SGD in float64 (a library routine),
 a float64 textbook loop written here, the first-step closed form, the
-bf16 + 16-bit ECC identity (a lossless split must reproduce a plain float32
-master bit for bit), and the storage byte count the pages give.
+update's float32 arithmetic against exact rationals rounded once per
+operation (inputs chosen where multiplying by a rounded reciprocal instead of
+dividing changes the result), the bf16 + 16-bit ECC identity (a lossless
+split must reproduce a plain float32 master bit for bit), and the storage
+byte count the pages give.
 """
+
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -12,6 +17,8 @@ import torch
 
 import oracle as O
 from oracle.optim import fresh_adamw_state, fresh_sgdm_state
+
+from exact_fp import f32, rn32, rn32_sqrt
 
 HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
 
@@ -217,3 +224,89 @@ def test_sgd_variants_match_torch(nesterov, dampening):
         ref = p.detach().numpy()
         assert np.max(np.abs(th - ref)) <= 1e-6 * np.max(np.abs(ref))
         assert np.max(np.abs((th - x0) - (ref - x0))) <= 1e-4 * np.max(np.abs(ref - x0))
+
+
+def test_adamw_quotient_is_one_division():
+    # With beta1 = beta2 = 0, lr = 1, wd = 0 and theta = 0 the update reduces
+    # to theta' = -RN32(g / RN32(|g| + eps)): m = g, v = g*g, sqrt(v) = |g|
+    # (exact for a correctly rounded square of a float), step size 1.  The
+    # quotient must be the exact rational g/d rounded once; the inputs are
+    # kept where g * RN32(1/d) rounds to another float, so a reciprocal-
+    # multiply (one rounding more) fails here.
+    rng = np.random.default_rng(50)
+    g = (rng.choice([-1, 1], 20000) * 10.0 ** rng.uniform(-3, 0, 20000)).astype(np.float32)
+    eps = (10.0 ** rng.uniform(-4, 0, 20000)).astype(np.float32)
+    d = (np.abs(g) + eps).astype(np.float32)
+    recip = (g * (np.float32(1) / d)).astype(np.float32)
+    div = (g / d).astype(np.float32)
+    pick = np.nonzero(recip != div)[0][:300]
+    assert pick.size >= 200
+    for i in pick:
+        S = O.adamw_scalars(1.0, 0.0, 0.0, float(eps[i]), 0.0, 1)
+        assert S.step_size == 1 and S.ibc2 == 1 and S.decay == 1 and S.eps == eps[i]
+        th, m, v, w = O.adamw_update(np.zeros(1, np.float32), g[i:i + 1], np.zeros(1, np.float32),
+                                     np.zeros(1, np.float32), S)
+        dd = rn32(abs(Fraction(float(g[i]))) + Fraction(float(eps[i])))
+        want = -rn32(Fraction(float(g[i])) / dd)
+        assert w[0] == abs(g[i])
+        assert th[0] == f32(want), (float(g[i]), float(eps[i]), float(th[0]), float(want))
+
+
+def test_adamw_update_rounds_once_per_operation():
+    # The whole float32 sequence of the update (U3, and U6 for Adam) against
+    # the same operations on exact rationals, each rounded once to binary32:
+    # no contraction into fused multiply-adds, no wider intermediate, no
+    # reordering.  Random moments, weights and hyperparameters.
+    rng = np.random.default_rng(51)
+    for trial in range(400):
+        l2 = bool(trial % 3 == 0)
+        hp = dict(lr=float(10 ** rng.uniform(-4, -1)), beta1=float(rng.uniform(0, 0.99)),
+                  beta2=float(rng.uniform(0.9, 0.9999)), eps=float(10 ** rng.uniform(-9, -5)),
+                  weight_decay=float(rng.uniform(0, 0.2)), step=int(rng.integers(1, 1000)))
+        S = O.adamw_scalars(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"],
+                            hp["step"], l2=l2)
+        th0 = np.float32(rng.standard_normal() * 0.02)
+        g0 = np.float32(rng.standard_t(3) * 1e-3)
+        m0 = np.float32(rng.standard_t(3) * 1e-3)
+        v0 = np.float32((rng.standard_t(3) * 1e-3) ** 2)
+        th, m, v, w = O.adamw_update(np.array([th0]), np.array([g0]), np.array([m0]), np.array([v0]), S)
+        F = lambda x: Fraction(float(x))
+        T, G, M, V = F(th0), F(g0), F(m0), F(v0)
+        if l2:
+            G = rn32(G + rn32(F(S.wd) * T))
+        M1 = rn32(rn32(F(S.b1) * M) + rn32(F(S.omb1) * G))
+        V1 = rn32(rn32(F(S.b2) * V) + rn32(F(S.omb2) * rn32(G * G)))
+        T1 = rn32(T * F(S.decay))
+        W = rn32_sqrt(V1)
+        D = rn32(rn32(W * F(S.ibc2)) + F(S.eps))
+        T2 = rn32(T1 - rn32(F(S.step_size) * rn32(M1 / D)))
+        assert (m[0], v[0], w[0], th[0]) == (f32(M1), f32(V1), f32(W), f32(T2)), (trial, hp)
+
+
+def test_sgd_momentum0_ignores_dampening_like_torch():
+    # U4: torch.optim.SGD with momentum 0 keeps no buffer, so dampening has no
+    # effect; the oracle's buffer is then d at every step
+    rng = np.random.default_rng(52)
+    x0 = (rng.standard_normal((7, 5)) * 0.02).astype(np.float32)
+    grads = [(rng.standard_normal((7, 5)) * 1e-2).astype(np.float32) for _ in range(6)]
+    p = torch.nn.Parameter(torch.tensor(x0, dtype=torch.float64))
+    opt = torch.optim.SGD([p], lr=0.1, momentum=0.0, weight_decay=1e-4, dampening=0.5, foreach=False)
+    S = O.sgdm_scalars(0.1, 0.0, 1e-4, 0.5)
+    th = x0.copy(); b = np.zeros_like(th)
+    for t, g in enumerate(grads, start=1):
+        p.grad = torch.tensor(g, dtype=torch.float64)
+        opt.step()
+        th, b = O.sgdm_update(th, g, b, S, first=O.sgdm_first(t, 0.0))
+        ref = p.detach().numpy()
+        assert np.max(np.abs(th - ref)) <= 1e-6 * np.max(np.abs(ref))
+        assert np.max(np.abs((th - x0) - (ref - x0))) <= 1e-4 * np.max(np.abs(ref - x0))
+    # the fused step: every step is theta - lr*d, split again
+    st = fresh_sgdm_state(x0.ravel())
+    for t, g in enumerate(grads, start=1):
+        gb = (g.ravel().view(np.uint32) + 0x8000 >> 16).astype(np.uint16)
+        gw = (gb.astype(np.uint32) << 16).view(np.float32)
+        th0 = O.reconstruct_weights(st["w16"], st["ecc"])
+        st = O.sgdm_step(st, gb, dict(lr=0.1, momentum=0.0, weight_decay=1e-4, dampening=0.5, step=t))
+        want = th0 - np.float32(0.1) * (gw + np.float32(1e-4) * th0)
+        w16, ecc = O.split_weights(want)
+        assert np.array_equal(st["w16"], w16) and np.array_equal(st["ecc"], ecc)
