@@ -20,9 +20,34 @@
  *            gradient release; same blog, Conclusion & Perspective (drop-in
  *            torch.optim replacements).
  *
- * Numerical definitions (rounding modes, operation order, scale format,
- * compander formulas) are those of the CPU oracle shipped with the tests; the
- * pages leave them open and the chosen readings are documented with it.
+ * Numerical definitions.  The pages leave rounding modes, operation order,
+ * scale format and compander formulas open; this library fixes them as
+ * follows.  RN(.) is one IEEE binary32 rounding to nearest even; every
+ * division and square root is the correctly rounded IEEE operation (the
+ * kernels reach it through exact fast sequences, with IEEE fallbacks).
+ *   Split: theta' = x rounded to the 16-bit format to nearest, ties away from
+ *     zero; ECC = round_half_even((|x| - |theta'|) * 2^N / spacing), with the
+ *     format's spacing on x's side of theta' (half the spacing above, below a
+ *     power of two above the smallest normal), clamped to the N-bit range.
+ *     NaN -> quiet NaN with ECC 0, +-Inf -> +-Inf with ECC 0, finite values
+ *     past the format's range saturate to +-max with the ECC clamped.
+ *   Blocks: 32 consecutive elements; the last block of a tensor holds n mod 32
+ *     elements.  Scale = the smallest binary16 >= the block's maximum
+ *     (momentum: max|m|; variance: RN(sqrt(max v))), saturating at 65504; the
+ *     maximum ignores NaN elements, so a block whose valid elements are all
+ *     NaN gets a NaN scale.
+ *   Momentum codes (int8, [-127, 127]), companded: z = RN(m / s),
+ *     q = sign(z) * round_half_even(127 * phi(min(|z|, 1))) with
+ *     phi(a) = 2a / (1 + a), the rounding exact for the float z; decode
+ *     RN(s * RN(q / (254 - |q|))) (code -128 decodes as -127).  Linear:
+ *     q = clamp(rne(RN(127 * RN(m / s))), -127, 127); decode RN(D * q), D = RN(s / 127).
+ *   Variance codes (uint8), companded: q = clamp(rne(RN(255 * RN(RN(sqrt(v)) / s))),
+ *     0, 255); decode t = RN(D * q), D = RN(s / 255), v = RN(t * t).  Linear:
+ *     q = clamp(rne(RN(255 * RN(v / RN(s * s)))), 0, 255); decode RN(D * q),
+ *     D = RN(RN(s * s) / 255).
+ *   A NaN state element gets code 0 (the rule of saturating float-to-integer
+ *   conversion); +-Inf takes the end codes.
+ *   Updates: see fo_fused_adamw_step and fo_fused_sgdm_step.
  *
  * Conventions for every entry point
  *   - All data pointers are DEVICE pointers owned by the caller; the library
@@ -58,7 +83,9 @@
 extern "C" {
 #endif
 
-#define FO_ABI_VERSION 2   /* 2: l2_decay in fo_adamw_hparams; dampening, nesterov in fo_sgdm_hparams */
+#define FO_ABI_VERSION 3   /* 2: l2_decay in fo_adamw_hparams; dampening, nesterov in fo_sgdm_hparams;
+                              3: correctly rounded quotients in the update and the codecs, NaN codes 0,
+                                 NaN-only short last blocks keep a NaN scale, SGD momentum 0 as torch */
 
 enum fo_status {
   FO_OK = 0,
@@ -160,9 +187,15 @@ typedef struct fo_adamw_hparams {
  * 2^18 wave tiles (2^29 elements; one kernel for most lists); with
  * hp->l2_decay = 1 the step is Adam with the weight decay added to the
  * gradient (torch.optim.Adam).  Per element: widen the gradient,
- * reconstruct the f32 master, decode m and v, update in float32 with a fixed
- * operation order, split the new master into theta' + ECC, recompute the
- * block scales of the new m and v and re-encode them.  Blocks never cross
+ * reconstruct the f32 master, decode m and v, update in float32, split the
+ * new master into theta' + ECC, recompute the block scales of the new m and v
+ * and re-encode them.  The update, with the f32 constants b1, b2, 1-b1, 1-b2,
+ * decay = 1 - lr*wd (1 for Adam), step_size = lr / (1 - b1^t),
+ * ibc2 = 1 / sqrt(1 - b2^t) computed in double and rounded once, is
+ *   [Adam: g = g + wd*theta]  m = b1*m + (1-b1)*g;  v = b2*v + (1-b2)*(g*g);
+ *   theta = theta*decay;  d = sqrt(v)*ibc2 + eps;  theta = theta - step_size*(m/d)
+ * with every operation rounded once (no fused multiply-add) and m/d, sqrt(v)
+ * correctly rounded.  Blocks never cross
  * tensors; a short last block is handled per tensor.  Any sub-list (e.g. the
  * one tensor whose gradient just arrived) may be stepped on its own; the
  * result is bitwise identical to stepping it inside a larger list.
@@ -194,8 +227,10 @@ typedef struct fo_sgdm_hparams {
 /*
  * fo_fused_sgdm_step -- [UPDATE] with [SPLIT] and [STATE]
  * One SGD-with-momentum step over a list of tensors, as torch.optim.SGD:
- * d = g + wd*theta; buffer = d at step 1, else momentum*buffer + (1-dampening)*d;
- * theta -= lr * (Nesterov ? d + momentum*buffer : buffer).  The momentum
+ * d = g + wd*theta; buffer = d at step 1 (and at every step when momentum is
+ * 0, where torch keeps no buffer, so dampening has no effect), else
+ * momentum*buffer + (1-dampening)*d; theta -= lr * (Nesterov ? d + momentum*buffer
+ * : buffer), each operation rounded once in float32.  The momentum
  * buffer uses the momentum codec.  Same layout, ownership and error rules as
  * fo_fused_adamw_step (FO_EINVAL also for dampening outside [0,1] and for
  * Nesterov without momentum or with dampening).
@@ -215,15 +250,24 @@ int fo_stream_probe(const fo_adamw_tensor* list, int32_t count, int32_t wfmt,
 
 /*
  * fo_selftest -- verification of the exact fast arithmetic the fused kernels
- * use on this device.  Over the f32 bit patterns [lo, lo + count) it counts
- * (synchronously, into *mismatches) where
- *   what 0: the Newton-refined hardware reciprocal differs from IEEE 1/x
- *           (the kernels use it for positive normal x < 2^126);
- *   what 1: the neighbour-corrected hardware square root differs from the
- *           IEEE square root (used for x = 0 and x >= 2^-96);
- *   what 2: the hardware float-to-u8 conversion differs from
- *           clamp(round_half_even(x), 0, 255) (NaN skipped).
- * Errors: FO_EINVAL (bad `what`, NULL output, range past 2^32), FO_ENOMEM, FO_EHIP.
+ * use on this device.  It counts (synchronously, into *mismatches):
+ *   what 0: f32 patterns x in [lo, lo + count) where the Newton-refined
+ *           hardware reciprocal differs from IEEE 1/x (the kernels use it for
+ *           positive normal x < 2^126);
+ *   what 1: patterns where the neighbour-corrected hardware square root
+ *           differs from the IEEE square root (used for x = 0, x >= 2^-96);
+ *   what 2: patterns where the hardware float-to-u8 conversion differs from
+ *           clamp(round_half_even(x), 0, 255), NaN -> 0;
+ *   what 3: of `count` pairs (a, b) drawn from a counter-based generator
+ *           seeded by lo (b positive normal below 2^126, |a| in [2^-100,
+ *           2^101) or 0; pairs whose quotient is neither 0 nor of magnitude
+ *           in [2^-125, 2^120) are skipped), those where the
+ *           residual-corrected quotient differs from IEEE a/b;
+ *   what 4: the same with b a positive finite binary16 value and |a| <= b;
+ *   what 5: as 3 over the pairs whose quotient is a nonzero subnormal, which
+ *           the fused AdamW step keeps out of its fast form.
+ * Errors: FO_EINVAL (bad `what`, NULL output, a pattern range past 2^32),
+ * FO_ENOMEM, FO_EHIP.
  */
 int fo_selftest(int what, uint32_t lo, uint64_t count, uint64_t* mismatches, void* stream);
 

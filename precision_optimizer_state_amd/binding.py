@@ -60,7 +60,7 @@ class SGDMHParams(ctypes.Structure):
 
 
 _lib = None
-ABI_VERSION = 2          # FO_ABI_VERSION of include/foamd.h (struct layouts below)
+ABI_VERSION = 3          # FO_ABI_VERSION of include/foamd.h (struct layouts below)
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -236,8 +236,11 @@ def fo_stream_probe(tlist, wfmt="bf16", ecc_bits=8, key=0, stream=None) -> None:
 
 
 def fo_selftest(what: int, lo: int, count: int, stream=None) -> int:
-    """Mismatch count of the device's fast exact arithmetic over f32 patterns
-    [lo, lo + count): 0 = reciprocal, 1 = square root, 2 = float-to-u8."""
+    """Mismatch count of the device's fast exact arithmetic: over the f32
+    patterns [lo, lo + count) for 0 = reciprocal, 1 = square root,
+    2 = float-to-u8; over `count` seeded (by lo) pairs for 3 = division
+    (normal quotients), 4 = division by a block scale, 5 = division with a
+    subnormal quotient (outside the fast step's domain)."""
     out = ctypes.c_uint64(0)
     _check(load().fo_selftest(int(what), int(lo), int(count), ctypes.byref(out), _stream(stream)))
     return int(out.value)

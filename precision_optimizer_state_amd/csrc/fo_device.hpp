@@ -180,15 +180,17 @@ __device__ __forceinline__ void split8(const float (&x)[8], uint32_t (&wo)[4], u
 #pragma unroll
       for (int i = 0; i < 4; ++i) wo[i] = perm(t[2 * i + 1], t[2 * i], 0x07060302u);
       if constexpr (ECC == 8) {
-        // rho = round_half_even(L / 256) clamped to 127, L = sext16(low half):
-        // 128 + L/256 is exact in one FMA, v_cvt_pk_u8_f32 rounds it half to
-        // even, saturates at 255 (rho = 127) and writes it into its byte, and
-        // the XOR with 0x80 turns offset binary into two's complement (checked
-        // against the integer form on all 2^16 low halves)
+        // rho = round_half_even(L / 256) clamped to 127, L = sext16(low half).
+        // The low half of t = bits + 0x8000 is T = L + 2^15, so the float with
+        // pattern 0x4B000000 | T is 2^23 + T and one FMA forms T/256 = 128 +
+        // L/256 exactly; v_cvt_pk_u8_f32 rounds it half to even, saturates
+        // at 255 (rho = 127) and writes it into its byte, and the XOR with 0x80
+        // turns offset binary into two's complement (checked against the
+        // integer form on all 2^16 low halves)
         uint32_t e0 = 0u, e1 = 0u;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const float y = __builtin_fmaf((float)(int16_t)f2u(x[k]), 0x1p-8f, 128.0f);
+          const float y = __builtin_fmaf(u2f((t[k] & 0xFFFFu) | 0x4B000000u), 0x1p-8f, -32768.0f);
           if (k < 4) e0 = __builtin_amdgcn_cvt_pk_u8_f32(y, k, e0);
           else e1 = __builtin_amdgcn_cvt_pk_u8_f32(y, k - 4, e1);
         }
@@ -296,8 +298,8 @@ __device__ __forceinline__ float quad_bcast(float x) { return dpp_f<qp_bcast<J>(
 // within one ulp, and the residuals v - s'*s of the two neighbours decide the
 // rounding exactly (no float lies strictly between s_lo*s and the squared
 // midpoint).  The residuals are exact for v >= 2^-96; v = 0, inf and NaN pass
-// through unchanged.  Callers fall back to the IEEE expansion when any lane
-// has 0 < v < 2^-96 (sqrt_needs_scaling).
+// through unchanged.  Callers keep v out of (0, 2^-96) or fall back to the
+// IEEE expansion.
 __device__ __forceinline__ float sqrt_corrected(float v) {
   float s = __builtin_amdgcn_sqrtf(v);
   const float s_dn = u2f(f2u(s) - 1u), s_up = u2f(f2u(s) + 1u);
@@ -318,22 +320,50 @@ __device__ __forceinline__ float rcp_refined(float b) {
   const float e = __builtin_fmaf(-b, y0, 1.0f);
   return __builtin_fmaf(e, y0, y0);
 }
+// Correctly rounded quotient a/b from r = RN(1/b): q0 = RN(a*r) is within two
+// ulps of a/b; the residual e = b*q0 - a is formed by one FMA, and one more
+// FMA q0 - e*r lands within a few 2^-24 ulps of a/b, closer than any binary32
+// quotient comes to a rounding midpoint (Markstein's residual correction; the
+// negated residual keeps the sign of a zero quotient).  Valid while no
+// intermediate leaves the normal range: |a| >= 2^-100 or a = 0, |a/b| < 2^120.
+// Checked on the CPU against IEEE division on every pair whose quotient lies
+// within 16*2^-47 (relative) of a midpoint, exhaustively for divisors with
+// 22-bit significands, and on random pairs; on the device by fo_selftest.
+__device__ __forceinline__ float div_refined(float a, float b, float r) {
+  const float q0 = a * r;
+  const float e = __builtin_fmaf(b, q0, -a);
+  return __builtin_fmaf(-e, r, q0);
+}
 
 // ---------------------------------------------------------------------------
 // State codecs
 // ---------------------------------------------------------------------------
-// Momentum encode by interval table: a in [0,1] is keyed by the top 15 bits of
-// its f32 pattern (sign, exponent and 6 mantissa bits), counted from 2^-9 (every
-// a below 2^-9 shares key 0).  Every key interval holds at most one of the code
-// thresholds (2k+1)/(507-2k) (checked exactly for all 577 keys; one mantissa bit
-// fewer would put two thresholds into some intervals just below 1), so
+// A state block has a binary16 scale s.  Encoding normalises with one
+// correctly rounded division z = x/s (div_refined with R = RN(1/s), computed
+// once per block); decoding multiplies the code by the block's level spacing:
+//   momentum, companded:  m = RN(s * LUT[q])                 (multiplier s)
+//   momentum, linear:     m = RN(D * q),  D = RN(s/127)
+//   variance, companded:  t = RN(D * q),  D = RN(s/255), v = RN(t*t)
+//   variance, linear:     v = RN(D * q),  D = RN(RN(s*s)/255)
+// (RN(s*s) is exact: binary16 significands have 11 bits.)  A NaN element gets
+// code 0; values past the end codes saturate.
+
+// Momentum encode by interval table: a = |z| in [0,1] is keyed by bits 17..30
+// of its f32 pattern (exponent and 6 mantissa bits), clamped to
+// [MENC_BASE, MENC_BASE + MENC_NAN]: every a below 2^-9 shares the first key,
+// and keys above a = 1 (which the fast encode only sees for NaN) share the
+// last, whose code is 0 and whose threshold (NaN) no value reaches.  Every
+// other key interval holds at most one of the code thresholds (2k+1)/(507-2k)
+// (checked exactly for all 577 keys; one mantissa bit fewer would put two
+// thresholds into some intervals just below 1), so
 // code(a) = menc[key].code + (a >= menc[key].thr).
 struct MEnc { float thr; int32_t code; };
 constexpr int MENC_SHIFT = 17;
 constexpr uint32_t MENC_BASE = 0x3B000000u >> MENC_SHIFT;                 // 2^-9
 constexpr int MENC_N = (int)((0x3F800000u >> MENC_SHIFT) - MENC_BASE) + 1;  // keys up to a = 1
+constexpr int MENC_NAN = MENC_N;                                           // NaN (and a > 1)
 constexpr int MENC_CAP = 640;                            // pads the tables to 6 KiB
-static_assert(MENC_CAP >= MENC_N, "interval table capacity");
+static_assert(MENC_CAP > MENC_NAN, "interval table capacity");
 // Codec tables (built once per device by k_init_tables, copied into LDS):
 //   lut[q + 128] = RN32(q / (254 - |q|)) for q in [-127, 127]: momentum levels;
 //                  lut[0] (code -128, never written by the encoder) = lut[1]
@@ -343,7 +373,7 @@ constexpr int LUT_BIAS = 128;
 static_assert(sizeof(CodecTables) == 6 * 1024, "six 1-KiB chunks: one 64-lane x 16-B load each");
 
 // Builds the tables (one workgroup).  thr[k] = smallest f32 >= (2k+1)/(507-2k),
-// the |z| at which round(127*phi(|z|)) steps from k to k+1.
+// the a at which round(127*phi(a)) steps from k to k+1.
 __device__ __forceinline__ void build_tables(FO_GLOBAL CodecTables* out, float* thr, int tid, int nthreads) {
   for (int i = tid; i < 256; i += nthreads) {
     const int q = max(i - LUT_BIAS, -127);
@@ -367,42 +397,55 @@ __device__ __forceinline__ void build_tables(FO_GLOBAL CodecTables* out, float* 
       e.code = code;
       e.thr = (code < 127 && thr[code] < hi) ? thr[code] : 2.0f;
     } else {
-      e.code = 127;
-      e.thr = 2.0f;
+      e.code = 0;
+      e.thr = __builtin_nanf("");
     }
     out->menc[key].thr = e.thr;
     out->menc[key].code = e.code;
   }
 }
 
-// momentum, companded: z = m*R (R = RN32(1/s)); q = sign(z)*round(127*phi(min(|z|,1)))
-__device__ __forceinline__ int32_t encode_m_companded(float m, float R, const CodecTables& T) {
-  const float z = m * R;
-  const float a = fminf(fabsf(z), 1.0f);                  // NaN -> 1
-  const uint32_t key = __builtin_elementwise_sub_sat(f2u(a) >> MENC_SHIFT, MENC_BASE);
+// Code of a = |z| for 0 <= a <= 1 or NaN (NaN -> 0), sign of z applied.
+__device__ __forceinline__ int32_t momentum_code(float z, const CodecTables& T) {
+  const uint32_t kb = __builtin_amdgcn_ubfe(f2u(z), MENC_SHIFT, 14);
+  const uint32_t key = min(max(kb, MENC_BASE), MENC_BASE + (uint32_t)MENC_NAN) - MENC_BASE;   // v_med3_u32
   const MEnc e = T.menc[key];
-  const int32_t q = e.code + (a >= e.thr ? 1 : 0);
+  const int32_t q = e.code + (fabsf(z) >= e.thr ? 1 : 0);
   return (z < 0.0f) ? -q : q;
 }
 
-// Clamping happens in float with IEEE minNum/maxNum, which also sends NaN to
-// the upper bound, so the float->int conversions below always see in-range values.
-__device__ __forceinline__ int32_t encode_m_linear(float m, float C) {
-  const float y = fmaxf(fminf(m * C, 127.0f), -127.0f);   // C = RN32(127/s); NaN -> 127
-  return (int32_t)__builtin_rintf(y);
+// momentum, companded, fast form: s > 0 finite with |m| <= s, or s = 0 / NaN
+// (then z is NaN and the code 0).  R = RN(1/s).
+__device__ __forceinline__ int32_t encode_m_companded(float m, float s, float R, const CodecTables& T) {
+  return momentum_code(div_refined(m, s, R), T);
+}
+// momentum, companded, any m and s (IEEE division, clamp at |z| = 1)
+__device__ __forceinline__ int32_t encode_m_companded_ieee(float m, float s, const CodecTables& T) {
+  const float z = m / s;
+  if (z != z) return 0;
+  return momentum_code(__builtin_copysignf(fminf(fabsf(z), 1.0f), z), T);
+}
+// momentum, linear: y = RN(127 * RN(m/s)); fast form for |m| <= s, the IEEE
+// form clamps |y| to 127; NaN -> 0
+__device__ __forceinline__ int32_t encode_m_linear(float m, float s, float R) {
+  const float y = 127.0f * div_refined(m, s, R);
+  return (y == y) ? (int32_t)__builtin_rintf(y) : 0;
+}
+__device__ __forceinline__ int32_t encode_m_linear_ieee(float m, float s) {
+  const float y = 127.0f * (m / s);
+  return (y == y) ? (int32_t)__builtin_rintf(fmaxf(fminf(y, 127.0f), -127.0f)) : 0;
 }
 
-// variance: y = x*C, C = RN32(255/s) (companded, x = sqrt(v)) or RN32(255/s^2)
-// (linear, x = v); code = clamp(round_half_even(y), 0, 255) written into byte
-// `k` of `acc` (v_cvt_pk_u8_f32 rounds half to even and saturates; verified
-// against rint+clamp over every non-NaN f32 by fo_selftest; it turns NaN into
-// 0, hence the fminf first).
-__device__ __forceinline__ uint32_t encode_v_into(float x, float C, uint32_t k, uint32_t acc) {
-  const float y = fminf(x * C, 255.0f);                    // x*C >= 0; NaN -> 255
-  return __builtin_amdgcn_cvt_pk_u8_f32(y, k, acc);
+// variance: y = RN(255 * RN(x/s)), x = sqrt_rn(v) with the companded codec's
+// scale s, or x = v with the linear codec's s*s; the code clamp(rne(y), 0, 255)
+// goes into byte `k` of `acc`.  v_cvt_pk_u8_f32 rounds half to even,
+// saturates, and turns NaN into 0 (checked over every f32 by fo_selftest).
+// The fast form needs x finite; the IEEE form takes any x.
+__device__ __forceinline__ uint32_t encode_v_into(float x, float s, float R, uint32_t k, uint32_t acc) {
+  return __builtin_amdgcn_cvt_pk_u8_f32(255.0f * div_refined(x, s, R), k, acc);
 }
-
-constexpr float K127 = 1.0f / 127.0f;   // RN32(1/127), constant-folded
-constexpr float K255 = 1.0f / 255.0f;   // RN32(1/255)
+__device__ __forceinline__ uint32_t encode_v_into_ieee(float x, float s, uint32_t k, uint32_t acc) {
+  return __builtin_amdgcn_cvt_pk_u8_f32(255.0f * (x / s), k, acc);
+}
 
 }  // namespace fo

@@ -65,14 +65,22 @@ static_assert(sizeof(TensorDesc) == 80, "descriptor layout");
 
 struct AdamWConsts {
   float b1, b2, omb1, omb2, decay, step_size, ibc2, eps;
-  float wd;       // coupled (L2) weight decay of Adam; unused by AdamW
-  int fast_rcp;   // eps >= 2^-126: every denominator is a positive normal >= eps
+  float wd;         // coupled (L2) weight decay of Adam; unused by AdamW
+  // Range of (effective) gradients for which the exact fast arithmetic holds:
+  // g = 0 or g_lo <= |g| <= g_hi.  The host derives it from the
+  // hyperparameters and the ranges of the decoded states, so that every
+  // variance lies outside (0, 2^-96), every denominator in [eps, 2^126), every
+  // nonzero momentum at or above 2^-100 and every quotient below 2^120
+  // (the preconditions of sqrt_corrected, rcp_refined and div_refined).
+  uint32_t g_lo2;   // 2 * bits(g_lo) - 2: compared with 2 * bits(g) - 2
+  float g_hi;
+  int fast;         // 0: no such range (e.g. eps = 0); every wave takes the IEEE form
 };
 struct SGDMConsts {
   float lr, mu, wd;
   float damp1;    // 1 - dampening
   int nesterov;
-  int first;      // step 1: the buffer is set to the (decayed) gradient
+  int first;      // step 1 (and every step at momentum 0): the buffer is set to d
 };
 
 template <typename T> using gp = FO_GLOBAL T*;
@@ -155,62 +163,152 @@ __device__ __forceinline__ float bcast_j(float x, int j) {   // j is a compile-t
 }
 
 // ---------------------------------------------------------------------------
-// shared pieces of the fused update
+// state codecs inside a tile
 // ---------------------------------------------------------------------------
-// w = sqrt(v) correctly rounded for 8 values (IEEE expansion when any lane of
-// the wave needs scaling)
-__device__ __forceinline__ void sqrt8(const float (&v)[EPL], float (&w)[EPL]) {
-  uint64_t slow = 0;
-#pragma unroll
-  for (int k = 0; k < EPL; ++k) {
-    w[k] = sqrt_corrected(v[k]);
-    slow |= __builtin_amdgcn_ballot_w64(sqrt_needs_scaling(v[k]));
-  }
-  if (slow) {
-#pragma unroll
-    for (int k = 0; k < EPL; ++k) w[k] = __builtin_sqrtf(v[k]);
+enum { MOMENTUM_STATE = 0, VARIANCE_STATE = 1 };
+
+// decode multiplier of a block with scale s (see the codec summary in fo_device.hpp)
+template <int KIND, int CODEC>
+__device__ __forceinline__ float decode_mult(float s) {
+  if constexpr (KIND == MOMENTUM_STATE) return (CODEC == COMPANDED) ? s : s / 127.0f;
+  else return (CODEC == COMPANDED) ? s / 255.0f : (s * s) / 255.0f;
+}
+template <int KIND, int CODEC>
+__device__ __forceinline__ float decode_state(const DW<2>& q, int i, float dm, const CodecTables& T) {
+  if constexpr (KIND == MOMENTUM_STATE) {
+    const int32_t c = s8(q, i);
+    return (CODEC == COMPANDED) ? dm * T.lut[c + LUT_BIAS] : dm * (float)c;
+  } else {
+    const float t = dm * (float)u8(q, i);
+    return (CODEC == COMPANDED) ? t * t : t;
   }
 }
+// The value a state's block maximum and its codes are taken from: the state
+// itself, or for a variance-kind state under the companded codec its square
+// root (which the rule supplies).
+template <int KIND, int CODEC> constexpr bool encodes_root = (KIND == VARIANCE_STATE && CODEC == COMPANDED);
 
-// r = RN(1/d) for 8 denominators (IEEE division when any lane is outside the
-// verified range, or when eps does not keep denominators normal)
-__device__ __forceinline__ void rcp8(const float (&d)[EPL], float (&r)[EPL], int fast) {
-  uint64_t slow = fast ? 0ull : ~0ull;
-#pragma unroll
-  for (int k = 0; k < EPL; ++k) {
-    r[k] = rcp_refined(d[k]);
-    slow |= __builtin_amdgcn_ballot_w64(!(d[k] < 0x1p126f));
-  }
-  if (slow) {
-#pragma unroll
-    for (int k = 0; k < EPL; ++k) r[k] = 1.0f / d[k];
-  }
+// ---------------------------------------------------------------------------
+// update rules
+// ---------------------------------------------------------------------------
+// A fused step is one pass per element: widen the gradient, reconstruct the
+// f32 master, decode the rule's states, apply the rule, split the new master,
+// recompute the block scales of the new states and re-encode them.  All of it
+// but the rule is shared (fused_tile below).  A rule is a type with
+//   static constexpr int NSTATE;               1 or 2 stored 8-bit states
+//   template <int K> static constexpr int KIND; MOMENTUM_STATE (int8 codes,
+//                                              softsign-like compander) or
+//                                              VARIANCE_STATE (uint8 codes,
+//                                              square-root compander)
+//   using Consts = ...;                        per-step scalars from the host
+//   static void update(const Consts&, bool ieee, float (&th)[EPL],
+//                      const float (&g)[EPL], float (&st)[NSTATE][EPL],
+//                      float (&root)[NSTATE][EPL]);
+// update() gets the decoded master th, the widened gradient g and the decoded
+// states st of EPL elements of one lane, and leaves the new master in th and
+// the new states in st.  For each VARIANCE_STATE it also leaves the correctly
+// rounded square root of the new state in root (only read under the companded
+// codec).  The whole wave calls update() together, so a rule may branch
+// wave-uniformly (ballot) between a fast exact form and the IEEE form; ieee
+// (wave-uniform) asks for the IEEE form, because a stored scale of the tile is
+// not finite.  A new rule needs a kernel that runs fused_tile with it and a
+// host entry point that fills its Consts.
+
+// AdamW (decoupled decay) or, with L2, Adam (decay added to the gradient):
+// m = b1*m + (1-b1)*g; v = b2*v + (1-b2)*g*g; th = th*decay;
+// th = th - step_size * (m / (sqrt(v)*ibc2 + eps)), each operation one IEEE
+// rounding (division and square root correctly rounded).
+__device__ __forceinline__ bool grad_in_fast_range(float g, uint32_t lo2, float hi) {
+  return ((f2u(g) << 1) - 2u) >= lo2 && fabsf(g) <= hi;    // g = +-0 wraps to the top: in range
 }
+template <bool L2>
+struct AdamWRule {
+  static constexpr int NSTATE = 2;
+  template <int K> static constexpr int KIND = (K == 0) ? MOMENTUM_STATE : VARIANCE_STATE;
+  using Consts = AdamWConsts;
+  static __device__ __forceinline__ void update(const Consts& c, bool ieee, float (&th)[EPL], const float (&g)[EPL],
+                                                float (&st)[2][EPL], float (&root)[2][EPL]) {
+    uint64_t slow = (c.fast && !ieee) ? 0ull : ~0ull;
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) {
+      float gk = g[k];
+      if constexpr (L2) gk = gk + c.wd * th[k];
+      st[0][k] = c.b1 * st[0][k] + c.omb1 * gk;
+      st[1][k] = c.b2 * st[1][k] + c.omb2 * (gk * gk);
+      th[k] = th[k] * c.decay;
+      slow |= __builtin_amdgcn_ballot_w64(!grad_in_fast_range(gk, c.g_lo2, c.g_hi));
+    }
+    float q[EPL];
+    if (!slow) {
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) {
+        root[1][k] = sqrt_corrected(st[1][k]);
+        const float den = root[1][k] * c.ibc2 + c.eps;
+        q[k] = div_refined(st[0][k], den, rcp_refined(den));
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < EPL; ++k) {
+        root[1][k] = __builtin_sqrtf(st[1][k]);
+        const float den = root[1][k] * c.ibc2 + c.eps;
+        q[k] = st[0][k] / den;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) th[k] = th[k] - c.step_size * q[k];
+  }
+};
+
+// SGD with momentum (torch.optim.SGD): d = g + wd*th; b = d at the first step
+// (and every step at momentum 0), else b = mu*b + (1-dampening)*d;
+// th = th - lr * (Nesterov ? d + mu*b : b).
+struct SGDMRule {
+  static constexpr int NSTATE = 1;
+  template <int K> static constexpr int KIND = MOMENTUM_STATE;
+  using Consts = SGDMConsts;
+  static __device__ __forceinline__ void update(const Consts& c, bool, float (&th)[EPL], const float (&g)[EPL],
+                                                float (&st)[1][EPL], float (&)[1][EPL]) {
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) {
+      const float dd = g[k] + c.wd * th[k];
+      const float b = c.first ? dd : c.mu * st[0][k] + c.damp1 * dd;
+      const float u = c.nesterov ? dd + c.mu * b : b;
+      th[k] = th[k] - c.lr * u;
+      st[0][k] = b;
+    }
+  }
+};
 
 // ---------------------------------------------------------------------------
-// fused AdamW: one wave tile
+// fused step: one wave tile for any update rule
 // ---------------------------------------------------------------------------
-template <int WFMT, int ECC, int CODEC, bool L2, bool FULL>
-__device__ __forceinline__ void adamw_tile(const TensorDesc& d, int64_t e0, int lane,
-                                           const CodecTables& tabs, const AdamWConsts& c) {
+template <class R, int WFMT, int ECC, int CODEC, bool FULL>
+__device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int lane, const CodecTables& tabs,
+                                           const typename R::Consts& c) {
+  constexpr int NS = R::NSTATE;
   constexpr int EB = ECC / 8;                                  // ECC bytes per element
+  constexpr int K0 = R::template KIND<0>;
+  constexpr int K1 = R::template KIND<NS - 1>;
   const int Q = lane >> 2, p = lane & 3;
-  const int64_t n = d.n;
   const gp<const uint8_t> grad = (gp<const uint8_t>)d.grad + e0 * 2;
   const gp<uint8_t> w16 = (gp<uint8_t>)d.w16 + e0 * 2;
   const gp<uint8_t> ecc = (gp<uint8_t>)d.ecc + e0 * EB;
-  const gp<uint8_t> mq = (gp<uint8_t>)d.q1 + e0;
-  const gp<uint8_t> vq = (gp<uint8_t>)d.q2 + e0;
-  const gp<uint16_t> ms = (gp<uint16_t>)d.s1 + (e0 >> 5);
-  const gp<uint16_t> vs = (gp<uint16_t>)d.s2 + (e0 >> 5);
-  const int64_t rem = n - e0;                                  // valid elements from e0 on
+  gp<uint8_t> qp[NS];
+  gp<uint16_t> sp[NS];
+  qp[0] = (gp<uint8_t>)d.q1 + e0;
+  sp[0] = (gp<uint16_t>)d.s1 + (e0 >> 5);
+  if constexpr (NS == 2) {
+    qp[NS - 1] = (gp<uint8_t>)d.q2 + e0;
+    sp[NS - 1] = (gp<uint16_t>)d.s2 + (e0 >> 5);
+  }
+  const int64_t rem = d.n - e0;                                // valid elements from e0 on
   const int own = p * 16 + Q;                                  // owned block within the tile
   const bool own_ok = FULL || (int64_t)own * 32 < rem;
 
   // ---- issue every load of the tile -------------------------------------
   DW<4> G[NSUB], W[NSUB];
   DW<2 * EB> E[NSUB];
-  DW<2> MQ[NSUB], VQ[NSUB];
+  DW<2> SQ[NS][NSUB];
   int cnt[NSUB];
 #pragma unroll
   for (int j = 0; j < NSUB; ++j) {
@@ -219,47 +317,40 @@ __device__ __forceinline__ void adamw_tile(const TensorDesc& d, int64_t e0, int 
     G[j] = load8<2, FULL>(grad + off * 2, cnt[j]);
     W[j] = load8<2, FULL>(w16 + off * 2, cnt[j]);
     E[j] = load8<EB, FULL>(ecc + off * EB, cnt[j]);
-    MQ[j] = load8<1, FULL>(mq + off, cnt[j]);
-    VQ[j] = load8<1, FULL>(vq + off, cnt[j]);
+#pragma unroll
+    for (int k = 0; k < NS; ++k) SQ[k][j] = load8<1, FULL>(qp[k] + off, cnt[j]);
   }
-  const uint32_t sm_old = own_ok ? (uint32_t)__builtin_nontemporal_load(ms + own) : 0u;
-  const uint32_t sv_old = own_ok ? (uint32_t)__builtin_nontemporal_load(vs + own) : 0u;
+  float dm_own[NS];
+  bool nonfinite = false;
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    const float sold = h2f(own_ok ? (uint32_t)__builtin_nontemporal_load(sp[k] + own) : 0u);
+    dm_own[k] = (k == 0) ? decode_mult<K0, CODEC>(sold) : decode_mult<K1, CODEC>(sold);
+    nonfinite |= !(fabsf(sold) <= 65504.0f);
+  }
+  // a NaN or infinite stored scale (the encoder writes NaN only for an all-NaN
+  // block) makes NaN or infinite states: the rule then takes its IEEE form
+  const bool ieee = __builtin_amdgcn_ballot_w64(nonfinite) != 0;
 
-  // ---- per-block decode constants (owned block) -------------------------
-  const float smf = h2f(sm_old), svf = h2f(sv_old);
-  const float dm_own = (CODEC == COMPANDED) ? smf : smf * K127;
-  const float dv_own = (CODEC == COMPANDED) ? svf * K255 : (svf * svf) * K255;
-
-  float Mn[NSUB][EPL], Xn[NSUB][EPL];       // fresh m and (sqrt(v) | v) for re-encoding
-  // block maxima start at NaN: IEEE maxNum returns any non-NaN element (the
-  // zeros of a partial block included), so only an all-NaN block keeps NaN
-  // and gets a NaN scale, which carries the NaN into the decoded state
-  float own_mmax = 0.0f, own_xmax = 0.0f;
+  float X[NS][NSUB][EPL];                  // what each state's codes are taken from
+  float own_max[NS];
+#pragma unroll
+  for (int k = 0; k < NS; ++k) own_max[k] = 0.0f;
 
 #pragma unroll
   for (int j = 0; j < NSUB; ++j) {
-    const float dm = bcast_j(dm_own, j), dv = bcast_j(dv_own, j);
-    float th[EPL], m[EPL], v[EPL], w[EPL], den[EPL], r[EPL];
+    float th[EPL], g[EPL], st[NS][EPL], root[NS][EPL];
+    float dm[NS];
 #pragma unroll
-    for (int k = 0; k < EPL; ++k) {
-      float g = wid<WFMT>(G[j], k);
-      th[k] = ecc_decode<WFMT, ECC>(wid<WFMT>(W[j], k), rho_at<ECC>(E[j], k));
-      if constexpr (L2) g = g + c.wd * th[k];                  // Adam: decay folded into the gradient
-      const int32_t qm = s8(MQ[j], k);
-      const float mh = (CODEC == COMPANDED) ? dm * tabs.lut[qm + LUT_BIAS] : dm * (float)qm;
-      const float tv = dv * (float)u8(VQ[j], k);
-      const float vh = (CODEC == COMPANDED) ? tv * tv : tv;
-      // update (fixed float32 order, one rounding per operation)
-      m[k] = c.b1 * mh + c.omb1 * g;
-      v[k] = c.b2 * vh + c.omb2 * (g * g);
-      th[k] = th[k] * c.decay;
+    for (int k = 0; k < NS; ++k) dm[k] = bcast_j(dm_own[k], j);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      g[i] = wid<WFMT>(G[j], i);
+      th[i] = ecc_decode<WFMT, ECC>(wid<WFMT>(W[j], i), rho_at<ECC>(E[j], i));
+      st[0][i] = decode_state<K0, CODEC>(SQ[0][j], i, dm[0], tabs);
+      if constexpr (NS == 2) st[NS - 1][i] = decode_state<K1, CODEC>(SQ[NS - 1][j], i, dm[NS - 1], tabs);
     }
-    sqrt8(v, w);
-#pragma unroll
-    for (int k = 0; k < EPL; ++k) den[k] = w[k] * c.ibc2 + c.eps;
-    rcp8(den, r, c.fast_rcp);
-#pragma unroll
-    for (int k = 0; k < EPL; ++k) th[k] = th[k] - c.step_size * (m[k] * r[k]);
+    R::update(c, ieee, th, g, st, root);
 
     // split the new master and store it
     uint32_t wo[4], eo[ECC / 4];
@@ -268,133 +359,78 @@ __device__ __forceinline__ void adamw_tile(const TensorDesc& d, int64_t e0, int 
     store8<2, FULL>(w16 + off * 2, wo, cnt[j]);
     store8<EB, FULL>(ecc + off * EB, eo, cnt[j]);
 
-    float mmax = __builtin_nanf(""), xmax = __builtin_nanf("");
+    // block maxima: maxNum skips NaN, and lanes past the end of a short last
+    // block feed NaN, so only the block's valid elements count and a block
+    // whose valid elements are all NaN keeps a NaN maximum (and scale)
 #pragma unroll
-    for (int k = 0; k < EPL; ++k) {
-      const float x = (CODEC == COMPANDED) ? w[k] : v[k];
-      Mn[j][k] = m[k];
-      Xn[j][k] = x;
-      mmax = fmaxf(mmax, fabsf(m[k]));
-      xmax = fmaxf(xmax, x);
+    for (int k = 0; k < NS; ++k) {
+      const bool root_k = (k == 0) ? encodes_root<K0, CODEC> : encodes_root<K1, CODEC>;
+      const bool mom_k = ((k == 0) ? K0 : K1) == MOMENTUM_STATE;
+      float mx = __builtin_nanf("");
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        const float x = root_k ? root[k][i] : st[k][i];
+        X[k][j][i] = x;
+        const float a = mom_k ? fabsf(x) : x;
+        mx = fmaxf(mx, (FULL || i < cnt[j]) ? a : __builtin_nanf(""));
+      }
+      mx = quad_max(mx);
+      own_max[k] = (p == j) ? mx : own_max[k];
     }
-    mmax = quad_max(mmax);
-    xmax = quad_max(xmax);
-    own_mmax = (p == j) ? mmax : own_mmax;
-    own_xmax = (p == j) ? xmax : own_xmax;
   }
 
   // ---- new block scales and encode constants (owned block) ---------------
-  const uint32_t smb = ru_fp16(own_mmax);
-  const uint32_t svb = ru_fp16((CODEC == COMPANDED) ? own_xmax : __builtin_sqrtf(own_xmax));
-  if (own_ok) {
-    __builtin_nontemporal_store((uint16_t)smb, ms + own);
-    __builtin_nontemporal_store((uint16_t)svb, vs + own);
+  float s_own[NS], r_own[NS];
+  bool sat = false;
+#pragma unroll
+  for (int k = 0; k < NS; ++k) {
+    const int kind = (k == 0) ? K0 : K1;
+    const bool lin_var = (kind == VARIANCE_STATE && CODEC == LINEAR);
+    const uint32_t sb = ru_fp16(lin_var ? __builtin_sqrtf(own_max[k]) : own_max[k]);
+    if (own_ok) __builtin_nontemporal_store((uint16_t)sb, sp[k] + own);
+    const float sf = h2f(sb);
+    s_own[k] = lin_var ? sf * sf : sf;                       // the divisor of the normalisation (exact)
+    r_own[k] = 1.0f / s_own[k];                              // IEEE: s = 0 -> inf, NaN -> NaN
+    // the fast encodes need |x| <= s (momentum) or a finite x (variance)
+    sat |= (kind == MOMENTUM_STATE) ? (own_max[k] > 65504.0f) : (own_max[k] == __builtin_inff());
   }
-  const float sm = h2f(smb), sv = h2f(svb);
-  float cm_own, cv_own;
-  if constexpr (CODEC == COMPANDED) {
-    cm_own = (sm > 0.0f) ? 1.0f / sm : 0.0f;
-    cv_own = (sv > 0.0f) ? 255.0f / sv : 0.0f;
-  } else {
-    const float sv2 = sv * sv;
-    cm_own = (sm > 0.0f) ? 127.0f / sm : 0.0f;
-    cv_own = (sv2 > 0.0f) ? 255.0f / sv2 : 0.0f;
-  }
+  const bool sat_wave = __builtin_amdgcn_ballot_w64(sat) != 0;
 
 #pragma unroll
   for (int j = 0; j < NSUB; ++j) {
-    const float cm = bcast_j(cm_own, j), cv = bcast_j(cv_own, j);
-    uint32_t qm[EPL], vo[2] = {0u, 0u};
+    const int off = j * SUB + lane * EPL;
 #pragma unroll
-    for (int k = 0; k < EPL; ++k) {
-      qm[k] = (uint32_t)((CODEC == COMPANDED) ? encode_m_companded(Mn[j][k], cm, tabs)
-                                              : encode_m_linear(Mn[j][k], cm));
-      vo[k >> 2] = encode_v_into(Xn[j][k], cv, k & 3, vo[k >> 2]);
+    for (int k = 0; k < NS; ++k) {
+      const int kind = (k == 0) ? K0 : K1;
+      const float sdiv = bcast_j(s_own[k], j), rdiv = bcast_j(r_own[k], j);
+      uint32_t o[2];
+      if (kind == MOMENTUM_STATE) {
+        uint32_t q[EPL];
+        if (!sat_wave) {
+#pragma unroll
+          for (int i = 0; i < EPL; ++i)
+            q[i] = (uint32_t)((CODEC == COMPANDED) ? encode_m_companded(X[k][j][i], sdiv, rdiv, tabs)
+                                                   : encode_m_linear(X[k][j][i], sdiv, rdiv));
+        } else {
+#pragma unroll
+          for (int i = 0; i < EPL; ++i)
+            q[i] = (uint32_t)((CODEC == COMPANDED) ? encode_m_companded_ieee(X[k][j][i], sdiv, tabs)
+                                                   : encode_m_linear_ieee(X[k][j][i], sdiv));
+        }
+        o[0] = pack4_byte0(q[0], q[1], q[2], q[3]);
+        o[1] = pack4_byte0(q[4], q[5], q[6], q[7]);
+      } else {
+        o[0] = o[1] = 0u;
+        if (!sat_wave) {
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) o[i >> 2] = encode_v_into(X[k][j][i], sdiv, rdiv, i & 3, o[i >> 2]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < EPL; ++i) o[i >> 2] = encode_v_into_ieee(X[k][j][i], sdiv, i & 3, o[i >> 2]);
+        }
+      }
+      store8<1, FULL>(qp[k] + off, o, cnt[j]);
     }
-    const uint32_t mo[2] = {pack4_byte0(qm[0], qm[1], qm[2], qm[3]), pack4_byte0(qm[4], qm[5], qm[6], qm[7])};
-    const int off = j * SUB + lane * EPL;
-    store8<1, FULL>(mq + off, mo, cnt[j]);
-    store8<1, FULL>(vq + off, vo, cnt[j]);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// fused SGD with momentum: one wave tile
-// ---------------------------------------------------------------------------
-template <int WFMT, int ECC, int CODEC, bool FULL>
-__device__ __forceinline__ void sgdm_tile(const TensorDesc& d, int64_t e0, int lane,
-                                          const CodecTables& tabs, const SGDMConsts& c) {
-  constexpr int EB = ECC / 8;
-  const int Q = lane >> 2, p = lane & 3;
-  const int64_t n = d.n;
-  const gp<const uint8_t> grad = (gp<const uint8_t>)d.grad + e0 * 2;
-  const gp<uint8_t> w16 = (gp<uint8_t>)d.w16 + e0 * 2;
-  const gp<uint8_t> ecc = (gp<uint8_t>)d.ecc + e0 * EB;
-  const gp<uint8_t> bq = (gp<uint8_t>)d.q1 + e0;
-  const gp<uint16_t> bs = (gp<uint16_t>)d.s1 + (e0 >> 5);
-  const int64_t rem = n - e0;
-  const int own = p * 16 + Q;
-  const bool own_ok = FULL || (int64_t)own * 32 < rem;
-
-  DW<4> G[NSUB], W[NSUB];
-  DW<2 * EB> E[NSUB];
-  DW<2> BQ[NSUB];
-  int cnt[NSUB];
-#pragma unroll
-  for (int j = 0; j < NSUB; ++j) {
-    const int off = j * SUB + lane * EPL;
-    cnt[j] = FULL ? 8 : (int)max((int64_t)0, min((int64_t)8, rem - off));
-    G[j] = load8<2, FULL>(grad + off * 2, cnt[j]);
-    W[j] = load8<2, FULL>(w16 + off * 2, cnt[j]);
-    E[j] = load8<EB, FULL>(ecc + off * EB, cnt[j]);
-    BQ[j] = load8<1, FULL>(bq + off, cnt[j]);
-  }
-  const uint32_t sb_old = own_ok ? (uint32_t)__builtin_nontemporal_load(bs + own) : 0u;
-  const float sbf = h2f(sb_old);
-  const float db_own = (CODEC == COMPANDED) ? sbf : sbf * K127;
-
-  float Bn[NSUB][EPL];
-  float own_bmax = 0.0f;
-#pragma unroll
-  for (int j = 0; j < NSUB; ++j) {
-    const float db = bcast_j(db_own, j);
-    float th[EPL], b[EPL];
-    float bmax = __builtin_nanf("");          // all-NaN block -> NaN scale
-#pragma unroll
-    for (int k = 0; k < EPL; ++k) {
-      const float g = wid<WFMT>(G[j], k);
-      const float t0 = ecc_decode<WFMT, ECC>(wid<WFMT>(W[j], k), rho_at<ECC>(E[j], k));
-      const int32_t qb = s8(BQ[j], k);
-      const float bh = (CODEC == COMPANDED) ? db * tabs.lut[qb + LUT_BIAS] : db * (float)qb;
-      const float dd = g + c.wd * t0;
-      b[k] = c.first ? dd : c.mu * bh + c.damp1 * dd;
-      const float u = c.nesterov ? dd + c.mu * b[k] : b[k];
-      th[k] = t0 - c.lr * u;
-      Bn[j][k] = b[k];
-      bmax = fmaxf(bmax, fabsf(b[k]));
-    }
-    uint32_t wo[4], eo[ECC / 4];
-    split8<WFMT, ECC>(th, wo, eo);
-    const int off = j * SUB + lane * EPL;
-    store8<2, FULL>(w16 + off * 2, wo, cnt[j]);
-    store8<EB, FULL>(ecc + off * EB, eo, cnt[j]);
-    bmax = quad_max(bmax);
-    own_bmax = (p == j) ? bmax : own_bmax;
-  }
-  const uint32_t sbb = ru_fp16(own_bmax);
-  if (own_ok) __builtin_nontemporal_store((uint16_t)sbb, bs + own);
-  const float sb = h2f(sbb);
-  const float cb_own = (sb > 0.0f) ? ((CODEC == COMPANDED) ? 1.0f : 127.0f) / sb : 0.0f;
-#pragma unroll
-  for (int j = 0; j < NSUB; ++j) {
-    const float cb = bcast_j(cb_own, j);
-    uint32_t q[EPL];
-#pragma unroll
-    for (int k = 0; k < EPL; ++k)
-      q[k] = (uint32_t)((CODEC == COMPANDED) ? encode_m_companded(Bn[j][k], cb, tabs)
-                                             : encode_m_linear(Bn[j][k], cb));
-    const uint32_t bo[2] = {pack4_byte0(q[0], q[1], q[2], q[3]), pack4_byte0(q[4], q[5], q[6], q[7])};
-    store8<1, FULL>(bq + j * SUB + lane * EPL, bo, cnt[j]);
   }
 }
 
@@ -537,8 +573,8 @@ k_fused_adamw(const TensorDesc* __restrict__ tab, int count, int64_t tile0, int6
   __shared__ CodecTables wtabs[adamw_tile_waves<ECC>];
   const CodecTables& tabs = wave_tables(wtabs, gtabs);
   tile_loop<adamw_tile_waves<ECC>>(tab, count, tile0, tile_end, [&](const TensorDesc& d, int64_t e0, int lane) {
-    if (e0 + TILE <= d.n) adamw_tile<WFMT, ECC, CODEC, L2, true>(d, e0, lane, tabs, c);
-    else adamw_tile<WFMT, ECC, CODEC, L2, false>(d, e0, lane, tabs, c);
+    if (e0 + TILE <= d.n) fused_tile<AdamWRule<L2>, WFMT, ECC, CODEC, true>(d, e0, lane, tabs, c);
+    else fused_tile<AdamWRule<L2>, WFMT, ECC, CODEC, false>(d, e0, lane, tabs, c);
   });
 }
 
@@ -549,8 +585,8 @@ __global__ void __launch_bounds__(WAVE * SGDM_TILE_WAVES) k_fused_sgdm(const Ten
   __shared__ CodecTables wtabs[SGDM_TILE_WAVES];
   const CodecTables& tabs = wave_tables(wtabs, gtabs);
   tile_loop<SGDM_TILE_WAVES>(tab, count, tile0, tile_end, [&](const TensorDesc& d, int64_t e0, int lane) {
-    if (e0 + TILE <= d.n) sgdm_tile<WFMT, ECC, CODEC, true>(d, e0, lane, tabs, c);
-    else sgdm_tile<WFMT, ECC, CODEC, false>(d, e0, lane, tabs, c);
+    if (e0 + TILE <= d.n) fused_tile<SGDMRule, WFMT, ECC, CODEC, true>(d, e0, lane, tabs, c);
+    else fused_tile<SGDMRule, WFMT, ECC, CODEC, false>(d, e0, lane, tabs, c);
   });
 }
 
@@ -635,7 +671,8 @@ __global__ void __launch_bounds__(WG) k_quantize(const float* __restrict__ x, in
   const gp<const float> xs = (gp<const float>)x;
   const int64_t stride = (int64_t)gridDim.x * WG * EPL;
   // all lanes iterate together (stride multiple of 512), so the 4 lanes of a
-  // block are active at the same time; lanes past n contribute zeros
+  // block are active at the same time; lanes past n contribute NaN to the
+  // block maximum (skipped by maxNum) and store nothing
   for (int64_t i0 = (int64_t)blockIdx.x * WG * EPL; i0 < n; i0 += stride) {
     const int64_t i = i0 + threadIdx.x * EPL;
     const int cnt = (int)max((int64_t)0, min((int64_t)8, n - i));
@@ -645,11 +682,20 @@ __global__ void __launch_bounds__(WG) k_quantize(const float* __restrict__ x, in
       v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     } else {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = (k < cnt) ? xs[i + k] : 0.0f;
+      for (int k = 0; k < 8; ++k) v[k] = (k < cnt) ? xs[i + k] : __builtin_nanf("");
     }
     float e[8];
     if (KIND == 1 && CODEC == COMPANDED) {
-      sqrt8(v, e);
+      uint64_t slow = 0;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        e[k] = sqrt_corrected(v[k]);
+        slow |= __builtin_amdgcn_ballot_w64(sqrt_needs_scaling(v[k]));
+      }
+      if (slow) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) e[k] = __builtin_sqrtf(v[k]);
+      }
     } else {
 #pragma unroll
       for (int k = 0; k < 8; ++k) e[k] = v[k];
@@ -660,23 +706,35 @@ __global__ void __launch_bounds__(WG) k_quantize(const float* __restrict__ x, in
     mx = quad_max(mx);
     const uint32_t sb = ru_fp16((KIND == 1 && CODEC == LINEAR) ? __builtin_sqrtf(mx) : mx);
     if ((threadIdx.x & 3) == 0 && cnt > 0) ((gp<uint16_t>)scales)[i >> 5] = (uint16_t)sb;
-    const float s = h2f(sb);
-    float C;
-    if (KIND == 0) C = (s > 0.0f) ? ((CODEC == COMPANDED) ? 1.0f : 127.0f) / s : 0.0f;
-    else if (CODEC == COMPANDED) C = (s > 0.0f) ? 255.0f / s : 0.0f;
-    else { const float s2 = s * s; C = (s2 > 0.0f) ? 255.0f / s2 : 0.0f; }
+    const float sf = h2f(sb);
+    const float sdiv = (KIND == 1 && CODEC == LINEAR) ? sf * sf : sf;
+    const float rdiv = 1.0f / sdiv;
+    const bool sat_wave = __builtin_amdgcn_ballot_w64((KIND == 0) ? (mx > 65504.0f) : (mx == __builtin_inff())) != 0;
     uint32_t o[2];
     if (KIND == 0) {
       uint32_t q[8];
+      if (!sat_wave) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        q[k] = (uint32_t)((CODEC == COMPANDED) ? encode_m_companded(e[k], C, tabs) : encode_m_linear(e[k], C));
+        for (int k = 0; k < 8; ++k)
+          q[k] = (uint32_t)((CODEC == COMPANDED) ? encode_m_companded(e[k], sdiv, rdiv, tabs)
+                                                 : encode_m_linear(e[k], sdiv, rdiv));
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          q[k] = (uint32_t)((CODEC == COMPANDED) ? encode_m_companded_ieee(e[k], sdiv, tabs)
+                                                 : encode_m_linear_ieee(e[k], sdiv));
+      }
       o[0] = pack4_byte0(q[0], q[1], q[2], q[3]);
       o[1] = pack4_byte0(q[4], q[5], q[6], q[7]);
     } else {
       o[0] = o[1] = 0u;
+      if (!sat_wave) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) o[k >> 2] = encode_v_into(e[k], C, k & 3, o[k >> 2]);
+        for (int k = 0; k < 8; ++k) o[k >> 2] = encode_v_into(e[k], sdiv, rdiv, k & 3, o[k >> 2]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) o[k >> 2] = encode_v_into_ieee(e[k], sdiv, k & 3, o[k >> 2]);
+      }
     }
     if (cnt == 8) store8<1, true>((gp<uint8_t>)codes + i, o, 8);
     else if (cnt > 0) store8<1, false>((gp<uint8_t>)codes + i, o, cnt);
@@ -691,23 +749,16 @@ __global__ void __launch_bounds__(WG) k_dequantize(const uint8_t* __restrict__ c
   load_tables(tabs, gtabs);
   const gp<float> o = (gp<float>)out;
   const int64_t stride = (int64_t)gridDim.x * WG * EPL;
+  constexpr int SK = (KIND == 0) ? MOMENTUM_STATE : VARIANCE_STATE;
   for (int64_t i = ((int64_t)blockIdx.x * WG + threadIdx.x) * EPL; i < n; i += stride) {
     const int cnt = (int)min((int64_t)8, n - i);
     const gp<const uint8_t> cp = (gp<const uint8_t>)codes + i;
     const DW<2> q = (cnt == 8) ? load8<1, true>(cp, 8) : load8<1, false>(cp, cnt);
-    const float s = h2f(((gp<const uint16_t>)scales)[i >> 5]);
+    // the 8 elements of a thread lie in one 32-element block
+    const float dm = decode_mult<SK, CODEC>(h2f(((gp<const uint16_t>)scales)[i >> 5]));
     float v[8];
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      if (KIND == 0) {
-        const int32_t cq = s8(q, k);
-        v[k] = (CODEC == COMPANDED) ? s * tabs.lut[cq + LUT_BIAS] : (s * K127) * (float)cq;
-      } else {
-        const float cq = (float)u8(q, k);
-        if (CODEC == COMPANDED) { const float t = (s * K255) * cq; v[k] = t * t; }
-        else v[k] = ((s * s) * K255) * cq;
-      }
-    }
+    for (int k = 0; k < 8; ++k) v[k] = decode_state<SK, CODEC>(q, k, dm, tabs);
     if (cnt == 8) {
       *(gp<f32x4>)(o + i) = f32x4{v[0], v[1], v[2], v[3]};
       *(gp<f32x4>)(o + i + 4) = f32x4{v[4], v[5], v[6], v[7]};
@@ -723,20 +774,55 @@ __global__ void __launch_bounds__(WG) k_dequantize(const uint8_t* __restrict__ c
 // ---------------------------------------------------------------------------
 // what 0: rcp_refined vs IEEE 1/b on the f32 patterns [lo, lo+count)
 // what 1: sqrt_corrected vs the IEEE square root
-// what 2: v_cvt_pk_u8_f32 vs clamp(round_half_even(x), 0, 255) (NaN skipped)
+// what 2: v_cvt_pk_u8_f32 vs clamp(round_half_even(x), 0, 255), NaN -> 0
+// what 3: div_refined(a, b, rcp_refined(b)) vs IEEE a/b on `count` pairs drawn
+//         from a counter-based generator seeded by lo: b over every exponent of
+//         the refined reciprocal's range, a over the dividend range of the
+//         fast AdamW step (|a| in [2^-100, 2^101) or 0), quotient 0 or of
+//         magnitude in [2^-125, 2^120) (pairs outside are skipped)
+// what 4: the same division with b an fp16 value (a block scale) and |a| <= b
+// what 5: as 3, but only pairs whose quotient is a nonzero subnormal: the
+//         range the AdamW step's guard keeps out of the fast form
+__device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
+  x += 0x9E3779B97F4A7C15ull;
+  x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
+  x = (x ^ (x >> 27)) * 0x94D049BB133111EBull;
+  return x ^ (x >> 31);
+}
 __global__ void __launch_bounds__(WG) k_selftest(int what, uint32_t lo, uint64_t count,
                                                  unsigned long long* __restrict__ bad) {
   const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
   unsigned long long nb = 0;
   for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
-    const float x = u2f(lo + (uint32_t)i);
     bool ok;
-    if (what == 0) ok = f2u(rcp_refined(x)) == f2u(1.0f / x);
-    else if (what == 1) ok = f2u(sqrt_corrected(x)) == f2u(__builtin_sqrtf(x));
-    else {
-      const uint32_t got = __builtin_amdgcn_cvt_pk_u8_f32(x, 0, 0u) & 0xFFu;
-      const uint32_t ref = (uint32_t)__builtin_rintf(fmaxf(fminf(x, 255.0f), 0.0f));
-      ok = (x != x) || got == ref;
+    if (what <= 2) {
+      const float x = u2f(lo + (uint32_t)i);
+      if (what == 0) ok = f2u(rcp_refined(x)) == f2u(1.0f / x);
+      else if (what == 1) ok = f2u(sqrt_corrected(x)) == f2u(__builtin_sqrtf(x));
+      else {
+        const uint32_t got = __builtin_amdgcn_cvt_pk_u8_f32(x, 0, 0u) & 0xFFu;
+        const uint32_t ref = (x != x) ? 0u : (uint32_t)__builtin_rintf(fmaxf(fminf(x, 255.0f), 0.0f));
+        ok = got == ref;
+      }
+    } else {
+      const uint64_t h = splitmix64(((uint64_t)lo << 32) ^ i);
+      float a, b;
+      if (what != 4) {
+        const uint32_t eb = 1u + (uint32_t)((h >> 23) % 252u);                  // b in [2^-126, 2^126)
+        b = u2f((eb << 23) | (uint32_t)(h & 0x7FFFFFu));
+        const uint32_t ea = 27u + (uint32_t)((h >> 31) % 201u);                 // |a| in [2^-100, 2^101)
+        a = u2f(((uint32_t)(h >> 63) << 31) | (ea << 23) | (uint32_t)((h >> 40) & 0x7FFFFFu));
+        if (((h >> 12) & 1023u) == 0u) a = 0.0f;
+        const float q = fabsf(a / b);
+        const bool fast_domain = q == 0.0f || (q >= 0x1p-125f && q < 0x1p120f);
+        const bool subnormal = q > 0.0f && q < 0x1p-126f;
+        if (what == 3 ? !fast_domain : !subnormal) continue;
+      } else {
+        b = h2f(1u + (uint32_t)((h >> 48) % 0x7BFFu));                          // positive finite fp16
+        const float t = u2f((uint32_t)(h & 0x7FFFFFu) | 0x3F000000u) * 2.0f - 1.0f;   // [-1, 1)
+        a = b * t;
+      }
+      ok = f2u(div_refined(a, b, rcp_refined(b))) == f2u(a / b);
     }
     nb += ok ? 0 : 1;
   }

@@ -337,6 +337,45 @@ int launch_check(const char* what) {
   return FO_OK;
 }
 
+// Range of (effective) gradients for which the fused AdamW step's fast
+// arithmetic is exact: g = 0 or g_lo <= |g| <= g_hi (see AdamWConsts).  It
+// follows from the f32 step constants and the ranges every finite stored
+// state decodes into:
+//   momentum |m_hat| in {0} u [2^-33, 66021]  (scale >= 2^-24: level >= 2^-24/253;
+//                                              linear code -128: 128/127 * 65504)
+//   variance  v_hat  in {0} u [2^-66, 2^33]
+// Conditions, each with a margin for the rounding of the products:
+//   v = b2*v_hat + (1-b2)*g*g outside (0, 2^-96) (the corrected square root
+//     is exact) and so small that den = sqrt(v)*ibc2 + eps <= 2^52;
+//   a nonzero m = b1*m_hat + (1-b1)*g at least 2^-73: both terms are 0 or at
+//     least 2^-50, and a sum of such floats that does not vanish is a nonzero
+//     multiple of 2^-73;
+//   so every nonzero quotient m/den is a normal number (>= 2^-125), and
+//   |m/den| < 2^119 because den >= eps.
+// That keeps rcp_refined, div_refined and sqrt_corrected in their exact
+// ranges.  When no such range exists (eps not a normal number, b1 or b2 tiny,
+// ibc2 huge) every wave takes the IEEE form.
+static void adamw_fast_range(AdamWConsts* c) {
+  c->fast = 0;
+  c->g_lo2 = 0xFFFFFFFEu;
+  c->g_hi = 0.0f;
+  const double b1 = c->b1, b2 = c->b2, omb1 = c->omb1, omb2 = c->omb2, eps = c->eps, ibc2 = c->ibc2;
+  if (!(eps >= 0x1p-126) || !(omb1 > 0.0) || !(omb2 > 0.0) || !(ibc2 > 0.0 && ibc2 < 0x1p35)) return;
+  if (b1 != 0.0 && b1 < 0x1p-17) return;
+  if (b2 != 0.0 && b2 < 0x1p-29) return;
+  const double v_hi = std::min(0x1p100, std::pow((0x1p52 - eps) / ibc2, 2.0)) * (1.0 - 0x1p-20);
+  const double lo = std::max(std::sqrt(0x1p-95 / omb2), 0x1p-49 / omb1);
+  const double hi = std::min(std::sqrt((v_hi - 0x1p34) / omb2), (0x1p119 * eps - 66021.0 * b1 - 1.0) / omb1);
+  const float flo = std::nextafter((float)lo, INFINITY);        // rounded outwards: conservative
+  const float fhi = std::nextafter((float)hi, 0.0f);
+  if (!(flo > 0.0f) || !(fhi > flo) || !std::isfinite(fhi)) return;
+  uint32_t blo;
+  std::memcpy(&blo, &flo, 4);
+  c->g_lo2 = 2u * blo - 2u;
+  c->g_hi = fhi;
+  c->fast = 1;
+}
+
 }  // namespace
 
 extern "C" {
@@ -517,7 +556,7 @@ int fo_fused_adamw_step(const fo_adamw_tensor* list, int32_t count, const fo_ada
   c.eps = (float)hp->eps;
   c.wd = hp->l2_decay ? (float)hp->weight_decay : 0.0f;
   if (hp->l2_decay) c.decay = 1.0f;                 // Adam: no decoupled decay
-  c.fast_rcp = (c.eps >= 0x1p-126f) ? 1 : 0;
+  adamw_fast_range(&c);
   void (*kern)(const TensorDesc*, int, int64_t, int64_t, const CodecTables*, AdamWConsts) = nullptr;
   if (hp->l2_decay) FO_SELECT3(k_fused_adamw_l2, hp->wfmt, hp->ecc_bits, hp->codec, kern);
   else FO_SELECT3(k_fused_adamw_dec, hp->wfmt, hp->ecc_bits, hp->codec, kern);
@@ -601,7 +640,9 @@ int fo_fused_sgdm_step(const fo_sgdm_tensor* list, int32_t count, const fo_sgdm_
   c.wd = (float)hp->weight_decay;
   c.damp1 = (float)(1.0 - hp->dampening);
   c.nesterov = hp->nesterov;
-  c.first = (hp->step == 1) ? 1 : 0;
+  // step 1 sets the buffer to d; with momentum 0 every step does (torch.optim.SGD
+  // keeps no buffer then, so dampening has no effect)
+  c.first = (hp->step == 1 || hp->momentum == 0.0) ? 1 : 0;
   void (*kern)(const TensorDesc*, int, int64_t, int64_t, const CodecTables*, SGDMConsts) = nullptr;
   FO_SELECT3(k_fused_sgdm, hp->wfmt, hp->ecc_bits, hp->codec, kern);
   int grid;
@@ -619,9 +660,9 @@ int fo_fused_sgdm_step(const fo_sgdm_tensor* list, int32_t count, const fo_sgdm_
 
 int fo_selftest(int what, uint32_t lo, uint64_t count, uint64_t* mismatches, void* stream) {
   g_err.clear();
-  if (what < 0 || what > 2) return fail(FO_EINVAL, "bad self-test %d", what);
+  if (what < 0 || what > 5) return fail(FO_EINVAL, "bad self-test %d", what);
   if (!mismatches) return fail(FO_EINVAL, "mismatches is NULL");
-  if (count > (1ull << 32) - lo) return fail(FO_EINVAL, "range exceeds the f32 patterns");
+  if (what <= 2 && count > (1ull << 32) - lo) return fail(FO_EINVAL, "range exceeds the f32 patterns");
   hipStream_t s = as_stream(stream);
   unsigned long long* d = nullptr;
   hipError_t e = hipMalloc((void**)&d, sizeof(*d));

@@ -386,6 +386,4 @@ class FlashSGD(_FlashBase):
     def _launch(self, tl, group, step):
         B.fo_fused_sgdm_step(tl, B.sgdm_hparams(group["lr"], group["momentum"], group["weight_decay"], step,
                                                 self.wfmt, self.ecc_bits, self.codec,
-                                                # with momentum 0 torch ignores dampening (no buffer)
-                                                group["dampening"] if group["momentum"] else 0.0,
-                                                group["nesterov"]))
+                                                group["dampening"], group["nesterov"]))

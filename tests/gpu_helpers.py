@@ -1,13 +1,18 @@
 """Shared helpers of the GPU parity tests: host<->device conversion of state
-arrays and the acceptance bar.
+arrays, the lock-step runner and the acceptance checks.
 
-Acceptance bar (per step, per array): codes, ECCs and 16-bit weights
-identical on >= 99.99% of elements and within one unit on the rest
-(for (theta', rho) pairs: adjacent in the ordered (theta', rho) sequence,
-i.e. reconstructed masters within one ECC step); block scales identical on
->= 99.99% of blocks.  The kernels take every decision in the same float32
-operations as the oracle, so the expected mismatch count is zero; the
-tests print it.
+Lock-step: before every GPU step the test copies the device state to the
+host, the oracle steps that copy with the same gradient and hyperparameters,
+and the result is compared with the device state after its step.  Each step
+is therefore checked on its own, from identical inputs, and a difference can
+never compound.
+
+Acceptance: the kernels take every decision with the oracle's float32
+operations (exact fast arithmetic, verified on the device), so the tests
+require bitwise equality of every array: 16-bit weights, ECCs, codes and
+block scales.  (The stated bar of the task -- identical on >= 99.99% of
+elements, within one unit on the rest -- is implied.)  NaN weights are
+compared as NaN: the position must match, the payload may differ.
 """
 
 from __future__ import annotations
@@ -16,8 +21,6 @@ import numpy as np
 import torch
 
 import oracle as O
-
-FRACTION = 0.9999
 
 
 def to_host(t: torch.Tensor) -> np.ndarray:
@@ -34,59 +37,85 @@ def to_dev(a: np.ndarray, dtype, device="cuda") -> torch.Tensor:
     return torch.from_numpy(a).to(device)
 
 
+ADAMW_KEYS = ("w16", "ecc", "m_q", "m_s", "v_q", "v_s")
+SGDM_KEYS = ("w16", "ecc", "b_q", "b_s")
+
+
 def adamw_state_to_host(st: dict) -> dict:
-    return {k: to_host(st[k]) for k in ("w16", "ecc", "m_q", "m_s", "v_q", "v_s")}
+    return {k: to_host(st[k]) for k in ADAMW_KEYS}
 
 
 def sgdm_state_to_host(st: dict) -> dict:
-    return {k: to_host(st[k]) for k in ("w16", "ecc", "b_q", "b_s")}
+    return {k: to_host(st[k]) for k in SGDM_KEYS}
 
 
-def _frac_equal(a, b):
-    if a.size == 0:
-        return 1.0, 0
-    eq = a == b
-    return float(np.mean(eq)), int(a.size - np.count_nonzero(eq))
+def _mismatches(a, b) -> int:
+    return int(a.size - np.count_nonzero(a == b)) if a.size else 0
 
 
-def check_codes(name, got, want, lsb=1):
-    f, bad = _frac_equal(got, want)
-    assert f >= FRACTION, f"{name}: identical on {f:.6f} ({bad} differ)"
+def check_codes(name, got, want):
+    bad = _mismatches(got, want)
     if bad:
-        d = np.abs(got.astype(np.int64) - want.astype(np.int64))
-        assert d.max() <= lsb, f"{name}: max code difference {d.max()}"
-    return bad
+        idx = np.nonzero(got != want)[0][:8]
+        raise AssertionError(f"{name}: {bad} of {got.size} differ; first at {list(idx)}: "
+                             f"got {list(got[idx])}, want {list(want[idx])}")
+    return 0
 
 
 def check_weights(name, w_got, e_got, w_want, e_want, fmt, ecc_bits):
-    eq = (w_got == w_want) & (e_got == e_want)
-    f = float(np.mean(eq)) if eq.size else 1.0
-    bad = int(eq.size - np.count_nonzero(eq))
-    assert f >= FRACTION, f"{name}: (theta', rho) identical on {f:.6f} ({bad} differ)"
-    if bad:
-        idx = ~eq
-        xg = O.reconstruct_weights(w_got[idx], e_got[idx], fmt, ecc_bits).astype(np.float64)
-        xw = O.reconstruct_weights(w_want[idx], e_want[idx], fmt, ecc_bits).astype(np.float64)
-        from oracle.numerics import bits_to_value, spacing_out
-        a = np.abs(bits_to_value(w_want[idx], fmt))
-        step = spacing_out(a, fmt) * 2.0 ** -ecc_bits
-        assert np.all(np.abs(xg - xw) <= step * (1 + 1e-9)), f"{name}: differing masters more than one ECC step apart"
-    return bad
+    nan = np.isnan(O.reconstruct_weights(w_want, e_want, fmt, ecc_bits))
+    nan_got = np.isnan(O.reconstruct_weights(w_got, e_got, fmt, ecc_bits))
+    assert np.array_equal(nan, nan_got), f"{name}: NaN weights at different elements"
+    check_codes(f"{name} w16", np.where(nan, w_want, w_got), w_want)
+    check_codes(f"{name} ecc", e_got, e_want)
+    return 0
 
 
-def check_adamw_state(tag, got: dict, want: dict, fmt="bf16", ecc_bits=8):
-    bad = {}
-    bad["w"] = check_weights(f"{tag} w16/ecc", got["w16"], got["ecc"], want["w16"], want["ecc"], fmt, ecc_bits)
-    bad["m_q"] = check_codes(f"{tag} m_q", got["m_q"], want["m_q"])
-    bad["v_q"] = check_codes(f"{tag} v_q", got["v_q"], want["v_q"])
-    bad["m_s"] = check_codes(f"{tag} m_s", got["m_s"], want["m_s"], lsb=1)
-    bad["v_s"] = check_codes(f"{tag} v_s", got["v_s"], want["v_s"], lsb=1)
-    return bad
+def check_state(tag, got: dict, want: dict, fmt="bf16", ecc_bits=8):
+    check_weights(f"{tag} w16/ecc", got["w16"], got["ecc"], want["w16"], want["ecc"], fmt, ecc_bits)
+    for k in got:
+        if k not in ("w16", "ecc"):
+            check_codes(f"{tag} {k}", got[k], want[k])
 
 
-def check_sgdm_state(tag, got: dict, want: dict, fmt="bf16", ecc_bits=8):
-    bad = {}
-    bad["w"] = check_weights(f"{tag} w16/ecc", got["w16"], got["ecc"], want["w16"], want["ecc"], fmt, ecc_bits)
-    bad["b_q"] = check_codes(f"{tag} b_q", got["b_q"], want["b_q"])
-    bad["b_s"] = check_codes(f"{tag} b_s", got["b_s"], want["b_s"], lsb=1)
-    return bad
+def run_lockstep(kind, dev, steps, grads, hp, fmt="bf16", ecc_bits=8, codec="companded", tag="t",
+                 step_list=None):
+    """Lock-step GPU vs oracle.
+
+    kind: "adamw" (AdamW, or Adam with hp["l2_decay"]) or "sgdm".
+    dev: list of device states (dicts of tensors, grads included), initialised.
+    grads(i, step) -> the 16-bit gradient bit pattern of tensor i at `step`.
+    Runs steps 1..steps (or the steps of step_list) and checks every tensor
+    after every step; returns the number of (tensor, step) checks made.
+    """
+    from precision_optimizer_state_amd import binding as B
+    dtype = {"bf16": torch.bfloat16, "fp16": torch.float16}[fmt]
+    adam = kind == "adamw"
+    host_state = adamw_state_to_host if adam else sgdm_state_to_host
+    tl = B.AdamWList(dev) if adam else B.SGDMList(dev)
+    checks = 0
+    for step in (step_list if step_list is not None else range(1, steps + 1)):
+        torch.cuda.synchronize()
+        before = [host_state(st) for st in dev]
+        gbs = []
+        for i, st in enumerate(dev):
+            gb = grads(i, step)
+            gbs.append(gb)
+            if st["w16"].numel():
+                st["grad"].copy_(to_dev(gb, dtype))
+        if adam:
+            B.fo_fused_adamw_step(tl, B.adamw_hparams(step=step, wfmt=fmt, ecc_bits=ecc_bits, codec=codec, **hp))
+        else:
+            B.fo_fused_sgdm_step(tl, B.sgdm_hparams(step=step, wfmt=fmt, ecc_bits=ecc_bits, codec=codec, **hp))
+        torch.cuda.synchronize()
+        for i, st in enumerate(dev):
+            if not st["w16"].numel():
+                continue
+            if adam:
+                want = O.adamw_step(before[i], gbs[i], dict(hp, step=step), fmt, ecc_bits, codec)
+            else:
+                want = O.sgdm_step(before[i], gbs[i], dict(hp, step=step), fmt, ecc_bits, codec)
+            check_state(f"{tag} step {step} tensor {i} (n={st['w16'].numel()})", host_state(st), want,
+                        fmt, ecc_bits)
+            checks += 1
+    return checks

@@ -16,14 +16,7 @@ import oracle as O
 from oracle.numerics import split_weights
 from precision_optimizer_state_amd import binding as B
 from precision_optimizer_state_amd.state import alloc_adamw_state, alloc_sgdm_state
-from tests.gpu_helpers import (
-    adamw_state_to_host,
-    check_adamw_state,
-    check_sgdm_state,
-    sgdm_state_to_host,
-    to_dev,
-    to_host,
-)
+from tests.gpu_helpers import run_lockstep, to_dev
 from workloads import host_grad_bits, host_grads, host_weights
 
 pytestmark = pytest.mark.gpu
@@ -63,12 +56,10 @@ def test_dequantize_every_momentum_code(codec):
 def test_fused_adam_from_arbitrary_states(fmt, ecc_bits, codec, l2):
     rng = np.random.default_rng(17)
     hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
-    ref, dev = [], []
+    dev = []
     for i, n in enumerate(SIZES):
         w16, ecc = split_weights(host_weights("arb", i, n), fmt, ecc_bits)
         m_q, m_s, v_q, v_s = _random_codes(rng, n)
-        st = {"w16": w16, "ecc": ecc, "m_q": m_q, "m_s": m_s, "v_q": v_q, "v_s": v_s}
-        ref.append(st)
         d = alloc_adamw_state(n, fmt, ecc_bits)
         d["w16"].copy_(to_dev(w16, DT[fmt]))
         d["ecc"].copy_(to_dev(ecc, d["ecc"].dtype))
@@ -77,21 +68,10 @@ def test_fused_adam_from_arbitrary_states(fmt, ecc_bits, codec, l2):
         d["m_s"].copy_(to_dev(m_s, torch.float16))
         d["v_s"].copy_(to_dev(v_s, torch.float16))
         dev.append(d)
-    tl = B.AdamWList(dev)
-    for step in (7, 8, 9):
-        gbs = []
-        for i, n in enumerate(SIZES):
-            gb = host_grad_bits(host_grads("arb", i, step, n, "t3"), fmt)
-            gbs.append(gb)
-            dev[i]["grad"].copy_(to_dev(gb, DT[fmt]))
-        B.fo_fused_adamw_step(tl, B.adamw_hparams(step=step, wfmt=fmt, ecc_bits=ecc_bits, codec=codec,
-                                                  l2_decay=l2, **hp))
-        for i in range(len(SIZES)):
-            ref[i] = O.adamw_step(ref[i], gbs[i], dict(hp, step=step, l2_decay=l2), fmt, ecc_bits, codec)
-        torch.cuda.synchronize()
-        for i in range(len(SIZES)):
-            check_adamw_state(f"arbitrary {fmt}/{ecc_bits}/{codec} l2={l2} step {step} tensor {i}",
-                              adamw_state_to_host(dev[i]), ref[i], fmt, ecc_bits)
+    run_lockstep("adamw", dev, 0,
+                 lambda i, step: host_grad_bits(host_grads("arb", i, step, SIZES[i], "t3"), fmt),
+                 dict(hp, l2_decay=l2), fmt, ecc_bits, codec, f"arbitrary {fmt}/{ecc_bits}/{codec} l2={l2}",
+                 step_list=(7, 8, 9))
 
 
 @pytest.mark.parametrize("fmt,ecc_bits,codec", [("bf16", 8, "companded"), ("fp16", 8, "companded"),
@@ -100,28 +80,17 @@ def test_fused_adam_from_arbitrary_states(fmt, ecc_bits, codec, l2):
 def test_fused_sgd_from_arbitrary_states(fmt, ecc_bits, codec, nesterov, dampening):
     rng = np.random.default_rng(23)
     hp = dict(lr=0.05, momentum=0.9, weight_decay=1e-4, dampening=dampening, nesterov=nesterov)
-    ref, dev = [], []
+    dev = []
     for i, n in enumerate(SIZES):
         w16, ecc = split_weights(host_weights("arbs", i, n), fmt, ecc_bits)
         b_q, b_s, _, _ = _random_codes(rng, n)
-        ref.append({"w16": w16, "ecc": ecc, "b_q": b_q, "b_s": b_s})
         d = alloc_sgdm_state(n, fmt, ecc_bits)
         d["w16"].copy_(to_dev(w16, DT[fmt]))
         d["ecc"].copy_(to_dev(ecc, d["ecc"].dtype))
         d["b_q"].copy_(to_dev(b_q, torch.int8))
         d["b_s"].copy_(to_dev(b_s, torch.float16))
         dev.append(d)
-    tl = B.SGDMList(dev)
-    for step in (4, 5):
-        gbs = []
-        for i, n in enumerate(SIZES):
-            gb = host_grad_bits(host_grads("arbs", i, step, n, "t3"), fmt)
-            gbs.append(gb)
-            dev[i]["grad"].copy_(to_dev(gb, DT[fmt]))
-        B.fo_fused_sgdm_step(tl, B.sgdm_hparams(step=step, wfmt=fmt, ecc_bits=ecc_bits, codec=codec, **hp))
-        for i in range(len(SIZES)):
-            ref[i] = O.sgdm_step(ref[i], gbs[i], dict(hp, step=step), fmt, ecc_bits, codec)
-        torch.cuda.synchronize()
-        for i in range(len(SIZES)):
-            check_sgdm_state(f"arbitrary sgd {fmt}/{codec} nesterov={nesterov} damp={dampening} step {step} "
-                             f"tensor {i}", sgdm_state_to_host(dev[i]), ref[i], fmt, ecc_bits)
+    run_lockstep("sgdm", dev, 0,
+                 lambda i, step: host_grad_bits(host_grads("arbs", i, step, SIZES[i], "t3"), fmt),
+                 hp, fmt, ecc_bits, codec, f"arbitrary sgd {fmt}/{codec} nesterov={nesterov} damp={dampening}",
+                 step_list=(4, 5))

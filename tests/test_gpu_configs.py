@@ -4,10 +4,11 @@ configuration bench.py times (one fused call over the whole parameter list;
 
 The oracle cannot run 8 billion elements, but 32-element blocks are
 independent: for a seeded sample of blocks of every tensor (always including
-the tensor's last, possibly partial, block) the test copies the f32 weights
-and each step's 16-bit gradients back from the device generators, runs the
-oracle on those blocks alone, and compares the final state of the same blocks
-element by element.  No value produced by the HIP path enters the oracle.
+the tensor's last, possibly partial, block) the test runs in lock-step on
+those blocks.  Before every step it gathers the sampled blocks' device state
+and gradients, the oracle steps them alone, and after the device step the
+same blocks must be bitwise equal.  The initial split of the sampled weights
+is compared with the oracle's split first.
 """
 
 import numpy as np
@@ -15,10 +16,9 @@ import pytest
 import torch
 
 import oracle as O
-from oracle.optim import fresh_adamw_state, fresh_sgdm_state
 from precision_optimizer_state_amd import binding as B
 from precision_optimizer_state_amd.state import alloc_adamw_state, alloc_sgdm_state
-from tests.gpu_helpers import check_adamw_state, check_sgdm_state, to_host
+from tests.gpu_helpers import check_state, check_weights, to_host
 from workloads import config, device_grads, device_weights
 from workloads.configs import Config
 from workloads.configs import RELEASE_CHUNKS
@@ -41,11 +41,21 @@ def _gather(t, idx_dev):
     return to_host(t[idx_dev])
 
 
+def _sampled_state(st, bdev, idev, adam):
+    got = {"w16": _gather(st["w16"], idev), "ecc": _gather(st["ecc"], idev)}
+    if adam:
+        got.update(m_q=_gather(st["m_q"], idev), m_s=_gather(st["m_s"], bdev),
+                   v_q=_gather(st["v_q"], idev), v_s=_gather(st["v_s"], bdev))
+    else:
+        got.update(b_q=_gather(st["b_q"], idev), b_s=_gather(st["b_s"], bdev))
+    return got
+
+
 def _run(cfg_name, steps, blocks_per_tensor, release=False, cfg=None, forced=()):
     cfg = cfg or config(cfg_name)
     rng = np.random.default_rng(7)
     adam = cfg.optimizer == "adamw"
-    states, samples, refs = [], [], []
+    states, samples = [], []
     print(f"{cfg_name}: {len(cfg.numels)} tensors, {cfg.params} params, {steps} steps", flush=True)
     for i, n in enumerate(cfg.numels):
         st = (alloc_adamw_state if adam else alloc_sgdm_state)(n, cfg.wfmt, cfg.ecc_bits)
@@ -55,9 +65,12 @@ def _run(cfg_name, steps, blocks_per_tensor, release=False, cfg=None, forced=())
         x0 = w[idx_dev].cpu().numpy()
         B.fo_split_weights(w, st["w16"], st["ecc"], cfg.wfmt, cfg.ecc_bits)
         del w
+        if n:
+            w_ref, e_ref = O.split_weights(x0, cfg.wfmt, cfg.ecc_bits)
+            check_weights(f"{cfg_name} split {i}", _gather(st["w16"], idx_dev), _gather(st["ecc"], idx_dev),
+                          w_ref, e_ref, cfg.wfmt, cfg.ecc_bits)
         states.append(st)
         samples.append((torch.from_numpy(blocks).cuda(), idx_dev))
-        refs.append((fresh_adamw_state if adam else fresh_sgdm_state)(x0, cfg.wfmt, cfg.ecc_bits))
     if adam and release:
         st = states[0]
         lists, lo = [], 0
@@ -70,11 +83,13 @@ def _run(cfg_name, steps, blocks_per_tensor, release=False, cfg=None, forced=())
             lo = hi
     else:
         lists = [B.AdamWList(states) if adam else B.SGDMList(states)]
+    total = 0
     for step in range(1, steps + 1):
-        gsamp = []
+        before, gsamp = [], []
         for i, (st, n) in enumerate(zip(states, cfg.numels)):
             device_grads(cfg.name, i, step, n, cfg.grad_kind, cfg.wfmt, out=st["grad"])
             gsamp.append(_gather(st["grad"], samples[i][1]))
+            before.append(_sampled_state(st, *samples[i], adam) if n else None)
         for tl in lists:
             if adam:
                 B.fo_fused_adamw_step(tl, B.adamw_hparams(step=step, wfmt=cfg.wfmt, ecc_bits=cfg.ecc_bits,
@@ -82,33 +97,19 @@ def _run(cfg_name, steps, blocks_per_tensor, release=False, cfg=None, forced=())
             else:
                 B.fo_fused_sgdm_step(tl, B.sgdm_hparams(step=step, wfmt=cfg.wfmt, ecc_bits=cfg.ecc_bits,
                                                         codec=cfg.codec, **cfg.hp))
-        for i in range(len(states)):
+        torch.cuda.synchronize()
+        for i, st in enumerate(states):
             if cfg.numels[i] == 0:
                 continue
             if adam:
-                refs[i] = O.adamw_step(refs[i], gsamp[i], dict(cfg.hp, step=step), cfg.wfmt, cfg.ecc_bits, cfg.codec)
+                want = O.adamw_step(before[i], gsamp[i], dict(cfg.hp, step=step), cfg.wfmt, cfg.ecc_bits, cfg.codec)
             else:
-                refs[i] = O.sgdm_step(refs[i], gsamp[i], dict(cfg.hp, step=step), cfg.wfmt, cfg.ecc_bits,
-                                       cfg.codec)
-    torch.cuda.synchronize()
-    total, bad = 0, 0
-    for i, st in enumerate(states):
-        bdev, idev = samples[i]
-        if cfg.numels[i] == 0:
-            continue
-        if adam:
-            got = {"w16": _gather(st["w16"], idev), "ecc": _gather(st["ecc"], idev),
-                   "m_q": _gather(st["m_q"], idev), "v_q": _gather(st["v_q"], idev),
-                   "m_s": _gather(st["m_s"], bdev), "v_s": _gather(st["v_s"], bdev)}
-            b = check_adamw_state(f"{cfg_name} tensor {i}", got, refs[i], cfg.wfmt, cfg.ecc_bits)
-        else:
-            got = {"w16": _gather(st["w16"], idev), "ecc": _gather(st["ecc"], idev),
-                   "b_q": _gather(st["b_q"], idev), "b_s": _gather(st["b_s"], bdev)}
-            b = check_sgdm_state(f"{cfg_name} tensor {i}", got, refs[i], cfg.wfmt, cfg.ecc_bits)
-        bad += sum(b.values())
-        total += idev.numel()
-    print(f"{cfg_name}{' release' if release else ''}: {total} sampled elements after {steps} steps, "
-          f"{bad} mismatches", flush=True)
+                want = O.sgdm_step(before[i], gsamp[i], dict(cfg.hp, step=step), cfg.wfmt, cfg.ecc_bits, cfg.codec)
+            check_state(f"{cfg_name} step {step} tensor {i}", _sampled_state(st, *samples[i], adam), want,
+                        cfg.wfmt, cfg.ecc_bits)
+            total += samples[i][1].numel()
+    print(f"{cfg_name}{' release' if release else ''}: {total} sampled element-steps over {steps} lock-steps, "
+          f"all bitwise equal", flush=True)
     del states, lists
     torch.cuda.empty_cache()
 

@@ -1,6 +1,7 @@
 """The drop-in optimizers (FlashAdamW, FlashAdam, FlashSGD) on a small model: every step
-matches the oracle bit for bit, gradient release matches the plain step,
-state_dict save/load resumes bit for bit, and training tracks
+matches the oracle bit for bit in lock-step (the oracle steps a host copy of
+the optimizer's state before each step), gradient release matches the plain
+step, state_dict save/load resumes bit for bit, and training tracks
 torch.optim.AdamW in float32."""
 
 import copy
@@ -10,9 +11,8 @@ import pytest
 import torch
 
 import oracle as O
-from oracle.optim import fresh_adamw_state, fresh_sgdm_state
 from precision_optimizer_state_amd import FlashAdam, FlashAdamW, FlashSGD
-from tests.gpu_helpers import check_adamw_state, check_sgdm_state, to_host
+from tests.gpu_helpers import check_state, check_weights, to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -39,50 +39,62 @@ def _loss(model, i):
 HP = dict(lr=3e-3, betas=(0.9, 0.95), eps=1e-8, weight_decay=0.1)
 
 
+def _host_state(opt, p, adam=True):
+    st = opt.state[p]
+    out = {"w16": to_host(p.data.view(-1)), "ecc": to_host(st["ecc"].view(-1))}
+    for k in (("m_q", "m_s", "v_q", "v_s") if adam else ("b_q", "b_s")):
+        out[k] = to_host(st[k].view(-1))
+    return out
+
+
+def _check_initial_split(opt, params, x0):
+    torch.cuda.synchronize()
+    for i, p in enumerate(params):
+        w_ref, e_ref = O.split_weights(x0[i])
+        check_weights(f"initial split param {i}", to_host(p.data.view(-1)), to_host(opt.state[p]["ecc"].view(-1)),
+                      w_ref, e_ref, "bf16", 8)
+
+
+def _lockstep(model, opt, steps, hp_of, adam=True, tag=""):
+    """Run `steps` optimizer steps; before each one the oracle takes a host
+    copy of every parameter's state, and after it the states must match."""
+    params = list(model.parameters())
+    for step in range(1, steps + 1):
+        opt.zero_grad(set_to_none=True)
+        _loss(model, step).backward()
+        grads = [to_host(p.grad.view(-1)) for p in params]
+        before = [_host_state(opt, p, adam) for p in params]
+        opt.step()
+        torch.cuda.synchronize()
+        for i, p in enumerate(params):
+            hp = dict(hp_of(p), step=step)
+            want = O.adamw_step(before[i], grads[i], hp) if adam else O.sgdm_step(before[i], grads[i], hp)
+            check_state(f"{tag} step {step} param {i}", _host_state(opt, p, adam), want)
+
+
 @pytest.mark.parametrize("cls", [FlashAdamW, FlashAdam])
 def test_flash_adamw_matches_oracle_every_step(cls):
     model = _model()
     x0 = [p.detach().float().cpu().numpy().ravel().copy() for p in model.parameters()]
     opt = cls(model.parameters(), **HP)
-    refs = [fresh_adamw_state(x) for x in x0]
-    for step in range(1, 6):
-        opt.zero_grad(set_to_none=True)
-        _loss(model, step).backward()
-        grads = [to_host(p.grad.view(-1)) for p in model.parameters()]
-        opt.step()
-        hp = dict(lr=HP["lr"], beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, step=step,
-                  l2_decay=cls is FlashAdam)
-        for i, p in enumerate(model.parameters()):
-            refs[i] = O.adamw_step(refs[i], grads[i], hp)
-            st = opt.state[p]
-            got = {"w16": to_host(p.data.view(-1)), "ecc": to_host(st["ecc"].view(-1)),
-                   "m_q": to_host(st["m_q"]), "v_q": to_host(st["v_q"]),
-                   "m_s": to_host(st["m_s"]).view(np.uint16), "v_s": to_host(st["v_s"]).view(np.uint16)}
-            bad = check_adamw_state(f"{cls.__name__} step {step} param {i}", got, refs[i])
-            assert sum(bad.values()) == 0
-    # master weights are the oracle's reconstruction
-    for i, p in enumerate(model.parameters()):
+    _check_initial_split(opt, list(model.parameters()), x0)
+    hp = dict(lr=HP["lr"], beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, l2_decay=cls is FlashAdam)
+    _lockstep(model, opt, 5, lambda p: hp, tag=cls.__name__)
+    # master weights are the oracle's reconstruction of the stored split
+    for p in model.parameters():
         mw = opt.master_weights(p).view(-1).cpu().numpy()
-        assert np.array_equal(mw.view(np.uint32), O.reconstruct_weights(refs[i]["w16"], refs[i]["ecc"]).view(np.uint32))
+        want = O.reconstruct_weights(to_host(p.data.view(-1)), to_host(opt.state[p]["ecc"].view(-1)))
+        assert np.array_equal(mw.view(np.uint32), want.view(np.uint32))
 
 
-@pytest.mark.parametrize("extra", [{}, {"nesterov": True}, {"dampening": 0.3}])
+@pytest.mark.parametrize("extra", [{}, {"nesterov": True}, {"dampening": 0.3}, {"momentum": 0.0, "dampening": 0.5}])
 def test_flash_sgd_matches_oracle_every_step(extra):
     model = _model(1)
     x0 = [p.detach().float().cpu().numpy().ravel().copy() for p in model.parameters()]
-    opt = FlashSGD(model.parameters(), lr=0.05, momentum=0.9, weight_decay=1e-4, **extra)
-    refs = [fresh_sgdm_state(x) for x in x0]
-    for step in range(1, 6):
-        opt.zero_grad(set_to_none=True)
-        _loss(model, step).backward()
-        grads = [to_host(p.grad.view(-1)) for p in model.parameters()]
-        opt.step()
-        for i, p in enumerate(model.parameters()):
-            refs[i] = O.sgdm_step(refs[i], grads[i], dict(lr=0.05, momentum=0.9, weight_decay=1e-4, step=step, **extra))
-            st = opt.state[p]
-            got = {"w16": to_host(p.data.view(-1)), "ecc": to_host(st["ecc"].view(-1)),
-                   "b_q": to_host(st["b_q"]), "b_s": to_host(st["b_s"]).view(np.uint16)}
-            assert sum(check_sgdm_state(f"FlashSGD step {step} param {i}", got, refs[i]).values()) == 0
+    kw = dict(dict(lr=0.05, momentum=0.9, weight_decay=1e-4), **extra)
+    opt = FlashSGD(model.parameters(), **kw)
+    _check_initial_split(opt, list(model.parameters()), x0)
+    _lockstep(model, opt, 5, lambda p: kw, adam=False, tag=f"FlashSGD {extra}")
 
 
 def _train(model, opt, steps, start=1):
@@ -240,23 +252,13 @@ def test_param_groups_use_their_own_hyperparameters():
     with its own hyperparameters at every step."""
     model = _model(6)
     params = list(model.parameters())
-    x0 = [p.detach().float().cpu().numpy().ravel().copy() for p in params]
     groups = [{"params": [p for p in params if p.dim() > 1], "lr": 2e-3, "weight_decay": 0.1},
               {"params": [p for p in params if p.dim() == 1], "lr": 5e-3, "weight_decay": 0.0}]
     opt = FlashAdamW(groups, betas=(0.9, 0.95), eps=1e-8)
-    hp_of = {id(p): g for g in opt.param_groups for p in g["params"]}
-    refs = [fresh_adamw_state(x) for x in x0]
-    for step in range(1, 4):
-        opt.zero_grad(set_to_none=True)
-        _loss(model, step).backward()
-        grads = [to_host(p.grad.view(-1)) for p in params]
-        opt.step()
-        for i, p in enumerate(params):
-            g = hp_of[id(p)]
-            hp = dict(lr=g["lr"], beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=g["weight_decay"], step=step)
-            refs[i] = O.adamw_step(refs[i], grads[i], hp)
-            st = opt.state[p]
-            got = {"w16": to_host(p.data.view(-1)), "ecc": to_host(st["ecc"].view(-1)),
-                   "m_q": to_host(st["m_q"]), "v_q": to_host(st["v_q"]),
-                   "m_s": to_host(st["m_s"]).view(np.uint16), "v_s": to_host(st["v_s"]).view(np.uint16)}
-            assert sum(check_adamw_state(f"group step {step} param {i}", got, refs[i]).values()) == 0
+    group_of = {id(p): g for g in opt.param_groups for p in g["params"]}
+
+    def hp_of(p):
+        g = group_of[id(p)]
+        return dict(lr=g["lr"], beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=g["weight_decay"])
+
+    _lockstep(model, opt, 3, hp_of, tag="groups")

@@ -1,9 +1,10 @@
 """GPU parity of the HIP path against the CPU oracle, through the C ABI.
 
 Sizes are ones the oracle finishes in seconds while spanning many wave tiles
-and ragged tails.  Full-size workloads are in test_gpu_configs.py.
-Runs are free-running from the same seeded inputs (no state is ever copied
-from the GPU into the oracle).
+and ragged tails.  Full-size workloads are in test_gpu_configs.py.  The fused
+steps run in lock-step (tests/gpu_helpers.py: the oracle steps a host copy of
+the device state before each step) and must match bitwise; the device split
+of the initial weights is compared with the oracle's split first.
 """
 
 import os
@@ -14,16 +15,12 @@ import torch
 
 import oracle as O
 from oracle.numerics import FORMATS, bits_to_value, spacing_in, spacing_out
-from oracle.optim import fresh_adamw_state, fresh_sgdm_state
 from precision_optimizer_state_amd import binding as B
 from precision_optimizer_state_amd.state import alloc_adamw_state, alloc_sgdm_state
 from tests.gpu_helpers import (
-    adamw_state_to_host,
-    check_adamw_state,
     check_codes,
-    check_sgdm_state,
     check_weights,
-    sgdm_state_to_host,
+    run_lockstep,
     to_dev,
     to_host,
 )
@@ -190,9 +187,8 @@ def test_quantize_dequantize_match_oracle(kind, codec, n):
     out = torch.empty(n, dtype=torch.float32, device="cuda")
     B.fo_dequantize(to_dev(q_ref, codes.dtype), to_dev(s_ref, torch.float16), out, kind, codec)
     torch.cuda.synchronize()
-    bq = check_codes(f"quantize {kind}/{codec} codes", to_host(codes), q_ref)
-    bs = check_codes(f"quantize {kind}/{codec} scales", to_host(scales), s_ref)
-    print(f"quantize {kind}/{codec} n={n}: code mismatches {bq}, scale mismatches {bs}", flush=True)
+    check_codes(f"quantize {kind}/{codec} codes", to_host(codes), q_ref)
+    check_codes(f"quantize {kind}/{codec} scales", to_host(scales), s_ref)
     d_ref = O.dequantize_state(q_ref, s_ref, kind, codec)
     assert np.array_equal(out.cpu().numpy().view(np.uint32), d_ref.view(np.uint32))
 
@@ -275,37 +271,34 @@ def test_momentum_encode_every_f32_in_unit_interval():
     assert bool((neg == codes.neg()).all())
 
 
+def _init_states(kind, sizes, fmt, ecc_bits, tag):
+    """Device states from seeded f32 weights split on the device; the split
+    must equal the oracle's."""
+    dev = []
+    for i, n in enumerate(sizes):
+        x = host_weights(tag, i, n)
+        st = (alloc_adamw_state if kind == "adamw" else alloc_sgdm_state)(n, fmt, ecc_bits)
+        if n:
+            B.fo_split_weights(torch.from_numpy(x).cuda(), st["w16"], st["ecc"], fmt, ecc_bits)
+            w_ref, e_ref = O.split_weights(x, fmt, ecc_bits)
+            torch.cuda.synchronize()
+            check_weights(f"{tag} initial split tensor {i}", to_host(st["w16"]), to_host(st["ecc"]), w_ref, e_ref,
+                          fmt, ecc_bits)
+        dev.append(st)
+    return dev
+
+
 def _run_adamw(sizes, steps, hp, fmt="bf16", ecc_bits=8, codec="companded", tag="t", inject=None):
-    """Free-running GPU vs oracle over `steps` steps on a list of tensors."""
-    xs = [host_weights(tag, i, n) for i, n in enumerate(sizes)]
-    dev = [alloc_adamw_state(n, fmt, ecc_bits) for n in sizes]
-    ref = [fresh_adamw_state(x, fmt, ecc_bits) for x in xs]
-    for st, x in zip(dev, xs):
-        B.fo_split_weights(torch.from_numpy(x).cuda(), st["w16"], st["ecc"], fmt, ecc_bits)
-    tl = B.AdamWList(dev)
-    total_bad = 0
-    for step in range(1, steps + 1):
-        gbs = []
-        for i, (st, n) in enumerate(zip(dev, sizes)):
-            g = host_grads(tag, i, step, n, "t3")
-            if inject is not None:
-                g = inject(i, step, g)
-            gb = host_grad_bits(g, fmt)
-            gbs.append(gb)
-            st["grad"].copy_(to_dev(gb, DT[fmt]))
-        B.fo_fused_adamw_step(tl, B.adamw_hparams(step=step, wfmt=fmt, ecc_bits=ecc_bits, codec=codec, **hp))
-        for i in range(len(sizes)):
-            ref[i] = O.adamw_step(ref[i], gbs[i], dict(hp, step=step), fmt, ecc_bits, codec)
-        torch.cuda.synchronize()
-        for i in range(len(sizes)):
-            got = adamw_state_to_host(dev[i])
-            if inject is not None:
-                nan = np.isnan(O.reconstruct_weights(ref[i]["w16"], ref[i]["ecc"], fmt, ecc_bits))
-                assert np.array_equal(nan, np.isnan(O.reconstruct_weights(got["w16"], got["ecc"], fmt, ecc_bits)))
-                got["w16"] = np.where(nan, ref[i]["w16"], got["w16"])
-            bad = check_adamw_state(f"step {step} tensor {i} (n={sizes[i]})", got, ref[i], fmt, ecc_bits)
-            total_bad += sum(bad.values())
-    return total_bad
+    """Lock-step GPU vs oracle over `steps` AdamW steps on a list of tensors."""
+    dev = _init_states("adamw", sizes, fmt, ecc_bits, tag)
+
+    def grads(i, step):
+        g = host_grads(tag, i, step, sizes[i], "t3")
+        if inject is not None:
+            g = inject(i, step, g)
+        return host_grad_bits(g, fmt)
+
+    return run_lockstep("adamw", dev, steps, grads, hp, fmt, ecc_bits, codec, tag)
 
 
 HP_C1 = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
@@ -313,8 +306,8 @@ HP_LM = dict(lr=6e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
 
 
 def test_fused_adamw_flat_1m_10_steps():
-    bad = _run_adamw([1 << 20], 10, HP_C1, tag="c1_flat1m")
-    print(f"c1 flat 1M, 10 steps: {bad} mismatching elements", flush=True)
+    checks = _run_adamw([1 << 20], 10, HP_C1, tag="c1_flat1m")
+    print(f"c1 flat 1M: {checks} lock-step checks, all bitwise equal", flush=True)
 
 
 TAIL_SIZES = list(range(1, 34)) + [63, 64, 65, 1000, 2047, 2048, 2049, 4095, 4096, 4097, 8191, 8193, 20000]
@@ -323,8 +316,8 @@ TAIL_SIZES = list(range(1, 34)) + [63, 64, 65, 1000, 2047, 2048, 2049, 4095, 409
 def test_fused_adamw_ragged_tails_multi_tensor():
     rng = np.random.default_rng(7)
     sizes = TAIL_SIZES + [int(v) for v in rng.integers(1, 100_000, 6)]
-    bad = _run_adamw(sizes, 3, HP_LM, tag="tails")
-    print(f"{len(sizes)} ragged tensors, 3 steps: {bad} mismatching elements", flush=True)
+    checks = _run_adamw(sizes, 3, HP_LM, tag="tails")
+    print(f"{len(sizes)} ragged tensors: {checks} lock-step checks, all bitwise equal", flush=True)
 
 
 @pytest.mark.parametrize("fmt,ecc_bits,codec", [("fp16", 8, "companded"), ("bf16", 16, "companded"),
@@ -332,19 +325,22 @@ def test_fused_adamw_ragged_tails_multi_tensor():
                                                 ("bf16", 16, "linear")])
 def test_fused_adamw_variants(fmt, ecc_bits, codec):
     sizes = [300_000, 4097, 33, 1]
-    bad = _run_adamw(sizes, 4, HP_C1, fmt, ecc_bits, codec, tag=f"var_{fmt}{ecc_bits}{codec}")
-    print(f"variant {fmt}+{ecc_bits}/{codec}: {bad} mismatching elements", flush=True)
+    _run_adamw(sizes, 4, HP_C1, fmt, ecc_bits, codec, tag=f"var_{fmt}{ecc_bits}{codec}")
 
 
 def _inject_specials(i, step, g):
-    """Isolated NaN/inf gradients, and whole 32-element blocks of NaN and of
-    inf: an all-NaN block gets a NaN scale, which keeps the state NaN."""
+    """Isolated NaN/inf gradients, whole 32-element blocks of NaN and of inf
+    (an all-NaN block gets a NaN scale, which keeps the state NaN), and a
+    short last block (the tensor has 8192 + 5 elements) whose valid elements
+    are all NaN, which must keep a NaN scale too."""
     g = g.copy()
     g[5] = np.nan
     g[77] = np.inf
     g[4000] = -np.inf
     g[2048 + 64: 2048 + 96] = np.nan
     g[6144 + 32: 6144 + 64] = np.inf
+    if g.size % 32:
+        g[g.size - g.size % 32:] = np.nan
     return g
 
 
@@ -365,70 +361,37 @@ def test_fused_adamw_degenerate_hyperparameters(name, hp):
     """Hyperparameters at the edges of their ranges take the same path through
     the oracle and the kernel (eps below the smallest normal switches the
     kernel to its IEEE reciprocal)."""
-    bad = _run_adamw([20000, 33], 3, hp, tag=f"hp_{name}")
-    print(f"degenerate hp {name}: {bad} mismatching elements", flush=True)
+    _run_adamw([20000, 33], 3, hp, tag=f"hp_{name}")
 
 
 def test_fused_adamw_late_step_and_zero_eps():
     """Bias correction near 1 at step 10^6, and eps = 0, where blocks whose
     variance decodes to zero divide by zero: NaN and Inf must appear at the
-    same elements on both sides (NaN payloads are compared as NaN)."""
-    sizes = [4096 + 7]
-    xs = [host_weights("late", 0, sizes[0])]
+    same elements on both sides (NaN weights are compared as NaN)."""
+    n = 4096 + 7
     for hp, step0 in ((dict(HP_C1), 10 ** 6), (dict(HP_C1, eps=0.0), 1)):
-        dev = [alloc_adamw_state(n) for n in sizes]
-        ref = [fresh_adamw_state(x) for x in xs]
-        B.fo_split_weights(torch.from_numpy(xs[0]).cuda(), dev[0]["w16"], dev[0]["ecc"], "bf16", 8)
-        tl = B.AdamWList(dev)
-        for step in range(step0, step0 + 3):
-            g = host_grads("late", 0, step, sizes[0], "t3")
+        dev = _init_states("adamw", [n], "bf16", 8, "late")
+
+        def grads(i, step):
+            g = host_grads("late", 0, step, n, "t3")
             g[:64] = 0.0                                    # whole zero blocks: v stays 0
-            gb = host_grad_bits(g, "bf16")
-            dev[0]["grad"].copy_(to_dev(gb, DT["bf16"]))
-            B.fo_fused_adamw_step(tl, B.adamw_hparams(step=step, **hp))
-            ref[0] = O.adamw_step(ref[0], gb, dict(hp, step=step))
-        torch.cuda.synchronize()
-        got = adamw_state_to_host(dev[0])
-        r_ref = O.reconstruct_weights(ref[0]["w16"], ref[0]["ecc"])
-        r_got = O.reconstruct_weights(got["w16"], got["ecc"])
-        nan = np.isnan(r_ref)
-        assert np.array_equal(nan, np.isnan(r_got))
-        got["w16"] = np.where(nan, ref[0]["w16"], got["w16"])
-        bad = check_adamw_state(f"step0={step0} eps={hp['eps']}", got, ref[0])
-        print(f"late/zero-eps case step0={step0} eps={hp['eps']}: {sum(bad.values())} mismatches, "
-              f"{int(nan.sum())} NaN weights", flush=True)
+            return host_grad_bits(g, "bf16")
+
+        run_lockstep("adamw", dev, 0, grads, hp, tag=f"late step0={step0} eps={hp['eps']}",
+                     step_list=range(step0, step0 + 3))
 
 
 def _run_sgdm(sizes, steps, hp, fmt="bf16", ecc_bits=8, codec="companded", tag="s", inject=None):
-    xs = [host_weights(tag, i, n) for i, n in enumerate(sizes)]
-    dev = [alloc_sgdm_state(n, fmt, ecc_bits) for n in sizes]
-    ref = [fresh_sgdm_state(x, fmt, ecc_bits) for x in xs]
-    for st, x in zip(dev, xs):
-        B.fo_split_weights(torch.from_numpy(x).cuda(), st["w16"], st["ecc"], fmt, ecc_bits)
-    tl = B.SGDMList(dev)
-    total = 0
-    for step in range(1, steps + 1):
-        gbs = []
-        for i, (st, n) in enumerate(zip(dev, sizes)):
-            g = host_grads(tag, i, step, n, "normal_outliers")
-            if inject is not None:
-                g = inject(i, step, g)
-            gb = host_grad_bits(g, fmt)
-            gbs.append(gb)
-            st["grad"].copy_(to_dev(gb, DT[fmt]))
-        B.fo_fused_sgdm_step(tl, B.sgdm_hparams(step=step, wfmt=fmt, ecc_bits=ecc_bits, codec=codec, **hp))
-        for i in range(len(sizes)):
-            ref[i] = O.sgdm_step(ref[i], gbs[i], dict(hp, step=step), fmt, ecc_bits, codec)
-        torch.cuda.synchronize()
-        for i in range(len(sizes)):
-            got = sgdm_state_to_host(dev[i])
-            if inject is not None:
-                nan = np.isnan(O.reconstruct_weights(ref[i]["w16"], ref[i]["ecc"], fmt, ecc_bits))
-                assert np.array_equal(nan, np.isnan(O.reconstruct_weights(got["w16"], got["ecc"], fmt, ecc_bits)))
-                got["w16"] = np.where(nan, ref[i]["w16"], got["w16"])
-            bad = check_sgdm_state(f"sgdm step {step} tensor {i} (n={sizes[i]})", got, ref[i], fmt, ecc_bits)
-            total += sum(bad.values())
-    return total
+    """Lock-step GPU vs oracle over `steps` SGD-M steps on a list of tensors."""
+    dev = _init_states("sgdm", sizes, fmt, ecc_bits, tag)
+
+    def grads(i, step):
+        g = host_grads(tag, i, step, sizes[i], "normal_outliers")
+        if inject is not None:
+            g = inject(i, step, g)
+        return host_grad_bits(g, fmt)
+
+    return run_lockstep("sgdm", dev, steps, grads, hp, fmt, ecc_bits, codec, tag)
 
 
 HP_C4 = dict(lr=0.1, momentum=0.9, weight_decay=1e-4)
@@ -443,16 +406,14 @@ def test_fused_sgdm_nan_inf_grads_propagate(fmt, codec):
                                                 ("fp16", 8, "companded"), ("bf16", 8, "linear")])
 def test_fused_sgdm_matches_oracle(fmt, ecc_bits, codec):
     sizes = [9408, 64, 64, 4096, 36864, 16384, 1000, 2_048_000 // 8, 33, 1]
-    bad = _run_sgdm(sizes, 5, HP_C4, fmt, ecc_bits, codec, tag=f"sgdm_{fmt}{ecc_bits}{codec}")
-    print(f"sgdm {fmt}+{ecc_bits}/{codec}: {bad} mismatching elements", flush=True)
+    _run_sgdm(sizes, 5, HP_C4, fmt, ecc_bits, codec, tag=f"sgdm_{fmt}{ecc_bits}{codec}")
 
 
 @pytest.mark.parametrize("nesterov,dampening", [(True, 0.0), (False, 0.5), (False, 1.0)])
 def test_fused_sgd_nesterov_and_dampening_match_oracle(nesterov, dampening):
     sizes = [9408, 4096, 2049, 33, 1, 100_000]
     hp = dict(HP_C4, nesterov=nesterov, dampening=dampening)
-    bad = _run_sgdm(sizes, 4, hp, tag=f"sgd_n{int(nesterov)}_d{dampening}")
-    print(f"sgd nesterov={nesterov} dampening={dampening}: {bad} mismatching elements", flush=True)
+    _run_sgdm(sizes, 4, hp, tag=f"sgd_n{int(nesterov)}_d{dampening}")
 
 
 @pytest.mark.parametrize("fmt,ecc_bits,codec", [("bf16", 8, "companded"), ("fp16", 8, "companded"),
@@ -460,18 +421,19 @@ def test_fused_sgd_nesterov_and_dampening_match_oracle(nesterov, dampening):
 def test_fused_adam_l2_decay_matches_oracle(fmt, ecc_bits, codec):
     sizes = [300_000, 4097, 33, 1]
     hp = dict(HP_C1, weight_decay=0.05, l2_decay=True)
-    bad = _run_adamw(sizes, 4, hp, fmt, ecc_bits, codec, tag=f"adam_l2_{fmt}{ecc_bits}{codec}")
-    print(f"Adam (L2) {fmt}+{ecc_bits}/{codec}: {bad} mismatching elements", flush=True)
+    _run_adamw(sizes, 4, hp, fmt, ecc_bits, codec, tag=f"adam_l2_{fmt}{ecc_bits}{codec}")
 
 
 @pytest.mark.parametrize("name,hp", [
     ("momentum_0", dict(lr=0.1, momentum=0.0, weight_decay=1e-4)),
+    ("momentum_0_dampening", dict(lr=0.1, momentum=0.0, weight_decay=1e-4, dampening=0.5)),
     ("lr_0", dict(lr=0.0, momentum=0.9, weight_decay=1e-4)),
     ("no_decay", dict(lr=0.1, momentum=0.99, weight_decay=0.0)),
 ])
 def test_fused_sgd_degenerate_hyperparameters(name, hp):
-    bad = _run_sgdm([20000, 33], 3, hp, tag=f"sgd_hp_{name}")
-    print(f"sgd degenerate hp {name}: {bad} mismatching elements", flush=True)
+    """Momentum 0 takes the first-step rule at every step (torch keeps no
+    buffer then, so dampening has no effect)."""
+    _run_sgdm([20000, 33], 3, hp, tag=f"sgd_hp_{name}")
 
 
 def test_gradient_release_chunks_equal_whole_tensor():

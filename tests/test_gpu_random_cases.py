@@ -1,19 +1,18 @@
 """Seeded random cases through the C ABI against the oracle: random tensor
 lists (sizes 0 to 200K, ragged tails, empty tensors), every weight format /
 ECC / codec combination, AdamW, Adam (L2) and SGD-M (plain, Nesterov,
-dampening) with hyperparameters drawn across their ranges, 2-3 free-running
-steps each.  Every case must be identical to the oracle on >= 99.99% of
-elements and within one LSB / one ECC step on the rest."""
+dampening) with hyperparameters drawn across their ranges, 2-3 lock-step
+steps each.  Every array of every case must be bitwise equal to the
+oracle's."""
 
 import numpy as np
 import pytest
 import torch
 
 import oracle as O
-from oracle.optim import fresh_adamw_state, fresh_sgdm_state
 from precision_optimizer_state_amd import binding as B
 from precision_optimizer_state_amd.state import alloc_adamw_state, alloc_sgdm_state
-from tests.gpu_helpers import adamw_state_to_host, check_adamw_state, check_sgdm_state, sgdm_state_to_host, to_dev
+from tests.gpu_helpers import check_weights, run_lockstep, to_host
 from workloads import host_grad_bits, host_grads, host_weights
 
 pytestmark = pytest.mark.gpu
@@ -53,37 +52,17 @@ def test_random_case_matches_oracle(i):
     tag = f"rand{i}"
     print(f"case {i}: {kind} {fmt}+{ecc} {codec} sizes={sizes} steps={steps} hp={hp}", flush=True)
     adam = kind != "sgd"
-    xs = [host_weights(tag, j, n) for j, n in enumerate(sizes)]
-    dev = [(alloc_adamw_state if adam else alloc_sgdm_state)(n, fmt, ecc) for n in sizes]
-    ref = [(fresh_adamw_state if adam else fresh_sgdm_state)(x, fmt, ecc) for x in xs]
-    for st, x in zip(dev, xs):
-        B.fo_split_weights(torch.from_numpy(x).cuda(), st["w16"], st["ecc"], fmt, ecc)
-    tl = B.AdamWList(dev) if adam else B.SGDMList(dev)
-    for step in range(1, steps + 1):
-        gbs = []
-        for j, (st, n) in enumerate(zip(dev, sizes)):
-            gb = host_grad_bits(host_grads(tag, j, step, n, grad_kind), fmt)
-            gbs.append(gb)
-            st["grad"].copy_(to_dev(gb, DT[fmt]))
-        if adam:
-            B.fo_fused_adamw_step(tl, B.adamw_hparams(step=step, wfmt=fmt, ecc_bits=ecc, codec=codec, **hp))
-        else:
-            B.fo_fused_sgdm_step(tl, B.sgdm_hparams(step=step, wfmt=fmt, ecc_bits=ecc, codec=codec, **hp))
-        for j in range(len(sizes)):
-            if sizes[j] == 0:
-                continue
-            if adam:
-                ref[j] = O.adamw_step(ref[j], gbs[j], dict(hp, step=step), fmt, ecc, codec)
-            else:
-                ref[j] = O.sgdm_step(ref[j], gbs[j], dict(hp, step=step), fmt, ecc, codec)
-    torch.cuda.synchronize()
-    bad = 0
-    for j in range(len(sizes)):
-        if sizes[j] == 0:
-            continue
-        if adam:
-            b = check_adamw_state(f"case {i} tensor {j}", adamw_state_to_host(dev[j]), ref[j], fmt, ecc)
-        else:
-            b = check_sgdm_state(f"case {i} tensor {j}", sgdm_state_to_host(dev[j]), ref[j], fmt, ecc)
-        bad += sum(b.values())
-    print(f"case {i}: {bad} mismatching elements", flush=True)
+    dev = []
+    for j, n in enumerate(sizes):
+        st = (alloc_adamw_state if adam else alloc_sgdm_state)(n, fmt, ecc)
+        if n:
+            x = host_weights(tag, j, n)
+            B.fo_split_weights(torch.from_numpy(x).cuda(), st["w16"], st["ecc"], fmt, ecc)
+            w_ref, e_ref = O.split_weights(x, fmt, ecc)
+            torch.cuda.synchronize()
+            check_weights(f"case {i} split {j}", to_host(st["w16"]), to_host(st["ecc"]), w_ref, e_ref, fmt, ecc)
+        dev.append(st)
+    checks = run_lockstep("adamw" if adam else "sgdm", dev, steps,
+                          lambda j, step: host_grad_bits(host_grads(tag, j, step, sizes[j], grad_kind), fmt),
+                          hp, fmt, ecc, codec, f"case {i}")
+    print(f"case {i}: {checks} lock-step checks, all bitwise equal", flush=True)

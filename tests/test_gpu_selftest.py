@@ -3,8 +3,10 @@ table-driven momentum encode, through the C ABI.
 
 fo_selftest compares, on the device, the Newton-refined hardware reciprocal
 and the neighbour-corrected hardware square root with the IEEE operations,
-and the hardware float-to-u8 conversion with round-half-even + clamp, over
-every f32 pattern of the ranges the kernels use them on.
+and the hardware float-to-u8 conversion with round-half-even + clamp (NaN to
+0), over every f32 pattern of the ranges the kernels use them on; and the
+residual-corrected division with IEEE division on billions of seeded pairs
+from the ranges the kernels admit.
 """
 
 from fractions import Fraction
@@ -32,13 +34,30 @@ def test_corrected_sqrt_exact_from_2_minus_96_to_inf():
 
 
 def test_cvt_pk_u8_is_round_half_even_and_saturating_everywhere():
+    # every f32 pattern, NaN included (NaN must give 0: the codes of NaN states)
     assert B.fo_selftest(2, 0, 1 << 32) == 0
 
 
+@pytest.mark.parametrize("seed", [1, 2])
+def test_corrected_division_equals_ieee_division(seed):
+    # divisors over the whole range of the refined reciprocal, dividends over
+    # the range the fast AdamW step admits (and zero), quotients normal
+    assert B.fo_selftest(3, seed, 1 << 32) == 0
+
+
+def test_corrected_division_by_block_scales_equals_ieee_division():
+    # fp16 divisors (block scales) with |dividend| <= divisor: the encodes
+    assert B.fo_selftest(4, 7, 1 << 32) == 0
+
+
 def test_selftest_detects_the_range_the_fast_paths_avoid():
-    # the fallbacks exist for a reason: the fast forms are wrong on denormals
+    # the fallbacks exist for a reason: the fast forms are wrong on denormals,
+    # and the corrected division is wrong for some subnormal quotients (two
+    # of the pairs of seed 1, found again by the CPU reproduction of the
+    # generator), which the AdamW step's gradient range keeps out
     assert B.fo_selftest(0, 1, 0x00800000 - 1) > 0
     assert B.fo_selftest(1, 1, 0x0F800000 - 1) > 0
+    assert B.fo_selftest(5, 1, 1 << 32) > 0
 
 
 def test_momentum_codes_exact_around_every_threshold():
