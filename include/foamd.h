@@ -205,6 +205,25 @@ typedef struct fo_adamw_hparams {
 int fo_fused_adamw_step(const fo_adamw_tensor* list, int32_t count,
                         const fo_adamw_hparams* hp, void* stream);
 
+/*
+ * fo_fused_adamw_step_noalloc -- for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): the same step as fo_fused_adamw_step, bitwise, with no
+ * hipMalloc, hipFree, pinned-host allocation, event or synchronisation.
+ *   The codec tables and the call's launch table (descriptors and tile-bucket
+ *   index) live in one fixed device array per GPU (438 KiB, held until the
+ *   process ends), written on `stream` at every call; the first call on a
+ *   device also builds the codec tables there.
+ *   Limit: at most 2048 tensors per call (count > 2048 -> FO_EINVAL); sizes
+ *   are otherwise unlimited.
+ *   Calls on one GPU share that array and must not overlap: order them on
+ *   one stream (or order the streams); overlapping calls race.  The first
+ *   call on a device must be ordered before any call on another stream.
+ * Errors: as fo_fused_adamw_step, plus FO_EINVAL for lists over the limit.
+ */
+int fo_fused_adamw_step_noalloc(const fo_adamw_tensor* list, int32_t count,
+                                const fo_adamw_hparams* hp, void* stream);
+
 /* One tensor of a fused SGD-with-momentum step. */
 typedef struct fo_sgdm_tensor {
   void*        w16;

@@ -22,8 +22,8 @@ FO_MOMENTUM, FO_VARIANCE = 0, 1
 
 EXPORTS = (
     "fo_split_weights", "fo_reconstruct_weights", "fo_companded_quantize", "fo_dequantize",
-    "fo_fused_adamw_step", "fo_fused_sgdm_step", "fo_stream_probe", "fo_selftest", "fo_last_error",
-    "fo_abi_version",
+    "fo_fused_adamw_step", "fo_fused_adamw_step_noalloc", "fo_fused_sgdm_step", "fo_stream_probe", "fo_selftest",
+    "fo_last_error", "fo_abi_version",
 )
 
 WFMT = {"bf16": FO_BF16, "fp16": FO_FP16}
@@ -78,6 +78,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fo_companded_quantize.argtypes = [P, c_int64, c_int, c_int, P, P, P]
     lib.fo_dequantize.argtypes = [P, P, c_int64, c_int, c_int, P, P]
     lib.fo_fused_adamw_step.argtypes = [ctypes.POINTER(AdamWTensor), c_int32, ctypes.POINTER(AdamWHParams), P]
+    lib.fo_fused_adamw_step_noalloc.argtypes = [ctypes.POINTER(AdamWTensor), c_int32, ctypes.POINTER(AdamWHParams), P]
     lib.fo_fused_sgdm_step.argtypes = [ctypes.POINTER(SGDMTensor), c_int32, ctypes.POINTER(SGDMHParams), P]
     lib.fo_stream_probe.argtypes = [ctypes.POINTER(AdamWTensor), c_int32, c_int32, c_int32, c_uint32, P]
     lib.fo_selftest.argtypes = [c_int, c_uint32, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64), P]
@@ -218,6 +219,17 @@ def fo_fused_adamw_step(tlist, hp, stream=None) -> None:
     if not isinstance(hp, AdamWHParams):
         hp = adamw_hparams(**hp)
     _check(load().fo_fused_adamw_step(tlist.array, len(tlist), ctypes.byref(hp), _stream(stream)))
+
+
+def fo_fused_adamw_step_noalloc(tlist, hp, stream=None) -> None:
+    """fo_fused_adamw_step without any device allocation (the library's fixed
+    per-GPU array holds the codec and launch tables; at most 2048 tensors;
+    calls on one GPU must not overlap)."""
+    if not isinstance(tlist, AdamWList):
+        tlist = AdamWList(tlist)
+    if not isinstance(hp, AdamWHParams):
+        hp = adamw_hparams(**hp)
+    _check(load().fo_fused_adamw_step_noalloc(tlist.array, len(tlist), ctypes.byref(hp), _stream(stream)))
 
 
 def fo_fused_sgdm_step(tlist, hp, stream=None) -> None:

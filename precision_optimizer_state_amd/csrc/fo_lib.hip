@@ -166,13 +166,14 @@ TableEntry* find_entry(int dev, const std::vector<uint8_t>& key) {
 
 struct Range { uintptr_t lo, hi; };
 
-int check_alias(std::vector<Range>& r) {
-  std::sort(r.begin(), r.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
-  for (size_t i = 1; i < r.size(); ++i)
+int check_alias(Range* r, size_t n) {
+  std::sort(r, r + n, [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < n; ++i)
     if (r[i].lo < r[i - 1].hi) return fail(FO_EALIAS, "arrays of the tensor list overlap (%p .. %p)",
                                             (void*)r[i - 1].lo, (void*)r[i].lo);
   return FO_OK;
 }
+int check_alias(std::vector<Range>& r) { return check_alias(r.data(), r.size()); }
 
 // Build (or fetch) the device table for `descs` (already validated, n > 0 only).
 // On success *out stays the caller's while it holds g_tab_mu.
@@ -244,44 +245,53 @@ struct ArraySpec { const void* p; size_t elem_bytes; bool per_block; const char*
 // keeps every byte-range computation below within int64 / uintptr_t.
 constexpr int64_t kMaxElems = int64_t(1) << 56;
 
-int build_descs(int ntens, const std::vector<std::vector<ArraySpec>>& arrays, const std::vector<int64_t>& ns,
-                std::vector<TensorDesc>* descs, std::vector<int32_t>* buckets, int64_t* total_tiles) {
-  std::vector<Range> ranges;
-  std::vector<TensorDesc> body;
-  descs->clear();
+constexpr int kArraysPerTensor = 7;          // w16, ecc, grad, codes 1, scales 1, codes 2, scales 2
+constexpr int kMaxBucketEntries = 65536 + 2;  // the index has (tiles >> shift) + 2 <= 65537 entries
+
+// Launch table of a tensor list, built on caller storage: arrays[i * 7 + a]
+// (a < na) and ns[i] describe tensor i < ntens; body holds ntens descriptors,
+// ranges ntens * na, descs ntens + 1 (the non-empty tensors and the
+// sentinel: *ndesc of them), buckets kMaxBucketEntries (*nbuckets used).
+int build_descs_into(int ntens, int na, const ArraySpec* arrays, const int64_t* ns, TensorDesc* body, Range* ranges,
+                     TensorDesc* descs, int* ndesc, int32_t* buckets, int* nbuckets, int64_t* total_tiles) {
+  int nbody = 0;
+  size_t nranges = 0;
   int64_t tiles = 0;
   for (int i = 0; i < ntens; ++i) {
     const int64_t n = ns[i];
     if (n < 0 || n > kMaxElems) return fail(FO_EINVAL, "tensor %d: n out of range (%lld)", i, (long long)n);
     if (n == 0) continue;
     const int64_t nb = (n + 31) / 32;
-    uint64_t ptr[7] = {0, 0, 0, 0, 0, 0, 0};
-    for (size_t a = 0; a < arrays[i].size(); ++a) {
-      const ArraySpec& s = arrays[i][a];
+    uint64_t ptr[kArraysPerTensor] = {0, 0, 0, 0, 0, 0, 0};
+    for (int a = 0; a < na; ++a) {
+      const ArraySpec& s = arrays[(size_t)i * kArraysPerTensor + a];
       if (!s.p) return fail(FO_EINVAL, "tensor %d: %s is NULL", i, s.name);
       if (!aligned(s.p, s.per_block ? 2 : 16)) return fail(FO_EINVAL, "tensor %d: %s is not %d-byte aligned", i, s.name,
                                                             s.per_block ? 2 : 16);
       const uintptr_t lo = reinterpret_cast<uintptr_t>(s.p);
-      ranges.push_back({lo, lo + (uintptr_t)((s.per_block ? nb : n) * (int64_t)s.elem_bytes)});
+      ranges[nranges++] = {lo, lo + (uintptr_t)((s.per_block ? nb : n) * (int64_t)s.elem_bytes)};
       ptr[a] = (uint64_t)lo;
     }
     TensorDesc d;
     d.w16 = ptr[0]; d.ecc = ptr[1]; d.grad = ptr[2]; d.q1 = ptr[3]; d.s1 = ptr[4]; d.q2 = ptr[5]; d.s2 = ptr[6];
     d.n = n;
-    body.push_back(d);
+    d.tile_begin = 0;
+    body[nbody++] = d;
   }
-  int rc = check_alias(ranges);
+  int rc = check_alias(ranges, nranges);
   if (rc) return rc;
   // Tile order: tensors whose last tile is partial come first, so their
   // masked tiles run in a launch's first wave round, where the other waves
   // hide their extra latency, instead of stretching its tail.  Tensors are
   // independent, so the order changes no result.
+  int nd = 0;
   for (int pass = 0; pass < 2; ++pass) {
-    for (TensorDesc d : body) {
+    for (int i = 0; i < nbody; ++i) {
+      TensorDesc d = body[i];
       if ((d.n % TILE != 0) != (pass == 0)) continue;
       d.tile_begin = tiles;
       tiles += (d.n + TILE - 1) / TILE;
-      descs->push_back(d);
+      descs[nd++] = d;
     }
   }
   // Tile-bucket index: bucket b (tiles [b << shift, (b + 1) << shift)) records
@@ -289,24 +299,40 @@ int build_descs(int ntens, const std::vector<std::vector<ArraySpec>>& arrays, co
   // adjacent entries.  At most 65536 buckets; the shift rides in the sentinel.
   int shift = TILE_BUCKET_SHIFT_MIN;
   while ((tiles >> shift) > 65535) ++shift;
-  buckets->clear();
+  int nbk_entries = 0;
   if (tiles > 0) {
     const int64_t nbk = (tiles >> shift) + 1;
-    buckets->resize((size_t)nbk + 1);
+    nbk_entries = (int)nbk + 1;
     int t = 0;
-    const int ndesc = (int)descs->size();
     for (int64_t b = 0; b <= nbk; ++b) {
       const int64_t first = std::min<int64_t>(b << shift, tiles - 1);
-      while (t + 1 < ndesc && (*descs)[t + 1].tile_begin <= first) ++t;
-      (*buckets)[(size_t)b] = t;
+      while (t + 1 < nd && descs[t + 1].tile_begin <= first) ++t;
+      buckets[b] = t;
     }
   }
   TensorDesc sentinel;
   std::memset(&sentinel, 0, sizeof(sentinel));
   sentinel.tile_begin = tiles;
   sentinel.n = shift;
-  descs->push_back(sentinel);
+  descs[nd++] = sentinel;
+  *ndesc = nd;
+  *nbuckets = nbk_entries;
   *total_tiles = tiles;
+  return FO_OK;
+}
+
+int build_descs(int ntens, int na, const std::vector<ArraySpec>& arrays, const std::vector<int64_t>& ns,
+                std::vector<TensorDesc>* descs, std::vector<int32_t>* buckets, int64_t* total_tiles) {
+  std::vector<TensorDesc> body((size_t)ntens);
+  std::vector<Range> ranges((size_t)ntens * na);
+  descs->resize((size_t)ntens + 1);
+  buckets->resize(kMaxBucketEntries);
+  int nd = 0, nbk = 0;
+  const int rc = build_descs_into(ntens, na, arrays.data(), ns.data(), body.data(), ranges.data(), descs->data(), &nd,
+                                  buckets->data(), &nbk, total_tiles);
+  if (rc) return rc;
+  descs->resize((size_t)nd);
+  buckets->resize((size_t)nbk);
   return FO_OK;
 }
 
@@ -485,23 +511,37 @@ int fo_dequantize(const void* codes, const uint16_t* scales, int64_t n, int kind
 // where no device is usable.  `fill` describes each tensor's arrays.  The
 // caller holds g_tab_mu; the entry stays the caller's until its use is
 // recorded.
-using FillArrays = std::function<void(std::vector<std::vector<ArraySpec>>&, std::vector<int64_t>&)>;
-static int list_table(const std::vector<uint8_t>& key, int32_t count, const FillArrays& fill, hipStream_t stream,
-                      TableEntry** entry) {
+// fill(arrays, ns): arrays[i * kArraysPerTensor + a] for the `na` arrays of tensor i
+using FillArrays = std::function<void(ArraySpec*, int64_t*)>;
+static int list_table(const std::vector<uint8_t>& key, int32_t count, int na, const FillArrays& fill,
+                      hipStream_t stream, TableEntry** entry) {
   int dev = -1;
   const int dev_rc = current_device(&dev);
   if (dev_rc == FO_OK && (*entry = find_entry(dev, key))) return FO_OK;
-  std::vector<std::vector<ArraySpec>> arrays(count);
+  std::vector<ArraySpec> arrays((size_t)count * kArraysPerTensor);
   std::vector<int64_t> ns(count);
-  fill(arrays, ns);
+  fill(arrays.data(), ns.data());
   std::vector<TensorDesc> descs;
   std::vector<int32_t> buckets;
   int64_t tiles = 0;
-  const int rc = build_descs(count, arrays, ns, &descs, &buckets, &tiles);
+  const int rc = build_descs(count, na, arrays, ns, &descs, &buckets, &tiles);
   if (rc) return rc;
   if (tiles == 0) { *entry = nullptr; g_err.clear(); return FO_OK; }   // only empty tensors: nothing to do
   if (dev_rc) return dev_rc;                  // its message is still the current one
   return get_table(dev, key, descs, buckets, tiles, stream, entry);
+}
+
+static void fill_adamw_arrays(const fo_adamw_tensor* list, int32_t count, int ecc_bits, ArraySpec* arrays,
+                              int64_t* ns) {
+  const size_t eb = (size_t)ecc_bits / 8;
+  for (int i = 0; i < count; ++i) {
+    const fo_adamw_tensor& t = list[i];
+    ns[i] = t.n;
+    ArraySpec* a = arrays + (size_t)i * kArraysPerTensor;
+    a[0] = {t.w16, 2, false, "w16"}; a[1] = {t.ecc, eb, false, "ecc"}; a[2] = {t.grad, 2, false, "grad"};
+    a[3] = {t.m_q, 1, false, "m_q"}; a[4] = {t.m_s, 2, true, "m_s"}; a[5] = {t.v_q, 1, false, "v_q"};
+    a[6] = {t.v_s, 2, true, "v_s"};
+  }
 }
 
 static int adamw_like_table(const fo_adamw_tensor* list, int32_t count, int wfmt, int ecc_bits, uint8_t tag,
@@ -511,20 +551,14 @@ static int adamw_like_table(const fo_adamw_tensor* list, int32_t count, int wfmt
   std::memcpy(&key[1], &wfmt, 4);
   std::memcpy(&key[5], &ecc_bits, 4);
   if (count) std::memcpy(&key[9], list, (size_t)count * sizeof(fo_adamw_tensor));
-  const size_t eb = (size_t)ecc_bits / 8;
-  return list_table(key, count, [&](std::vector<std::vector<ArraySpec>>& arrays, std::vector<int64_t>& ns) {
-    for (int i = 0; i < count; ++i) {
-      const fo_adamw_tensor& t = list[i];
-      ns[i] = t.n;
-      arrays[i] = {{t.w16, 2, false, "w16"}, {t.ecc, eb, false, "ecc"}, {t.grad, 2, false, "grad"},
-                   {t.m_q, 1, false, "m_q"}, {t.m_s, 2, true, "m_s"}, {t.v_q, 1, false, "v_q"},
-                   {t.v_s, 2, true, "v_s"}};
-    }
+  return list_table(key, count, 7, [&](ArraySpec* arrays, int64_t* ns) {
+    fill_adamw_arrays(list, count, ecc_bits, arrays, ns);
   }, stream, entry);
 }
 
-int fo_fused_adamw_step(const fo_adamw_tensor* list, int32_t count, const fo_adamw_hparams* hp, void* stream) {
-  g_err.clear();
+// Argument checks, step constants, kernel choice and launches of the fused
+// AdamW step, shared by fo_fused_adamw_step and fo_fused_adamw_step_noalloc.
+static int adamw_check_args(const fo_adamw_tensor* list, int32_t count, const fo_adamw_hparams* hp) {
   if (!hp) return fail(FO_EINVAL, "hp is NULL");
   if (count < 0) return fail(FO_EINVAL, "count < 0");
   if (count > 0 && !list) return fail(FO_EINVAL, "list is NULL");
@@ -536,14 +570,11 @@ int fo_fused_adamw_step(const fo_adamw_tensor* list, int32_t count, const fo_ada
     return fail(FO_EINVAL, "betas must lie in [0, 1)");
   if (!(hp->lr >= 0.0) || !(hp->eps >= 0.0) || !(hp->weight_decay >= 0.0))
     return fail(FO_EINVAL, "lr, eps and weight_decay must be >= 0");
-  if (count == 0) return FO_OK;
-  hipStream_t s = as_stream(stream);
-  std::lock_guard<std::mutex> lk(g_tab_mu);   // table slot stays ours until the use is recorded
-  TableEntry* e = nullptr;
-  int rc = adamw_like_table(list, count, hp->wfmt, hp->ecc_bits, 'A', s, &e);
-  if (rc) return rc;
-  if (!e || e->total_tiles == 0) return FO_OK;
-  // per-step float32 constants: double arithmetic, one rounding each
+  return FO_OK;
+}
+
+// per-step float32 constants: double arithmetic, one rounding each
+static AdamWConsts adamw_consts(const fo_adamw_hparams* hp) {
   const double t = (double)hp->step;
   AdamWConsts c;
   c.b1 = (float)hp->beta1;
@@ -557,21 +588,122 @@ int fo_fused_adamw_step(const fo_adamw_tensor* list, int32_t count, const fo_ada
   c.wd = hp->l2_decay ? (float)hp->weight_decay : 0.0f;
   if (hp->l2_decay) c.decay = 1.0f;                 // Adam: no decoupled decay
   adamw_fast_range(&c);
+  return c;
+}
+
+static int adamw_launch(const fo_adamw_hparams* hp, const TensorDesc* tab, int count, int64_t total_tiles,
+                        const CodecTables* tables, hipStream_t s) {
+  const AdamWConsts c = adamw_consts(hp);
   void (*kern)(const TensorDesc*, int, int64_t, int64_t, const CodecTables*, AdamWConsts) = nullptr;
   if (hp->l2_decay) FO_SELECT3(k_fused_adamw_l2, hp->wfmt, hp->ecc_bits, hp->codec, kern);
   else FO_SELECT3(k_fused_adamw_dec, hp->wfmt, hp->ecc_bits, hp->codec, kern);
-  int dev, grid;
   const int waves = adamw_waves(hp->ecc_bits);
+  int grid, rc;
+  for (int64_t t0 = 0; t0 < total_tiles; t0 += kLaunchTiles) {
+    const int64_t t1 = std::min<int64_t>(t0 + kLaunchTiles, total_tiles);
+    if ((rc = tile_grid(t1 - t0, waves, &grid))) return rc;
+    hipLaunchKernelGGL(kern, grid, WAVE * waves, 0, s, tab, count, t0, t1, tables, c);
+  }
+  return launch_check("k_fused_adamw launch");
+}
+
+int fo_fused_adamw_step(const fo_adamw_tensor* list, int32_t count, const fo_adamw_hparams* hp, void* stream) {
+  g_err.clear();
+  int rc = adamw_check_args(list, count, hp);
+  if (rc || count == 0) return rc;
+  hipStream_t s = as_stream(stream);
+  std::lock_guard<std::mutex> lk(g_tab_mu);   // table slot stays ours until the use is recorded
+  TableEntry* e = nullptr;
+  rc = adamw_like_table(list, count, hp->wfmt, hp->ecc_bits, 'A', s, &e);
+  if (rc) return rc;
+  if (!e || e->total_tiles == 0) return FO_OK;
+  int dev;
   const CodecTables* tb = nullptr;
   if ((rc = current_device(&dev)) || (rc = device_tables(dev, s, &tb))) return rc;
-  for (int64_t t0 = 0; t0 < e->total_tiles; t0 += kLaunchTiles) {
-    const int64_t t1 = std::min<int64_t>(t0 + kLaunchTiles, e->total_tiles);
-    if ((rc = tile_grid(t1 - t0, waves, &grid))) return rc;
-    hipLaunchKernelGGL(kern, grid, WAVE * waves, 0, s, (const TensorDesc*)e->dptr, e->count, t0, t1, tb, c);
-  }
-  rc = launch_check("k_fused_adamw launch");
-  if (rc) return rc;
+  if ((rc = adamw_launch(hp, (const TensorDesc*)e->dptr, e->count, e->total_tiles, tb, s))) return rc;
   return record_use(e, s);
+}
+
+// ---------------------------------------------------------------------------
+// allocation-free AdamW step
+// ---------------------------------------------------------------------------
+// The library's device memory of this entry point is one file-scope device
+// array per GPU, held until the process ends: the codec tables, then the
+// launch table (descriptors, sentinel, tile-bucket index) of the current
+// call.  Host staging is static as well, so a call allocates nothing.  The
+// array's device address comes from hipGetSymbolAddress, taken once per
+// device with that device current; host code uses only that address.
+static constexpr int kNoAllocMaxTensors = 2048;
+constexpr size_t kScratchDescOff = sizeof(CodecTables);                 // tables first
+constexpr size_t kScratchTableBytes = (size_t)(kNoAllocMaxTensors + 1) * sizeof(TensorDesc) +
+                                      (size_t)kMaxBucketEntries * sizeof(int32_t);
+constexpr size_t kScratchBytes = kScratchDescOff + kScratchTableBytes;   // 438 KiB
+static_assert(kScratchDescOff % 16 == 0, "descriptor alignment");
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kNoAllocMaxDevices = 64;
+struct NoAllocDevice { uint8_t* ptr = nullptr; bool tables_built = false; };
+static std::mutex g_na_mu;
+static NoAllocDevice g_na_dev[kNoAllocMaxDevices];
+static ArraySpec g_na_arrays[(size_t)kNoAllocMaxTensors * kArraysPerTensor];
+static int64_t g_na_ns[kNoAllocMaxTensors];
+static TensorDesc g_na_body[kNoAllocMaxTensors];
+static Range g_na_ranges[(size_t)kNoAllocMaxTensors * kArraysPerTensor];
+static TensorDesc g_na_descs[kNoAllocMaxTensors + 1];
+static int32_t g_na_buckets[kMaxBucketEntries];
+alignas(16) static uint8_t g_na_stage[kScratchTableBytes];
+
+// The device's scratch address (hipGetSymbolAddress on the first call on the
+// device) and its codec tables (built into it by k_init_tables on the stream
+// of that first call; the caller orders later calls on other streams after it).
+static int noalloc_scratch(int dev, hipStream_t s, uint8_t** out) {
+  if (dev < 0 || dev >= kNoAllocMaxDevices) return fail(FO_EINVAL, "device %d beyond the %d the library serves", dev,
+                                                        kNoAllocMaxDevices);
+  NoAllocDevice& d = g_na_dev[dev];
+  if (!d.ptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    d.ptr = static_cast<uint8_t*>(p);
+  }
+  if (!d.tables_built) {
+    hipLaunchKernelGGL(k_init_tables, 1, WG, 0, s, reinterpret_cast<CodecTables*>(d.ptr));
+    const int rc = launch_check("k_init_tables launch");
+    if (rc) return rc;
+    d.tables_built = true;
+  }
+  *out = d.ptr;
+  return FO_OK;
+}
+
+int fo_fused_adamw_step_noalloc(const fo_adamw_tensor* list, int32_t count, const fo_adamw_hparams* hp,
+                                void* stream) {
+  g_err.clear();
+  int rc = adamw_check_args(list, count, hp);
+  if (rc || count == 0) return rc;
+  if (count > kNoAllocMaxTensors)
+    return fail(FO_EINVAL, "the allocation-free step takes at most %d tensors (got %d)", kNoAllocMaxTensors, count);
+  hipStream_t s = as_stream(stream);
+  std::lock_guard<std::mutex> lk(g_na_mu);
+  fill_adamw_arrays(list, count, hp->ecc_bits, g_na_arrays, g_na_ns);
+  int nd = 0, nbk = 0;
+  int64_t tiles = 0;
+  rc = build_descs_into(count, 7, g_na_arrays, g_na_ns, g_na_body, g_na_ranges, g_na_descs, &nd, g_na_buckets, &nbk,
+                        &tiles);
+  if (rc) return rc;
+  if (tiles == 0) return FO_OK;
+  int dev;
+  uint8_t* ptr = nullptr;
+  if ((rc = current_device(&dev)) || (rc = noalloc_scratch(dev, s, &ptr))) return rc;
+  // descriptors, then the bucket index right after them (where the kernels look)
+  const size_t desc_bytes = (size_t)nd * sizeof(TensorDesc);
+  const size_t bytes = desc_bytes + (size_t)nbk * sizeof(int32_t);
+  std::memcpy(g_na_stage, g_na_descs, desc_bytes);
+  std::memcpy(g_na_stage + desc_bytes, g_na_buckets, (size_t)nbk * sizeof(int32_t));
+  const hipError_t he = hipMemcpyAsync(ptr + kScratchDescOff, g_na_stage, bytes, hipMemcpyHostToDevice, s);
+  if (he != hipSuccess) return hip_fail(he, "hipMemcpyAsync(launch table)");
+  return adamw_launch(hp, reinterpret_cast<const TensorDesc*>(ptr + kScratchDescOff), nd - 1, tiles,
+                      reinterpret_cast<const CodecTables*>(ptr), s);
 }
 
 int fo_stream_probe(const fo_adamw_tensor* list, int32_t count, int32_t wfmt, int32_t ecc_bits, uint32_t key,
@@ -624,12 +756,13 @@ int fo_fused_sgdm_step(const fo_sgdm_tensor* list, int32_t count, const fo_sgdm_
   TableEntry* e = nullptr;
   std::lock_guard<std::mutex> lk(g_tab_mu);
   const size_t eb = (size_t)hp->ecc_bits / 8;
-  int rc = list_table(key, count, [&](std::vector<std::vector<ArraySpec>>& arrays, std::vector<int64_t>& ns) {
+  int rc = list_table(key, count, 5, [&](ArraySpec* arrays, int64_t* ns) {
     for (int i = 0; i < count; ++i) {
       const fo_sgdm_tensor& t = list[i];
       ns[i] = t.n;
-      arrays[i] = {{t.w16, 2, false, "w16"}, {t.ecc, eb, false, "ecc"}, {t.grad, 2, false, "grad"},
-                   {t.b_q, 1, false, "b_q"}, {t.b_s, 2, true, "b_s"}};
+      ArraySpec* a = arrays + (size_t)i * kArraysPerTensor;
+      a[0] = {t.w16, 2, false, "w16"}; a[1] = {t.ecc, eb, false, "ecc"}; a[2] = {t.grad, 2, false, "grad"};
+      a[3] = {t.b_q, 1, false, "b_q"}; a[4] = {t.b_s, 2, true, "b_s"};
     }
   }, s, &e);
   if (rc) return rc;

@@ -1,0 +1,61 @@
+"""The allocation-free AdamW entry point (fo_fused_adamw_step_noalloc) through
+the C ABI: bitwise equal to fo_fused_adamw_step on a copy of the same state,
+on two calls in a row, the second with a smaller list (the fixed device
+array then holds the first call's larger table beyond the second's); lists
+over the limit are rejected before any device work."""
+
+import pytest
+import torch
+
+from precision_optimizer_state_amd import binding as B
+from precision_optimizer_state_amd.state import alloc_adamw_state
+from workloads import device_grads, device_weights
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ("w16", "ecc", "m_q", "m_s", "v_q", "v_s")
+HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+
+
+def _states(sizes, tag):
+    out = []
+    for i, n in enumerate(sizes):
+        st = alloc_adamw_state(n)
+        B.fo_split_weights(device_weights(tag, i, n), st["w16"], st["ecc"], "bf16", 8)
+        device_grads(tag, i, 1, n, "t3", "bf16", out=st["grad"])
+        out.append(st)
+    return out
+
+
+def _clone(states):
+    return [{k: (v.clone() if v is not None else None) for k, v in st.items()} for st in states]
+
+
+@pytest.mark.parametrize("sizes_a,sizes_b", [
+    # many tensors and ragged tails, then fewer and smaller ones
+    ([(1 << 20) + 77, 33, 0, 4096, 2049, 300_000], [5000, 31]),
+    # more than 2^18 wave tiles (two launches), then one small tensor
+    ([(1 << 29) + 4097], [70_001]),
+])
+def test_noalloc_step_equals_cached_step(sizes_a, sizes_b):
+    for call, sizes in enumerate((sizes_a, sizes_b)):
+        print(f"no-alloc call {call}: sizes {sizes}", flush=True)
+        a = _states(sizes, f"noalloc{call}")
+        b = _clone(a)
+        for step in (1, 2):
+            hp = dict(HP, step=step)
+            B.fo_fused_adamw_step(a, hp)
+            B.fo_fused_adamw_step_noalloc(b, hp)
+        torch.cuda.synchronize()
+        for i, (sa, sb) in enumerate(zip(a, b)):
+            for k in KEYS:
+                assert torch.equal(sa[k].view(torch.uint8), sb[k].view(torch.uint8)), (call, i, k)
+        del a, b
+        torch.cuda.empty_cache()
+
+
+def test_noalloc_rejects_lists_over_the_limit():
+    st = alloc_adamw_state(64)
+    with pytest.raises(B.FoError) as ei:
+        B.fo_fused_adamw_step_noalloc([st] * 2049, dict(HP, step=1))
+    assert ei.value.code == B.FO_EINVAL and "2048" in str(ei.value)
