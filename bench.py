@@ -139,8 +139,10 @@ def make_launch(cfg, states, release_chunks=None):
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle, unchanged, on a bounded sample of the workload
 # ---------------------------------------------------------------------------
-def _oracle_task(args):
-    cfg_name, t_idx, lo, m = args
+def _oracle_worker(cfg_name, tasks, barrier, out):
+    """One worker process: generate the inputs of its segments, wait for every
+    worker to be ready, then run the oracle's step on them and report the
+    compute phase's monotonic clock interval (system-wide on Linux)."""
     import numpy as np
 
     import oracle as O
@@ -148,21 +150,42 @@ def _oracle_task(args):
     from workloads import config, host_grad_bits, host_grads
 
     cfg = config(cfg_name)
-    rng = np.random.default_rng([t_idx, lo])
-    x = (rng.standard_normal(m, dtype=np.float32) * np.float32(0.02)).astype(np.float32)
-    gb = host_grad_bits(host_grads(cfg_name, t_idx, 1, m, cfg.grad_kind), cfg.wfmt)
-    if cfg.optimizer == "adamw":
-        st = fresh_adamw_state(x, cfg.wfmt, cfg.ecc_bits)
-        t0 = time.perf_counter()
-        O.adamw_step(st, gb, dict(cfg.hp, step=1), cfg.wfmt, cfg.ecc_bits, cfg.codec)
-    else:
-        st = fresh_sgdm_state(x, cfg.wfmt, cfg.ecc_bits)
-        t0 = time.perf_counter()
-        O.sgdm_step(st, gb, dict(cfg.hp, step=2), cfg.wfmt, cfg.ecc_bits, cfg.codec)
-    return m, time.perf_counter() - t0
+    inputs = []
+    for t_idx, lo, m in tasks:
+        rng = np.random.default_rng([t_idx, lo])
+        x = (rng.standard_normal(m, dtype=np.float32) * np.float32(0.02)).astype(np.float32)
+        gb = host_grad_bits(host_grads(cfg_name, t_idx, 1, m, cfg.grad_kind), cfg.wfmt)
+        fresh = fresh_adamw_state if cfg.optimizer == "adamw" else fresh_sgdm_state
+        inputs.append((fresh(x, cfg.wfmt, cfg.ecc_bits), gb))
+    barrier.wait()
+    t0 = time.perf_counter()
+    elems = 0
+    for st, gb in inputs:
+        if cfg.optimizer == "adamw":
+            O.adamw_step(st, gb, dict(cfg.hp, step=1), cfg.wfmt, cfg.ecc_bits, cfg.codec)
+        else:
+            O.sgdm_step(st, gb, dict(cfg.hp, step=2), cfg.wfmt, cfg.ecc_bits, cfg.codec)
+        elems += gb.size
+    out.put((elems, t0, time.perf_counter()))
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(cfg, segments=96, seg=1 << 20, log=print):
+    """The oracle, unchanged, on `segments` seeded segments of the workload,
+    in worker processes on this host's cores (at most 16, the host share of
+    one GPU).  value = elements / wall time of the compute phase: from the
+    first worker's start to the last worker's end, all workers released
+    together after generating their inputs."""
     import multiprocessing as mp
 
     import numpy as np
@@ -174,23 +197,64 @@ def cpu_baseline(cfg, segments=96, seg=1 << 20, log=print):
         t = int(rng.choice(len(sizes), p=sizes / sizes.sum()))
         m = int(min(seg, sizes[t]))
         lo = int(rng.integers(0, (sizes[t] - m) // 32 + 1)) * 32
-        tasks.append((cfg.name, t, lo, m))
+        tasks.append((t, lo, m))
     cores = max(1, min(16, len(os.sched_getaffinity(0))))
     ctx = mp.get_context("spawn")
-    t0 = time.perf_counter()
-    with ctx.Pool(cores) as pool:
-        res = pool.map(_oracle_task, tasks, chunksize=1)
-    wall = time.perf_counter() - t0
+    barrier = ctx.Barrier(cores)
+    out = ctx.Queue()
+    procs = [ctx.Process(target=_oracle_worker, args=(cfg.name, tasks[w::cores], barrier, out)) for w in range(cores)]
+    for p in procs:
+        p.start()
+    res = [out.get() for _ in procs]
+    for p in procs:
+        p.join()
     elems = sum(r[0] for r in res)
-    cpu_s = sum(r[1] for r in res)
-    # the step computations of all workers run concurrently: throughput is the
-    # summed element count over the summed compute time, times the worker count
-    value = elems / cpu_s * cores
-    log(f"cpu baseline: {elems} elements, {cpu_s:.1f} s of oracle compute on {cores} workers (wall {wall:.1f}s)")
+    wall = max(r[2] for r in res) - min(r[1] for r in res)
+    value = elems / wall
+    model = _cpu_model()
+    log(f"cpu baseline: {elems} elements in {wall:.2f} s of wall time on {cores} worker processes ({model})")
     return {"value": value, "unit": "params/s", "cores": cores, "kind": "oracle",
             "sample": f"{segments} segments of up to {seg} consecutive elements at seeded 32-aligned offsets "
-                      f"across the parameter list (one optimizer step each, inputs from the same generators); "
-                      f"{cpu_s:.1f} s of oracle compute"}
+                      f"across the parameter list, one optimizer step each; {elems} elements in {wall:.2f} s "
+                      f"wall (compute phase) on {cores} processes, {model}"}
+
+
+# ---------------------------------------------------------------------------
+# HBM ceilings on this device: plain streams next to the fused step
+# ---------------------------------------------------------------------------
+def hbm_ceiling(read_bytes_per_elem, write_bytes_per_elem, steps=10, gib=16, log=print):
+    """Read-only, write-only and copy streams over `gib` GiB buffers in the
+    fused kernels' access style (fo_hbm_probe), timed with HIP events on the
+    launch stream, and the estimate for the fused step's read/write mix if
+    reads and writes shared the time: (R + W) / (R / read + W / write)."""
+    import torch
+
+    from precision_optimizer_state_amd import binding as B
+
+    n = gib << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+    B.fo_hbm_probe(src, None, n, "write", 0x5A5A5A5A)        # defined contents
+    stream = torch.cuda.current_stream()
+    out = {}
+    for mode, moved in (("read", n), ("write", n), ("copy", 2 * n)):
+        for _ in range(2):
+            B.fo_hbm_probe(dst, src, n, mode, 0xFFFFFFFF)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            B.fo_hbm_probe(dst, src, n, mode, 0xFFFFFFFF)
+        b.record(stream)
+        torch.cuda.synchronize()
+        out[f"{mode}_gbs"] = moved * steps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    r, w = read_bytes_per_elem, write_bytes_per_elem
+    out["mix_estimate_gbs"] = (r + w) / (r / out["read_gbs"] + w / out["write_gbs"])
+    out["buffer_gib"] = gib
+    log("hbm ceiling: read {read_gbs:.0f}, write {write_gbs:.0f}, copy {copy_gbs:.0f} GB/s; "
+        "read/write mix estimate {mix_estimate_gbs:.0f} GB/s".format(**out))
+    return out
 
 
 # ---------------------------------------------------------------------------
@@ -296,6 +360,8 @@ def main(argv=None):
     ap.add_argument("--release", action="store_true", help="gradient-release mode: one call per chunk (c5 shapes)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="also time plain read / write / copy HBM streams in this process (fo_hbm_probe)")
     ap.add_argument("--copy-calib", action="store_true", help="also run a plain device copy of 4 GiB (counter calibration)")
     ap.add_argument("--variant", default=None, choices=sorted(VARIANTS),
                     help="optimizer variant: Adam with L2 decay (AdamW lists) or SGD with "
@@ -441,6 +507,17 @@ def main(argv=None):
         "vs_stream_probe": (achieved / probe_gbs) if probe_gbs else None,
         "kernel_src_sha": kernel_source_hash(),
     }
+    if args.ceiling:
+        del states, lists
+        states = lists = None
+        torch.cuda.empty_cache()
+        rb, wb = cfg.read_write_bytes_per_param()
+        ceil = hbm_ceiling(rb, wb, log=log)
+        if probe_gbs:
+            ceil["stream_probe_gbs"] = probe_gbs
+        ceil["fused_vs_mix_estimate"] = achieved / ceil["mix_estimate_gbs"]
+        ceil["fused_vs_copy"] = achieved / ceil["copy_gbs"]
+        line["ceiling"] = ceil
     if not args.no_cpu_baseline:
         del states, lists
         torch.cuda.empty_cache()

@@ -61,7 +61,10 @@
  *     synchronises `stream` once, and a launch-table cache miss that evicts
  *     a slot waits for that slot's last use.  Make one call per tensor list
  *     before capturing a HIP graph; later calls with the same list are
- *     capture-safe (no allocation, no synchronisation, no memset).
+ *     capture-safe (no allocation, no synchronisation, no memset).  A call
+ *     made under capture pins its list's launch table until the process ends,
+ *     so the graph stays valid however many other lists are stepped later;
+ *     once all 1024 slots are pinned, a new list fails with FO_ENOMEM.
  *   - The library keeps, per device, one codec-table buffer and up to 1024
  *     cached launch tables (device + pinned host memory, a few KB each for
  *     ordinary lists), held until the process ends.
@@ -268,6 +271,20 @@ int fo_stream_probe(const fo_adamw_tensor* list, int32_t count, int32_t wfmt,
                     int32_t ecc_bits, uint32_t key, void* stream);
 
 /*
+ * fo_hbm_probe -- measurement only.
+ * Plain HBM streams in the fused kernels' access style (one wave per 8-KiB
+ * chunk, 16-byte nontemporal accesses), to measure the attainable read,
+ * write and copy bandwidth next to the fused step:
+ *   mode 0: read `bytes` of src (dst receives at most one 4-byte word, only
+ *           if the XOR of all words read equals `key`);
+ *   mode 1: write `key` over `bytes` of dst;
+ *   mode 2: copy `bytes` from src to dst.
+ * bytes must be a multiple of 8192; pointers 16-byte aligned device memory.
+ * Errors: FO_EINVAL, FO_EHIP.
+ */
+int fo_hbm_probe(void* dst, const void* src, int64_t bytes, int32_t mode, uint32_t key, void* stream);
+
+/*
  * fo_selftest -- verification of the exact fast arithmetic the fused kernels
  * use on this device.  It counts (synchronously, into *mismatches):
  *   what 0: f32 patterns x in [lo, lo + count) where the Newton-refined
@@ -289,6 +306,10 @@ int fo_stream_probe(const fo_adamw_tensor* list, int32_t count, int32_t wfmt,
  * FO_ENOMEM, FO_EHIP.
  */
 int fo_selftest(int what, uint32_t lo, uint64_t count, uint64_t* mismatches, void* stream);
+
+/* Number of launch-table cache slots pinned by calls made under HIP graph
+ * capture (all devices).  Host-only query; never fails. */
+int fo_cache_pinned(void);
 
 /* Message of the last failing call on this thread ("" if none). */
 const char* fo_last_error(void);

@@ -22,8 +22,8 @@ FO_MOMENTUM, FO_VARIANCE = 0, 1
 
 EXPORTS = (
     "fo_split_weights", "fo_reconstruct_weights", "fo_companded_quantize", "fo_dequantize",
-    "fo_fused_adamw_step", "fo_fused_adamw_step_noalloc", "fo_fused_sgdm_step", "fo_stream_probe", "fo_selftest",
-    "fo_last_error", "fo_abi_version",
+    "fo_fused_adamw_step", "fo_fused_adamw_step_noalloc", "fo_fused_sgdm_step", "fo_stream_probe", "fo_hbm_probe",
+    "fo_selftest", "fo_cache_pinned", "fo_last_error", "fo_abi_version",
 )
 
 WFMT = {"bf16": FO_BF16, "fp16": FO_FP16}
@@ -81,9 +81,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fo_fused_adamw_step_noalloc.argtypes = [ctypes.POINTER(AdamWTensor), c_int32, ctypes.POINTER(AdamWHParams), P]
     lib.fo_fused_sgdm_step.argtypes = [ctypes.POINTER(SGDMTensor), c_int32, ctypes.POINTER(SGDMHParams), P]
     lib.fo_stream_probe.argtypes = [ctypes.POINTER(AdamWTensor), c_int32, c_int32, c_int32, c_uint32, P]
+    lib.fo_hbm_probe.argtypes = [P, P, c_int64, c_int32, c_uint32, P]
     lib.fo_selftest.argtypes = [c_int, c_uint32, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64), P]
     for name in EXPORTS:
         getattr(lib, name).restype = c_int
+    lib.fo_cache_pinned.argtypes = []
     lib.fo_last_error.restype = ctypes.c_char_p
     lib.fo_last_error.argtypes = []
     lib.fo_abi_version.argtypes = []
@@ -245,6 +247,16 @@ def fo_stream_probe(tlist, wfmt="bf16", ecc_bits=8, key=0, stream=None) -> None:
         tlist = AdamWList(tlist)
     _check(load().fo_stream_probe(tlist.array, len(tlist), _fmt(wfmt, WFMT), int(ecc_bits), int(key),
                                   _stream(stream)))
+
+
+HBM_PROBE_MODES = {"read": 0, "write": 1, "copy": 2}
+
+
+def fo_hbm_probe(dst, src, nbytes, mode="copy", key=0, stream=None) -> None:
+    """Measurement only: plain read / write / copy streams of nbytes (a
+    multiple of 8192) in the fused kernels' access style."""
+    _check(load().fo_hbm_probe(_ptr(dst), _ptr(src), int(nbytes), _fmt(mode, HBM_PROBE_MODES), int(key),
+                               _stream(stream)))
 
 
 def fo_selftest(what: int, lo: int, count: int, stream=None) -> int:

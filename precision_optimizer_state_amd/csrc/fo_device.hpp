@@ -71,6 +71,27 @@ __device__ __forceinline__ float widen(uint32_t w, int half) {
 // ---------------------------------------------------------------------------
 // ECC decode: theta' (already widened to f32, exact) + rho -> f32 master
 // ---------------------------------------------------------------------------
+// The same decode straight from the packed words for bf16: one byte permute
+// forms u = (theta' << 16) | (rho's low bits << SH) from the weight word and
+// the ECC word, and (u ^ B) - B with B the rho field's sign bit turns the
+// field from two's complement into the signed addend, giving
+// bits(theta') + (rho << SH) in one XOR-add.  h: the weight's half in
+// `w`; b: rho's byte (ECC8) or half (ECC16) in `e`.
+template <int ECC>
+__device__ __forceinline__ float ecc_decode_bf16_packed(uint32_t w, uint32_t e, int h, int b) {
+  uint32_t sel, bias;
+  if constexpr (ECC == 8) {
+    sel = ((uint32_t)(5 + 2 * h) << 24) | ((uint32_t)(4 + 2 * h) << 16) | ((uint32_t)b << 8) | 0x0Cu;
+    bias = 0x8000u;
+  } else {
+    sel = ((uint32_t)(5 + 2 * h) << 24) | ((uint32_t)(4 + 2 * h) << 16) | ((uint32_t)(2 * b + 1) << 8) |
+          (uint32_t)(2 * b);
+    bias = 0x8000u;
+  }
+  const uint32_t u = __builtin_amdgcn_perm(w, e, sel);
+  return u2f((u ^ bias) - bias);
+}
+
 template <int WFMT, int ECC>
 __device__ __forceinline__ float ecc_decode(float t, int32_t rho) {
   if constexpr (WFMT == BF16) {

@@ -167,11 +167,18 @@ __device__ __forceinline__ float bcast_j(float x, int j) {   // j is a compile-t
 // ---------------------------------------------------------------------------
 enum { MOMENTUM_STATE = 0, VARIANCE_STATE = 1 };
 
-// decode multiplier of a block with scale s (see the codec summary in fo_device.hpp)
+// decode multiplier of a block with scale s (see the codec summary in
+// fo_device.hpp).  The level spacings RN(s/127), RN(s/255), RN(s*s/255) are
+// correctly rounded divisions by a constant: div_refined with the constant's
+// rounded reciprocal (exact for every dividend: the CPU check covers all
+// divisors with 11-bit significands).  A non-finite s divides to itself.
 template <int KIND, int CODEC>
 __device__ __forceinline__ float decode_mult(float s) {
-  if constexpr (KIND == MOMENTUM_STATE) return (CODEC == COMPANDED) ? s : s / 127.0f;
-  else return (CODEC == COMPANDED) ? s / 255.0f : (s * s) / 255.0f;
+  constexpr float R127 = 1.0f / 127.0f, R255 = 1.0f / 255.0f;   // RN(1/127), RN(1/255)
+  if constexpr (KIND == MOMENTUM_STATE && CODEC == COMPANDED) return s;
+  const float x = (KIND == VARIANCE_STATE && CODEC == LINEAR) ? s * s : s;
+  const float q = (KIND == MOMENTUM_STATE) ? div_refined(x, 127.0f, R127) : div_refined(x, 255.0f, R255);
+  return (fabsf(x) <= 0x1p126f) ? q : x;
 }
 template <int KIND, int CODEC>
 __device__ __forceinline__ float decode_state(const DW<2>& q, int i, float dm, const CodecTables& T) {
@@ -218,9 +225,10 @@ template <int KIND, int CODEC> constexpr bool encodes_root = (KIND == VARIANCE_S
 // m = b1*m + (1-b1)*g; v = b2*v + (1-b2)*g*g; th = th*decay;
 // th = th - step_size * (m / (sqrt(v)*ibc2 + eps)), each operation one IEEE
 // rounding (division and square root correctly rounded).
-__device__ __forceinline__ bool grad_in_fast_range(float g, uint32_t lo2, float hi) {
-  return ((f2u(g) << 1) - 2u) >= lo2 && fabsf(g) <= hi;    // g = +-0 wraps to the top: in range
-}
+// the two ways out of the fast range, each one compare: 0 < |g| < g_lo
+// (2*bits(g) - 2 wraps to the top for g = +-0), and |g| > g_hi or NaN
+__device__ __forceinline__ bool grad_below_fast_range(float g, uint32_t lo2) { return ((f2u(g) << 1) - 2u) < lo2; }
+__device__ __forceinline__ bool grad_above_fast_range(float g, float hi) { return !(fabsf(g) <= hi); }
 template <bool L2>
 struct AdamWRule {
   static constexpr int NSTATE = 2;
@@ -236,7 +244,8 @@ struct AdamWRule {
       st[0][k] = c.b1 * st[0][k] + c.omb1 * gk;
       st[1][k] = c.b2 * st[1][k] + c.omb2 * (gk * gk);
       th[k] = th[k] * c.decay;
-      slow |= __builtin_amdgcn_ballot_w64(!grad_in_fast_range(gk, c.g_lo2, c.g_hi));
+      slow |= __builtin_amdgcn_ballot_w64(grad_below_fast_range(gk, c.g_lo2)) |
+              __builtin_amdgcn_ballot_w64(grad_above_fast_range(gk, c.g_hi));
     }
     float q[EPL];
     if (!slow) {
@@ -346,7 +355,10 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       g[i] = wid<WFMT>(G[j], i);
-      th[i] = ecc_decode<WFMT, ECC>(wid<WFMT>(W[j], i), rho_at<ECC>(E[j], i));
+      if constexpr (WFMT == BF16)
+        th[i] = ecc_decode_bf16_packed<ECC>(W[j].w[i >> 1], E[j].w[(i * ECC) >> 5], i & 1, (ECC == 8) ? (i & 3) : (i & 1));
+      else
+        th[i] = ecc_decode<WFMT, ECC>(wid<WFMT>(W[j], i), rho_at<ECC>(E[j], i));
       st[0][i] = decode_state<K0, CODEC>(SQ[0][j], i, dm[0], tabs);
       if constexpr (NS == 2) st[NS - 1][i] = decode_state<K1, CODEC>(SQ[NS - 1][j], i, dm[NS - 1], tabs);
     }
@@ -390,7 +402,9 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
     if (own_ok) __builtin_nontemporal_store((uint16_t)sb, sp[k] + own);
     const float sf = h2f(sb);
     s_own[k] = lin_var ? sf * sf : sf;                       // the divisor of the normalisation (exact)
-    r_own[k] = 1.0f / s_own[k];                              // IEEE: s = 0 -> inf, NaN -> NaN
+    // RN(1/divisor) for the fast encodes; a zero divisor gives NaN, which
+    // codes the block's zeros (and NaNs) 0 as the division 0/0 would
+    r_own[k] = rcp_refined(s_own[k]);
     // the fast encodes need |x| <= s (momentum) or a finite x (variance)
     sat |= (kind == MOMENTUM_STATE) ? (own_max[k] > 65504.0f) : (own_max[k] == __builtin_inff());
   }
@@ -486,6 +500,36 @@ __device__ __forceinline__ void probe_tile(const TensorDesc& d, int64_t e0, int 
 }
 
 // ---------------------------------------------------------------------------
+// HBM probe: plain read, write or copy streams with the fused kernels' access
+// style (one wave per 8-KiB chunk, 16-byte nontemporal accesses, each
+// instruction covering 1 KiB)
+// ---------------------------------------------------------------------------
+constexpr int HBM_PROBE_CHUNK = WAVE * 16 * 8;   // bytes per wave
+__global__ void __launch_bounds__(WAVE) k_hbm_probe(uint8_t* __restrict__ dst, const uint8_t* __restrict__ src,
+                                                    int64_t chunk0, int mode, uint32_t key) {
+  const int lane = threadIdx.x;
+  const int64_t base = (chunk0 + blockIdx.x) * HBM_PROBE_CHUNK + lane * 16;
+  if (mode == 1) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_nontemporal_store(u32x4{key, key, key, key}, (gp<u32x4>)(dst + base + i * 1024));
+    return;
+  }
+  u32x4 v[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = __builtin_nontemporal_load((gp<const u32x4>)(src + base + i * 1024));
+  if (mode == 2) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) __builtin_nontemporal_store(v[i], (gp<u32x4>)(dst + base + i * 1024));
+    return;
+  }
+  uint32_t acc = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+  if (acc == key) ((gp<uint32_t>)dst)[0] = acc;   // keeps the loads; key is chosen not to match
+}
+
+// ---------------------------------------------------------------------------
 // multi-tensor kernels
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ int find_tensor(const TensorDesc* __restrict__ tab, int count, int64_t T) {
@@ -544,9 +588,13 @@ __device__ __forceinline__ void load_tables(CodecTables& dst, const CodecTables*
 // barrier keeps them ahead of the tile's loads.
 typedef __attribute__((address_space(3))) void lds_void;
 constexpr int BUFFER_RSRC_WORD3 = 0x00020000;   // raw buffer, 32-bit data format
+// With one wave per workgroup the wave's copy is the workgroup's only LDS
+// allocation: its address is the constant 0, so table addresses fold into the
+// LDS instructions' offsets.
+template <int WPG>
 __device__ __forceinline__ const CodecTables& wave_tables(CodecTables* lds, const CodecTables* __restrict__ src) {
   constexpr int CHUNKS = sizeof(CodecTables) / (16 * WAVE);
-  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wid = (WPG == 1) ? 0 : __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & (WAVE - 1);
   const __amdgpu_buffer_rsrc_t r =
       __builtin_amdgcn_make_buffer_rsrc((void*)src, 0, (int)sizeof(CodecTables), BUFFER_RSRC_WORD3);
@@ -571,7 +619,7 @@ __global__ void __launch_bounds__(WAVE * adamw_tile_waves<ECC>) __attribute__((a
 k_fused_adamw(const TensorDesc* __restrict__ tab, int count, int64_t tile0, int64_t tile_end,
               const CodecTables* __restrict__ gtabs, AdamWConsts c) {
   __shared__ CodecTables wtabs[adamw_tile_waves<ECC>];
-  const CodecTables& tabs = wave_tables(wtabs, gtabs);
+  const CodecTables& tabs = wave_tables<adamw_tile_waves<ECC>>(wtabs, gtabs);
   tile_loop<adamw_tile_waves<ECC>>(tab, count, tile0, tile_end, [&](const TensorDesc& d, int64_t e0, int lane) {
     if (e0 + TILE <= d.n) fused_tile<AdamWRule<L2>, WFMT, ECC, CODEC, true>(d, e0, lane, tabs, c);
     else fused_tile<AdamWRule<L2>, WFMT, ECC, CODEC, false>(d, e0, lane, tabs, c);
@@ -583,7 +631,7 @@ __global__ void __launch_bounds__(WAVE * SGDM_TILE_WAVES) k_fused_sgdm(const Ten
                                                                  int64_t tile0, int64_t tile_end,
                                                                  const CodecTables* __restrict__ gtabs, SGDMConsts c) {
   __shared__ CodecTables wtabs[SGDM_TILE_WAVES];
-  const CodecTables& tabs = wave_tables(wtabs, gtabs);
+  const CodecTables& tabs = wave_tables<SGDM_TILE_WAVES>(wtabs, gtabs);
   tile_loop<SGDM_TILE_WAVES>(tab, count, tile0, tile_end, [&](const TensorDesc& d, int64_t e0, int lane) {
     if (e0 + TILE <= d.n) fused_tile<SGDMRule, WFMT, ECC, CODEC, true>(d, e0, lane, tabs, c);
     else fused_tile<SGDMRule, WFMT, ECC, CODEC, false>(d, e0, lane, tabs, c);

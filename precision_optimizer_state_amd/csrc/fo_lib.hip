@@ -20,6 +20,7 @@
 
 #include "../../include/foamd.h"
 #include "fo_kernels.hpp"
+#include "fo_slots.hpp"
 
 using namespace fo;
 
@@ -128,25 +129,23 @@ int elementwise_grid(int dev, int64_t n, int* grid) {
 // ---------------------------------------------------------------------------
 struct TableEntry {
   int dev = -1;
-  std::vector<uint8_t> key;
   TensorDesc* dptr = nullptr;
   TensorDesc* hptr = nullptr;   // pinned staging copy
   size_t cap = 0;               // bytes
   hipEvent_t ev = nullptr;      // last stream-ordered use of dptr/hptr
   bool ev_recorded = false;
-  uint64_t stamp = 0;
   int count = 0;                // non-empty tensors
   int64_t total_tiles = 0;
 };
 
 // Enough slots for one list per parameter of a large model (gradient release
 // can step parameters one by one or in small buckets), so such lists do not
-// evict each other; the index makes a lookup O(1) in the number of slots.
+// evict each other; the slot index makes a lookup O(1) in the number of
+// slots.  Slots read by a captured HIP graph are pinned (fo_slots.hpp).
 constexpr size_t kCacheEntries = 1024;
 std::mutex g_tab_mu;
 std::vector<TableEntry> g_tab(kCacheEntries);
-std::unordered_map<std::string, size_t> g_index;   // (device, key) -> slot
-uint64_t g_stamp = 0;
+SlotCache g_slots(kCacheEntries);
 
 std::string index_key(int dev, const std::vector<uint8_t>& key) {
   std::string k(sizeof(int) + key.size(), '\0');
@@ -157,11 +156,8 @@ std::string index_key(int dev, const std::vector<uint8_t>& key) {
 
 // caller holds g_tab_mu
 TableEntry* find_entry(int dev, const std::vector<uint8_t>& key) {
-  auto it = g_index.find(index_key(dev, key));
-  if (it == g_index.end()) return nullptr;
-  TableEntry& e = g_tab[it->second];
-  e.stamp = ++g_stamp;
-  return &e;
+  const long slot = g_slots.find(index_key(dev, key));
+  return slot < 0 ? nullptr : &g_tab[(size_t)slot];
 }
 
 struct Range { uintptr_t lo, hi; };
@@ -180,12 +176,12 @@ int check_alias(std::vector<Range>& r) { return check_alias(r.data(), r.size());
 int get_table(int dev, const std::vector<uint8_t>& key, const std::vector<TensorDesc>& descs,
               const std::vector<int32_t>& buckets, int64_t total_tiles, hipStream_t stream, TableEntry** out) {
   if ((*out = find_entry(dev, key))) return FO_OK;
-  // miss: evict the least recently used entry of the cache
-  size_t vi = 0;
-  for (size_t i = 1; i < g_tab.size(); ++i) if (g_tab[i].stamp < g_tab[vi].stamp) vi = i;
-  TableEntry& e = g_tab[vi];
-  if (!e.key.empty()) g_index.erase(index_key(e.dev, e.key));
-  e.key.clear();
+  // miss: refill the least recently used slot that no captured graph reads
+  const long vi = g_slots.victim();
+  if (vi < 0)
+    return fail(FO_ENOMEM, "all %zu launch-table slots are held by captured HIP graphs", kCacheEntries);
+  TableEntry& e = g_tab[(size_t)vi];
+  g_slots.drop(vi);
   hipError_t he;
   if (e.ev_recorded) {
     he = hipEventSynchronize(e.ev);           // previous users of this slot are done
@@ -214,23 +210,31 @@ int get_table(int dev, const std::vector<uint8_t>& key, const std::vector<Tensor
   std::memcpy(e.hptr, descs.data(), desc_bytes);
   std::memcpy(reinterpret_cast<uint8_t*>(e.hptr) + desc_bytes, buckets.data(), buckets.size() * sizeof(int32_t));
   he = hipMemcpyAsync(e.dptr, e.hptr, need, hipMemcpyHostToDevice, stream);
-  if (he != hipSuccess) { e.key.clear(); return hip_fail(he, "hipMemcpyAsync(launch table)"); }
+  if (he != hipSuccess) return hip_fail(he, "hipMemcpyAsync(launch table)");
   // the staging copy is in flight: mark the slot used now, so that a later
   // eviction waits for it even if the launch that follows fails
   he = hipEventRecord(e.ev, stream);
-  if (he != hipSuccess) { e.key.clear(); return hip_fail(he, "hipEventRecord(launch table)"); }
+  if (he != hipSuccess) return hip_fail(he, "hipEventRecord(launch table)");
   e.ev_recorded = true;
-  e.key = key;
-  g_index[index_key(dev, key)] = vi;
+  g_slots.store(vi, index_key(dev, key));
   e.count = (int)descs.size() - 1;
   e.total_tiles = total_tiles;
-  e.stamp = ++g_stamp;
   *out = &e;
   return FO_OK;
 }
 
-int record_use(TableEntry* e, hipStream_t stream) {
-  hipError_t he = hipEventRecord(e->ev, stream);
+// After the launches that read `e`: record their stream-ordered use (a later
+// refill of the slot waits for it), or, when `stream` is being captured into
+// a HIP graph, pin the slot, since the graph may replay them at any time.
+int use_entry(TableEntry* e, hipStream_t stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t he = hipStreamIsCapturing(stream, &cs);
+  if (he != hipSuccess) return hip_fail(he, "hipStreamIsCapturing");
+  if (cs != hipStreamCaptureStatusNone) {
+    g_slots.pin((long)(e - g_tab.data()));
+    return FO_OK;
+  }
+  he = hipEventRecord(e->ev, stream);
   if (he != hipSuccess) return hip_fail(he, "hipEventRecord");
   e->ev_recorded = true;
   return FO_OK;
@@ -407,6 +411,11 @@ static void adamw_fast_range(AdamWConsts* c) {
 extern "C" {
 
 int fo_abi_version(void) { return FO_ABI_VERSION; }
+
+int fo_cache_pinned(void) {
+  std::lock_guard<std::mutex> lk(g_tab_mu);
+  return (int)g_slots.pinned_count();
+}
 
 const char* fo_last_error(void) { return g_err.c_str(); }
 
@@ -621,7 +630,7 @@ int fo_fused_adamw_step(const fo_adamw_tensor* list, int32_t count, const fo_ada
   const CodecTables* tb = nullptr;
   if ((rc = current_device(&dev)) || (rc = device_tables(dev, s, &tb))) return rc;
   if ((rc = adamw_launch(hp, (const TensorDesc*)e->dptr, e->count, e->total_tiles, tb, s))) return rc;
-  return record_use(e, s);
+  return use_entry(e, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -729,7 +738,24 @@ int fo_stream_probe(const fo_adamw_tensor* list, int32_t count, int32_t wfmt, in
   }
   rc = launch_check("k_stream_probe launch");
   if (rc) return rc;
-  return record_use(e, s);
+  return use_entry(e, s);
+}
+
+int fo_hbm_probe(void* dst, const void* src, int64_t bytes, int32_t mode, uint32_t key, void* stream) {
+  g_err.clear();
+  if (mode < 0 || mode > 2) return fail(FO_EINVAL, "bad probe mode %d", mode);
+  if (bytes < 0 || bytes % HBM_PROBE_CHUNK != 0)
+    return fail(FO_EINVAL, "bytes must be a non-negative multiple of %d", HBM_PROBE_CHUNK);
+  if (bytes == 0) return FO_OK;
+  if ((mode != 1 && !src) || !dst) return fail(FO_EINVAL, "NULL pointer");
+  if (!aligned(dst, 16) || (src && !aligned(src, 16))) return fail(FO_EINVAL, "pointer not 16-byte aligned");
+  hipStream_t s = as_stream(stream);
+  const int64_t chunks = bytes / HBM_PROBE_CHUNK;
+  for (int64_t c0 = 0; c0 < chunks; c0 += kLaunchTiles) {
+    const int grid = (int)std::min<int64_t>(kLaunchTiles, chunks - c0);
+    hipLaunchKernelGGL(k_hbm_probe, grid, WAVE, 0, s, (uint8_t*)dst, (const uint8_t*)src, c0, (int)mode, key);
+  }
+  return launch_check("k_hbm_probe launch");
 }
 
 int fo_fused_sgdm_step(const fo_sgdm_tensor* list, int32_t count, const fo_sgdm_hparams* hp, void* stream) {
@@ -788,7 +814,7 @@ int fo_fused_sgdm_step(const fo_sgdm_tensor* list, int32_t count, const fo_sgdm_
   }
   rc = launch_check("k_fused_sgdm launch");
   if (rc) return rc;
-  return record_use(e, s);
+  return use_entry(e, s);
 }
 
 int fo_selftest(int what, uint32_t lo, uint64_t count, uint64_t* mismatches, void* stream) {

@@ -28,3 +28,16 @@ def test_launch_count_follows_the_tile_ranges():
     assert bench.launches_per_call(config("c3_llama8b").numels) == 15
     assert bench.launches_per_call(config("c5_flat1g_bf16e8").numels) == 2
     assert sum(bench.launches_per_call([m]) for m in RELEASE_CHUNKS) == len(RELEASE_CHUNKS)
+
+
+def test_cpu_baseline_is_a_measured_wall_rate():
+    # the oracle leg runs in worker processes released together at a barrier;
+    # its value is elements / wall time of the compute phase, and every worker
+    # is joined (none terminated)
+    sys.path.insert(0, ROOT)
+    import bench
+    from workloads import config
+    res = bench.cpu_baseline(config("c1_flat1m"), segments=6, seg=4096, log=lambda m: None)
+    assert res["kind"] == "oracle" and res["unit"] == "params/s"
+    assert 1 <= res["cores"] <= 16 and res["value"] > 0
+    assert "6 segments" in res["sample"] and "wall" in res["sample"]

@@ -53,3 +53,39 @@ def test_captured_step_replays_match_eager_calls(sizes):
             for k in KEYS:
                 assert torch.equal(a[k].view(torch.uint8), b[k].view(torch.uint8)), f"replay {r}: tensor {i} {k} differs"
     print(f"graph replays ({len(sizes)} tensors): 4 replays bitwise equal to eager calls", flush=True)
+
+
+def test_captured_table_survives_eviction_by_other_lists():
+    """The launch table a graph captured stays valid after more distinct lists
+    than the cache holds have been stepped eagerly (its slot is pinned)."""
+    hp = B.adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 3)
+    n = 200_000 + 33
+    a = _state(n, "pin_a")
+    tl_a = B.AdamWList([a])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        B.fo_fused_adamw_step(tl_a, hp)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    b = {k: v.clone() for k, v in a.items()}
+    tl_b = B.AdamWList([b])
+    pinned = B.load().fo_cache_pinned()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.fo_fused_adamw_step(tl_a, hp)
+    # the captured call pinned its slot (checked before any eviction happens)
+    assert B.load().fo_cache_pinned() == pinned + 1
+    # 1100 distinct one-block lists, views into one state: more lists than cache slots
+    many = _state(1100 * 32, "pin_many")
+    for i in range(1100):
+        sl = {k: v[i * 32:(i + 1) * 32] if k not in ("m_s", "v_s") else v[i:i + 1] for k, v in many.items()}
+        B.fo_fused_adamw_step(B.AdamWList([sl]), hp)
+    torch.cuda.synchronize()
+    for r in range(2):
+        g.replay()
+        B.fo_fused_adamw_step(tl_b, hp)
+        torch.cuda.synchronize()
+        for k in KEYS:
+            assert torch.equal(a[k].view(torch.uint8), b[k].view(torch.uint8)), f"replay {r}: {k} differs"
+    print("captured table pinned: replays after 1100 other lists bitwise equal to eager calls", flush=True)

@@ -27,14 +27,18 @@ class Config:
     def params(self) -> int:
         return sum(self.numels)
 
-    def bytes_per_param(self) -> float:
-        """Algorithmic HBM bytes moved per parameter by one fused step."""
+    def read_write_bytes_per_param(self):
+        """Algorithmic HBM bytes (read, written) per parameter by one fused step."""
+        e = self.ecc_bits // 8
         if self.optimizer == "adamw":
             # read: grad 2, w16 2, ecc E, m 1, v 1, scales 4/32; write: w16 2, ecc E, m 1, v 1, scales 4/32
-            e = self.ecc_bits // 8
-            return (2 + 2 + e + 1 + 1 + 4 / 32) + (2 + e + 1 + 1 + 4 / 32)
-        e = self.ecc_bits // 8
-        return (2 + 2 + e + 1 + 2 / 32) + (2 + e + 1 + 2 / 32)
+            return (2 + 2 + e + 1 + 1 + 4 / 32), (2 + e + 1 + 1 + 4 / 32)
+        return (2 + 2 + e + 1 + 2 / 32), (2 + e + 1 + 2 / 32)
+
+    def bytes_per_param(self) -> float:
+        """Algorithmic HBM bytes moved per parameter by one fused step."""
+        r, w = self.read_write_bytes_per_param()
+        return r + w
 
 
 ADAMW_C1 = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
