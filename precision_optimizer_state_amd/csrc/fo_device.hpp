@@ -297,16 +297,46 @@ __device__ __forceinline__ uint32_t ru_fp16(float x) {
 // ---------------------------------------------------------------------------
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+  // quad_perm reads a lane of the same quad, so every lane has a source and
+  // the old value is never used (bound_ctrl set: no copy of it is made)
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
 }
 // quad_perm selectors
 constexpr int QP_SWAP1 = 0xB1;   // [1,0,3,2]
 constexpr int QP_SWAP2 = 0x4E;   // [2,3,0,1]
 template <int J> constexpr int qp_bcast() { return J * 0x55; }   // [J,J,J,J]
 
+// IEEE maxNum (a quiet NaN operand loses to a number) of operands that are
+// never signaling NaNs.  fmaxf has to quiet a signaling NaN first, so the
+// compiler puts a canonicalising v_max_f32 x, x, x in front of every operand
+// it cannot prove quiet (here: all of them, after selects and lane moves);
+// writing v_max_f32 / v_max3_f32 directly drops those.  Callers pass only
+// arithmetic results, lane copies of them and the quiet NaN constant.
+__device__ __forceinline__ float max_quiet(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3_quiet(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+// maxNum(|a|, |b|) and maxNum(m, |a|, |b|)
+__device__ __forceinline__ float max_abs_quiet(float a, float b) {
+  float r;
+  asm("v_max_f32_e64 %0, |%1|, |%2|" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3_abs_quiet(float m, float a, float b) {
+  float r;
+  asm("v_max3_f32 %0, %1, |%2|, |%3|" : "=v"(r) : "v"(m), "v"(a), "v"(b));
+  return r;
+}
+
 __device__ __forceinline__ float quad_max(float x) {   // IEEE maxNum over the 4 lanes
-  x = fmaxf(x, dpp_f<QP_SWAP1>(x));
-  x = fmaxf(x, dpp_f<QP_SWAP2>(x));
+  x = max_quiet(x, dpp_f<QP_SWAP1>(x));
+  x = max_quiet(x, dpp_f<QP_SWAP2>(x));
   return x;
 }
 template <int J>

@@ -378,14 +378,17 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
     for (int k = 0; k < NS; ++k) {
       const bool root_k = (k == 0) ? encodes_root<K0, CODEC> : encodes_root<K1, CODEC>;
       const bool mom_k = ((k == 0) ? K0 : K1) == MOMENTUM_STATE;
-      float mx = __builtin_nanf("");
+      float a[EPL];
 #pragma unroll
       for (int i = 0; i < EPL; ++i) {
         const float x = root_k ? root[k][i] : st[k][i];
         X[k][j][i] = x;
-        const float a = mom_k ? fabsf(x) : x;
-        mx = fmaxf(mx, (FULL || i < cnt[j]) ? a : __builtin_nanf(""));
+        a[i] = (FULL || i < cnt[j]) ? x : __builtin_nanf("");
       }
+      static_assert(EPL == 8, "maxima of 8 elements per lane");
+      float mx = mom_k ? max_abs_quiet(a[0], a[1]) : max_quiet(a[0], a[1]);
+#pragma unroll
+      for (int i = 2; i < EPL; i += 2) mx = mom_k ? max3_abs_quiet(mx, a[i], a[i + 1]) : max3_quiet(mx, a[i], a[i + 1]);
       mx = quad_max(mx);
       own_max[k] = (p == j) ? mx : own_max[k];
     }
