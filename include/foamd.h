@@ -215,13 +215,18 @@ int fo_fused_adamw_step(const fo_adamw_tensor* list, int32_t count,
  * hipMalloc, hipFree, pinned-host allocation, event or synchronisation.
  *   The codec tables and the call's launch table (descriptors and tile-bucket
  *   index) live in one fixed device array per GPU (438 KiB, held until the
- *   process ends), written on `stream` at every call; the first call on a
- *   device also builds the codec tables there.
+ *   process ends), written on `stream` at every call: the descriptors travel
+ *   as kernel arguments (3-KiB chunks) and the bucket index is computed on
+ *   the device, so nothing on the host is read after the call returns and a
+ *   call captured into a HIP graph replays its own table.  The first call on
+ *   a device outside capture also builds the codec tables there (a captured
+ *   call builds them in its graph).
  *   Limit: at most 2048 tensors per call (count > 2048 -> FO_EINVAL); sizes
  *   are otherwise unlimited.
- *   Calls on one GPU share that array and must not overlap: order them on
- *   one stream (or order the streams); overlapping calls race.  The first
- *   call on a device must be ordered before any call on another stream.
+ *   Calls and graph replays on one GPU share that array and must not
+ *   overlap: order them on one stream (or order the streams); overlapping
+ *   calls race.  The first call on a device must be ordered before any call
+ *   on another stream.
  * Errors: as fo_fused_adamw_step, plus FO_EINVAL for lists over the limit.
  */
 int fo_fused_adamw_step_noalloc(const fo_adamw_tensor* list, int32_t count,

@@ -609,6 +609,44 @@ __device__ __forceinline__ const CodecTables& wave_tables(CodecTables* lds, cons
   return lds[wid];
 }
 
+// ---------------------------------------------------------------------------
+// launch table written from kernel arguments (allocation-free entry point)
+// ---------------------------------------------------------------------------
+// A chunk of the descriptor array travels by value in the kernel arguments
+// (copied at launch, or into the node of a captured graph), so nothing on the
+// host has to outlive the call.  TABLE_CHUNK keeps the arguments far below
+// the 4-KiB kernel-argument limit together with the implicit arguments.
+constexpr int TABLE_CHUNK = 3072;
+struct alignas(16) TableChunk {
+  uint8_t data[TABLE_CHUNK];
+  uint32_t offset;   // byte offset of the chunk in the table
+  uint32_t bytes;    // a multiple of 16, at most TABLE_CHUNK
+};
+__global__ void __launch_bounds__(WG) k_put_table(uint8_t* __restrict__ dst, TableChunk c) {
+  const int i = threadIdx.x;                       // one 16-byte word per thread
+  if ((uint32_t)i * 16u < c.bytes) {
+    const u32x4 v = reinterpret_cast<const u32x4*>(c.data)[i];
+    ((gp<u32x4>)(dst + c.offset))[i] = v;
+  }
+}
+static_assert(WG * 16 >= TABLE_CHUNK, "one workgroup writes a whole chunk");
+
+// Tile-bucket index of a descriptor table already on the device: entry b
+// (0 <= b < nbk) is the last tensor whose first tile is at or before
+// min(b << shift, tiles - 1), found by binary search over tile_begin.
+__global__ void __launch_bounds__(WG) k_bucket_index(const TensorDesc* __restrict__ tab, int count, int shift,
+                                                     int nbk, int64_t tiles, int32_t* __restrict__ buckets) {
+  const int b = blockIdx.x * WG + threadIdx.x;
+  if (b >= nbk) return;
+  const int64_t first = min((int64_t)b << shift, tiles - 1);
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (tab[mid].tile_begin <= first) lo = mid; else hi = mid - 1;
+  }
+  buckets[b] = lo;
+}
+
 __global__ void __launch_bounds__(WG) k_init_tables(CodecTables* out) {
   __shared__ float thr[128];
   build_tables((gp<CodecTables>)out, thr, threadIdx.x, blockDim.x);

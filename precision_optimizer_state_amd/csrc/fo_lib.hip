@@ -639,9 +639,13 @@ int fo_fused_adamw_step(const fo_adamw_tensor* list, int32_t count, const fo_ada
 // The library's device memory of this entry point is one file-scope device
 // array per GPU, held until the process ends: the codec tables, then the
 // launch table (descriptors, sentinel, tile-bucket index) of the current
-// call.  Host staging is static as well, so a call allocates nothing.  The
-// array's device address comes from hipGetSymbolAddress, taken once per
-// device with that device current; host code uses only that address.
+// call.  The descriptors reach it as kernel arguments (k_put_table, in
+// chunks) and the bucket index is computed there from them
+// (k_bucket_index), so no host buffer is read after the call returns: the
+// call neither allocates nor synchronises, and a captured call replays its
+// own table.  The array's device address comes from hipGetSymbolAddress,
+// taken once per device with that device current; host code uses only that
+// address.
 static constexpr int kNoAllocMaxTensors = 2048;
 constexpr size_t kScratchDescOff = sizeof(CodecTables);                 // tables first
 constexpr size_t kScratchTableBytes = (size_t)(kNoAllocMaxTensors + 1) * sizeof(TensorDesc) +
@@ -660,11 +664,13 @@ static TensorDesc g_na_body[kNoAllocMaxTensors];
 static Range g_na_ranges[(size_t)kNoAllocMaxTensors * kArraysPerTensor];
 static TensorDesc g_na_descs[kNoAllocMaxTensors + 1];
 static int32_t g_na_buckets[kMaxBucketEntries];
-alignas(16) static uint8_t g_na_stage[kScratchTableBytes];
+static TableChunk g_na_chunk;
 
 // The device's scratch address (hipGetSymbolAddress on the first call on the
 // device) and its codec tables (built into it by k_init_tables on the stream
-// of that first call; the caller orders later calls on other streams after it).
+// of that first call; the caller orders later calls on other streams after
+// it).  Under graph capture the build becomes part of the graph and is made
+// again by the next call outside capture.
 static int noalloc_scratch(int dev, hipStream_t s, uint8_t** out) {
   if (dev < 0 || dev >= kNoAllocMaxDevices) return fail(FO_EINVAL, "device %d beyond the %d the library serves", dev,
                                                         kNoAllocMaxDevices);
@@ -676,10 +682,13 @@ static int noalloc_scratch(int dev, hipStream_t s, uint8_t** out) {
     d.ptr = static_cast<uint8_t*>(p);
   }
   if (!d.tables_built) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    const hipError_t e = hipStreamIsCapturing(s, &cs);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
     hipLaunchKernelGGL(k_init_tables, 1, WG, 0, s, reinterpret_cast<CodecTables*>(d.ptr));
     const int rc = launch_check("k_init_tables launch");
     if (rc) return rc;
-    d.tables_built = true;
+    d.tables_built = (cs == hipStreamCaptureStatusNone);
   }
   *out = d.ptr;
   return FO_OK;
@@ -704,14 +713,23 @@ int fo_fused_adamw_step_noalloc(const fo_adamw_tensor* list, int32_t count, cons
   int dev;
   uint8_t* ptr = nullptr;
   if ((rc = current_device(&dev)) || (rc = noalloc_scratch(dev, s, &ptr))) return rc;
-  // descriptors, then the bucket index right after them (where the kernels look)
+  // descriptors (with the sentinel, which holds the bucket shift), then the
+  // bucket index right after them, where the kernels look
+  uint8_t* table = ptr + kScratchDescOff;
   const size_t desc_bytes = (size_t)nd * sizeof(TensorDesc);
-  const size_t bytes = desc_bytes + (size_t)nbk * sizeof(int32_t);
-  std::memcpy(g_na_stage, g_na_descs, desc_bytes);
-  std::memcpy(g_na_stage + desc_bytes, g_na_buckets, (size_t)nbk * sizeof(int32_t));
-  const hipError_t he = hipMemcpyAsync(ptr + kScratchDescOff, g_na_stage, bytes, hipMemcpyHostToDevice, s);
-  if (he != hipSuccess) return hip_fail(he, "hipMemcpyAsync(launch table)");
-  return adamw_launch(hp, reinterpret_cast<const TensorDesc*>(ptr + kScratchDescOff), nd - 1, tiles,
+  static_assert(sizeof(TensorDesc) % 16 == 0 && TABLE_CHUNK % 16 == 0, "16-byte chunk words");
+  for (size_t off = 0; off < desc_bytes; off += TABLE_CHUNK) {
+    const size_t b = std::min<size_t>(TABLE_CHUNK, desc_bytes - off);
+    std::memcpy(g_na_chunk.data, reinterpret_cast<const uint8_t*>(g_na_descs) + off, b);
+    g_na_chunk.offset = (uint32_t)off;
+    g_na_chunk.bytes = (uint32_t)b;
+    hipLaunchKernelGGL(k_put_table, 1, WG, 0, s, table, g_na_chunk);
+  }
+  const int shift = (int)g_na_descs[nd - 1].n;
+  hipLaunchKernelGGL(k_bucket_index, (nbk + WG - 1) / WG, WG, 0, s, reinterpret_cast<const TensorDesc*>(table),
+                     nd - 1, shift, nbk, tiles, reinterpret_cast<int32_t*>(table + desc_bytes));
+  if ((rc = launch_check("launch-table kernels"))) return rc;
+  return adamw_launch(hp, reinterpret_cast<const TensorDesc*>(table), nd - 1, tiles,
                       reinterpret_cast<const CodecTables*>(ptr), s);
 }
 

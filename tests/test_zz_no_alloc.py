@@ -1,8 +1,9 @@
 """The allocation-free AdamW entry point (fo_fused_adamw_step_noalloc) through
 the C ABI: bitwise equal to fo_fused_adamw_step on a copy of the same state,
 on two calls in a row, the second with a smaller list (the fixed device
-array then holds the first call's larger table beyond the second's); lists
-over the limit are rejected before any device work."""
+array then holds the first call's larger table beyond the second's), and
+when captured into a HIP graph and replayed between calls on another list;
+lists over the limit are rejected before any device work."""
 
 import pytest
 import torch
@@ -59,3 +60,29 @@ def test_noalloc_rejects_lists_over_the_limit():
     with pytest.raises(B.FoError) as ei:
         B.fo_fused_adamw_step_noalloc([st] * 2049, dict(HP, step=1))
     assert ei.value.code == B.FO_EINVAL and "2048" in str(ei.value)
+
+
+def test_noalloc_captured_call_replays_its_own_table():
+    """A captured allocation-free call carries its launch table in the graph
+    (kernel arguments): eager allocation-free calls on another list rewrite
+    the shared device array between replays, and every replay still equals
+    the cached entry point's step on a copy of the state."""
+    hp = dict(HP, step=3)
+    a = _states([300_000 + 77, 4099], "nacap_a")
+    ref = _clone(a)
+    other = _states([70_001, 33, 5000], "nacap_b")
+    tl_a, tl_other = B.AdamWList(a), B.AdamWList(other)
+    B.fo_fused_adamw_step_noalloc(tl_other, hp)            # codec tables built outside capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.fo_fused_adamw_step_noalloc(tl_a, hp)
+    for r in range(3):
+        B.fo_fused_adamw_step_noalloc(tl_other, hp)        # another table in the shared array
+        g.replay()
+        B.fo_fused_adamw_step(ref, hp)
+        torch.cuda.synchronize()
+        for i, (sa, sb) in enumerate(zip(a, ref)):
+            for k in KEYS:
+                assert torch.equal(sa[k].view(torch.uint8), sb[k].view(torch.uint8)), (r, i, k)
+    print("captured no-alloc call: 3 replays bitwise equal to cached eager calls", flush=True)
