@@ -15,10 +15,11 @@ from .binding import (  # noqa: F401
     fo_companded_quantize,
     fo_dequantize,
     fo_fused_adamw_step,
+    fo_fused_adamw_step_noalloc,
     fo_fused_sgdm_step,
     fo_reconstruct_weights,
     fo_split_weights,
     fo_stream_probe,
 )
-from .state import AdamWState, SGDMState, alloc_adamw_state, alloc_sgdm_state  # noqa: F401
+from .state import alloc_adamw_state, alloc_sgdm_state  # noqa: F401
 from .optim import FlashAdam, FlashAdamW, FlashSGD  # noqa: F401

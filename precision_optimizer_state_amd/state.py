@@ -19,14 +19,6 @@ def nblocks(n: int) -> int:
     return (n + 31) // 32
 
 
-def AdamWState(**kw):  # noqa: N802 - a plain dict keeps the binding's mapping interface
-    return dict(**kw)
-
-
-def SGDMState(**kw):  # noqa: N802
-    return dict(**kw)
-
-
 def alloc_adamw_state(n: int, wfmt: str = "bf16", ecc_bits: int = 8, device="cuda", with_grad: bool = True) -> dict:
     nb = nblocks(n)
     st = {
