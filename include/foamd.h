@@ -306,7 +306,9 @@ int fo_hbm_probe(void* dst, const void* src, int64_t bytes, int32_t mode, uint32
  *           residual-corrected quotient differs from IEEE a/b;
  *   what 4: the same with b a positive finite binary16 value and |a| <= b;
  *   what 5: as 3 over the pairs whose quotient is a nonzero subnormal, which
- *           the fused AdamW step keeps out of its fast form.
+ *           the fused AdamW step keeps out of its fast form;
+ *   what 6: as 1 for the square root from the estimate of the successor
+ *           with one residual test (used for x = 0 and 2^-96 <= x <= 2^100).
  * Errors: FO_EINVAL (bad `what`, NULL output, a pattern range past 2^32),
  * FO_ENOMEM, FO_EHIP.
  */

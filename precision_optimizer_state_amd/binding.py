@@ -262,9 +262,10 @@ def fo_hbm_probe(dst, src, nbytes, mode="copy", key=0, stream=None) -> None:
 def fo_selftest(what: int, lo: int, count: int, stream=None) -> int:
     """Mismatch count of the device's fast exact arithmetic: over the f32
     patterns [lo, lo + count) for 0 = reciprocal, 1 = square root,
-    2 = float-to-u8; over `count` seeded (by lo) pairs for 3 = division
-    (normal quotients), 4 = division by a block scale, 5 = division with a
-    subnormal quotient (outside the fast step's domain)."""
+    2 = float-to-u8, 6 = square root from the successor's estimate; over
+    `count` seeded (by lo) pairs for 3 = division (normal quotients),
+    4 = division by a block scale, 5 = division with a subnormal quotient
+    (outside the fast step's domain)."""
     out = ctypes.c_uint64(0)
     _check(load().fo_selftest(int(what), int(lo), int(count), ctypes.byref(out), _stream(stream)))
     return int(out.value)

@@ -360,6 +360,19 @@ __device__ __forceinline__ float sqrt_corrected(float v) {
   s = (r_up > 0.0f) ? s_up : s;
   return s;
 }
+// Cheaper correctly rounded square root for v = 0 and 2^-96 <= v < 2^128 - 2^104
+// (every finite v from 2^-96 up but the largest): on gfx950 the hardware
+// estimate a of the square root of v's successor is never below RN(sqrt(v))
+// and at most one ulp above it (fo_selftest mode 6 checks every v of that
+// range), so only the lower neighbour dn of a is a candidate, and the
+// residual v - dn*a decides between them as in sqrt_corrected.  For v = 0 the
+// successor is not taken: a = 0, dn is a NaN pattern and the test fails.
+__device__ __forceinline__ float sqrt_fast(float v) {
+  const uint32_t u = f2u(v);
+  const float a = __builtin_amdgcn_sqrtf(u2f(u + (u != 0u ? 1u : 0u)));
+  const float dn = u2f(f2u(a) - 1u);
+  return (__builtin_fmaf(-dn, a, v) <= 0.0f) ? dn : a;
+}
 __device__ __forceinline__ bool sqrt_needs_scaling(float v) {   // 0 < v < 2^-96
   return (f2u(v) - 1u) < 0x0F7FFFFFu;
 }

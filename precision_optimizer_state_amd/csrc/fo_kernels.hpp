@@ -71,7 +71,7 @@ struct AdamWConsts {
   // hyperparameters and the ranges of the decoded states, so that every
   // variance lies outside (0, 2^-96), every denominator in [eps, 2^126), every
   // nonzero momentum at or above 2^-100 and every quotient below 2^120
-  // (the preconditions of sqrt_corrected, rcp_refined and div_refined).
+  // (the preconditions of sqrt_fast, rcp_refined and div_refined).
   uint32_t g_lo2;   // 2 * bits(g_lo) - 2: compared with 2 * bits(g) - 2
   float g_hi;
   int fast;         // 0: no such range (e.g. eps = 0); every wave takes the IEEE form
@@ -251,7 +251,7 @@ struct AdamWRule {
     if (!slow) {
 #pragma unroll
       for (int k = 0; k < EPL; ++k) {
-        root[1][k] = sqrt_corrected(st[1][k]);
+        root[1][k] = sqrt_fast(st[1][k]);
         const float den = root[1][k] * c.ibc2 + c.eps;
         q[k] = div_refined(st[0][k], den, rcp_refined(den));
       }
@@ -884,10 +884,11 @@ __global__ void __launch_bounds__(WG) k_selftest(int what, uint32_t lo, uint64_t
   unsigned long long nb = 0;
   for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) {
     bool ok;
-    if (what <= 2) {
+    if (what <= 2 || what == 6) {
       const float x = u2f(lo + (uint32_t)i);
       if (what == 0) ok = f2u(rcp_refined(x)) == f2u(1.0f / x);
       else if (what == 1) ok = f2u(sqrt_corrected(x)) == f2u(__builtin_sqrtf(x));
+      else if (what == 6) ok = f2u(sqrt_fast(x)) == f2u(__builtin_sqrtf(x));
       else {
         const uint32_t got = __builtin_amdgcn_cvt_pk_u8_f32(x, 0, 0u) & 0xFFu;
         const uint32_t ref = (x != x) ? 0u : (uint32_t)__builtin_rintf(fmaxf(fminf(x, 255.0f), 0.0f));

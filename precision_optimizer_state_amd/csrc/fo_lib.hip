@@ -837,9 +837,9 @@ int fo_fused_sgdm_step(const fo_sgdm_tensor* list, int32_t count, const fo_sgdm_
 
 int fo_selftest(int what, uint32_t lo, uint64_t count, uint64_t* mismatches, void* stream) {
   g_err.clear();
-  if (what < 0 || what > 5) return fail(FO_EINVAL, "bad self-test %d", what);
+  if (what < 0 || what > 6) return fail(FO_EINVAL, "bad self-test %d", what);
   if (!mismatches) return fail(FO_EINVAL, "mismatches is NULL");
-  if (what <= 2 && count > (1ull << 32) - lo) return fail(FO_EINVAL, "range exceeds the f32 patterns");
+  if ((what <= 2 || what == 6) && count > (1ull << 32) - lo) return fail(FO_EINVAL, "range exceeds the f32 patterns");
   hipStream_t s = as_stream(stream);
   unsigned long long* d = nullptr;
   hipError_t e = hipMalloc((void**)&d, sizeof(*d));

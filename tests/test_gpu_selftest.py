@@ -2,7 +2,8 @@
 table-driven momentum encode, through the C ABI.
 
 fo_selftest compares, on the device, the Newton-refined hardware reciprocal
-and the neighbour-corrected hardware square root with the IEEE operations,
+and the corrected hardware square roots (both neighbours of the estimate, or
+one neighbour of the successor's estimate) with the IEEE operations,
 and the hardware float-to-u8 conversion with round-half-even + clamp (NaN to
 0), over every f32 pattern of the ranges the kernels use them on; and the
 residual-corrected division with IEEE division on billions of seeded pairs
@@ -31,6 +32,21 @@ def test_corrected_sqrt_exact_from_2_minus_96_to_inf():
     assert B.fo_selftest(1, lo, hi - lo) == 0
     # zero takes the fast path too
     assert B.fo_selftest(1, 0, 1) == 0
+
+
+def test_successor_sqrt_exact_on_the_fast_step_domain():
+    # every f32 from 2^-96 up to the largest finite one (excluded), and zero;
+    # the AdamW step takes it for variances 0 and [2^-96, 2^100]
+    lo, hi = 0x0F800000, 0x7F7FFFFF
+    assert B.fo_selftest(6, lo, hi - lo) == 0
+    assert B.fo_selftest(6, 0, 1) == 0
+
+
+def test_successor_sqrt_fails_where_it_is_not_used():
+    # the largest finite float (its successor is infinite) and the tiny
+    # variances below 2^-96, which the gradient range keeps off the fast path
+    assert B.fo_selftest(6, 0x7F7FFFFF, 1) == 1
+    assert B.fo_selftest(6, 1, 0x0F800000 - 1) > 0
 
 
 def test_cvt_pk_u8_is_round_half_even_and_saturating_everywhere():
