@@ -74,6 +74,9 @@ struct AdamWConsts {
   // (the preconditions of sqrt_fast, rcp_refined and div_refined).
   uint32_t g_lo2;   // 2 * bits(g_lo) - 2: compared with 2 * bits(g) - 2
   float g_hi;
+  // the same range on the 16-bit gradient patterns' magnitudes a (AdamW):
+  // a = 0 or g16_lo < a <= g16_hi, g16_lo the largest pattern below g_lo
+  uint32_t g16_lo, g16_hi;
   int fast;         // 0: no such range (e.g. eps = 0); every wave takes the IEEE form
 };
 struct SGDMConsts {
@@ -208,6 +211,10 @@ template <int KIND, int CODEC> constexpr bool encodes_root = (KIND == VARIANCE_S
 //                                              VARIANCE_STATE (uint8 codes,
 //                                              square-root compander)
 //   using Consts = ...;                        per-step scalars from the host
+//   template <int NSUB> static bool tile_slow(const Consts&,
+//                      const DW<4> (&G)[NSUB]);  the tile's 16-bit gradient
+//                                              words as loaded: true (wave-
+//                                              uniform) asks for the IEEE form
 //   static void update(const Consts&, bool ieee, float (&th)[EPL],
 //                      const float (&g)[EPL], float (&st)[NSTATE][EPL],
 //                      float (&root)[NSTATE][EPL]);
@@ -218,8 +225,8 @@ template <int KIND, int CODEC> constexpr bool encodes_root = (KIND == VARIANCE_S
 // codec).  The whole wave calls update() together, so a rule may branch
 // wave-uniformly (ballot) between a fast exact form and the IEEE form; ieee
 // (wave-uniform) asks for the IEEE form, because a stored scale of the tile is
-// not finite.  A new rule needs a kernel that runs fused_tile with it and a
-// host entry point that fills its Consts.
+// not finite or tile_slow said so.  A new rule needs a kernel that runs
+// fused_tile with it and a host entry point that fills its Consts.
 
 // AdamW (decoupled decay) or, with L2, Adam (decay added to the gradient):
 // m = b1*m + (1-b1)*g; v = b2*v + (1-b2)*g*g; th = th*decay;
@@ -229,11 +236,41 @@ template <int KIND, int CODEC> constexpr bool encodes_root = (KIND == VARIANCE_S
 // (2*bits(g) - 2 wraps to the top for g = +-0), and |g| > g_hi or NaN
 __device__ __forceinline__ bool grad_below_fast_range(float g, uint32_t lo2) { return ((f2u(g) << 1) - 2u) < lo2; }
 __device__ __forceinline__ bool grad_above_fast_range(float g, float hi) { return !(fabsf(g) <= hi); }
+// The same test for a whole tile of 16-bit gradients, on the words as
+// loaded: with a the magnitude pattern of a gradient (monotone in |g|, NaN
+// above infinity), a gradient is out of range when a > g16_hi, or when
+// a - 1 < g16_lo (a - 1 wraps to 0xFFFF for a = 0).  Two packed 16-bit
+// maxima / minima per word keep the largest a and the smallest a - 1 of the
+// lane; wave-uniform result.
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+template <int NSUBT>
+__device__ __forceinline__ bool tile_grads_out_of_range(const DW<4> (&G)[NSUBT], uint32_t g16_lo, uint32_t g16_hi) {
+  u16x2 mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
+  const u16x2 one = {1, 1};
+#pragma unroll
+  for (int j = 0; j < NSUBT; ++j)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const u16x2 a = __builtin_bit_cast(u16x2, G[j].w[w] & 0x7FFF7FFFu);
+      mx = __builtin_elementwise_max(mx, a);
+      mn = __builtin_elementwise_min(mn, a - one);
+    }
+  const uint32_t hi = max((uint32_t)mx.x, (uint32_t)mx.y), lo = min((uint32_t)mn.x, (uint32_t)mn.y);
+  return __builtin_amdgcn_ballot_w64(hi > g16_hi || lo < g16_lo) != 0;
+}
 template <bool L2>
 struct AdamWRule {
   static constexpr int NSTATE = 2;
   template <int K> static constexpr int KIND = (K == 0) ? MOMENTUM_STATE : VARIANCE_STATE;
   using Consts = AdamWConsts;
+  // AdamW's gradient is the 16-bit input: its range is checked once per tile
+  // on the loaded words; Adam's effective gradient g + wd*th is checked
+  // element by element in update()
+  template <int NSUBT>
+  static __device__ __forceinline__ bool tile_slow(const Consts& c, const DW<4> (&G)[NSUBT]) {
+    if constexpr (L2) return false;
+    else return tile_grads_out_of_range(G, c.g16_lo, c.g16_hi);
+  }
   static __device__ __forceinline__ void update(const Consts& c, bool ieee, float (&th)[EPL], const float (&g)[EPL],
                                                 float (&st)[2][EPL], float (&root)[2][EPL]) {
     uint64_t slow = (c.fast && !ieee) ? 0ull : ~0ull;
@@ -244,8 +281,9 @@ struct AdamWRule {
       st[0][k] = c.b1 * st[0][k] + c.omb1 * gk;
       st[1][k] = c.b2 * st[1][k] + c.omb2 * (gk * gk);
       th[k] = th[k] * c.decay;
-      slow |= __builtin_amdgcn_ballot_w64(grad_below_fast_range(gk, c.g_lo2)) |
-              __builtin_amdgcn_ballot_w64(grad_above_fast_range(gk, c.g_hi));
+      if constexpr (L2)
+        slow |= __builtin_amdgcn_ballot_w64(grad_below_fast_range(gk, c.g_lo2)) |
+                __builtin_amdgcn_ballot_w64(grad_above_fast_range(gk, c.g_hi));
     }
     float q[EPL];
     if (!slow) {
@@ -275,6 +313,8 @@ struct SGDMRule {
   static constexpr int NSTATE = 1;
   template <int K> static constexpr int KIND = MOMENTUM_STATE;
   using Consts = SGDMConsts;
+  template <int NSUBT>
+  static __device__ __forceinline__ bool tile_slow(const Consts&, const DW<4> (&)[NSUBT]) { return false; }
   static __device__ __forceinline__ void update(const Consts& c, bool, float (&th)[EPL], const float (&g)[EPL],
                                                 float (&st)[1][EPL], float (&)[1][EPL]) {
 #pragma unroll
@@ -319,11 +359,17 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
   DW<2 * EB> E[NSUB];
   DW<2> SQ[NS][NSUB];
   int cnt[NSUB];
+  // the gradients first: the rule's tile-wide range check waits for them
+  // only (the vector memory counter retires loads in issue order)
 #pragma unroll
   for (int j = 0; j < NSUB; ++j) {
     const int off = j * SUB + lane * EPL;
     cnt[j] = FULL ? 8 : (int)max((int64_t)0, min((int64_t)8, rem - off));
     G[j] = load8<2, FULL>(grad + off * 2, cnt[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < NSUB; ++j) {
+    const int off = j * SUB + lane * EPL;
     W[j] = load8<2, FULL>(w16 + off * 2, cnt[j]);
     E[j] = load8<EB, FULL>(ecc + off * EB, cnt[j]);
 #pragma unroll
@@ -339,7 +385,8 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
   }
   // a NaN or infinite stored scale (the encoder writes NaN only for an all-NaN
   // block) makes NaN or infinite states: the rule then takes its IEEE form
-  const bool ieee = __builtin_amdgcn_ballot_w64(nonfinite) != 0;
+  // (or the rule finds the tile's gradients outside its fast range)
+  const bool ieee = (__builtin_amdgcn_ballot_w64(nonfinite) != 0) || R::tile_slow(c, G);
 
   float X[NS][NSUB][EPL];                  // what each state's codes are taken from
   float own_max[NS];
@@ -472,11 +519,17 @@ __device__ __forceinline__ void probe_tile(const TensorDesc& d, int64_t e0, int 
   DW<2 * EB> E[NSUB];
   DW<2> MQ[NSUB], VQ[NSUB];
   int cnt[NSUB];
+  // the gradients first: the rule's tile-wide range check waits for them
+  // only (the vector memory counter retires loads in issue order)
 #pragma unroll
   for (int j = 0; j < NSUB; ++j) {
     const int off = j * SUB + lane * EPL;
     cnt[j] = FULL ? 8 : (int)max((int64_t)0, min((int64_t)8, rem - off));
     G[j] = load8<2, FULL>(grad + off * 2, cnt[j]);
+  }
+#pragma unroll
+  for (int j = 0; j < NSUB; ++j) {
+    const int off = j * SUB + lane * EPL;
     W[j] = load8<2, FULL>(w16 + off * 2, cnt[j]);
     E[j] = load8<EB, FULL>(ecc + off * EB, cnt[j]);
     MQ[j] = load8<1, FULL>(mq + off, cnt[j]);

@@ -21,6 +21,7 @@
 #include "../../include/foamd.h"
 #include "fo_kernels.hpp"
 #include "fo_slots.hpp"
+#include "fo_grad16.hpp"
 
 using namespace fo;
 
@@ -385,10 +386,12 @@ int launch_check(const char* what) {
 // That keeps rcp_refined, div_refined and sqrt_corrected in their exact
 // ranges.  When no such range exists (eps not a normal number, b1 or b2 tiny,
 // ibc2 huge) every wave takes the IEEE form.
-static void adamw_fast_range(AdamWConsts* c) {
+static void adamw_fast_range(AdamWConsts* c, int wfmt) {
   c->fast = 0;
   c->g_lo2 = 0xFFFFFFFEu;
   c->g_hi = 0.0f;
+  c->g16_lo = 0xFFFFu;     // every nonzero pattern is below: no fast range
+  c->g16_hi = 0u;
   const double b1 = c->b1, b2 = c->b2, omb1 = c->omb1, omb2 = c->omb2, eps = c->eps, ibc2 = c->ibc2;
   if (!(eps >= 0x1p-126) || !(omb1 > 0.0) || !(omb2 > 0.0) || !(ibc2 > 0.0 && ibc2 < 0x1p35)) return;
   if (b1 != 0.0 && b1 < 0x1p-17) return;
@@ -403,6 +406,8 @@ static void adamw_fast_range(AdamWConsts* c) {
   std::memcpy(&blo, &flo, 4);
   c->g_lo2 = 2u * blo - 2u;
   c->g_hi = fhi;
+  c->g16_lo = grad16_last(wfmt == FO_BF16, flo, true);
+  c->g16_hi = grad16_last(wfmt == FO_BF16, fhi, false);
   c->fast = 1;
 }
 
@@ -596,7 +601,7 @@ static AdamWConsts adamw_consts(const fo_adamw_hparams* hp) {
   c.eps = (float)hp->eps;
   c.wd = hp->l2_decay ? (float)hp->weight_decay : 0.0f;
   if (hp->l2_decay) c.decay = 1.0f;                 // Adam: no decoupled decay
-  adamw_fast_range(&c);
+  adamw_fast_range(&c, hp->wfmt);
   return c;
 }
 
