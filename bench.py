@@ -223,10 +223,14 @@ def cpu_baseline(cfg, segments=96, seg=1 << 20, log=print):
 # HBM ceilings on this device: plain streams next to the fused step
 # ---------------------------------------------------------------------------
 def hbm_ceiling(read_bytes_per_elem, write_bytes_per_elem, steps=10, gib=16, log=print):
-    """Read-only, write-only and copy streams over `gib` GiB buffers in the
-    fused kernels' access style (fo_hbm_probe), timed with HIP events on the
-    launch stream, and the estimate for the fused step's read/write mix if
-    reads and writes shared the time: (R + W) / (R / read + W / write)."""
+    """Plain HBM streams (fo_hbm_probe) over `gib` GiB buffers: read-only,
+    write-only, copy and in-place update, each with one wave per 1, 2, 4 and
+    8 KiB, timed with HIP events on the launch stream.  From the best rates a
+    stream model of the fused step: its written streams are updated in place
+    (each written byte is read first), the rest is read only, and the two
+    kinds of traffic share the time:
+        estimate = (I + R) / (I / inplace + R / read),
+    I = 2 * written bytes, R = read bytes - written bytes (per element)."""
     import torch
 
     from precision_optimizer_state_amd import binding as B
@@ -235,25 +239,34 @@ def hbm_ceiling(read_bytes_per_elem, write_bytes_per_elem, steps=10, gib=16, log
     src = torch.empty(n, dtype=torch.uint8, device="cuda")
     dst = torch.empty(n, dtype=torch.uint8, device="cuda")
     B.fo_hbm_probe(src, None, n, "write", 0x5A5A5A5A)        # defined contents
+    B.fo_hbm_probe(dst, None, n, "write", 0x3C3C3C3C)
     stream = torch.cuda.current_stream()
-    out = {}
-    for mode, moved in (("read", n), ("write", n), ("copy", 2 * n)):
-        for _ in range(2):
-            B.fo_hbm_probe(dst, src, n, mode, 0xFFFFFFFF)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(steps):
-            B.fo_hbm_probe(dst, src, n, mode, 0xFFFFFFFF)
-        b.record(stream)
-        torch.cuda.synchronize()
-        out[f"{mode}_gbs"] = moved * steps / (a.elapsed_time(b) * 1e-3) / 1e9
+    out = {"buffer_gib": gib, "chunks": {}}
+    for kib in (1, 2, 4, 8):
+        row = {}
+        for mode, moved in (("read", n), ("write", n), ("copy", 2 * n), ("inplace", 2 * n)):
+            for _ in range(2):
+                B.fo_hbm_probe(dst, src, n, mode, 0xFFFFFFFF, chunk_kib=kib)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(steps):
+                B.fo_hbm_probe(dst, src, n, mode, 0xFFFFFFFF, chunk_kib=kib)
+            b.record(stream)
+            torch.cuda.synchronize()
+            row[f"{mode}_gbs"] = moved * steps / (a.elapsed_time(b) * 1e-3) / 1e9
+        out["chunks"][f"{kib}k"] = row
+        log("hbm ceiling, {} KiB per wave: read {read_gbs:.0f}, write {write_gbs:.0f}, copy {copy_gbs:.0f}, "
+            "in place {inplace_gbs:.0f} GB/s".format(kib, **row))
     del src, dst
     torch.cuda.empty_cache()
-    r, w = read_bytes_per_elem, write_bytes_per_elem
-    out["mix_estimate_gbs"] = (r + w) / (r / out["read_gbs"] + w / out["write_gbs"])
-    out["buffer_gib"] = gib
-    log("hbm ceiling: read {read_gbs:.0f}, write {write_gbs:.0f}, copy {copy_gbs:.0f} GB/s; "
-        "read/write mix estimate {mix_estimate_gbs:.0f} GB/s".format(**out))
+    for mode in ("read", "write", "copy", "inplace"):
+        out[f"best_{mode}_gbs"] = max(r[f"{mode}_gbs"] for r in out["chunks"].values())
+    inplace = 2.0 * write_bytes_per_elem
+    read_only = read_bytes_per_elem - write_bytes_per_elem
+    out["stream_model_gbs"] = (inplace + read_only) / (inplace / out["best_inplace_gbs"] +
+                                                       read_only / out["best_read_gbs"])
+    log("hbm ceiling: best read {best_read_gbs:.0f}, write {best_write_gbs:.0f}, copy {best_copy_gbs:.0f}, "
+        "in place {best_inplace_gbs:.0f} GB/s; stream model of the step {stream_model_gbs:.0f} GB/s".format(**out))
     return out
 
 
@@ -515,8 +528,8 @@ def main(argv=None):
         ceil = hbm_ceiling(rb, wb, log=log)
         if probe_gbs:
             ceil["stream_probe_gbs"] = probe_gbs
-        ceil["fused_vs_mix_estimate"] = achieved / ceil["mix_estimate_gbs"]
-        ceil["fused_vs_copy"] = achieved / ceil["copy_gbs"]
+        ceil["fused_vs_stream_model"] = achieved / ceil["stream_model_gbs"]
+        ceil["fused_vs_best_copy"] = achieved / ceil["best_copy_gbs"]
         line["ceiling"] = ceil
     if not args.no_cpu_baseline:
         del states, lists

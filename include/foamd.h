@@ -86,9 +86,10 @@
 extern "C" {
 #endif
 
-#define FO_ABI_VERSION 3   /* 2: l2_decay in fo_adamw_hparams; dampening, nesterov in fo_sgdm_hparams;
+#define FO_ABI_VERSION 4   /* 2: l2_decay in fo_adamw_hparams; dampening, nesterov in fo_sgdm_hparams;
                               3: correctly rounded quotients in the update and the codecs, NaN codes 0,
-                                 NaN-only short last blocks keep a NaN scale, SGD momentum 0 as torch */
+                                 NaN-only short last blocks keep a NaN scale, SGD momentum 0 as torch;
+                              4: fo_hbm_probe takes a chunk size (and an in-place mode) */
 
 enum fo_status {
   FO_OK = 0,
@@ -277,17 +278,21 @@ int fo_stream_probe(const fo_adamw_tensor* list, int32_t count, int32_t wfmt,
 
 /*
  * fo_hbm_probe -- measurement only.
- * Plain HBM streams in the fused kernels' access style (one wave per 8-KiB
- * chunk, 16-byte nontemporal accesses), to measure the attainable read,
- * write and copy bandwidth next to the fused step:
+ * Plain HBM streams in the fused kernels' access style (16-byte nontemporal
+ * accesses, each instruction covering 1 KiB), one wave per chunk of
+ * chunk_kib KiB (1, 2, 4 or 8), to measure the attainable bandwidth next to
+ * the fused step:
  *   mode 0: read `bytes` of src (dst receives at most one 4-byte word, only
  *           if the XOR of all words read equals `key`);
  *   mode 1: write `key` over `bytes` of dst;
- *   mode 2: copy `bytes` from src to dst.
- * bytes must be a multiple of 8192; pointers 16-byte aligned device memory.
- * Errors: FO_EINVAL, FO_EHIP.
+ *   mode 2: copy `bytes` from src to dst, each word XOR-ed with `key`;
+ *   mode 3: update `bytes` of dst in place (each word XOR-ed with `key`;
+ *           src is ignored).
+ * bytes must be a multiple of the chunk; pointers 16-byte aligned device
+ * memory.  Errors: FO_EINVAL, FO_EHIP.
  */
-int fo_hbm_probe(void* dst, const void* src, int64_t bytes, int32_t mode, uint32_t key, void* stream);
+int fo_hbm_probe(void* dst, const void* src, int64_t bytes, int32_t mode, int32_t chunk_kib,
+                 uint32_t key, void* stream);
 
 /*
  * fo_selftest -- verification of the exact fast arithmetic the fused kernels

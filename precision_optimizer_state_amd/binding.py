@@ -60,7 +60,7 @@ class SGDMHParams(ctypes.Structure):
 
 
 _lib = None
-ABI_VERSION = 3          # FO_ABI_VERSION of include/foamd.h (struct layouts below)
+ABI_VERSION = 4          # FO_ABI_VERSION of include/foamd.h (struct layouts below)
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:
@@ -81,7 +81,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.fo_fused_adamw_step_noalloc.argtypes = [ctypes.POINTER(AdamWTensor), c_int32, ctypes.POINTER(AdamWHParams), P]
     lib.fo_fused_sgdm_step.argtypes = [ctypes.POINTER(SGDMTensor), c_int32, ctypes.POINTER(SGDMHParams), P]
     lib.fo_stream_probe.argtypes = [ctypes.POINTER(AdamWTensor), c_int32, c_int32, c_int32, c_uint32, P]
-    lib.fo_hbm_probe.argtypes = [P, P, c_int64, c_int32, c_uint32, P]
+    lib.fo_hbm_probe.argtypes = [P, P, c_int64, c_int32, c_int32, c_uint32, P]
     lib.fo_selftest.argtypes = [c_int, c_uint32, ctypes.c_uint64, ctypes.POINTER(ctypes.c_uint64), P]
     for name in EXPORTS:
         getattr(lib, name).restype = c_int
@@ -249,14 +249,15 @@ def fo_stream_probe(tlist, wfmt="bf16", ecc_bits=8, key=0, stream=None) -> None:
                                   _stream(stream)))
 
 
-HBM_PROBE_MODES = {"read": 0, "write": 1, "copy": 2}
+HBM_PROBE_MODES = {"read": 0, "write": 1, "copy": 2, "inplace": 3}
 
 
-def fo_hbm_probe(dst, src, nbytes, mode="copy", key=0, stream=None) -> None:
-    """Measurement only: plain read / write / copy streams of nbytes (a
-    multiple of 8192) in the fused kernels' access style."""
-    _check(load().fo_hbm_probe(_ptr(dst), _ptr(src), int(nbytes), _fmt(mode, HBM_PROBE_MODES), int(key),
-                               _stream(stream)))
+def fo_hbm_probe(dst, src, nbytes, mode="copy", key=0, chunk_kib=8, stream=None) -> None:
+    """Measurement only: plain read / write / copy / in-place streams of nbytes
+    (a multiple of the chunk) in the fused kernels' access style, one wave
+    per chunk of chunk_kib (1, 2, 4 or 8) KiB."""
+    _check(load().fo_hbm_probe(_ptr(dst), _ptr(src), int(nbytes), _fmt(mode, HBM_PROBE_MODES), int(chunk_kib),
+                               int(key), _stream(stream)))
 
 
 def fo_selftest(what: int, lo: int, count: int, stream=None) -> int:

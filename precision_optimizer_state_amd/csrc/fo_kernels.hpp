@@ -556,32 +556,32 @@ __device__ __forceinline__ void probe_tile(const TensorDesc& d, int64_t e0, int 
 }
 
 // ---------------------------------------------------------------------------
-// HBM probe: plain read, write or copy streams with the fused kernels' access
-// style (one wave per 8-KiB chunk, 16-byte nontemporal accesses, each
-// instruction covering 1 KiB)
+// HBM probe: plain read, write, copy or in-place update streams in the fused
+// kernels' access style (16-byte nontemporal accesses, each instruction
+// covering 1 KiB), one wave per chunk of U KiB
 // ---------------------------------------------------------------------------
-constexpr int HBM_PROBE_CHUNK = WAVE * 16 * 8;   // bytes per wave
-__global__ void __launch_bounds__(WAVE) k_hbm_probe(uint8_t* __restrict__ dst, const uint8_t* __restrict__ src,
-                                                    int64_t chunk0, int mode, uint32_t key) {
+template <int U>
+__global__ void __launch_bounds__(WAVE) k_hbm_probe(uint8_t* dst, const uint8_t* src, int64_t chunk0, int mode,
+                                                    uint32_t key) {
   const int lane = threadIdx.x;
-  const int64_t base = (chunk0 + blockIdx.x) * HBM_PROBE_CHUNK + lane * 16;
+  const int64_t base = (chunk0 + blockIdx.x) * (int64_t)(1024 * U) + lane * 16;
   if (mode == 1) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < U; ++i)
       __builtin_nontemporal_store(u32x4{key, key, key, key}, (gp<u32x4>)(dst + base + i * 1024));
     return;
   }
-  u32x4 v[8];
+  u32x4 v[U];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = __builtin_nontemporal_load((gp<const u32x4>)(src + base + i * 1024));
-  if (mode == 2) {
+  for (int i = 0; i < U; ++i) v[i] = __builtin_nontemporal_load((gp<const u32x4>)(src + base + i * 1024));
+  if (mode >= 2) {                         // 2: copy to dst; 3: dst updated in place (src == dst)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) __builtin_nontemporal_store(v[i], (gp<u32x4>)(dst + base + i * 1024));
+    for (int i = 0; i < U; ++i) __builtin_nontemporal_store(v[i] ^ key, (gp<u32x4>)(dst + base + i * 1024));
     return;
   }
   uint32_t acc = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
+  for (int i = 0; i < U; ++i) acc ^= v[i].x ^ v[i].y ^ v[i].z ^ v[i].w;
   if (acc == key) ((gp<uint32_t>)dst)[0] = acc;   // keeps the loads; key is chosen not to match
 }
 

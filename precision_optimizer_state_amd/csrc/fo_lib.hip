@@ -764,19 +764,29 @@ int fo_stream_probe(const fo_adamw_tensor* list, int32_t count, int32_t wfmt, in
   return use_entry(e, s);
 }
 
-int fo_hbm_probe(void* dst, const void* src, int64_t bytes, int32_t mode, uint32_t key, void* stream) {
+int fo_hbm_probe(void* dst, const void* src, int64_t bytes, int32_t mode, int32_t chunk_kib, uint32_t key,
+                 void* stream) {
   g_err.clear();
-  if (mode < 0 || mode > 2) return fail(FO_EINVAL, "bad probe mode %d", mode);
-  if (bytes < 0 || bytes % HBM_PROBE_CHUNK != 0)
-    return fail(FO_EINVAL, "bytes must be a non-negative multiple of %d", HBM_PROBE_CHUNK);
+  if (mode < 0 || mode > 3) return fail(FO_EINVAL, "bad probe mode %d", mode);
+  if (chunk_kib != 1 && chunk_kib != 2 && chunk_kib != 4 && chunk_kib != 8)
+    return fail(FO_EINVAL, "chunk must be 1, 2, 4 or 8 KiB (got %d)", chunk_kib);
+  const int64_t chunk = 1024 * (int64_t)chunk_kib;
+  if (bytes < 0 || bytes % chunk != 0) return fail(FO_EINVAL, "bytes must be a non-negative multiple of %lld",
+                                                   (long long)chunk);
   if (bytes == 0) return FO_OK;
-  if ((mode != 1 && !src) || !dst) return fail(FO_EINVAL, "NULL pointer");
+  if (mode == 3) src = dst;                                     // in place: dst is read and rewritten
+  if (!dst || (mode != 1 && !src)) return fail(FO_EINVAL, "NULL pointer");
   if (!aligned(dst, 16) || (src && !aligned(src, 16))) return fail(FO_EINVAL, "pointer not 16-byte aligned");
   hipStream_t s = as_stream(stream);
-  const int64_t chunks = bytes / HBM_PROBE_CHUNK;
+  const int64_t chunks = bytes / chunk;
+  auto* d = (uint8_t*)dst;
+  auto* r = (const uint8_t*)src;
   for (int64_t c0 = 0; c0 < chunks; c0 += kLaunchTiles) {
     const int grid = (int)std::min<int64_t>(kLaunchTiles, chunks - c0);
-    hipLaunchKernelGGL(k_hbm_probe, grid, WAVE, 0, s, (uint8_t*)dst, (const uint8_t*)src, c0, (int)mode, key);
+    if (chunk_kib == 1) hipLaunchKernelGGL(k_hbm_probe<1>, grid, WAVE, 0, s, d, r, c0, (int)mode, key);
+    else if (chunk_kib == 2) hipLaunchKernelGGL(k_hbm_probe<2>, grid, WAVE, 0, s, d, r, c0, (int)mode, key);
+    else if (chunk_kib == 4) hipLaunchKernelGGL(k_hbm_probe<4>, grid, WAVE, 0, s, d, r, c0, (int)mode, key);
+    else hipLaunchKernelGGL(k_hbm_probe<8>, grid, WAVE, 0, s, d, r, c0, (int)mode, key);
   }
   return launch_check("k_hbm_probe launch");
 }

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(B.EXPORTS)
-    assert lib.fo_abi_version() == B.ABI_VERSION == 3
+    assert lib.fo_abi_version() == B.ABI_VERSION == 4
 
 
 def test_struct_layouts_match_header():
