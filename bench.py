@@ -271,6 +271,57 @@ def hbm_ceiling(read_bytes_per_elem, write_bytes_per_elem, steps=10, gib=16, log
 
 
 # ---------------------------------------------------------------------------
+# rocprofv3 output -> short text summaries (the files under profiles/)
+# ---------------------------------------------------------------------------
+def rocprof_summary(d, kernel="k_fused_adamw", launches_per_step=0, timed_steps=0):
+    """Summary of the rocprofv3 CSV files in directory d: the kernel
+    statistics (top entries), the trace of `kernel` (dispatches, average
+    duration, and with launches_per_step / timed_steps the summed kernel time
+    of each of the last timed_steps steps), and the counter totals of every
+    kernel whose name contains `kernel` or k_hbm_probe."""
+    import collections
+    import csv
+    import glob
+
+    lines = []
+    for f in sorted(glob.glob(os.path.join(d, "*_kernel_stats.csv"))):
+        rows = list(csv.DictReader(open(f)))
+        lines.append(f"kernel statistics ({os.path.basename(f)}), top entries:")
+        lines.append("| Kernel | Calls | Total (ns) | Average (ns) | % |")
+        lines.append("|---|---|---|---|---|")
+        for r in rows[:6]:
+            lines.append(f"| {r['Name'][:70]} | {r['Calls']} | {r['TotalDurationNs']} | "
+                         f"{float(r['AverageNs']):.0f} | {r['Percentage']} |")
+    for f in sorted(glob.glob(os.path.join(d, "*_kernel_trace.csv"))):
+        rows = [r for r in csv.DictReader(open(f)) if kernel in r["Kernel_Name"]]
+        durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
+        if not durs:
+            continue
+        lines.append(f"trace of {kernel} ({os.path.basename(f)}): {len(durs)} dispatches, "
+                     f"average {sum(durs) / len(durs):.0f} ns")
+        if launches_per_step and timed_steps and len(durs) >= launches_per_step * timed_steps:
+            tail = durs[-launches_per_step * timed_steps:]
+            per = [sum(tail[i * launches_per_step:(i + 1) * launches_per_step]) for i in range(timed_steps)]
+            lines.append(f"  last {timed_steps} steps ({launches_per_step} dispatches each): summed kernel time "
+                         f"per step mean {sum(per) / len(per) / 1e6:.4f} ms, min {min(per) / 1e6:.4f}, "
+                         f"max {max(per) / 1e6:.4f}")
+    for f in sorted(glob.glob(os.path.join(d, "*_counter_collection.csv"))):
+        tot = collections.defaultdict(float)
+        disp = collections.defaultdict(set)
+        for r in csv.DictReader(open(f)):
+            name = r["Kernel_Name"]
+            key = kernel if kernel in name else ("k_hbm_probe" if "k_hbm_probe" in name else None)
+            if key:
+                tot[(key, r["Counter_Name"])] += float(r["Counter_Value"])
+                disp[key].add(r["Dispatch_Id"])
+        lines.append(f"counters ({os.path.basename(f)}):")
+        for (key, counter), v in sorted(tot.items()):
+            nd = len(disp[key])
+            lines.append(f"  {key} {counter}: total {v:.0f} over {nd} dispatches, per dispatch {v / nd:.1f}")
+    return "\n".join(lines)
+
+
+# ---------------------------------------------------------------------------
 # optimizer variants on the same byte streams (hyperparameter additions)
 VARIANTS = {
     "adam_l2": ("adamw", {"l2_decay": True}),
@@ -383,7 +434,14 @@ def main(argv=None):
                     help="time FlashAdamW/FlashSGD.step() end to end instead of the raw fused call "
                          "(with --release: the gradient-release hooks in backward order)")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--rocprof-summary", metavar="DIR", default=None,
+                    help="print a text summary of the rocprofv3 CSV files in DIR and exit (no GPU use)")
+    ap.add_argument("--kernel", default="k_fused_adamw", help="kernel name filter of --rocprof-summary")
+    ap.add_argument("--launches-per-step", type=int, default=0, help="with --rocprof-summary: per-step sums")
     args = ap.parse_args(argv)
+    if args.rocprof_summary:
+        print(rocprof_summary(args.rocprof_summary, args.kernel, args.launches_per_step, args.steps))
+        return 0
 
     def log(msg):
         if not args.quiet:
@@ -465,12 +523,13 @@ def main(argv=None):
         log(f"stream probe (same bytes, no arithmetic): {pms:.3f} ms, {probe_gbs:.0f} GB/s")
 
     if args.copy_calib:
-        src = torch.empty(1 << 30, dtype=torch.float32, device="cuda")
+        # known traffic for the counters' scale: 4 GiB read + 4 GiB written per call
+        src = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            B.fo_hbm_probe(dst, src, 4 << 30, "copy", 0)
         torch.cuda.synchronize()
-        log("copy calibration: 3 x 4 GiB device copies done")
+        log("copy calibration: 3 x 4 GiB k_hbm_probe copies done")
         del src, dst
 
     line = {
