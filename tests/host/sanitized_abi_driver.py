@@ -70,7 +70,7 @@ for trial in range(300):
     count = rng.choice([1, 2, 3, 17, 64, 291, 300])
     sizes = [rng.choice([0, 1, 31, 32, 33, 2047, 2048, 2049, rng.randrange(1, 1 << 24),
                          (1 << 31) + 77, 1 << 40]) for _ in range(count)]
-    kind = trial % 4
+    kind = trial % 5
     if kind == 0:
         rc = lib.fo_fused_adamw_step(fake_adamw_list(sizes), count, ctypes.byref(hp if trial % 8 else hp_l2), None)
         want = {B.FO_EHIP} if any(sizes) else {B.FO_OK}
@@ -81,12 +81,30 @@ for trial in range(300):
     elif kind == 2:
         rc = lib.fo_fused_adamw_step(fake_adamw_list(sizes, misalign=True), count, ctypes.byref(hp), None)
         want = {B.FO_EINVAL} if sizes[count // 2] else ({B.FO_EHIP} if any(sizes) else {B.FO_OK})
-    else:
+    elif kind == 3:
         rc = lib.fo_fused_sgdm_step(fake_sgdm_list(sizes), count, ctypes.byref(sh), None)
         want = {B.FO_EHIP} if any(sizes) else {B.FO_OK}
+    else:
+        # the allocation-free entry point: the same validation into its static
+        # host arrays, then its first device call
+        lst = fake_adamw_list(sizes, overlap=trial % 10 == 4)
+        rc = lib.fo_fused_adamw_step_noalloc(lst, count, ctypes.byref(hp), None)
+        want = {B.FO_EALIAS} if overlaps(lst, sizes) else ({B.FO_EHIP} if any(sizes) else {B.FO_OK})
     assert rc in want, (trial, kind, sizes[:5], rc, want, B.fo_last_error())
     seen.add((kind, rc))
     assert isinstance(B.fo_last_error(), str)
+
+# the allocation-free entry point takes at most 2048 tensors, and a full-size
+# list fills its static descriptor and range arrays to the end
+assert lib.fo_fused_adamw_step_noalloc(fake_adamw_list([64] * 2049), 2049, ctypes.byref(hp), None) == B.FO_EINVAL
+assert lib.fo_fused_adamw_step_noalloc(fake_adamw_list([2049] * 2048), 2048, ctypes.byref(hp), None) == B.FO_EHIP
+assert lib.fo_cache_pinned() == 0
+
+# the bandwidth probe validates mode, chunk and size before its first device call
+assert lib.fo_hbm_probe(P(BASE), P(BASE + (1 << 40)), 1 << 20, 4, 8, 0, None) == B.FO_EINVAL
+assert lib.fo_hbm_probe(P(BASE), P(BASE + (1 << 40)), 1 << 20, 2, 3, 0, None) == B.FO_EINVAL
+assert lib.fo_hbm_probe(P(BASE), P(BASE + (1 << 40)), (1 << 20) + 1024, 2, 2, 0, None) == B.FO_EINVAL
+assert lib.fo_hbm_probe(P(BASE), None, 1 << 20, 3, 1, 0, None) == B.FO_EHIP
 
 # element counts beyond any device memory are rejected before any size arithmetic
 for huge in ((1 << 56) + 1, 1 << 62, (1 << 63) - 1):
