@@ -376,15 +376,15 @@ int launch_check(const char* what) {
 //                                              linear code -128: 128/127 * 65504)
 //   variance  v_hat  in {0} u [2^-66, 2^33]
 // Conditions, each with a margin for the rounding of the products:
-//   v = b2*v_hat + (1-b2)*g*g outside (0, 2^-96) (the corrected square root
-//     is exact) and so small that den = sqrt(v)*ibc2 + eps <= 2^52;
+//   v = b2*v_hat + (1-b2)*g*g outside (0, 2^-96) and at most 2^100 (the
+//     square root from the successor's estimate is exact there) and so
+//     small that den = sqrt(v)*ibc2 + eps <= 2^52;
 //   a nonzero m = b1*m_hat + (1-b1)*g at least 2^-73: both terms are 0 or at
 //     least 2^-50, and a sum of such floats that does not vanish is a nonzero
 //     multiple of 2^-73;
 //   so every nonzero quotient m/den is a normal number (>= 2^-125), and
 //   |m/den| < 2^119 because den >= eps.
-// That keeps rcp_refined, div_refined and sqrt_corrected in their exact
-// ranges.  When no such range exists (eps not a normal number, b1 or b2 tiny,
+// That keeps rcp_refined, div_refined and sqrt_fast in their exact ranges.  When no such range exists (eps not a normal number, b1 or b2 tiny,
 // ibc2 huge) every wave takes the IEEE form.
 static void adamw_fast_range(AdamWConsts* c, int wfmt) {
   c->fast = 0;
