@@ -310,3 +310,47 @@ def test_sgd_momentum0_ignores_dampening_like_torch():
         want = th0 - np.float32(0.1) * (gw + np.float32(1e-4) * th0)
         w16, ecc = O.split_weights(want)
         assert np.array_equal(st["w16"], w16) and np.array_equal(st["ecc"], ecc)
+
+
+@pytest.mark.parametrize("fmt,ecc_bits,codec", [("bf16", 8, "companded"), ("bf16", 16, "linear"),
+                                                ("fp16", 8, "companded")])
+def test_adamw_step_first_step_closed_form(fmt, ecc_bits, codec):
+    # The composition of adamw_step, pinned at step 1 from fresh states: the
+    # zero codes and scales decode to m = v = 0, so the new moments are
+    # m1 = RN((1-b1)*g), v1 = RN((1-b2)*RN(g*g)) and the new master is
+    # RN(RN(th*decay) - RN(step_size*RN(m1/d))), d = RN(RN(sqrt(v1)*ibc2) + eps),
+    # computed here on exact rationals.  The step must then hold exactly the
+    # split of that master and the block scales and codes of m1 and v1 (a
+    # wiring mistake -- old moments encoded, scales swapped, v's scale taken
+    # from v instead of its root, the split fed the pre-update master -- fails).
+    rng = np.random.default_rng(61)
+    n = 101                                            # three full blocks and a ragged one
+    x = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    g32 = (rng.standard_t(3, n) * 1e-3).astype(np.float32)
+    if fmt == "fp16":
+        gb = g32.astype(np.float16).view(np.uint16)
+    else:
+        gb = torch.tensor(g32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01, step=1)
+    st = fresh_adamw_state(x, fmt, ecc_bits)
+    out = O.adamw_step(st, gb, hp, fmt, ecc_bits, codec)
+    S = O.adamw_scalars(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"], hp["step"])
+    theta0 = O.reconstruct_weights(st["w16"], st["ecc"], fmt, ecc_bits)
+    g = (gb.view(np.float16).astype(np.float32) if fmt == "fp16"
+         else (gb.astype(np.uint32) << 16).view(np.float32))          # exact widening
+    F = lambda v: Fraction(float(v))
+    m1 = np.empty(n, np.float32); v1 = np.empty(n, np.float32); th1 = np.empty(n, np.float32)
+    for i in range(n):
+        G = F(g[i])
+        M = rn32(F(S.omb1) * G)
+        V = rn32(F(S.omb2) * rn32(G * G))
+        D = rn32(rn32(rn32_sqrt(V) * F(S.ibc2)) + F(S.eps))
+        T = rn32(rn32(F(theta0[i]) * F(S.decay)) - rn32(F(S.step_size) * rn32(M / D)))
+        m1[i], v1[i], th1[i] = f32(M), f32(V), f32(T)
+    w_want, e_want = O.split_weights(th1, fmt, ecc_bits)
+    ms, vs = O.block_scales(m1, "m"), O.block_scales(v1, "v")
+    assert np.array_equal(out["w16"], w_want) and np.array_equal(out["ecc"], e_want)
+    assert np.array_equal(out["m_s"], ms) and np.array_equal(out["v_s"], vs)
+    assert np.array_equal(out["m_q"], O.encode_momentum(m1, ms, codec))
+    assert np.array_equal(out["v_q"], O.encode_variance(v1, vs, codec))
+    assert np.count_nonzero(out["m_q"]) > n // 2 and np.count_nonzero(out["v_q"]) > n // 2
