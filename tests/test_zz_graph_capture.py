@@ -89,3 +89,36 @@ def test_captured_table_survives_eviction_by_other_lists():
         for k in KEYS:
             assert torch.equal(a[k].view(torch.uint8), b[k].view(torch.uint8)), f"replay {r}: {k} differs"
     print("captured table pinned: replays after 1100 other lists bitwise equal to eager calls", flush=True)
+
+
+def test_captured_sgdm_step_replays_match_eager_calls():
+    """fo_fused_sgdm_step captured after a warm-up call: every replay equals
+    an eager call on a copy of the state, and the capture pins the list's
+    launch table."""
+    from precision_optimizer_state_amd.state import alloc_sgdm_state
+    sizes = [250_000 + 13, 4097, 33]
+    sl = []
+    for i, n in enumerate(sizes):
+        st = alloc_sgdm_state(n)
+        B.fo_split_weights(device_weights(f"sgdcap{i}", 0, n), st["w16"], st["ecc"], "bf16", 8)
+        device_grads(f"sgdcap{i}", 0, 1, n, "normal_outliers", "bf16", out=st["grad"])
+        sl.append(st)
+    hp = B.sgdm_hparams(0.1, 0.9, 1e-4, 2, nesterov=True)
+    tl_a = B.SGDMList(sl)
+    B.fo_fused_sgdm_step(tl_a, hp)                          # warm-up: the launch table exists
+    torch.cuda.synchronize()
+    twin = [{k: (v.clone() if v is not None else None) for k, v in st.items()} for st in sl]
+    tl_b = B.SGDMList(twin)
+    pinned = B.load().fo_cache_pinned()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        B.fo_fused_sgdm_step(tl_a, hp)
+    assert B.load().fo_cache_pinned() == pinned + 1
+    for r in range(3):
+        g.replay()
+        B.fo_fused_sgdm_step(tl_b, hp)
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(sl, twin)):
+            for k in ("w16", "ecc", "b_q", "b_s"):
+                assert torch.equal(a[k].view(torch.uint8), b[k].view(torch.uint8)), f"replay {r}: tensor {i} {k} differs"
+    print("captured SGD-M step: 3 replays bitwise equal to eager calls", flush=True)

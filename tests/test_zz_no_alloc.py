@@ -86,3 +86,22 @@ def test_noalloc_captured_call_replays_its_own_table():
             for k in KEYS:
                 assert torch.equal(sa[k].view(torch.uint8), sb[k].view(torch.uint8)), (r, i, k)
     print("captured no-alloc call: 3 replays bitwise equal to cached eager calls", flush=True)
+
+
+def test_noalloc_full_list_of_2048_tensors():
+    """The largest list the allocation-free step takes: 2048 tensors (54
+    kernel-argument chunks of descriptors, ragged sizes), bitwise equal to the
+    cached step."""
+    import numpy as np
+    rng = np.random.default_rng(2048)
+    sizes = [int(s) for s in rng.integers(1, 6000, 2048)]
+    a = _states(sizes, "nafull")
+    b = _clone(a)
+    hp = dict(HP, step=1)
+    B.fo_fused_adamw_step(a, hp)
+    B.fo_fused_adamw_step_noalloc(b, hp)
+    torch.cuda.synchronize()
+    for i, (sa, sb) in enumerate(zip(a, b)):
+        for k in KEYS:
+            assert torch.equal(sa[k].view(torch.uint8), sb[k].view(torch.uint8)), (i, k)
+    print("no-alloc step over 2048 tensors bitwise equal to the cached step", flush=True)
