@@ -11,6 +11,9 @@
 //   * Per-block arithmetic (scale rounding, reciprocals) is done once per
 //     block: lane 4Q+j owns block (sub-tile j, quad Q), and the results are
 //     broadcast back to the quad with one DPP quad permute per sub-tile.
+//   * Every quotient and square root of the update and the codecs is
+//     correctly rounded, from corrected hardware estimates (fo_device.hpp)
+//     whose exactness fo_selftest checks on the device.
 //   * A launch covers a range of the step's wave tiles with one wave per tile
 //     (the host issues one launch per 2^18 tiles; the tile loop below also
 //     serves smaller grids).  A tile never crosses a tensor, and the last tile
@@ -925,6 +928,8 @@ __global__ void __launch_bounds__(WG) k_dequantize(const uint8_t* __restrict__ c
 // what 4: the same division with b an fp16 value (a block scale) and |a| <= b
 // what 5: as 3, but only pairs whose quotient is a nonzero subnormal: the
 //         range the AdamW step's guard keeps out of the fast form
+// what 6: sqrt_fast (from the successor's estimate) vs the IEEE square root
+//         on the f32 patterns [lo, lo+count)
 __device__ __forceinline__ uint64_t splitmix64(uint64_t x) {
   x += 0x9E3779B97F4A7C15ull;
   x = (x ^ (x >> 30)) * 0xBF58476D1CE4E5B9ull;
