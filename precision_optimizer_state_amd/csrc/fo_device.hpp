@@ -72,11 +72,13 @@ __device__ __forceinline__ float widen(uint32_t w, int half) {
 // ECC decode: theta' (already widened to f32, exact) + rho -> f32 master
 // ---------------------------------------------------------------------------
 // The same decode straight from the packed words for bf16: one byte permute
-// forms u = (theta' << 16) | (rho's low bits << SH) from the weight word and
-// the ECC word, and (u ^ B) - B with B the rho field's sign bit turns the
-// field from two's complement into the signed addend, giving
-// bits(theta') + (rho << SH) in one XOR-add.  h: the weight's half in
-// `w`; b: rho's byte (ECC8) or half (ECC16) in `e`.
+// (v_perm_b32: bytes 4-7 from `w`, 0-3 from `e`, selector 0x0C gives 0)
+// forms u = (theta' << 16) | (rho's bits << SH) -- rho's byte in bits 8-15
+// for ECC8, its half in bits 0-15 for ECC16 -- and (u ^ B) - B with
+// B = 0x8000, rho's sign bit in both layouts, turns the field from two's
+// complement into the signed addend, giving bits(theta') + (rho << SH) in
+// one XOR-add.  h: the weight's half in `w`; b: rho's byte (ECC8) or half
+// (ECC16) in `e`.
 template <int ECC>
 __device__ __forceinline__ float ecc_decode_bf16_packed(uint32_t w, uint32_t e, int h, int b) {
   uint32_t sel, bias;
