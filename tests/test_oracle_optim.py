@@ -354,3 +354,38 @@ def test_adamw_step_first_step_closed_form(fmt, ecc_bits, codec):
     assert np.array_equal(out["m_q"], O.encode_momentum(m1, ms, codec))
     assert np.array_equal(out["v_q"], O.encode_variance(v1, vs, codec))
     assert np.count_nonzero(out["m_q"]) > n // 2 and np.count_nonzero(out["v_q"]) > n // 2
+
+
+@pytest.mark.parametrize("nesterov,codec", [(False, "companded"), (True, "linear")])
+def test_sgdm_step_first_step_closed_form(nesterov, codec):
+    # The composition of sgdm_step at step 1 (U4): the buffer is set to
+    # d = RN(g + RN(wd*th)) whatever the stored codes hold, and the master
+    # moves by RN(lr*u), u = d (plain) or RN(d + RN(mu*d)) (Nesterov); on
+    # exact rationals here.  The step must hold exactly the split of that
+    # master and the block scales and codes of d.  Stored codes are random
+    # to show step 1 ignores them.
+    rng = np.random.default_rng(62)
+    n = 77
+    x = (rng.standard_normal(n) * 0.02).astype(np.float32)
+    g32 = (rng.standard_normal(n) * 1e-2).astype(np.float32)
+    gb = torch.tensor(g32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    st = fresh_sgdm_state(x)
+    st["b_q"] = rng.integers(-127, 128, n).astype(np.int8)
+    st["b_s"] = np.full(-(-n // 32), 0x3C00, np.uint16)            # scale 1.0
+    hp = dict(lr=0.1, momentum=0.9, weight_decay=1e-4, dampening=0.0, nesterov=nesterov, step=1)
+    out = O.sgdm_step(st, gb, hp, "bf16", 8, codec)
+    S = O.sgdm_scalars(hp["lr"], hp["momentum"], hp["weight_decay"], 0.0, nesterov)
+    theta0 = O.reconstruct_weights(st["w16"], st["ecc"], "bf16", 8)
+    g = (gb.astype(np.uint32) << 16).view(np.float32)                  # exact widening
+    F = lambda v: Fraction(float(v))
+    d1 = np.empty(n, np.float32); th1 = np.empty(n, np.float32)
+    for i in range(n):
+        T = F(theta0[i])
+        D = rn32(F(g[i]) + rn32(F(S.wd) * T))
+        U = rn32(D + rn32(F(S.mu) * D)) if nesterov else D
+        d1[i], th1[i] = f32(D), f32(rn32(T - rn32(F(S.lr) * U)))
+    w_want, e_want = O.split_weights(th1, "bf16", 8)
+    bs = O.block_scales(d1, "m")
+    assert np.array_equal(out["w16"], w_want) and np.array_equal(out["ecc"], e_want)
+    assert np.array_equal(out["b_s"], bs)
+    assert np.array_equal(out["b_q"], O.encode_momentum(d1, bs, codec))
