@@ -350,6 +350,38 @@ def test_fused_adamw_nan_inf_grads_propagate(fmt, ecc_bits, codec):
     _run_adamw([8192 + 5], 3, HP_C1, fmt, ecc_bits, codec, tag="nan", inject=_inject_specials)
 
 
+def _magnitude_band_grads(fmt, n_tiles, step, seed):
+    """Gradient bit patterns whose wave tile t (2048 elements) holds values of
+    one power-of-two band: |g| in [2^(e0+t), 2^(e0+t+1)) with random signs and
+    significands, e0 the smallest exponent of the format's subnormals.  The
+    bands run through every exponent of the format, so some tiles lie wholly
+    just inside the AdamW fast range, some straddle its edges and take the
+    IEEE form, and some overflow to infinity."""
+    rng = np.random.default_rng([seed, step])
+    e0 = -133 if fmt == "bf16" else -24
+    ex = e0 + np.repeat(np.arange(n_tiles), 2048)
+    mag = np.ldexp(1.0 + rng.random(ex.size), ex)
+    with np.errstate(over="ignore"):                # the top bands overflow to infinity on purpose
+        g = (mag * np.where(rng.random(ex.size) < 0.5, -1.0, 1.0)).astype(np.float32)
+    g[::97] = 0.0                                   # exact zeros stay on the fast path
+    return host_grad_bits(g, fmt)
+
+
+@pytest.mark.parametrize("fmt,hp", [("bf16", HP_C1), ("bf16", HP_LM), ("fp16", HP_C1),
+                                    ("bf16", dict(HP_C1, beta1=0.0, eps=1e-30))])
+def test_fused_adamw_gradient_magnitude_bands(fmt, hp):
+    """Lock-step over gradients swept through every exponent, tile by tile:
+    the per-tile choice between the exact fast form and the IEEE form must
+    never change a result (both must equal the oracle bitwise)."""
+    n_tiles = 262 if fmt == "bf16" else 42
+    sizes = [n_tiles * 2048 + 5]
+    dev = _init_states("adamw", sizes, fmt, 8, f"band_{fmt}")
+    checks = run_lockstep("adamw", dev, 3, lambda i, step: np.concatenate(
+        [_magnitude_band_grads(fmt, n_tiles, step, 91), host_grad_bits(np.full(5, 1e-3, np.float32), fmt)]),
+        hp, fmt, 8, "companded", f"bands {fmt}")
+    print(f"magnitude bands {fmt}: {checks} lock-step checks, all bitwise equal", flush=True)
+
+
 @pytest.mark.parametrize("name,hp", [
     ("beta1_0", dict(lr=1e-3, beta1=0.0, beta2=0.5, eps=1e-8, weight_decay=0.01)),
     ("lr_0", dict(lr=0.0, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1)),
