@@ -368,7 +368,8 @@ def _magnitude_band_grads(fmt, n_tiles, step, seed):
 
 
 @pytest.mark.parametrize("fmt,hp", [("bf16", HP_C1), ("bf16", HP_LM), ("fp16", HP_C1),
-                                    ("bf16", dict(HP_C1, beta1=0.0, eps=1e-30))])
+                                    ("bf16", dict(HP_C1, beta1=0.0, eps=1e-30)),
+                                    ("bf16", dict(HP_C1, l2_decay=True)), ("fp16", dict(HP_LM, l2_decay=True))])
 def test_fused_adamw_gradient_magnitude_bands(fmt, hp):
     """Lock-step over gradients swept through every exponent, tile by tile:
     the per-tile choice between the exact fast form and the IEEE form must
