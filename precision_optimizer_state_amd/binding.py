@@ -109,8 +109,16 @@ def _stream(stream):
 
 
 def _ptr(t) -> c_void_p:
+    """Device address of a contiguous tensor on the current GPU (the library
+    launches on the current device and dereferences the address there)."""
     if t is None:
         return c_void_p(0)
+    if t.device.type != "cuda":
+        raise ValueError(f"tensors passed to the library must live on the GPU (got one on {t.device})")
+    import torch
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"a tensor lives on {t.device}, but the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
     if not t.is_contiguous():
         raise ValueError("tensors passed to the library must be contiguous")
     return c_void_p(t.data_ptr())

@@ -84,3 +84,17 @@ def test_binding_fails_loudly_without_library(tmp_path):
             B.load(str(tmp_path / "missing.so"))
         finally:
             B._lib = B._lib_saved
+
+
+def test_binding_rejects_host_tensors():
+    # the binding hands the library device addresses only: a host tensor is
+    # refused before any call (no GPU needed to check)
+    import torch
+    w = torch.zeros(64, dtype=torch.float32)
+    st = {k: torch.zeros(64, dtype=torch.uint8) for k in ("w16", "ecc", "grad", "m_q", "m_s", "v_q", "v_s")}
+    with pytest.raises(ValueError, match="GPU"):
+        B.fo_split_weights(w, st["w16"], st["ecc"])
+    with pytest.raises(ValueError, match="GPU"):
+        B.AdamWList([st])
+    with pytest.raises(ValueError, match="GPU"):
+        B.SGDMList([{k: st[k] for k in ("w16", "ecc", "grad", "m_q", "m_s")} | {"b_q": st["m_q"], "b_s": st["m_s"]}])
