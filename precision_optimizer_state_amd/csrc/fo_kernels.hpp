@@ -357,7 +357,7 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
   const int own = p * 16 + Q;                                  // owned block within the tile
   const bool own_ok = FULL || (int64_t)own * 32 < rem;
 
-  // ---- issue every load of the tile -------------------------------------
+  // ---- issue the tile's loads ---------------------------------------------
   DW<4> G[NSUB], W[NSUB];
   DW<2 * EB> E[NSUB];
   DW<2> SQ[NS][NSUB];
@@ -370,14 +370,20 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
     cnt[j] = FULL ? 8 : (int)max((int64_t)0, min((int64_t)8, rem - off));
     G[j] = load8<2, FULL>(grad + off * 2, cnt[j]);
   }
-#pragma unroll
-  for (int j = 0; j < NSUB; ++j) {
+  // master, ECC and state codes of sub-tile j
+  auto issue_loads = [&](int j) {
     const int off = j * SUB + lane * EPL;
     W[j] = load8<2, FULL>(w16 + off * 2, cnt[j]);
     E[j] = load8<EB, FULL>(ecc + off * EB, cnt[j]);
 #pragma unroll
     for (int k = 0; k < NS; ++k) SQ[k][j] = load8<1, FULL>(qp[k] + off, cnt[j]);
-  }
+  };
+  // the first half now, the second half once sub-tile 0 is updated: fewer
+  // bytes in flight per wave at once measure about 0.7% faster on every
+  // format than issuing the whole tile up front (one sub-tile ahead is slower)
+  static_assert(NSUB == 4, "loads issued in two halves of two sub-tiles");
+  issue_loads(0);
+  issue_loads(1);
   float dm_own[NS];
   bool nonfinite = false;
 #pragma unroll
@@ -413,6 +419,12 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
       if constexpr (NS == 2) st[NS - 1][i] = decode_state<K1, CODEC>(SQ[NS - 1][j], i, dm[NS - 1], tabs);
     }
     R::update(c, ieee, th, g, st, root);
+    if (j == 0) {                       // the barriers keep the second half here
+      __builtin_amdgcn_sched_barrier(0);
+      issue_loads(2);
+      issue_loads(3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 
     // split the new master and store it
     uint32_t wo[4], eo[ECC / 4];
@@ -530,14 +542,16 @@ __device__ __forceinline__ void probe_tile(const TensorDesc& d, int64_t e0, int 
     cnt[j] = FULL ? 8 : (int)max((int64_t)0, min((int64_t)8, rem - off));
     G[j] = load8<2, FULL>(grad + off * 2, cnt[j]);
   }
-#pragma unroll
-  for (int j = 0; j < NSUB; ++j) {
+  // the same two halves as the fused tile
+  auto issue_loads = [&](int j) {
     const int off = j * SUB + lane * EPL;
     W[j] = load8<2, FULL>(w16 + off * 2, cnt[j]);
     E[j] = load8<EB, FULL>(ecc + off * EB, cnt[j]);
     MQ[j] = load8<1, FULL>(mq + off, cnt[j]);
     VQ[j] = load8<1, FULL>(vq + off, cnt[j]);
-  }
+  };
+  issue_loads(0);
+  issue_loads(1);
   const uint32_t sm = own_ok ? (uint32_t)ms[own] : 0u;
   const uint32_t sv = own_ok ? (uint32_t)vs[own] : 0u;
 #pragma unroll
@@ -549,6 +563,12 @@ __device__ __forceinline__ void probe_tile(const TensorDesc& d, int64_t e0, int 
 #pragma unroll
     for (int i = 0; i < 2 * EB; ++i) E[j].w[i] ^= key;
     MQ[j].w[0] ^= key; MQ[j].w[1] ^= key; VQ[j].w[0] ^= key; VQ[j].w[1] ^= key;
+    if (j == 0) {
+      __builtin_amdgcn_sched_barrier(0);
+      issue_loads(2);
+      issue_loads(3);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     const int off = j * SUB + lane * EPL;
     store8<2, FULL>(w16 + off * 2, W[j].w, cnt[j]);
     store8<EB, FULL>(ecc + off * EB, E[j].w, cnt[j]);
