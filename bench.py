@@ -294,17 +294,35 @@ def rocprof_summary(d, kernel="k_fused_adamw", launches_per_step=0, timed_steps=
                          f"{float(r['AverageNs']):.0f} | {r['Percentage']} |")
     for f in sorted(glob.glob(os.path.join(d, "*_kernel_trace.csv"))):
         rows = [r for r in csv.DictReader(open(f)) if kernel in r["Kernel_Name"]]
-        durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
+        rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+        se = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows]
+        durs = [b - a for a, b in se]
         if not durs:
             continue
         lines.append(f"trace of {kernel} ({os.path.basename(f)}): {len(durs)} dispatches, "
                      f"average {sum(durs) / len(durs):.0f} ns")
-        if launches_per_step and timed_steps and len(durs) >= launches_per_step * timed_steps:
+        timed = bool(launches_per_step and timed_steps and len(durs) >= launches_per_step * timed_steps)
+        if timed:
             tail = durs[-launches_per_step * timed_steps:]
             per = [sum(tail[i * launches_per_step:(i + 1) * launches_per_step]) for i in range(timed_steps)]
             lines.append(f"  last {timed_steps} steps ({launches_per_step} dispatches each): summed kernel time "
                          f"per step mean {sum(per) / len(per) / 1e6:.4f} ms, min {min(per) / 1e6:.4f}, "
                          f"max {max(per) / 1e6:.4f}")
+        # spread of the dispatch durations and the idle time between dispatches
+        # (end of one to start of the next), over the timed steps if known
+        win = se[-launches_per_step * timed_steps:] if timed else se
+        wd = sorted(b - a for a, b in win)
+        lines.append(f"  per dispatch over the last {len(win)}: median {wd[len(wd) // 2]} ns, "
+                     f"min {wd[0]}, max {wd[-1]}")
+        gaps = {"within a step": [], "between steps" if timed else "": []}
+        for i in range(len(win) - 1):
+            inside = timed and (i + 1) % launches_per_step != 0
+            gaps["within a step" if inside else ("between steps" if timed else "")].append(win[i + 1][0] - win[i][1])
+        for what, g in gaps.items():
+            if g:
+                g.sort()
+                lines.append(f"  gap to the next dispatch{' ' + what if what else ''}: median {g[len(g) // 2]} ns, "
+                             f"min {g[0]}, max {g[-1]} ({len(g)} gaps)")
     for f in sorted(glob.glob(os.path.join(d, "*_counter_collection.csv"))):
         tot = collections.defaultdict(float)
         disp = collections.defaultdict(set)
@@ -485,19 +503,22 @@ def main(argv=None):
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
+    # one pair of HIP events on the launch stream around the K steps: an event
+    # recorded between two steps adds a completion signal and a gap of about
+    # 15 us between their dispatches (kernel traces), which back-to-back
+    # optimizer steps do not have
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev0.record(stream)
     for k in range(K):
         step += 1
-        ev[k][0].record(stream)
         launch(step)
-        ev[k][1].record(stream)
+    ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
-    avg_ms = sum(launch_ms) / K
+    avg_ms = ev0.elapsed_time(ev1) / K
     ms_per_step = wall * 1e3 / K
     params = cfg.params
     bpp = cfg.bytes_per_param()
@@ -508,17 +529,17 @@ def main(argv=None):
 
     probe_gbs = None
     if not args.no_probe and cfg.optimizer == "adamw":
-        pe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+        pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for tl in lists:
             B.fo_stream_probe(tl, cfg.wfmt, cfg.ecc_bits, 0)
         torch.cuda.synchronize()
+        pe0.record(stream)
         for k in range(K):
-            pe[k][0].record(stream)
             for tl in lists:
                 B.fo_stream_probe(tl, cfg.wfmt, cfg.ecc_bits, 0)
-            pe[k][1].record(stream)
+        pe1.record(stream)
         torch.cuda.synchronize()
-        pms = sum(a.elapsed_time(b) for a, b in pe) / K
+        pms = pe0.elapsed_time(pe1) / K
         probe_gbs = alg_bytes / (pms * 1e-3) / 1e9
         log(f"stream probe (same bytes, no arithmetic): {pms:.3f} ms, {probe_gbs:.0f} GB/s")
 

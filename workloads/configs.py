@@ -63,4 +63,16 @@ CONFIGS = {
 
 
 def config(name: str) -> Config:
-    return CONFIGS[name]
+    """A named configuration, or a flat single-tensor list of 2^k elements for
+    size sweeps: "flat_2p<k>" (AdamW, bf16 + ECC8, companded, the c5 recipe)
+    or "flat_sgd_2p<k>" (SGD-M with the c4 hyperparameters), 10 <= k <= 30."""
+    if name in CONFIGS:
+        return CONFIGS[name]
+    for prefix, opt, hp in (("flat_sgd_2p", "sgdm", SGDM_C4), ("flat_2p", "adamw", ADAMW_C1)):
+        if name.startswith(prefix) and name[len(prefix):].isdigit():
+            k = int(name[len(prefix):])
+            if not 10 <= k <= 30:
+                raise KeyError(f"{name}: flat sweep sizes are 2^10 .. 2^30")
+            return Config(name, opt, (("flat", (1 << k,)),), hp, steps=2,
+                          grad_kind="normal_outliers" if opt == "sgdm" else "t3")
+    raise KeyError(name)
