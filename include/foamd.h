@@ -58,13 +58,20 @@
  *     asynchronous with respect to the host; kernel faults surface at the
  *     caller's next synchronisation.  Two exceptions block the host: the
  *     first call on a device that needs the codec tables builds them and
- *     synchronises `stream` once, and a launch-table cache miss that evicts
- *     a slot waits for that slot's last use.  Make one call per tensor list
+ *     synchronises `stream` once, and a launch-table cache miss that refills
+ *     a slot waits for that slot's earlier launches.  A slot read only from
+ *     `stream` is rewritten behind them in stream order (no wait, unless a
+ *     larger table replaces its memory: then `stream` is synchronised); a
+ *     slot read from another stream or device makes the call synchronise
+ *     that slot's device.  Calls record no event, so steps on one stream
+ *     follow one another with no gap.  Make one call per tensor list
  *     before capturing a HIP graph; later calls with the same list are
- *     capture-safe (no allocation, no synchronisation, no memset).  A call
- *     made under capture pins its list's launch table until the process ends,
- *     so the graph stays valid however many other lists are stepped later;
- *     once all 1024 slots are pinned, a new list fails with FO_ENOMEM.
+ *     capture-safe (no allocation, no synchronisation, no memset), and a
+ *     call under capture with a list that has no launch table yet fails with
+ *     FO_EINVAL.  A call made under capture pins its list's launch table
+ *     until the process ends, so the graph stays valid however many other
+ *     lists are stepped later; once all 1024 slots are pinned, a new list
+ *     fails with FO_ENOMEM.
  *   - The library keeps, per device, one codec-table buffer and up to 1024
  *     cached launch tables (device + pinned host memory, a few KB each for
  *     ordinary lists), held until the process ends.

@@ -133,8 +133,9 @@ struct TableEntry {
   TensorDesc* dptr = nullptr;
   TensorDesc* hptr = nullptr;   // pinned staging copy
   size_t cap = 0;               // bytes
-  hipEvent_t ev = nullptr;      // last stream-ordered use of dptr/hptr
+  hipEvent_t ev = nullptr;      // the staging copy of the last fill (hptr -> dptr)
   bool ev_recorded = false;
+  SlotUses uses;                // streams whose launches read dptr since the fill
   int count = 0;                // non-empty tensors
   int64_t total_tiles = 0;
 };
@@ -172,27 +173,60 @@ int check_alias(Range* r, size_t n) {
 }
 int check_alias(std::vector<Range>& r) { return check_alias(r.data(), r.size()); }
 
+// Wait for the device `dev` to finish all queued work (the current device is
+// restored afterwards).
+int sync_device(int dev) {
+  int cur = -1;
+  hipError_t he = hipGetDevice(&cur);
+  if (he != hipSuccess) return hip_fail(he, "hipGetDevice");
+  if (cur != dev && (he = hipSetDevice(dev)) != hipSuccess) return hip_fail(he, "hipSetDevice");
+  const hipError_t hs = hipDeviceSynchronize();
+  if (cur != dev && (he = hipSetDevice(cur)) != hipSuccess) return hip_fail(he, "hipSetDevice");
+  return hs == hipSuccess ? FO_OK : hip_fail(hs, "hipDeviceSynchronize");
+}
+
 // Build (or fetch) the device table for `descs` (already validated, n > 0 only).
-// On success *out stays the caller's while it holds g_tab_mu.
+// On success *out stays the caller's while it holds g_tab_mu.  A miss fills a
+// slot: that copies the table from pinned host memory and may wait for the
+// slot's earlier users, neither of which a graph capture can hold, so a miss
+// under capture is refused (the list must be stepped once before capture).
 int get_table(int dev, const std::vector<uint8_t>& key, const std::vector<TensorDesc>& descs,
               const std::vector<int32_t>& buckets, int64_t total_tiles, hipStream_t stream, TableEntry** out) {
   if ((*out = find_entry(dev, key))) return FO_OK;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t he = hipStreamIsCapturing(stream, &cs);
+  if (he != hipSuccess) return hip_fail(he, "hipStreamIsCapturing");
+  if (cs != hipStreamCaptureStatusNone)
+    return fail(FO_EINVAL, "this tensor list has no launch table yet: step it once outside HIP graph capture "
+                           "before capturing it");
   // miss: refill the least recently used slot that no captured graph reads
   const long vi = g_slots.victim();
   if (vi < 0)
     return fail(FO_ENOMEM, "all %zu launch-table slots are held by captured HIP graphs", kCacheEntries);
   TableEntry& e = g_tab[(size_t)vi];
   g_slots.drop(vi);
-  hipError_t he;
-  if (e.ev_recorded) {
-    he = hipEventSynchronize(e.ev);           // previous users of this slot are done
-    if (he != hipSuccess) return hip_fail(he, "hipEventSynchronize");
-    e.ev_recorded = false;
-  }
   // device layout: descriptors (with the sentinel), then the tile-bucket index
   const size_t desc_bytes = descs.size() * sizeof(TensorDesc);
   const size_t need = desc_bytes + buckets.size() * sizeof(int32_t);
-  if (e.dev != dev || e.cap < need) {
+  const bool replace = (e.dev != dev || e.cap < need);
+  // the slot's earlier readers: its last staging copy, then the launches
+  if (e.ev_recorded) {
+    he = hipEventSynchronize(e.ev);
+    if (he != hipSuccess) return hip_fail(he, "hipEventSynchronize");
+    e.ev_recorded = false;
+  }
+  int rc = FO_OK;
+  switch (refill_wait(e.uses, stream, replace, e.dev == dev)) {
+    case RefillWait::NONE: break;
+    case RefillWait::STREAM:
+      if ((he = hipStreamSynchronize(stream)) != hipSuccess) return hip_fail(he, "hipStreamSynchronize");
+      break;
+    case RefillWait::DEVICE:
+      if ((rc = sync_device(e.dev))) return rc;
+      break;
+  }
+  e.uses.clear();
+  if (replace) {
     if (e.dptr) { (void)hipFree(e.dptr); e.dptr = nullptr; }
     if (e.hptr) { (void)hipHostFree(e.hptr); e.hptr = nullptr; }
     if (e.ev) { (void)hipEventDestroy(e.ev); e.ev = nullptr; }
@@ -212,8 +246,7 @@ int get_table(int dev, const std::vector<uint8_t>& key, const std::vector<Tensor
   std::memcpy(reinterpret_cast<uint8_t*>(e.hptr) + desc_bytes, buckets.data(), buckets.size() * sizeof(int32_t));
   he = hipMemcpyAsync(e.dptr, e.hptr, need, hipMemcpyHostToDevice, stream);
   if (he != hipSuccess) return hip_fail(he, "hipMemcpyAsync(launch table)");
-  // the staging copy is in flight: mark the slot used now, so that a later
-  // eviction waits for it even if the launch that follows fails
+  // the next refill rewrites hptr from the host: it waits for this copy
   he = hipEventRecord(e.ev, stream);
   if (he != hipSuccess) return hip_fail(he, "hipEventRecord(launch table)");
   e.ev_recorded = true;
@@ -224,9 +257,11 @@ int get_table(int dev, const std::vector<uint8_t>& key, const std::vector<Tensor
   return FO_OK;
 }
 
-// After the launches that read `e`: record their stream-ordered use (a later
-// refill of the slot waits for it), or, when `stream` is being captured into
-// a HIP graph, pin the slot, since the graph may replay them at any time.
+// After the launches that read `e`: note their stream (a later refill of the
+// slot decides from the streams what it must wait for; no event is recorded
+// per call, since an event between two steps holds the next step's launch
+// back by several microseconds), or, when `stream` is being captured into a
+// HIP graph, pin the slot, since the graph may replay them at any time.
 int use_entry(TableEntry* e, hipStream_t stream) {
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   hipError_t he = hipStreamIsCapturing(stream, &cs);
@@ -235,9 +270,7 @@ int use_entry(TableEntry* e, hipStream_t stream) {
     g_slots.pin((long)(e - g_tab.data()));
     return FO_OK;
   }
-  he = hipEventRecord(e->ev, stream);
-  if (he != hipSuccess) return hip_fail(he, "hipEventRecord");
-  e->ev_recorded = true;
+  e->uses.add(stream);
   return FO_OK;
 }
 

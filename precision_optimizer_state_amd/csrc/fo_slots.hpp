@@ -1,6 +1,6 @@
 // Slot bookkeeping of the launch-table cache (host code only, no HIP): which
-// slot holds which key, least-recently-used choice of the slot to refill, and
-// pinning.
+// slot holds which key, least-recently-used choice of the slot to refill,
+// pinning, and what a refill must wait for.
 //
 // A slot is pinned once a HIP graph captures a launch that reads it: the
 // graph holds the slot's device address and replays it at any later time, so
@@ -16,6 +16,36 @@
 #include <vector>
 
 namespace fo {
+
+// The streams that launched work reading a slot since it was last filled:
+// none, exactly one (kept), or several.  Calls record no event per use; a
+// refill decides from this what it must wait for (refill_wait).
+struct SlotUses {
+  const void* stream = nullptr;   // the stream when count == 1
+  int count = 0;                  // 0, 1, or 2 for "two or more"
+  void add(const void* s) {
+    if (count == 0) { stream = s; count = 1; }
+    else if (count == 1 && s != stream) count = 2;
+  }
+  void clear() { stream = nullptr; count = 0; }
+};
+
+// What refilling a slot from a call on stream `s` must wait for, besides the
+// staging copy of the slot's previous fill (which has an event of its own):
+//   NONE    no use since the fill, or every use was on `s` and the slot's
+//           device memory is rewritten in place: the new copy is queued on
+//           `s` behind them;
+//   STREAM  every use was on `s` but the memory is freed and replaced, and
+//           freeing is not ordered on any stream: wait for `s`;
+//   DEVICE  a use on another stream, or the slot is on another device: no
+//           stream orders those uses before the new copy, so wait for the
+//           slot's device.
+enum class RefillWait { NONE, STREAM, DEVICE };
+inline RefillWait refill_wait(const SlotUses& u, const void* s, bool frees, bool same_device) {
+  if (u.count == 0) return RefillWait::NONE;
+  if (!same_device || u.count > 1 || u.stream != s) return RefillWait::DEVICE;
+  return frees ? RefillWait::STREAM : RefillWait::NONE;
+}
 
 class SlotCache {
  public:

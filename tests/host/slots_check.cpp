@@ -1,6 +1,7 @@
 // CPU check of the launch-table cache's slot bookkeeping (fo_slots.hpp):
-// least-recently-used refill, and pinned slots (read by captured HIP graphs)
-// never refilled.  Prints "ok" or the first failed condition and exits 1.
+// least-recently-used refill, pinned slots (read by captured HIP graphs)
+// never refilled, the per-slot record of the streams that read a slot, and
+// what a refill waits for.  Prints "ok" or the first failed condition and exits 1.
 #include <cstdio>
 #include <cstdlib>
 #include <string>
@@ -80,6 +81,46 @@ int main() {
     c.drop(a);
     CHECK(!c.holds(a) && c.find("a") < 0);
     CHECK(use(c, "b") >= 0);
+  }
+  // per-slot use tracking: none, one stream, or several
+  {
+    int A, B;                                 // two distinct stream handles
+    fo::SlotUses u;
+    CHECK(u.count == 0);
+    u.add(&A);
+    CHECK(u.count == 1 && u.stream == &A);
+    u.add(&A);
+    CHECK(u.count == 1 && u.stream == &A);   // the same stream again
+    u.add(&B);
+    CHECK(u.count == 2);
+    u.add(&A);
+    CHECK(u.count == 2);                      // several stays several
+    u.clear();
+    CHECK(u.count == 0 && u.stream == nullptr);
+    u.add(nullptr);                           // the null stream is a stream like any other
+    CHECK(u.count == 1 && u.stream == nullptr);
+    u.add(&A);
+    CHECK(u.count == 2);
+  }
+  // what a refill on stream S waits for
+  {
+    using fo::RefillWait;
+    int S, T;
+    fo::SlotUses none, onS, onT, both;
+    onS.add(&S);
+    onT.add(&T);
+    both.add(&S);
+    both.add(&T);
+    for (bool frees : {false, true})
+      for (bool same_dev : {false, true}) CHECK(fo::refill_wait(none, &S, frees, same_dev) == RefillWait::NONE);
+    CHECK(fo::refill_wait(onS, &S, false, true) == RefillWait::NONE);     // queued behind them on S
+    CHECK(fo::refill_wait(onS, &S, true, true) == RefillWait::STREAM);    // freeing is not stream-ordered
+    CHECK(fo::refill_wait(onT, &S, false, true) == RefillWait::DEVICE);   // nothing orders T before S
+    CHECK(fo::refill_wait(onT, &S, true, true) == RefillWait::DEVICE);
+    CHECK(fo::refill_wait(both, &S, false, true) == RefillWait::DEVICE);  // uses on S and T
+    CHECK(fo::refill_wait(both, &S, true, true) == RefillWait::DEVICE);
+    CHECK(fo::refill_wait(onS, &S, false, false) == RefillWait::DEVICE);  // the slot's device is another
+    CHECK(fo::refill_wait(onS, &S, true, false) == RefillWait::DEVICE);
   }
   std::printf("ok\n");
   return 0;

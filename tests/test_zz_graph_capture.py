@@ -122,3 +122,30 @@ def test_captured_sgdm_step_replays_match_eager_calls():
             for k in ("w16", "ecc", "b_q", "b_s"):
                 assert torch.equal(a[k].view(torch.uint8), b[k].view(torch.uint8)), f"replay {r}: tensor {i} {k} differs"
     print("captured SGD-M step: 3 replays bitwise equal to eager calls", flush=True)
+
+
+def test_capture_of_a_list_never_stepped_is_refused():
+    """A captured call whose list has no launch table yet fails before it
+    launches anything (filling a slot needs a copy and may need a wait, which
+    a capture cannot hold); the list then steps normally outside capture."""
+    hp = B.adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 1)
+    st = _state(50_000 + 3, "cold_capture")
+    before = {k: v.clone() for k, v in st.items()}
+    tl = B.AdamWList([st])
+    pinned = B.load().fo_cache_pinned()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(B.FoError, match="outside HIP graph capture"):
+        with torch.cuda.graph(g):
+            B.fo_fused_adamw_step(tl, hp)
+    torch.cuda.synchronize()
+    assert B.load().fo_cache_pinned() == pinned
+    for k in KEYS:
+        assert torch.equal(st[k].view(torch.uint8), before[k].view(torch.uint8)), f"{k} changed"
+    ref = {k: v.clone() for k, v in st.items()}
+    B.fo_fused_adamw_step(tl, hp)
+    B.fo_fused_adamw_step(B.AdamWList([ref]), hp)
+    torch.cuda.synchronize()
+    for k in KEYS:
+        assert torch.equal(st[k].view(torch.uint8), ref[k].view(torch.uint8)), f"{k} differs after the refusal"
+    print("captured call on a cold list refused; the list steps normally afterwards", flush=True)
