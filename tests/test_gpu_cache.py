@@ -148,3 +148,46 @@ def test_alternating_streams_keep_every_step():
     _assert_equal(x, ref, "list stepped on alternating streams")
     _assert_equal(many, whole, "one-block lists")
     print("alternating streams: every step bitwise as expected", flush=True)
+
+
+def test_sgdm_refill_from_another_stream_waits_for_the_queued_steps():
+    """The SGD-M entry point shares the cache: its list's slot refilled from
+    another stream while its steps may still run on the first."""
+    from precision_optimizer_state_amd.state import alloc_sgdm_state
+
+    def sgd_state(n, tag):
+        st = alloc_sgdm_state(n)
+        w = device_weights(tag, 0, n)
+        B.fo_split_weights(w, st["w16"], st["ecc"], "bf16", 8)
+        device_grads(tag, 0, 1, n, "normal_outliers", "bf16", out=st["grad"])
+        return st
+
+    def hp(t):
+        return B.sgdm_hparams(0.1, 0.9, 1e-4, t)
+
+    keys = ("w16", "ecc", "b_q", "b_s")
+    steps = 30
+    x = sgd_state((1 << 26) + 77, "cache_sgd_x")
+    ref = {k: v.clone() for k, v in x.items()}
+    many = sgd_state(1100 * 32, "cache_sgd_many")
+    whole = {k: v.clone() for k, v in many.items()}
+    small = [B.SGDMList([{k: (v[i:i + 1] if k == "b_s" else v[i * 32:(i + 1) * 32]) for k, v in many.items()}])
+             for i in range(1100)]
+    a, b = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(a):
+        for t in range(1, steps + 1):
+            B.fo_fused_sgdm_step(B.SGDMList([x]), hp(t))
+    with torch.cuda.stream(b):
+        for tl in small:
+            B.fo_fused_sgdm_step(tl, hp(1))
+    torch.cuda.synchronize()
+    for t in range(1, steps + 1):
+        B.fo_fused_sgdm_step(B.SGDMList([ref]), hp(t))
+    B.fo_fused_sgdm_step(B.SGDMList([whole]), hp(1))
+    torch.cuda.synchronize()
+    for k in keys:
+        assert torch.equal(x[k].view(torch.uint8), ref[k].view(torch.uint8)), f"SGD-M list: {k} differs"
+        assert torch.equal(many[k].view(torch.uint8), whole[k].view(torch.uint8)), f"one-block SGD-M lists: {k} differs"
+    print(f"SGD-M refill from another stream: {steps} queued steps and 1100 one-block lists bitwise as expected",
+          flush=True)
