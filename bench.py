@@ -433,6 +433,25 @@ def run_dropin(args, cfg, log):
     }
 
 
+def device_info(torch) -> dict:
+    """The GPU the run used: name, architecture, compute units, the HIP
+    runtime version, and the peak shader and memory clocks the runtime
+    reports (hipDeviceGetAttribute: hipDeviceAttributeClockRate = 5,
+    hipDeviceAttributeMemoryClockRate = 60, both in kHz)."""
+    import ctypes
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": p.gcnArchName, "cus": p.multi_processor_count, "hip": torch.version.hip}
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        for key, attr in (("peak_sclk_mhz", 5), ("peak_mclk_mhz", 60)):
+            v = ctypes.c_int(0)
+            if hip.hipDeviceGetAttribute(ctypes.byref(v), attr, torch.cuda.current_device()) == 0:
+                info[key] = v.value / 1000.0
+    except OSError:
+        pass
+    return info
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -503,11 +522,28 @@ def main(argv=None):
     torch.cuda.synchronize()
     log(f"warmup {args.warmup} steps done")
 
-    # one pair of HIP events on the launch stream around the K steps: an event
-    # recorded between two steps adds a completion signal and a gap of about
-    # 15 us between their dispatches (kernel traces), which back-to-back
-    # optimizer steps do not have
     K = args.steps
+    # K steps, each inside its own event pair, for the median and spread of
+    # single steps.  The pairs add a completion signal between steps, so these
+    # run before the timed region (a trace's last K steps stay the timed ones)
+    # and feed no headline figure.
+    pev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    for k in range(K):
+        step += 1
+        pev[k][0].record(stream)
+        launch(step)
+        pev[k][1].record(stream)
+    torch.cuda.synchronize()
+    single = sorted(a.elapsed_time(b) for a, b in pev)
+    per_step = {"median_ms": single[K // 2] if K % 2 else 0.5 * (single[K // 2 - 1] + single[K // 2]),
+                "min_ms": single[0], "max_ms": single[-1], "steps": K}
+    log(f"{K} single steps, one event pair each: median {per_step['median_ms']:.3f} ms, "
+        f"min {single[0]:.3f}, max {single[-1]:.3f}")
+
+    # the timed steps: one pair of HIP events on the launch stream around all
+    # K of them (an event recorded between two steps adds a completion signal
+    # and a gap of about 15 us between their dispatches, which back-to-back
+    # optimizer steps do not have)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -595,6 +631,8 @@ def main(argv=None):
         # ranges of 2^18 tiles); kernel_ms_avg and roofline cover all of them
         "launches_per_step": (sum(launches_per_call([m]) for m in release) if release
                               else launches_per_call(cfg.numels)),
+        "per_step_events": per_step,
+        "device": device_info(torch),
         "stream_probe_gbs": probe_gbs,
         # the fused kernel against the same byte streams moved with no arithmetic
         "vs_stream_probe": (achieved / probe_gbs) if probe_gbs else None,
