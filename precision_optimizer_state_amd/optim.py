@@ -27,8 +27,10 @@ invalidate_launch_cache() before the next step.
 
 from __future__ import annotations
 
+import importlib.util
 import itertools
 import operator
+import os
 from typing import Iterable
 
 import torch
@@ -43,18 +45,44 @@ def _nb(n: int) -> int:
     return (n + 31) // 32
 
 
+def _load_fill_rows():
+    """fill_rows of the host marshalling extension (lib/fo_marshal.so, built
+    with the library), or None when it has not been built: the optimizers then
+    marshal their launch rows in Python (the same rows, more host time)."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "fo_marshal.so")
+    if not os.path.exists(path):
+        return None
+    spec = importlib.util.spec_from_file_location("fo_marshal", path)
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod.fill_rows
+
+
+_fill_rows = _load_fill_rows()
+_STEP = operator.itemgetter("step")
+
+
 class _Plan:
     """What a parameter list needs at every step, built once per list: the
     parameters (held, so their ids stay theirs), their state dicts and the
     address-independent part of each launch row.  `gen` is unique per plan
-    and keys the marshalled lists built from it."""
+    and keys the marshalled lists built from it.  With the marshalling
+    extension the plan also holds those parts as an int64 matrix (`fixed`)
+    and one launch list (`tl`) whose rows the extension rewrites at every
+    step (the library reads a list only during the call)."""
 
-    __slots__ = ("params", "states", "static", "gen")
+    __slots__ = ("params", "states", "static", "gen", "fixed", "tl", "rows_addr")
     _gens = itertools.count()
 
-    def __init__(self, params, states, static):
+    def __init__(self, params, states, static, list_from_rows=None):
         self.params, self.states, self.static = params, states, static
         self.gen = next(_Plan._gens)
+        self.fixed = self.tl = self.rows_addr = None
+        if list_from_rows is not None and static:
+            import ctypes
+            self.fixed = torch.tensor(static, dtype=torch.int64)
+            self.tl = list_from_rows([(0,) * (len(static[0]) + 2)] * len(static))
+            self.rows_addr = ctypes.addressof(self.tl.array)
 
 
 class _FlashBase(torch.optim.Optimizer):
@@ -137,14 +165,15 @@ class _FlashBase(torch.optim.Optimizer):
                 self._plans.clear()
                 self._lists.clear()
             plan = self._plans[ids] = _Plan(list(params), [self.state[p] for p in params],
-                                            [self._static(p) for p in params])
+                                            [self._static(p) for p in params],
+                                            self._list_from_rows if _fill_rows is not None else None)
         return plan
 
-    def _list_for(self, plan, params, static):
+    def _list_for(self, plan, params, static, grads=None):
         # rows of raw addresses (w16, ecc, grad, states..., n); the ctypes array
         # is rebuilt only when a theta' or gradient address changes
         w = tuple([p.data_ptr() for p in params])
-        g = tuple([p.grad.data_ptr() for p in params])
+        g = tuple([x.data_ptr() for x in grads]) if grads is not None else tuple([p.grad.data_ptr() for p in params])
         key = (plan.gen, w, g)
         tl = self._lists.get(key)
         if tl is None:
@@ -154,14 +183,16 @@ class _FlashBase(torch.optim.Optimizer):
             tl = self._lists[key] = self._list_from_rows(rows)
         return tl
 
-    def _step_params(self, group, params):
-        plan = self._plan(params)
-        steps = []
+    def _step_params(self, group, params, grads=None, plan=None, tl=None):
+        plan = plan or self._plan(params)
+        if tl is None and plan.tl is not None and \
+                _fill_rows(params, plan.fixed, plan.rows_addr, _W16[self.wfmt]) == 0:
+            tl = plan.tl
         for st in plan.states:
             st["step"] += 1
-            steps.append(st["step"])
+        steps = list(map(_STEP, plan.states))
         if steps.count(steps[0]) == len(steps):
-            self._launch(self._list_for(plan, params, plan.static), group, steps[0])
+            self._launch(tl or self._list_for(plan, params, plan.static, grads), group, steps[0])
             return
         # parameters with different step counts (imported or reloaded states):
         # one launch per count
@@ -180,16 +211,30 @@ class _FlashBase(torch.optim.Optimizer):
                 loss = closure()
         wdt = _W16[self.wfmt]
         for group in self.param_groups:
-            ps = []
-            for p in group["params"]:
-                g = p.grad
-                if g is None:
+            ps = group["params"]
+            if not ps:
+                continue
+            if _fill_rows is not None:
+                # every gradient present, in theta's format and contiguous: the
+                # extension writes the plan's launch rows in one call
+                plan = self._plan(ps)
+                if _fill_rows(ps, plan.fixed, plan.rows_addr, wdt) == 0:
+                    self._step_params(group, ps, plan=plan, tl=plan.tl)
                     continue
-                if g.dtype is not wdt or not g.is_contiguous():
-                    p.grad = g.to(wdt).contiguous()
-                ps.append(p)
-            if ps:
-                self._step_params(group, ps)
+            # otherwise: drop parameters without gradients, convert the others
+            # where needed (the rows of the remaining list are then filled as above,
+            # or in Python without the extension)
+            gs = [p.grad for p in ps]
+            if any(map(operator.is_, gs, itertools.repeat(None))):
+                keep = [i for i, g in enumerate(gs) if g is not None]
+                ps, gs = [ps[i] for i in keep], [gs[i] for i in keep]
+            if not ps:
+                continue
+            # gradients in the 16-bit format of theta' and contiguous (what autograd
+            # produces for these parameters); anything else is converted here
+            for i in [i for i, g in enumerate(gs) if g.dtype is not wdt or not g.is_contiguous()]:
+                ps[i].grad = gs[i] = gs[i].to(wdt).contiguous()
+            self._step_params(group, ps, gs)
         return loss
 
     def _group(self, p):

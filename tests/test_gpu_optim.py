@@ -262,3 +262,44 @@ def test_param_groups_use_their_own_hyperparameters():
         return dict(lr=g["lr"], beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=g["weight_decay"])
 
     _lockstep(model, opt, 3, hp_of, tag="groups")
+
+
+@pytest.mark.parametrize("release", [False, True], ids=["step", "grad_release"])
+def test_native_row_marshalling_equals_python_marshalling(release):
+    """The launch rows written by the host extension (lib/fo_marshal.so) and
+    by the Python fallback drive the same steps: two copies of a model, one
+    stepped with each, end bitwise equal.  In step() mode the last layer's
+    bias is frozen (no gradient), so the extension first refuses the full
+    list and then fills the rows of the list without it; gradient release
+    steps buckets through the same rows."""
+    import precision_optimizer_state_amd.optim as optim_mod
+    if optim_mod._fill_rows is None:
+        pytest.skip("the marshalling extension is not built")
+    models, opts = [], []
+    for native in (True, False):
+        m = _model(5)
+        if not release:
+            m[2].bias.requires_grad_(False)
+        models.append(m)
+        opts.append(FlashAdamW(list(m.parameters()), **HP, grad_release=release, release_bucket=3000))
+    saved = optim_mod._fill_rows
+    try:
+        for i in range(4):
+            for native, (m, opt) in enumerate(zip(models, opts)):
+                optim_mod._fill_rows = saved if native == 0 else None
+                loss = _loss(m, i)
+                loss.backward()
+                if not release:
+                    opt.step()
+                opt.zero_grad(set_to_none=True)
+    finally:
+        optim_mod._fill_rows = saved
+    torch.cuda.synchronize()
+    for (na, pa), (nb, pb) in zip(models[0].named_parameters(), models[1].named_parameters()):
+        assert torch.equal(pa.data.view(torch.int16), pb.data.view(torch.int16)), f"{na}: theta' differs"
+        sa, sb = opts[0].state[pa], opts[1].state[pb]
+        for k in ("ecc", "m_q", "m_s", "v_q", "v_s"):
+            assert torch.equal(sa[k], sb[k]), f"{na}: {k} differs"
+        assert sa["step"] == sb["step"]
+    print(f"native and Python launch rows: 4 steps bitwise equal ({'gradient release' if release else 'step()'})",
+          flush=True)
