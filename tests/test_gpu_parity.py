@@ -522,6 +522,33 @@ def test_stream_probe_preserves_data_with_zero_key():
         assert torch.equal(before[k].view(torch.uint8), st[k].view(torch.uint8)), k
 
 
+def test_stream_probe_rewrites_every_byte_once():
+    """A nonzero key: every ECC, code and scale byte of the list comes back
+    XOR-ed with the key's byte at its position in the word (so each was read
+    and written exactly once, the ragged tail included), and theta' comes back
+    unchanged, because the probe folds the gradient into its key for theta'
+    and the gradients here are zero."""
+    key = 0x5AC3_961E
+    for n in (100_003, 2048 * 4 + 5):
+        st = alloc_adamw_state(n)
+        for k in ("w16", "ecc", "m_q", "v_q", "m_s", "v_s"):
+            st[k].view(torch.uint8).copy_(torch.randint(0, 256, (st[k].numel() * st[k].element_size(),),
+                                                        dtype=torch.uint8, device="cuda"))
+        st["grad"].zero_()
+        before = {k: v.clone() for k, v in st.items()}
+        B.fo_stream_probe([st], "bf16", 8, key)
+        torch.cuda.synchronize()
+        kb = torch.tensor([(key >> (8 * i)) & 0xFF for i in range(4)], dtype=torch.uint8, device="cuda")
+        for k in ("ecc", "m_q", "v_q"):
+            b = before[k].view(torch.uint8)
+            want = b ^ kb.repeat((b.numel() + 3) // 4)[:b.numel()]
+            assert torch.equal(st[k].view(torch.uint8), want), f"n={n}: {k}"
+        for k in ("m_s", "v_s"):
+            want = before[k].view(torch.int16) ^ torch.tensor(key & 0xFFFF, dtype=torch.int32).to(torch.int16).item()
+            assert torch.equal(st[k].view(torch.int16), want.to("cuda")), f"n={n}: {k}"
+        assert torch.equal(st["w16"].view(torch.uint8), before["w16"].view(torch.uint8)), f"n={n}: w16"
+
+
 def test_aliasing_list_rejected():
     st = alloc_adamw_state(4096)
     bad = dict(st)
