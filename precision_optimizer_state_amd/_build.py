@@ -54,6 +54,9 @@ def build_marshal(verbose: bool = False, out: str = MARSHAL_OUT) -> str:
     os.makedirs(os.path.dirname(out), exist_ok=True)
     tmp = out + ".tmp"
     libdirs = ce.library_paths()
+    # the defines are those torch.utils.cpp_extension.CppExtension passes for
+    # this (ROCm) build of torch, so its headers see the configuration they
+    # were built with; the source itself is host C++ with no GPU code
     cmd = ["g++", "-O2", "-std=c++17", "-fPIC", "-shared", "-Wall",
            f"-D_GLIBCXX_USE_CXX11_ABI={int(torch._C._GLIBCXX_USE_CXX11_ABI)}",
            "-DTORCH_API_INCLUDE_EXTENSION_H", "-DTORCH_EXTENSION_NAME=fo_marshal",
