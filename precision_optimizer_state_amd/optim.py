@@ -246,14 +246,17 @@ class _FlashBase(torch.optim.Optimizer):
             e = self._group_of[id(p)]
         return e[0]
 
-    @torch.no_grad()
     def _release_hook(self, p):
         """Runs when p's gradient is complete during backward.  Parameters are
         queued; a bucket of at least `release_bucket` elements is stepped in one
         fused call and its gradients freed at once, and whatever is still queued
-        when backward finishes is stepped then (the end-of-backward callback)."""
-        if p.grad.dtype != p.dtype or not p.grad.is_contiguous():
-            p.grad = p.grad.to(p.dtype).contiguous()
+        when backward finishes is stepped then (the end-of-backward callback).
+        It runs once per parameter, so it enters no grad-mode context unless it
+        converts a gradient (the bucket step enters its own)."""
+        g = p.grad
+        if g.dtype is not p.dtype or not g.is_contiguous():
+            with torch.no_grad():
+                p.grad = g.to(p.dtype).contiguous()
         self._pending.append(p)
         self._pending_elems += p.numel()
         if not self._flush_queued:
@@ -267,12 +270,15 @@ class _FlashBase(torch.optim.Optimizer):
 
     @torch.no_grad()
     def _step_pending(self):
-        by_group = {}
-        for q in self._pending:
-            g = self._group(q)
-            by_group.setdefault(id(g), (g, []))[1].append(q)
-        for g, ps in by_group.values():
-            self._step_params(g, ps)
+        if len(self.param_groups) == 1:
+            self._step_params(self.param_groups[0], self._pending)
+        else:
+            by_group = {}
+            for q in self._pending:
+                g = self._group(q)
+                by_group.setdefault(id(g), (g, []))[1].append(q)
+            for g, ps in by_group.values():
+                self._step_params(g, ps)
         for q in self._pending:
             q.grad = None       # freed in stream order by torch's caching allocator
         self._pending = []
