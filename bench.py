@@ -273,12 +273,15 @@ def hbm_ceiling(read_bytes_per_elem, write_bytes_per_elem, steps=10, gib=16, log
 # ---------------------------------------------------------------------------
 # rocprofv3 output -> short text summaries (the files under profiles/)
 # ---------------------------------------------------------------------------
-def rocprof_summary(d, kernel="k_fused_adamw", launches_per_step=0, timed_steps=0):
+def rocprof_summary(d, kernel="k_fused_adamw", launches_per_step=0, timed_steps=0, window=0):
     """Summary of the rocprofv3 CSV files in directory d: the kernel
     statistics (top entries), the trace of `kernel` (dispatches, average
     duration, and with launches_per_step / timed_steps the summed kernel time
     of each of the last timed_steps steps), and the counter totals of every
-    kernel whose name contains `kernel` or k_hbm_probe."""
+    kernel whose name contains `kernel` or k_hbm_probe.  With window > 0 it
+    also prints the median dispatch duration of every run of `window`
+    consecutive dispatches of `kernel`, with its start time after the first
+    dispatch (how the duration moves over a run)."""
     import collections
     import csv
     import glob
@@ -323,6 +326,13 @@ def rocprof_summary(d, kernel="k_fused_adamw", launches_per_step=0, timed_steps=
                 g.sort()
                 lines.append(f"  gap to the next dispatch{' ' + what if what else ''}: median {g[len(g) // 2]} ns, "
                              f"min {g[0]}, max {g[-1]} ({len(g)} gaps)")
+        if window > 0:
+            cells = []
+            for i in range(0, len(se), window):
+                ch = se[i:i + window]
+                ds = sorted(b - a for a, b in ch)
+                cells.append(f"{(ch[0][0] - se[0][0]) / 1e6:.1f} ms: {ds[len(ds) // 2] / 1e3:.0f} us")
+            lines.append(f"  median duration per {window} dispatches (start after the first dispatch): " + "; ".join(cells))
     for f in sorted(glob.glob(os.path.join(d, "*_counter_collection.csv"))):
         tot = collections.defaultdict(float)
         disp = collections.defaultdict(set)
@@ -475,9 +485,11 @@ def main(argv=None):
                     help="print a text summary of the rocprofv3 CSV files in DIR and exit (no GPU use)")
     ap.add_argument("--kernel", default="k_fused_adamw", help="kernel name filter of --rocprof-summary")
     ap.add_argument("--launches-per-step", type=int, default=0, help="with --rocprof-summary: per-step sums")
+    ap.add_argument("--window", type=int, default=0,
+                    help="with --rocprof-summary: median dispatch duration per window of this many dispatches")
     args = ap.parse_args(argv)
     if args.rocprof_summary:
-        print(rocprof_summary(args.rocprof_summary, args.kernel, args.launches_per_step, args.steps))
+        print(rocprof_summary(args.rocprof_summary, args.kernel, args.launches_per_step, args.steps, args.window))
         return 0
 
     def log(msg):

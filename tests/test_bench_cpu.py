@@ -73,6 +73,25 @@ def test_rocprof_summary_reports_dispatch_spread_and_gaps(tmp_path):
     assert "gap to the next dispatch: median 5 ns, min 5, max 50 (9 gaps)" in out
 
 
+
+def test_rocprof_summary_window_medians(tmp_path):
+    """--window: the median duration of each run of consecutive dispatches,
+    with the run's start after the first dispatch."""
+    import csv
+    sys.path.insert(0, ROOT)
+    import bench
+    rows = [{"Kernel_Name": "void fo::k_fused_adamw<0, 8, 0, false>(...)",
+             "Start_Timestamp": 5_000_000 + i * 1_000_000, "End_Timestamp": 5_000_000 + i * 1_000_000 + 100_000 + i * 1000}
+            for i in range(10)]                          # 1 ms apart, 100..109 us long
+    with open(tmp_path / "x_kernel_trace.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        w.writerows(rows)
+    out = bench.rocprof_summary(str(tmp_path), "k_fused_adamw", window=4)
+    line = [ln for ln in out.splitlines() if "per 4 dispatches" in ln][0]
+    assert line.endswith("0.0 ms: 102 us; 4.0 ms: 106 us; 8.0 ms: 109 us"), line
+
+
 def test_flat_sweep_configs():
     sys.path.insert(0, ROOT)
     import pytest
