@@ -47,3 +47,25 @@ def test_bench_prints_one_contract_line():
     dev = d["device"]
     assert dev["cus"] > 0 and dev["arch"].startswith("gfx")
     print(f"bench line: {rf['achieved']:.0f} GB/s on {dev['arch']} ({dev['cus']} CUs)", flush=True)
+
+
+@pytest.mark.parametrize("cfg,extra,cls", [("c1_flat1m", [], "FlashAdamW"),
+                                           ("c4_resnet50", ["--release"], "FlashSGD")])
+def test_bench_dropin_line(cfg, extra, cls):
+    """--dropin: one JSON line with the drop-in step's GPU and host times."""
+    sys.path.insert(0, ROOT)
+    import bench
+    from workloads.configs import config
+    out = io.StringIO()
+    with contextlib.redirect_stdout(out):
+        rc = bench.main(["--dropin", "--config", cfg, *extra, "--steps", "3", "--warmup", "1", "--quiet"])
+    assert rc in (0, None)
+    lines = [ln for ln in out.getvalue().splitlines() if ln.strip()]
+    assert len(lines) == 1, out.getvalue()
+    d = json.loads(lines[0])
+    assert d["steps"] == 3 and d["config"]["params"] == config(cfg).params
+    assert d["gpu_ms_per_step"] > 0 and d["host_ms_per_step"] > 0 and d["value"] > 0
+    assert d["config"]["workload"].startswith(f"{cls}.step() drop-in")
+    assert ("gradient release" in d["config"]["workload"]) == bool(extra)
+    r = d["roofline"]
+    assert r["frac"] == pytest.approx(r["achieved"] / r["peak"])
