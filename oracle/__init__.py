@@ -44,6 +44,9 @@ from .codecs import (  # noqa: F401
     dequantize_state,
     momentum_lut,
     level_spacing,
+    code_bytes,
+    pack_nibbles,
+    unpack_nibbles,
 )
 from .optim import (  # noqa: F401
     adamw_scalars,

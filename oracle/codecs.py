@@ -1,4 +1,4 @@
-"""Oracle: blockwise 8-bit state codecs (companded and linear).
+"""Oracle: blockwise state codecs (8-bit companded and linear, 4-bit companded).
 
 TEST INFRASTRUCTURE ONLY -- see the package docstring for who may import it.
 
@@ -58,6 +58,22 @@ C7  The one int8 pattern outside the momentum code range, -128, is never
     defines it: the companded LUT saturates it to -127 (so every code decodes
     into [-s, s]); the linear decode is the plain product for every int8.
 
+C8  4-bit states.  The pages name lower-bit states only as an outlook (blog,
+    Conclusion & Perspective, Future Outlook: 4-bit states might work given
+    a more aggressive transform) and define no transform, so the plainest
+    reading keeps everything of C1-C7 and narrows the codes: codec
+    "companded4".  Momentum: q = sign(z) * round_half_even(7 * phi(a)), codes
+    in [-7, 7] (no ties: the thresholds (2k+1)/(27-2k) have odd denominators
+    > 1); decode m = RN32(s * LUT4[q]), LUT4[q] = RN32(q / (14 - |q|)), the
+    inverse of phi at q/7; the pattern -8 is never written and decodes as -7.
+    Variance: w = sqrt_rn(v), z = w / s, y = RN32(15 * z),
+    q = clamp(round_half_even(y), 0, 15); decode D = RN32(s / 15),
+    t = RN32(D * q), v = RN32(t * t).  Storage: two codes per byte, element
+    2i in the low nibble and 2i+1 in the high one, momentum codes as 4-bit
+    two's complement; an odd-length tensor's last byte has a zero high
+    nibble.  Only the companded codec has a 4-bit form (the pages report
+    that plain linear codes diverge already at 8 bits).
+
 RN32(.) is one IEEE float32 rounding; numpy float32 arithmetic provides it
 (its division and square root are the correctly rounded IEEE operations).
 Every quotient above is such a division: there is no reciprocal-multiply
@@ -67,12 +83,13 @@ for its float32 argument (float64 is exact for that decision:
 |127*phi(a) - (k+1/2)| >= 2^-35 for every float32 a near a threshold, far
 above float64's error).
 
-Parity status: pinned (invertibility, monotone decode, phi(0)=0 and
+Parity status: pinned (for both code widths: invertibility, monotone decode, phi(0)=0 and
 phi(+-1)=+-1, exhaustive half-step bound over float32 z in [-1, 1] sampled
 densely, hand-computed golden codes, exact-rational codes for inputs where a
 reciprocal-multiply would differ from the division, RU16 against numpy's
 binary16 cast, companded-vs-linear error on heavy-tailed data, NaN and
-infinity codes, NaN-filled short last blocks; tests/test_oracle_codecs.py).
+infinity codes, NaN-filled short last blocks, hand-packed nibble bytes;
+tests/test_oracle_codecs.py).
 """
 
 from __future__ import annotations
@@ -131,22 +148,58 @@ def _per_elem(scale_bits: np.ndarray, n: int) -> np.ndarray:
     return np.repeat(s, BLOCK)[:n]
 
 
+# largest momentum code L and largest variance code of each codec (C3-C5, C8)
+CODE_MAX = {"companded": (127, 255), "linear": (127, 255), "companded4": (7, 15)}
+
+
+def code_bytes(n: int, codec: str) -> int:
+    """Bytes of one state's code array for n elements (C8: two 4-bit codes a byte)."""
+    return (n + 1) // 2 if codec == "companded4" else n
+
+
 def momentum_lut(codec: str = "companded") -> np.ndarray:
-    """LUT[q + 127] = RN32(q / (254 - |q|)) for q in [-127, 127] (C3)."""
-    q = np.arange(-127, 128, dtype=np.float32)
-    if codec != "companded":
-        raise ValueError("the momentum LUT exists for the companded codec only")
-    return q / (F32(254.0) - np.abs(q))
+    """LUT[q + L] = RN32(q / (2L - |q|)) for q in [-L, L], the inverse of phi
+    at q/L: L = 127 (C3) or 7 (C8)."""
+    if codec not in ("companded", "companded4"):
+        raise ValueError("the momentum LUT exists for the companded codecs only")
+    L = CODE_MAX[codec][0]
+    q = np.arange(-L, L + 1, dtype=np.float32)
+    return q / (F32(2 * L) - np.abs(q))
+
+
+def pack_nibbles(q: np.ndarray) -> np.ndarray:
+    """Codes in [-8, 15] -> bytes, element 2i in the low nibble, 2i+1 in the
+    high one (4-bit two's complement for negative codes); an odd count leaves
+    the last high nibble 0 (C8)."""
+    q = np.asarray(q).astype(np.int64).ravel()
+    if q.size % 2:
+        q = np.concatenate([q, np.zeros(1, np.int64)])
+    nib = q & 0xF
+    return (nib[0::2] | (nib[1::2] << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(b: np.ndarray, n: int, signed: bool) -> np.ndarray:
+    """The first n codes of a nibble-packed array (C8): int8 in [-8, 7] when
+    signed, else uint8 in [0, 15]."""
+    b = np.asarray(b, dtype=np.uint8).ravel().astype(np.int64)
+    nib = np.empty(2 * b.size, np.int64)
+    nib[0::2] = b & 0xF
+    nib[1::2] = b >> 4
+    nib = nib[:n]
+    if signed:
+        return np.where(nib >= 8, nib - 16, nib).astype(np.int8)
+    return nib.astype(np.uint8)
 
 
 def level_spacing(scale_bits: np.ndarray, kind: str, codec: str) -> np.ndarray:
-    """The block's level spacing D of the decodes in C4/C5 (float32 per block):
-    RN32(s/255) (variance, companded), RN32(s/127) (momentum, linear),
-    RN32(RN32(s*s)/255) (variance, linear)."""
+    """The block's level spacing D of the decodes in C4/C5/C8 (float32 per
+    block): RN32(s/255) (variance, companded), RN32(s/15) (variance,
+    companded4), RN32(s/127) (momentum, linear), RN32(RN32(s*s)/255)
+    (variance, linear)."""
     s = f16_bits_to_f32(scale_bits)
     with np.errstate(all="ignore"):
-        if kind == "v" and codec == "companded":
-            return (s / F32(255.0)).astype(F32)
+        if kind == "v" and codec in ("companded", "companded4"):
+            return (s / F32(CODE_MAX[codec][1])).astype(F32)
         if kind == "m" and codec == "linear":
             return (s / F32(127.0)).astype(F32)
         if kind == "v" and codec == "linear":
@@ -154,9 +207,12 @@ def level_spacing(scale_bits: np.ndarray, kind: str, codec: str) -> np.ndarray:
     raise ValueError((kind, codec))
 
 
-def _phi_code(a64: np.ndarray) -> np.ndarray:
-    """round_half_even(127 * phi(a)), phi(a) = 2a/(1+a), for 0 <= a <= 1 (C3)."""
-    return np.rint(254.0 * a64 / (1.0 + a64))
+def _phi_code(a64: np.ndarray, L: int = 127) -> np.ndarray:
+    """round_half_even(L * phi(a)), phi(a) = 2a/(1+a), for 0 <= a <= 1 (C3, C8).
+    float64 decides exactly: a float32 a lies at least 2^-35 (L = 127) or
+    2^-31 (L = 7) from every threshold in units of L*phi, far above float64's
+    error."""
+    return np.rint(2.0 * L * a64 / (1.0 + a64))
 
 
 def _saturating_code(y: np.ndarray, lo: int, hi: int) -> np.ndarray:
@@ -171,10 +227,10 @@ def encode_momentum(m: np.ndarray, scale_bits: np.ndarray, codec: str = "compand
     s = _per_elem(scale_bits, m.size)
     with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
         z = (m / s).astype(F32)                                   # one float32 division (C3, C5)
-        if codec == "companded":
+        if codec in ("companded", "companded4"):
             nan = np.isnan(z)
             a = np.fmin(np.abs(np.where(nan, F32(0), z)), F32(1.0)).astype(np.float64)
-            q = _phi_code(a)
+            q = _phi_code(a, CODE_MAX[codec][0])
             q = np.where(z < 0, -q, q)
             q = np.where(nan, 0, q)                               # C6
         elif codec == "linear":
@@ -186,10 +242,11 @@ def encode_momentum(m: np.ndarray, scale_bits: np.ndarray, codec: str = "compand
 
 def decode_momentum(q: np.ndarray, scale_bits: np.ndarray, codec: str = "companded") -> np.ndarray:
     q = np.asarray(q, dtype=np.int8).ravel()
-    if codec == "companded":
+    if codec in ("companded", "companded4"):
+        L = CODE_MAX[codec][0]
         s = _per_elem(scale_bits, q.size)
-        lut = momentum_lut("companded")
-        return (s * lut[np.maximum(q.astype(np.int64), -127) + 127]).astype(F32)   # C7
+        lut = momentum_lut(codec)
+        return (s * lut[np.maximum(q.astype(np.int64), -L) + L]).astype(F32)   # C7, C8
     if codec == "linear":
         d = np.repeat(level_spacing(scale_bits, "m", "linear"), BLOCK)[: q.size]
         return (d * q.astype(F32)).astype(F32)
@@ -200,16 +257,17 @@ def encode_variance(v: np.ndarray, scale_bits: np.ndarray, codec: str = "compand
     v = np.asarray(v, dtype=np.float32).ravel()
     s = _per_elem(scale_bits, v.size)
     with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
-        if codec == "companded":
-            w = np.sqrt(v).astype(F32)                            # correctly rounded (C4)
+        if codec in ("companded", "companded4"):
+            w = np.sqrt(v).astype(F32)                            # correctly rounded (C4, C8)
             z = (w / s).astype(F32)
         elif codec == "linear":
             s2 = (s * s).astype(F32)                              # exact: 11-bit significands
             z = (v / s2).astype(F32)
         else:
             raise ValueError(codec)
-        y = (F32(255.0) * z).astype(F32)
-        q = _saturating_code(y, 0, 255)
+        top = CODE_MAX[codec][1]
+        y = (F32(top) * z).astype(F32)
+        q = _saturating_code(y, 0, top)
     return q.astype(np.uint8)
 
 
@@ -217,7 +275,7 @@ def decode_variance(q: np.ndarray, scale_bits: np.ndarray, codec: str = "compand
     q = np.asarray(q, dtype=np.uint8).ravel()
     d = np.repeat(level_spacing(scale_bits, "v", codec), BLOCK)[: q.size]
     qf = q.astype(F32)
-    if codec == "companded":
+    if codec in ("companded", "companded4"):
         t = (d * qf).astype(F32)
         return (t * t).astype(F32)
     if codec == "linear":
@@ -226,7 +284,8 @@ def decode_variance(q: np.ndarray, scale_bits: np.ndarray, codec: str = "compand
 
 
 def quantize_state(x: np.ndarray, kind: str, codec: str = "companded"):
-    """f32 state -> (codes, fp16 scale bits)."""
+    """f32 state -> (codes, fp16 scale bits); one code per element (4-bit
+    codes unpacked: pack_nibbles gives their stored bytes)."""
     s = block_scales(x, kind)
     if kind == "m":
         return encode_momentum(x, s, codec), s

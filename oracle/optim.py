@@ -59,10 +59,13 @@ import numpy as np
 
 from .codecs import (
     block_scales,
+    code_bytes,
     decode_momentum,
     decode_variance,
     encode_momentum,
     encode_variance,
+    pack_nibbles,
+    unpack_nibbles,
 )
 from .numerics import bf16_bits_to_f32, f16_bits_to_f32, reconstruct_weights, split_weights
 
@@ -149,29 +152,46 @@ def widen_grad(grad_bits: np.ndarray, fmt: str) -> np.ndarray:
     return bf16_bits_to_f32(grad_bits) if fmt == "bf16" else f16_bits_to_f32(grad_bits)
 
 
+def _stored_codes(stored: np.ndarray, n: int, codec: str, signed: bool) -> np.ndarray:
+    """A state's code array as stored -> one code per element (C8 packs two
+    4-bit codes a byte)."""
+    if codec == "companded4":
+        return unpack_nibbles(stored, n, signed)
+    return np.asarray(stored).ravel()
+
+
+def _stored_form(q: np.ndarray, codec: str) -> np.ndarray:
+    """One code per element -> the state's code array as stored."""
+    if codec == "companded4":
+        return pack_nibbles(q)
+    return q
+
+
 def adamw_step(state: dict, grad_bits: np.ndarray, hp: dict, fmt: str = "bf16",
                ecc_bits: int = 8, codec: str = "companded") -> dict:
     """One fused AdamW step on one tensor.
 
     state: {"w16": uint16, "ecc": int8|int16, "m_q": int8, "m_s": uint16 (fp16 bits),
             "v_q": uint8, "v_s": uint16}; hp: lr, beta1, beta2, eps, weight_decay, step.
+    With codec "companded4" m_q and v_q are the nibble-packed uint8 arrays.
     Returns the new state (same keys).  Steps: widen grad, reconstruct master,
     decode states, update (U3), split, block scales, encode.
     """
     S = adamw_scalars(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"], hp["step"],
                       l2=hp.get("l2_decay", False))
     theta = reconstruct_weights(state["w16"], state["ecc"], fmt, ecc_bits)
+    n = theta.size
     g = widen_grad(grad_bits, fmt)
-    m = decode_momentum(state["m_q"], state["m_s"], codec)
-    v = decode_variance(state["v_q"], state["v_s"], codec)
+    m = decode_momentum(_stored_codes(state["m_q"], n, codec, True), state["m_s"], codec)
+    v = decode_variance(_stored_codes(state["v_q"], n, codec, False), state["v_s"], codec)
     th, m1, v1, _ = adamw_update(theta, g, m, v, S)
     w16, ecc = split_weights(th, fmt, ecc_bits)
     m_s = block_scales(m1, "m")
     v_s = block_scales(v1, "v")
     return {
         "w16": w16, "ecc": ecc,
-        "m_q": encode_momentum(m1, m_s, codec), "m_s": m_s,
-        "v_q": encode_variance(v1, v_s, codec), "v_s": v_s,
+        "m_q": _stored_form(encode_momentum(m1, m_s, codec), codec), "m_s": m_s,
+        "v_q": _stored_form(encode_variance(v1, v_s, codec), codec), "v_s": v_s,
     }
 
 
@@ -186,26 +206,28 @@ def sgdm_step(state: dict, grad_bits: np.ndarray, hp: dict, fmt: str = "bf16",
                      hp.get("nesterov", False))
     theta = reconstruct_weights(state["w16"], state["ecc"], fmt, ecc_bits)
     g = widen_grad(grad_bits, fmt)
-    b = decode_momentum(state["b_q"], state["b_s"], codec)
+    b = decode_momentum(_stored_codes(state["b_q"], theta.size, codec, True), state["b_s"], codec)
     th, b1 = sgdm_update(theta, g, b, S, first=sgdm_first(hp["step"], hp["momentum"]))
     w16, ecc = split_weights(th, fmt, ecc_bits)
     b_s = block_scales(b1, "m")
-    return {"w16": w16, "ecc": ecc, "b_q": encode_momentum(b1, b_s, codec), "b_s": b_s}
+    return {"w16": w16, "ecc": ecc, "b_q": _stored_form(encode_momentum(b1, b_s, codec), codec), "b_s": b_s}
 
 
-def fresh_adamw_state(x32: np.ndarray, fmt: str = "bf16", ecc_bits: int = 8) -> dict:
+def fresh_adamw_state(x32: np.ndarray, fmt: str = "bf16", ecc_bits: int = 8, codec: str = "companded") -> dict:
     """Split an f32 weight and attach zero states (zero codes and zero scales
     decode to exactly 0)."""
     w16, ecc = split_weights(x32, fmt, ecc_bits)
     n = w16.size
     nb = -(-n // 32)
+    qt = np.uint8 if codec == "companded4" else np.int8
     return {"w16": w16, "ecc": ecc,
-            "m_q": np.zeros(n, np.int8), "m_s": np.zeros(nb, np.uint16),
-            "v_q": np.zeros(n, np.uint8), "v_s": np.zeros(nb, np.uint16)}
+            "m_q": np.zeros(code_bytes(n, codec), qt), "m_s": np.zeros(nb, np.uint16),
+            "v_q": np.zeros(code_bytes(n, codec), np.uint8), "v_s": np.zeros(nb, np.uint16)}
 
 
-def fresh_sgdm_state(x32: np.ndarray, fmt: str = "bf16", ecc_bits: int = 8) -> dict:
+def fresh_sgdm_state(x32: np.ndarray, fmt: str = "bf16", ecc_bits: int = 8, codec: str = "companded") -> dict:
     w16, ecc = split_weights(x32, fmt, ecc_bits)
     n = w16.size
+    qt = np.uint8 if codec == "companded4" else np.int8
     return {"w16": w16, "ecc": ecc,
-            "b_q": np.zeros(n, np.int8), "b_s": np.zeros(-(-n // 32), np.uint16)}
+            "b_q": np.zeros(code_bytes(n, codec), qt), "b_s": np.zeros(-(-n // 32), np.uint16)}
