@@ -91,9 +91,9 @@ def build_states(cfg, log):
     t0 = time.perf_counter()
     for i, n in enumerate(cfg.numels):
         if cfg.optimizer == "adamw":
-            st = alloc_adamw_state(n, cfg.wfmt, cfg.ecc_bits)
+            st = alloc_adamw_state(n, cfg.wfmt, cfg.ecc_bits, codec=cfg.codec)
         else:
-            st = alloc_sgdm_state(n, cfg.wfmt, cfg.ecc_bits)
+            st = alloc_sgdm_state(n, cfg.wfmt, cfg.ecc_bits, codec=cfg.codec)
         w = device_weights(cfg.name, i, n)
         B.fo_split_weights(w, st["w16"], st["ecc"], cfg.wfmt, cfg.ecc_bits)
         del w
@@ -156,7 +156,7 @@ def _oracle_worker(cfg_name, tasks, barrier, out):
         x = (rng.standard_normal(m, dtype=np.float32) * np.float32(0.02)).astype(np.float32)
         gb = host_grad_bits(host_grads(cfg_name, t_idx, 1, m, cfg.grad_kind), cfg.wfmt)
         fresh = fresh_adamw_state if cfg.optimizer == "adamw" else fresh_sgdm_state
-        inputs.append((fresh(x, cfg.wfmt, cfg.ecc_bits), gb))
+        inputs.append((fresh(x, cfg.wfmt, cfg.ecc_bits, cfg.codec), gb))
     barrier.wait()
     t0 = time.perf_counter()
     elems = 0
@@ -576,7 +576,8 @@ def main(argv=None):
         f"{achieved:.0f} GB/s algorithmic")
 
     probe_gbs = None
-    if not args.no_probe and cfg.optimizer == "adamw":
+    # the stream probe moves the bytes of a step with 8-bit state codes
+    if not args.no_probe and cfg.optimizer == "adamw" and cfg.codec != "companded4":
         pe0, pe1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         for tl in lists:
             B.fo_stream_probe(tl, cfg.wfmt, cfg.ecc_bits, 0)
@@ -618,6 +619,11 @@ def main(argv=None):
         "config": {
             "workload": {
                 "c3_llama8b": "Llama-3.1-8B-shaped parameter list, fused AdamW, bf16 + 8-bit ECC, companded 8-bit states",
+                "c3_llama8b_s4": "Llama-3.1-8B-shaped parameter list, fused AdamW, bf16 + 8-bit ECC, "
+                                 "companded 4-bit states",
+                "c4_resnet50_s4": "ResNet-50-shaped parameter list, fused SGD-M, bf16 + 8-bit ECC, "
+                                  "companded 4-bit states",
+                "c5_flat1g_s4": "one 2^30-element tensor, fused AdamW, bf16 + 8-bit ECC, companded 4-bit states",
             }.get(cfg.name, cfg.name),
             "name": cfg.name,
             "optimizer": cfg.optimizer,

@@ -19,6 +19,9 @@
  *            optimizers, on gradients kept in backward precision and on
  *            gradient release; same blog, Conclusion & Perspective (drop-in
  *            torch.optim replacements).
+ *   [LOWER]  Same blog, Conclusion & Perspective (Future Outlook): states
+ *            below 8 bits as the next step, with no transform given; the
+ *            4-bit codec keeps the 8-bit one's blocks, scales and companders.
  *
  * Numerical definitions.  The pages leave rounding modes, operation order,
  * scale format and compander formulas open; this library fixes them as
@@ -45,6 +48,12 @@
  *     0, 255); decode t = RN(D * q), D = RN(s / 255), v = RN(t * t).  Linear:
  *     q = clamp(rne(RN(255 * RN(v / RN(s * s)))), 0, 255); decode RN(D * q),
  *     D = RN(RN(s * s) / 255).
+ *   4-bit companded codes [LOWER] (FO_COMPANDED4): as the companded codes
+ *     with 7 for 127 (momentum codes in [-7, 7], decode RN(s * RN(q / (14 - |q|))),
+ *     the pattern -8 decodes as -7) and 15 for 255 (variance codes in [0, 15],
+ *     D = RN(s / 15)).  Two codes per byte: element 2i in the low nibble,
+ *     2i+1 in the high one, momentum codes in 4-bit two's complement; a code
+ *     array holds ceil(n/2) bytes and an odd n leaves the last high nibble 0.
  *   A NaN state element gets code 0 (the rule of saturating float-to-integer
  *   conversion); +-Inf takes the end codes.
  *   Updates: see fo_fused_adamw_step and fo_fused_sgdm_step.
@@ -93,10 +102,11 @@
 extern "C" {
 #endif
 
-#define FO_ABI_VERSION 4   /* 2: l2_decay in fo_adamw_hparams; dampening, nesterov in fo_sgdm_hparams;
+#define FO_ABI_VERSION 5   /* 2: l2_decay in fo_adamw_hparams; dampening, nesterov in fo_sgdm_hparams;
                               3: correctly rounded quotients in the update and the codecs, NaN codes 0,
                                  NaN-only short last blocks keep a NaN scale, SGD momentum 0 as torch;
-                              4: fo_hbm_probe takes a chunk size (and an in-place mode) */
+                              4: fo_hbm_probe takes a chunk size (and an in-place mode);
+                              5: FO_COMPANDED4, 4-bit state codes */
 
 enum fo_status {
   FO_OK = 0,
@@ -109,10 +119,11 @@ enum fo_status {
 /* 16-bit downcast format of theta' (and of the gradients). */
 enum fo_wfmt { FO_BF16 = 0, FO_FP16 = 1 };
 /* State code mapping: companded (softsign-like momentum, square-root
- * variance) or the linear ablation with the same scales. */
-enum fo_codec { FO_COMPANDED = 0, FO_LINEAR = 1 };
-/* State kind: signed momentum-like (int8 codes in [-127,127]) or unsigned
- * variance-like (uint8 codes in [0,255]). */
+ * variance), the linear ablation with the same scales, or the companded
+ * mapping onto 4-bit codes, two per byte. */
+enum fo_codec { FO_COMPANDED = 0, FO_LINEAR = 1, FO_COMPANDED4 = 2 };
+/* State kind: signed momentum-like (int8 codes in [-127,127]; [-7,7] as
+ * 4-bit codes) or unsigned variance-like (uint8 codes in [0,255]; [0,15]). */
 enum fo_kind { FO_MOMENTUM = 0, FO_VARIANCE = 1 };
 
 /*
@@ -145,12 +156,13 @@ int fo_reconstruct_weights(const void* w16, const void* ecc, int64_t n, int wfmt
                            int ecc_bits, float* w32_out, void* stream);
 
 /*
- * fo_companded_quantize -- [STATE]
- * Quantises an f32 state to 8-bit codes plus one fp16 scale per 32 elements.
+ * fo_companded_quantize -- [STATE], [LOWER]
+ * Quantises an f32 state to 8-bit (or 4-bit) codes plus one fp16 scale per
+ * 32 elements.
  *   x          : n float32 (read); variance states must be >= 0
  *   kind       : FO_MOMENTUM (int8 codes) or FO_VARIANCE (uint8 codes)
- *   codec      : FO_COMPANDED or FO_LINEAR
- *   codes_out  : n bytes (written)
+ *   codec      : FO_COMPANDED, FO_LINEAR or FO_COMPANDED4
+ *   codes_out  : n bytes, or ceil(n/2) under FO_COMPANDED4 (written)
  *   scales_out : ceil(n/32) fp16 bit patterns (written)
  * Momentum scale = smallest fp16 >= max|x| of the block; variance scale =
  * smallest fp16 >= sqrt(max x) of the block (both saturate at 65504).
@@ -160,15 +172,17 @@ int fo_companded_quantize(const float* x, int64_t n, int kind, int codec,
 
 /*
  * fo_dequantize -- [STATE]
- * Decodes 8-bit codes and fp16 block scales back to f32 (inverse mapping of
- * fo_companded_quantize for the same kind and codec).
- *   codes : n bytes (read);  scales : ceil(n/32) fp16 (read);  x_out : n float32 (written)
+ * Decodes 8-bit (or 4-bit) codes and fp16 block scales back to f32 (inverse
+ * mapping of fo_companded_quantize for the same kind and codec).
+ *   codes : n bytes, or ceil(n/2) under FO_COMPANDED4 (read);
+ *   scales : ceil(n/32) fp16 (read);  x_out : n float32 (written)
  */
 int fo_dequantize(const void* codes, const uint16_t* scales, int64_t n, int kind,
                   int codec, float* x_out, void* stream);
 
 /* One tensor of a fused AdamW step.  All arrays hold n elements except the
- * scale arrays, which hold ceil(n/32).  w16/ecc/codes/scales are updated in
+ * scale arrays, which hold ceil(n/32), and the code arrays under
+ * FO_COMPANDED4, which hold ceil(n/2) bytes.  w16/ecc/codes/scales are updated in
  * place; grad (same 16-bit format as w16) is only read. */
 typedef struct fo_adamw_tensor {
   void*        w16;   /* theta', bf16 or fp16 */
@@ -245,7 +259,7 @@ typedef struct fo_sgdm_tensor {
   void*        w16;
   void*        ecc;
   const void*  grad;
-  int8_t*      b_q;   /* momentum-buffer codes */
+  int8_t*      b_q;   /* momentum-buffer codes (ceil(n/2) bytes under FO_COMPANDED4) */
   uint16_t*    b_s;   /* momentum-buffer scales (fp16 bits) */
   int64_t      n;
 } fo_sgdm_tensor;

@@ -32,7 +32,9 @@
 namespace fo {
 
 enum { BF16 = 0, FP16 = 1 };
-enum { COMPANDED = 0, LINEAR = 1 };
+// state codecs: 8-bit companded, 8-bit linear, 4-bit companded (two codes a byte)
+enum { COMPANDED = 0, LINEAR = 1, COMPANDED4 = 2 };
+template <int CODEC> constexpr int code_bits = (CODEC == COMPANDED4) ? 4 : 8;
 
 // Pointers into device memory are declared in the global address space so the
 // compiler emits global_* (not flat_*) memory instructions: flat accesses share
@@ -428,40 +430,71 @@ constexpr int MENC_SHIFT = 17;
 constexpr uint32_t MENC_BASE = 0x3B000000u >> MENC_SHIFT;                 // 2^-9
 constexpr int MENC_N = (int)((0x3F800000u >> MENC_SHIFT) - MENC_BASE) + 1;  // keys up to a = 1
 constexpr int MENC_NAN = MENC_N;                                           // NaN (and a > 1)
-constexpr int MENC_CAP = 640;                            // pads the tables to 6 KiB
+// The 4-bit momentum code round(7*phi(a)) (codec COMPANDED4) is taken the
+// same way from a table keyed by bits 21..30 of a (exponent and 2 mantissa
+// bits), clamped to [M4_BASE, M4_BASE + M4_NAN]: every a below 2^-5 shares the
+// first key, and every other key interval holds at most one of the seven
+// thresholds (2k+1)/(27-2k) (they are 1/27, 3/25, 5/23, 1/3, 9/19, 11/17 and
+// 13/15, each in its own quarter-binade at or above 2^-5).
+constexpr int M4_SHIFT = 21;
+constexpr uint32_t M4_BASE = 0x3D000000u >> M4_SHIFT;                     // 2^-5
+constexpr int M4_N = (int)((0x3F800000u >> M4_SHIFT) - M4_BASE) + 1;      // keys up to a = 1
+constexpr int M4_NAN = M4_N;
+constexpr int M4_CAP = 24;
+static_assert(M4_CAP > M4_NAN, "4-bit interval table capacity");
+constexpr int MENC_CAP = 608;                            // pads the tables to 6 KiB
 static_assert(MENC_CAP > MENC_NAN, "interval table capacity");
 // Codec tables (built once per device by k_init_tables, copied into LDS):
-//   lut[q + 128] = RN32(q / (254 - |q|)) for q in [-127, 127]: momentum levels;
-//                  lut[0] (code -128, never written by the encoder) = lut[1]
-//   menc[k]      = interval table of the momentum code as above
-struct CodecTables { float lut[256]; MEnc menc[MENC_CAP]; };
+//   lut[q + 128]  = RN32(q / (254 - |q|)) for q in [-127, 127]: momentum levels;
+//                   lut[0] (code -128, never written by the encoder) = lut[1]
+//   menc[k]       = interval table of the momentum code as above
+//   lut4[q + 8]   = RN32(q / (14 - |q|)) for q in [-7, 7]: 4-bit momentum
+//                   levels; lut4[0] (pattern -8, never written) = lut4[1]
+//   menc4[k]      = interval table of the 4-bit momentum code
+struct CodecTables { float lut[256]; MEnc menc[MENC_CAP]; float lut4[16]; MEnc menc4[M4_CAP]; };
 constexpr int LUT_BIAS = 128;
+constexpr int LUT4_BIAS = 8;
 static_assert(sizeof(CodecTables) == 6 * 1024, "six 1-KiB chunks: one 64-lane x 16-B load each");
 
-// Builds the tables (one workgroup).  thr[k] = smallest f32 >= (2k+1)/(507-2k),
-// the a at which round(127*phi(a)) steps from k to k+1.
+// thr[k] = smallest f32 >= (2k+1)/(4L-1-2k), the a at which round(L*phi(a))
+// steps from k to k+1 (k < L): L*2a/(1+a) = k + 1/2 solved for a
+__device__ __forceinline__ float code_threshold(int k, int L) {
+  const float a = (float)(2 * k + 1), b = (float)(4 * L - 1 - 2 * k);
+  float t = a / b;                                      // nearest
+  if (__builtin_fmaf(t, b, -a) < 0.0f) t = u2f(f2u(t) + 1u);     // exact residual: step up
+  return t;
+}
+// interval table entry of key interval [lo, hi) for thresholds thr[0..L)
+__device__ __forceinline__ MEnc interval_entry(float lo, float hi, const float* thr, int L) {
+  int code = 0;
+  for (int k = 0; k < L; ++k) code += (thr[k] <= lo) ? 1 : 0;
+  MEnc e;
+  e.code = code;
+  e.thr = (code < L && thr[code] < hi) ? thr[code] : 2.0f;
+  return e;
+}
+
+// Builds the tables (one workgroup; thr holds 127 + 7 floats).
 __device__ __forceinline__ void build_tables(FO_GLOBAL CodecTables* out, float* thr, int tid, int nthreads) {
+  float* thr4 = thr + 127;
   for (int i = tid; i < 256; i += nthreads) {
     const int q = max(i - LUT_BIAS, -127);
     const int aq = q < 0 ? -q : q;
     out->lut[i] = (float)q / (float)(254 - aq);         // IEEE division
   }
-  for (int k = tid; k < 127; k += nthreads) {
-    const float a = (float)(2 * k + 1), b = (float)(507 - 2 * k);
-    float t = a / b;                                    // nearest
-    if (__builtin_fmaf(t, b, -a) < 0.0f) t = u2f(f2u(t) + 1u);   // exact residual: step up
-    thr[k] = t;
+  for (int i = tid; i < 16; i += nthreads) {
+    const int q = max(i - LUT4_BIAS, -7);
+    const int aq = q < 0 ? -q : q;
+    out->lut4[i] = (float)q / (float)(14 - aq);
   }
+  for (int k = tid; k < 127; k += nthreads) thr[k] = code_threshold(k, 127);
+  for (int k = tid; k < 7; k += nthreads) thr4[k] = code_threshold(k, 7);
   __syncthreads();
   for (int key = tid; key < MENC_CAP; key += nthreads) {
     MEnc e;
     if (key < MENC_N) {
-      const float lo = (key == 0) ? 0.0f : u2f((MENC_BASE + key) << MENC_SHIFT);
-      const float hi = u2f((MENC_BASE + key + 1) << MENC_SHIFT);
-      int code = 0;
-      for (int k = 0; k < 127; ++k) code += (thr[k] <= lo) ? 1 : 0;
-      e.code = code;
-      e.thr = (code < 127 && thr[code] < hi) ? thr[code] : 2.0f;
+      e = interval_entry((key == 0) ? 0.0f : u2f((MENC_BASE + key) << MENC_SHIFT),
+                         u2f((MENC_BASE + key + 1) << MENC_SHIFT), thr, 127);
     } else {
       e.code = 0;
       e.thr = __builtin_nanf("");
@@ -469,27 +502,50 @@ __device__ __forceinline__ void build_tables(FO_GLOBAL CodecTables* out, float* 
     out->menc[key].thr = e.thr;
     out->menc[key].code = e.code;
   }
+  for (int key = tid; key < M4_CAP; key += nthreads) {
+    MEnc e;
+    if (key < M4_N) {
+      e = interval_entry((key == 0) ? 0.0f : u2f((M4_BASE + key) << M4_SHIFT),
+                         u2f((M4_BASE + key + 1) << M4_SHIFT), thr4, 7);
+    } else {
+      e.code = 0;
+      e.thr = __builtin_nanf("");
+    }
+    out->menc4[key].thr = e.thr;
+    out->menc4[key].code = e.code;
+  }
 }
 
-// Code of a = |z| for 0 <= a <= 1 or NaN (NaN -> 0), sign of z applied.
+// Code of a = |z| for 0 <= a <= 1 or NaN (NaN -> 0), sign of z applied; BITS
+// = 8 (codes in [-127, 127]) or 4 (codes in [-7, 7]).
+template <int BITS>
 __device__ __forceinline__ int32_t momentum_code(float z, const CodecTables& T) {
-  const uint32_t kb = __builtin_amdgcn_ubfe(f2u(z), MENC_SHIFT, 14);
-  const uint32_t key = min(max(kb, MENC_BASE), MENC_BASE + (uint32_t)MENC_NAN) - MENC_BASE;   // v_med3_u32
-  const MEnc e = T.menc[key];
+  MEnc e;
+  if constexpr (BITS == 8) {
+    const uint32_t kb = __builtin_amdgcn_ubfe(f2u(z), MENC_SHIFT, 14);
+    const uint32_t key = min(max(kb, MENC_BASE), MENC_BASE + (uint32_t)MENC_NAN) - MENC_BASE;   // v_med3_u32
+    e = T.menc[key];
+  } else {
+    const uint32_t kb = __builtin_amdgcn_ubfe(f2u(z), M4_SHIFT, 10);
+    const uint32_t key = min(max(kb, M4_BASE), M4_BASE + (uint32_t)M4_NAN) - M4_BASE;
+    e = T.menc4[key];
+  }
   const int32_t q = e.code + (fabsf(z) >= e.thr ? 1 : 0);
   return (z < 0.0f) ? -q : q;
 }
 
 // momentum, companded, fast form: s > 0 finite with |m| <= s, or s = 0 / NaN
 // (then z is NaN and the code 0).  R = RN(1/s).
+template <int BITS = 8>
 __device__ __forceinline__ int32_t encode_m_companded(float m, float s, float R, const CodecTables& T) {
-  return momentum_code(div_refined(m, s, R), T);
+  return momentum_code<BITS>(div_refined(m, s, R), T);
 }
 // momentum, companded, any m and s (IEEE division, clamp at |z| = 1)
+template <int BITS = 8>
 __device__ __forceinline__ int32_t encode_m_companded_ieee(float m, float s, const CodecTables& T) {
   const float z = m / s;
   if (z != z) return 0;
-  return momentum_code(__builtin_copysignf(fminf(fabsf(z), 1.0f), z), T);
+  return momentum_code<BITS>(__builtin_copysignf(fminf(fabsf(z), 1.0f), z), T);
 }
 // momentum, linear: y = RN(127 * RN(m/s)); fast form for |m| <= s, the IEEE
 // form clamps |y| to 127; NaN -> 0
@@ -512,6 +568,24 @@ __device__ __forceinline__ uint32_t encode_v_into(float x, float s, float R, uin
 }
 __device__ __forceinline__ uint32_t encode_v_into_ieee(float x, float s, uint32_t k, uint32_t acc) {
   return __builtin_amdgcn_cvt_pk_u8_f32(255.0f * (x / s), k, acc);
+}
+
+// 4-bit variance: y = RN(15 * RN(x/s)), code clamp(rne(y), 0, 15) into byte k
+// of acc.  The fast form needs x <= s (then y <= 15; NaN still gives 0); the
+// IEEE form takes any x and clamps the byte to 15.
+__device__ __forceinline__ uint32_t encode_v4_into(float x, float s, float R, uint32_t k, uint32_t acc) {
+  return __builtin_amdgcn_cvt_pk_u8_f32(15.0f * div_refined(x, s, R), k, acc);
+}
+__device__ __forceinline__ uint32_t encode_v4_ieee(float x, float s) {
+  return min(__builtin_amdgcn_cvt_pk_u8_f32(15.0f * (x / s), 0, 0u), 15u);
+}
+
+// Nibble packing of 8 codes of a lane (element i in bits [4i, 4i+4) of one
+// word: element 2b in the low nibble of byte b, 2b+1 in its high nibble).
+// even / odd hold the codes of elements 0,2,4,6 / 1,3,5,7 in their bytes
+// (any sign extension above the nibble is dropped).
+__device__ __forceinline__ uint32_t pack_nibbles(uint32_t even, uint32_t odd) {
+  return (even & 0x0F0F0F0Fu) | ((odd << 4) & 0xF0F0F0F0u);
 }
 
 }  // namespace fo

@@ -146,7 +146,49 @@ __device__ __forceinline__ void store8(gp<uint8_t> base, const uint32_t* w, int 
   }
 }
 
+// 8 4-bit codes of a lane (one word; element i in bits [4i, 4i+4)).  A
+// partial group of cnt < 8 elements reads and writes the (cnt+1)/2 bytes
+// that hold them; the unused high nibble of an odd count is written as 0.
+template <bool FULL>
+__device__ __forceinline__ DW<1> load_nib8(gp<const uint8_t> base, int cnt) {
+  DW<1> r;
+  if (FULL || cnt >= 8) {
+    r.w[0] = __builtin_nontemporal_load((gp<const uint32_t>)base);
+    return r;
+  }
+  r.w[0] = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    if (2 * b < cnt) r.w[0] |= (uint32_t)base[b] << (8 * b);
+  return r;
+}
+template <bool FULL>
+__device__ __forceinline__ void store_nib8(gp<uint8_t> base, uint32_t w, int cnt) {
+  if (FULL || cnt >= 8) {
+    __builtin_nontemporal_store(w, (gp<uint32_t>)base);
+    return;
+  }
+  w &= (1u << (4 * cnt)) - 1u;                 // cnt < 8: the nibbles past the end are 0
+#pragma unroll
+  for (int b = 0; b < 4; ++b)
+    if (2 * b < cnt) base[b] = (uint8_t)(w >> (8 * b));
+}
+// the code words of 8 elements under a codec: 2 words of bytes or 1 of nibbles
+template <int CODEC> constexpr int code_words = code_bits<CODEC> / 4;
+template <int CODEC, bool FULL>
+__device__ __forceinline__ DW<code_words<CODEC>> load_codes(gp<const uint8_t> base, int cnt) {
+  if constexpr (CODEC == COMPANDED4) return load_nib8<FULL>(base, cnt);
+  else return load8<1, FULL>(base, cnt);
+}
+template <int CODEC, bool FULL>
+__device__ __forceinline__ void store_codes(gp<uint8_t> base, const uint32_t* w, int cnt) {
+  if constexpr (CODEC == COMPANDED4) store_nib8<FULL>(base, w[0], cnt);
+  else store8<1, FULL>(base, w, cnt);
+}
+
 // element k of a packed group
+__device__ __forceinline__ int32_t s4(uint32_t w, int k) { return ((int32_t)(w << (28 - 4 * k))) >> 28; }
+__device__ __forceinline__ uint32_t u4(uint32_t w, int k) { return (w >> (4 * k)) & 0xFu; }
 __device__ __forceinline__ int32_t s8(const DW<2>& v, int k) {
   return ((int32_t)(v.w[k >> 2] << (24 - 8 * (k & 3)))) >> 24;
 }
@@ -180,15 +222,25 @@ enum { MOMENTUM_STATE = 0, VARIANCE_STATE = 1 };
 // divisors with 11-bit significands).  A non-finite s divides to itself.
 template <int KIND, int CODEC>
 __device__ __forceinline__ float decode_mult(float s) {
-  constexpr float R127 = 1.0f / 127.0f, R255 = 1.0f / 255.0f;   // RN(1/127), RN(1/255)
-  if constexpr (KIND == MOMENTUM_STATE && CODEC == COMPANDED) return s;
+  // RN(1/127), RN(1/255), RN(1/15)
+  constexpr float R127 = 1.0f / 127.0f, R255 = 1.0f / 255.0f, R15 = 1.0f / 15.0f;
+  if constexpr (KIND == MOMENTUM_STATE && CODEC != LINEAR) return s;
   const float x = (KIND == VARIANCE_STATE && CODEC == LINEAR) ? s * s : s;
-  const float q = (KIND == MOMENTUM_STATE) ? div_refined(x, 127.0f, R127) : div_refined(x, 255.0f, R255);
+  const float q = (CODEC == COMPANDED4)       ? div_refined(x, 15.0f, R15)
+                  : (KIND == MOMENTUM_STATE) ? div_refined(x, 127.0f, R127)
+                                             : div_refined(x, 255.0f, R255);
   return (fabsf(x) <= 0x1p126f) ? q : x;
 }
-template <int KIND, int CODEC>
-__device__ __forceinline__ float decode_state(const DW<2>& q, int i, float dm, const CodecTables& T) {
-  if constexpr (KIND == MOMENTUM_STATE) {
+template <int KIND, int CODEC, int NDW>
+__device__ __forceinline__ float decode_state(const DW<NDW>& q, int i, float dm, const CodecTables& T) {
+  if constexpr (CODEC == COMPANDED4) {
+    if constexpr (KIND == MOMENTUM_STATE) {
+      return dm * T.lut4[s4(q.w[0], i) + LUT4_BIAS];
+    } else {
+      const float t = dm * (float)u4(q.w[0], i);
+      return t * t;
+    }
+  } else if constexpr (KIND == MOMENTUM_STATE) {
     const int32_t c = s8(q, i);
     return (CODEC == COMPANDED) ? dm * T.lut[c + LUT_BIAS] : dm * (float)c;
   } else {
@@ -197,9 +249,9 @@ __device__ __forceinline__ float decode_state(const DW<2>& q, int i, float dm, c
   }
 }
 // The value a state's block maximum and its codes are taken from: the state
-// itself, or for a variance-kind state under the companded codec its square
+// itself, or for a variance-kind state under a companded codec its square
 // root (which the rule supplies).
-template <int KIND, int CODEC> constexpr bool encodes_root = (KIND == VARIANCE_STATE && CODEC == COMPANDED);
+template <int KIND, int CODEC> constexpr bool encodes_root = (KIND == VARIANCE_STATE && CODEC != LINEAR);
 
 // ---------------------------------------------------------------------------
 // update rules
@@ -332,6 +384,66 @@ struct SGDMRule {
 };
 
 // ---------------------------------------------------------------------------
+// codes of 8 elements of a lane
+// ---------------------------------------------------------------------------
+// x holds what the codes are taken from (the state, or the variance's square
+// root under a companded codec), s the block's divisor and R = RN(1/s);
+// ieee (wave-uniform) selects the forms that take any x and s.  o receives
+// the packed codes: 2 words of bytes, or 1 word of nibbles.
+template <int CODEC>
+__device__ __forceinline__ void encode_group(int kind, const float (&x)[EPL], float s, float R, bool ieee,
+                                             const CodecTables& tabs, uint32_t* o) {
+  static_assert(EPL == 8, "8 codes per lane");
+  if (kind == MOMENTUM_STATE) {
+    uint32_t q[EPL];
+    if (!ieee) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        q[i] = (uint32_t)((CODEC == LINEAR)      ? encode_m_linear(x[i], s, R)
+                          : (CODEC == COMPANDED) ? encode_m_companded<8>(x[i], s, R, tabs)
+                                                 : encode_m_companded<4>(x[i], s, R, tabs));
+    } else {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        q[i] = (uint32_t)((CODEC == LINEAR)      ? encode_m_linear_ieee(x[i], s)
+                          : (CODEC == COMPANDED) ? encode_m_companded_ieee<8>(x[i], s, tabs)
+                                                 : encode_m_companded_ieee<4>(x[i], s, tabs));
+    }
+    if constexpr (CODEC == COMPANDED4) {
+      o[0] = pack_nibbles(pack4_byte0(q[0], q[2], q[4], q[6]), pack4_byte0(q[1], q[3], q[5], q[7]));
+    } else {
+      o[0] = pack4_byte0(q[0], q[1], q[2], q[3]);
+      o[1] = pack4_byte0(q[4], q[5], q[6], q[7]);
+    }
+  } else if constexpr (CODEC == COMPANDED4) {
+    uint32_t ev = 0u, od = 0u;                 // codes of the even / odd elements, one per byte
+    if (!ieee) {
+#pragma unroll
+      for (int i = 0; i < EPL; i += 2) {
+        ev = encode_v4_into(x[i], s, R, i >> 1, ev);
+        od = encode_v4_into(x[i + 1], s, R, i >> 1, od);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < EPL; i += 2) {
+        ev |= encode_v4_ieee(x[i], s) << (4 * i);
+        od |= encode_v4_ieee(x[i + 1], s) << (4 * i);
+      }
+    }
+    o[0] = pack_nibbles(ev, od);
+  } else {
+    o[0] = o[1] = 0u;
+    if (!ieee) {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) o[i >> 2] = encode_v_into(x[i], s, R, i & 3, o[i >> 2]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) o[i >> 2] = encode_v_into_ieee(x[i], s, i & 3, o[i >> 2]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fused step: one wave tile for any update rule
 // ---------------------------------------------------------------------------
 template <class R, int WFMT, int ECC, int CODEC, bool FULL>
@@ -341,16 +453,17 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
   constexpr int EB = ECC / 8;                                  // ECC bytes per element
   constexpr int K0 = R::template KIND<0>;
   constexpr int K1 = R::template KIND<NS - 1>;
+  constexpr int QW = code_words<CODEC>;                        // code words per lane and sub-tile
   const int Q = lane >> 2, p = lane & 3;
   const gp<const uint8_t> grad = (gp<const uint8_t>)d.grad + e0 * 2;
   const gp<uint8_t> w16 = (gp<uint8_t>)d.w16 + e0 * 2;
   const gp<uint8_t> ecc = (gp<uint8_t>)d.ecc + e0 * EB;
   gp<uint8_t> qp[NS];
   gp<uint16_t> sp[NS];
-  qp[0] = (gp<uint8_t>)d.q1 + e0;
+  qp[0] = (gp<uint8_t>)d.q1 + e0 * QW / 2;                    // code bytes: e0 or e0 / 2
   sp[0] = (gp<uint16_t>)d.s1 + (e0 >> 5);
   if constexpr (NS == 2) {
-    qp[NS - 1] = (gp<uint8_t>)d.q2 + e0;
+    qp[NS - 1] = (gp<uint8_t>)d.q2 + e0 * QW / 2;
     sp[NS - 1] = (gp<uint16_t>)d.s2 + (e0 >> 5);
   }
   const int64_t rem = d.n - e0;                                // valid elements from e0 on
@@ -360,7 +473,7 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
   // ---- issue the tile's loads ---------------------------------------------
   DW<4> G[NSUB], W[NSUB];
   DW<2 * EB> E[NSUB];
-  DW<2> SQ[NS][NSUB];
+  DW<QW> SQ[NS][NSUB];
   int cnt[NSUB];
   // the gradients first: the rule's tile-wide range check waits for them
   // only (the vector memory counter retires loads in issue order)
@@ -376,7 +489,7 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
     W[j] = load8<2, FULL>(w16 + off * 2, cnt[j]);
     E[j] = load8<EB, FULL>(ecc + off * EB, cnt[j]);
 #pragma unroll
-    for (int k = 0; k < NS; ++k) SQ[k][j] = load8<1, FULL>(qp[k] + off, cnt[j]);
+    for (int k = 0; k < NS; ++k) SQ[k][j] = load_codes<CODEC, FULL>(qp[k] + off * QW / 2, cnt[j]);
   };
   // the first half now, the second half once sub-tile 0 is updated: fewer
   // bytes in flight per wave at once measure about 0.7% faster on every
@@ -470,8 +583,10 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
     // RN(1/divisor) for the fast encodes; a zero divisor gives NaN, which
     // codes the block's zeros (and NaNs) 0 as the division 0/0 would
     r_own[k] = rcp_refined(s_own[k]);
-    // the fast encodes need |x| <= s (momentum) or a finite x (variance)
-    sat |= (kind == MOMENTUM_STATE) ? (own_max[k] > 65504.0f) : (own_max[k] == __builtin_inff());
+    // the fast encodes need |x| <= s (momentum, and 4-bit variance, whose
+    // conversion saturates at 255 instead of 15) or a finite x (variance)
+    sat |= (kind == MOMENTUM_STATE || CODEC == COMPANDED4) ? (own_max[k] > 65504.0f)
+                                                           : (own_max[k] == __builtin_inff());
   }
   const bool sat_wave = __builtin_amdgcn_ballot_w64(sat) != 0;
 
@@ -482,33 +597,9 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
     for (int k = 0; k < NS; ++k) {
       const int kind = (k == 0) ? K0 : K1;
       const float sdiv = bcast_j(s_own[k], j), rdiv = bcast_j(r_own[k], j);
-      uint32_t o[2];
-      if (kind == MOMENTUM_STATE) {
-        uint32_t q[EPL];
-        if (!sat_wave) {
-#pragma unroll
-          for (int i = 0; i < EPL; ++i)
-            q[i] = (uint32_t)((CODEC == COMPANDED) ? encode_m_companded(X[k][j][i], sdiv, rdiv, tabs)
-                                                   : encode_m_linear(X[k][j][i], sdiv, rdiv));
-        } else {
-#pragma unroll
-          for (int i = 0; i < EPL; ++i)
-            q[i] = (uint32_t)((CODEC == COMPANDED) ? encode_m_companded_ieee(X[k][j][i], sdiv, tabs)
-                                                   : encode_m_linear_ieee(X[k][j][i], sdiv));
-        }
-        o[0] = pack4_byte0(q[0], q[1], q[2], q[3]);
-        o[1] = pack4_byte0(q[4], q[5], q[6], q[7]);
-      } else {
-        o[0] = o[1] = 0u;
-        if (!sat_wave) {
-#pragma unroll
-          for (int i = 0; i < EPL; ++i) o[i >> 2] = encode_v_into(X[k][j][i], sdiv, rdiv, i & 3, o[i >> 2]);
-        } else {
-#pragma unroll
-          for (int i = 0; i < EPL; ++i) o[i >> 2] = encode_v_into_ieee(X[k][j][i], sdiv, i & 3, o[i >> 2]);
-        }
-      }
-      store8<1, FULL>(qp[k] + off, o, cnt[j]);
+      uint32_t o[QW];
+      encode_group<CODEC>(kind, X[k][j], sdiv, rdiv, sat_wave, tabs, o);
+      store_codes<CODEC, FULL>(qp[k] + off * QW / 2, o, cnt[j]);
     }
   }
 }
@@ -724,7 +815,7 @@ __global__ void __launch_bounds__(WG) k_bucket_index(const TensorDesc* __restric
 }
 
 __global__ void __launch_bounds__(WG) k_init_tables(CodecTables* out) {
-  __shared__ float thr[128];
+  __shared__ float thr[127 + 7];
   build_tables((gp<CodecTables>)out, thr, threadIdx.x, blockDim.x);
 }
 
@@ -826,7 +917,8 @@ __global__ void __launch_bounds__(WG) k_reconstruct(const uint16_t* __restrict__
   }
 }
 
-// KIND 0 = momentum (int8), 1 = variance (uint8).  A quad of lanes = one block.
+// KIND 0 = momentum (int8, or signed nibbles under COMPANDED4), 1 = variance
+// (uint8, or nibbles).  A quad of lanes = one block.
 template <int KIND, int CODEC>
 __global__ void __launch_bounds__(WG) k_quantize(const float* __restrict__ x, int64_t n,
                                                  uint8_t* __restrict__ codes, uint16_t* __restrict__ scales,
@@ -850,7 +942,7 @@ __global__ void __launch_bounds__(WG) k_quantize(const float* __restrict__ x, in
       for (int k = 0; k < 8; ++k) v[k] = (k < cnt) ? xs[i + k] : __builtin_nanf("");
     }
     float e[8];
-    if (KIND == 1 && CODEC == COMPANDED) {
+    if (KIND == 1 && CODEC != LINEAR) {
       uint64_t slow = 0;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -874,35 +966,14 @@ __global__ void __launch_bounds__(WG) k_quantize(const float* __restrict__ x, in
     const float sf = h2f(sb);
     const float sdiv = (KIND == 1 && CODEC == LINEAR) ? sf * sf : sf;
     const float rdiv = 1.0f / sdiv;
-    const bool sat_wave = __builtin_amdgcn_ballot_w64((KIND == 0) ? (mx > 65504.0f) : (mx == __builtin_inff())) != 0;
-    uint32_t o[2];
-    if (KIND == 0) {
-      uint32_t q[8];
-      if (!sat_wave) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          q[k] = (uint32_t)((CODEC == COMPANDED) ? encode_m_companded(e[k], sdiv, rdiv, tabs)
-                                                 : encode_m_linear(e[k], sdiv, rdiv));
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-          q[k] = (uint32_t)((CODEC == COMPANDED) ? encode_m_companded_ieee(e[k], sdiv, tabs)
-                                                 : encode_m_linear_ieee(e[k], sdiv));
-      }
-      o[0] = pack4_byte0(q[0], q[1], q[2], q[3]);
-      o[1] = pack4_byte0(q[4], q[5], q[6], q[7]);
-    } else {
-      o[0] = o[1] = 0u;
-      if (!sat_wave) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) o[k >> 2] = encode_v_into(e[k], sdiv, rdiv, k & 3, o[k >> 2]);
-      } else {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) o[k >> 2] = encode_v_into_ieee(e[k], sdiv, k & 3, o[k >> 2]);
-      }
-    }
-    if (cnt == 8) store8<1, true>((gp<uint8_t>)codes + i, o, 8);
-    else if (cnt > 0) store8<1, false>((gp<uint8_t>)codes + i, o, cnt);
+    const bool sat_wave =
+        __builtin_amdgcn_ballot_w64((KIND == 0 || CODEC == COMPANDED4) ? (mx > 65504.0f) : (mx == __builtin_inff())) != 0;
+    constexpr int QW = code_words<CODEC>;
+    uint32_t o[QW];
+    encode_group<CODEC>(KIND == 0 ? MOMENTUM_STATE : VARIANCE_STATE, e, sdiv, rdiv, sat_wave, tabs, o);
+    const gp<uint8_t> cp = (gp<uint8_t>)codes + i * QW / 2;
+    if (cnt == 8) store_codes<CODEC, true>(cp, o, 8);
+    else if (cnt > 0) store_codes<CODEC, false>(cp, o, cnt);
   }
 }
 
@@ -917,8 +988,9 @@ __global__ void __launch_bounds__(WG) k_dequantize(const uint8_t* __restrict__ c
   constexpr int SK = (KIND == 0) ? MOMENTUM_STATE : VARIANCE_STATE;
   for (int64_t i = ((int64_t)blockIdx.x * WG + threadIdx.x) * EPL; i < n; i += stride) {
     const int cnt = (int)min((int64_t)8, n - i);
-    const gp<const uint8_t> cp = (gp<const uint8_t>)codes + i;
-    const DW<2> q = (cnt == 8) ? load8<1, true>(cp, 8) : load8<1, false>(cp, cnt);
+    constexpr int QW = code_words<CODEC>;
+    const gp<const uint8_t> cp = (gp<const uint8_t>)codes + i * QW / 2;
+    const DW<QW> q = (cnt == 8) ? load_codes<CODEC, true>(cp, 8) : load_codes<CODEC, false>(cp, cnt);
     // the 8 elements of a thread lie in one 32-element block
     const float dm = decode_mult<SK, CODEC>(h2f(((gp<const uint16_t>)scales)[i >> 5]));
     float v[8];

@@ -277,7 +277,16 @@ int use_entry(TableEntry* e, hipStream_t stream) {
 // ---------------------------------------------------------------------------
 // list validation -> device descriptors
 // ---------------------------------------------------------------------------
+// one array of a tensor: elem_bytes per element (per 32-element block when
+// per_block); elem_bytes 0 means 4-bit codes, two per byte
 struct ArraySpec { const void* p; size_t elem_bytes; bool per_block; const char* name; };
+inline int64_t array_extent(const ArraySpec& s, int64_t n, int64_t nb) {
+  if (s.per_block) return nb * (int64_t)s.elem_bytes;
+  return s.elem_bytes == 0 ? (n + 1) / 2 : n * (int64_t)s.elem_bytes;
+}
+// bytes per element of a codec's code array (0 = two codes per byte)
+inline size_t code_elem_bytes(int codec) { return codec == FO_COMPANDED4 ? 0 : 1; }
+inline bool codec_ok(int codec) { return codec == FO_COMPANDED || codec == FO_LINEAR || codec == FO_COMPANDED4; }
 
 // Element counts above 2^56 cannot describe device memory; rejecting them
 // keeps every byte-range computation below within int64 / uintptr_t.
@@ -307,7 +316,7 @@ int build_descs_into(int ntens, int na, const ArraySpec* arrays, const int64_t* 
       if (!aligned(s.p, s.per_block ? 2 : 16)) return fail(FO_EINVAL, "tensor %d: %s is not %d-byte aligned", i, s.name,
                                                             s.per_block ? 2 : 16);
       const uintptr_t lo = reinterpret_cast<uintptr_t>(s.p);
-      ranges[nranges++] = {lo, lo + (uintptr_t)((s.per_block ? nb : n) * (int64_t)s.elem_bytes)};
+      ranges[nranges++] = {lo, lo + (uintptr_t)array_extent(s, n, nb)};
       ptr[a] = (uint64_t)lo;
     }
     TensorDesc d;
@@ -387,6 +396,9 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
     else if (wfmt == FO_BF16 && ecc == 16 && codec == FO_LINEAR) OUT = KERNEL<BF16, 16, LINEAR>; \
     else if (wfmt == FO_FP16 && ecc == 8 && codec == FO_COMPANDED) OUT = KERNEL<FP16, 8, COMPANDED>; \
     else if (wfmt == FO_FP16 && ecc == 8 && codec == FO_LINEAR) OUT = KERNEL<FP16, 8, LINEAR>;  \
+    else if (wfmt == FO_BF16 && ecc == 8 && codec == FO_COMPANDED4) OUT = KERNEL<BF16, 8, COMPANDED4>; \
+    else if (wfmt == FO_BF16 && ecc == 16 && codec == FO_COMPANDED4) OUT = KERNEL<BF16, 16, COMPANDED4>; \
+    else if (wfmt == FO_FP16 && ecc == 8 && codec == FO_COMPANDED4) OUT = KERNEL<FP16, 8, COMPANDED4>; \
   } while (0)
 
 // AdamW (decoupled decay) and Adam (L2 decay folded into the gradient)
@@ -505,13 +517,14 @@ int fo_companded_quantize(const float* x, int64_t n, int kind, int codec, void* 
                           void* stream) {
   g_err.clear();
   if (kind != FO_MOMENTUM && kind != FO_VARIANCE) return fail(FO_EINVAL, "bad kind %d", kind);
-  if (codec != FO_COMPANDED && codec != FO_LINEAR) return fail(FO_EINVAL, "bad codec %d", codec);
+  if (!codec_ok(codec)) return fail(FO_EINVAL, "bad codec %d", codec);
   if (n < 0 || n > kMaxElems) return fail(FO_EINVAL, "n out of range (%lld)", (long long)n);
   if (n == 0) return FO_OK;
   if (!x || !codes_out || !scales_out) return fail(FO_EINVAL, "NULL pointer");
   if (!aligned(x, 16) || !aligned(codes_out, 16) || !aligned(scales_out, 2)) return fail(FO_EINVAL, "misaligned pointer");
   const int64_t nb = (n + 31) / 32;
-  std::vector<Range> r = {{(uintptr_t)x, (uintptr_t)x + n * 4}, {(uintptr_t)codes_out, (uintptr_t)codes_out + n},
+  const int64_t cb = array_extent({codes_out, code_elem_bytes(codec), false, "codes"}, n, nb);
+  std::vector<Range> r = {{(uintptr_t)x, (uintptr_t)x + n * 4}, {(uintptr_t)codes_out, (uintptr_t)codes_out + cb},
                           {(uintptr_t)scales_out, (uintptr_t)scales_out + nb * 2}};
   int rc = check_alias(r);
   if (rc) return rc;
@@ -520,23 +533,28 @@ int fo_companded_quantize(const float* x, int64_t n, int kind, int codec, void* 
   const CodecTables* tb = nullptr;
   if ((rc = current_device(&dev)) || (rc = elementwise_grid(dev, n, &grid)) || (rc = device_tables(dev, s, &tb))) return rc;
   auto* c = (uint8_t*)codes_out;
-  if (kind == FO_MOMENTUM && codec == FO_COMPANDED) hipLaunchKernelGGL((k_quantize<0, COMPANDED>), grid, WG, 0, s, x, n, c, scales_out, tb);
-  else if (kind == FO_MOMENTUM) hipLaunchKernelGGL((k_quantize<0, LINEAR>), grid, WG, 0, s, x, n, c, scales_out, tb);
-  else if (codec == FO_COMPANDED) hipLaunchKernelGGL((k_quantize<1, COMPANDED>), grid, WG, 0, s, x, n, c, scales_out, tb);
-  else hipLaunchKernelGGL((k_quantize<1, LINEAR>), grid, WG, 0, s, x, n, c, scales_out, tb);
+  void (*kern)(const float*, int64_t, uint8_t*, uint16_t*, const CodecTables*) =
+      (kind == FO_MOMENTUM) ? (codec == FO_COMPANDED ? k_quantize<0, COMPANDED>
+                               : codec == FO_LINEAR  ? k_quantize<0, LINEAR>
+                                                     : k_quantize<0, COMPANDED4>)
+                            : (codec == FO_COMPANDED ? k_quantize<1, COMPANDED>
+                               : codec == FO_LINEAR  ? k_quantize<1, LINEAR>
+                                                     : k_quantize<1, COMPANDED4>);
+  hipLaunchKernelGGL(kern, grid, WG, 0, s, x, n, c, scales_out, tb);
   return launch_check("k_quantize launch");
 }
 
 int fo_dequantize(const void* codes, const uint16_t* scales, int64_t n, int kind, int codec, float* x_out, void* stream) {
   g_err.clear();
   if (kind != FO_MOMENTUM && kind != FO_VARIANCE) return fail(FO_EINVAL, "bad kind %d", kind);
-  if (codec != FO_COMPANDED && codec != FO_LINEAR) return fail(FO_EINVAL, "bad codec %d", codec);
+  if (!codec_ok(codec)) return fail(FO_EINVAL, "bad codec %d", codec);
   if (n < 0 || n > kMaxElems) return fail(FO_EINVAL, "n out of range (%lld)", (long long)n);
   if (n == 0) return FO_OK;
   if (!codes || !scales || !x_out) return fail(FO_EINVAL, "NULL pointer");
   if (!aligned(codes, 16) || !aligned(scales, 2) || !aligned(x_out, 16)) return fail(FO_EINVAL, "misaligned pointer");
   const int64_t nb = (n + 31) / 32;
-  std::vector<Range> r = {{(uintptr_t)x_out, (uintptr_t)x_out + n * 4}, {(uintptr_t)codes, (uintptr_t)codes + n},
+  const int64_t cb = array_extent({codes, code_elem_bytes(codec), false, "codes"}, n, nb);
+  std::vector<Range> r = {{(uintptr_t)x_out, (uintptr_t)x_out + n * 4}, {(uintptr_t)codes, (uintptr_t)codes + cb},
                           {(uintptr_t)scales, (uintptr_t)scales + nb * 2}};
   int rc = check_alias(r);
   if (rc) return rc;
@@ -545,10 +563,14 @@ int fo_dequantize(const void* codes, const uint16_t* scales, int64_t n, int kind
   const CodecTables* tb = nullptr;
   if ((rc = current_device(&dev)) || (rc = elementwise_grid(dev, n, &grid)) || (rc = device_tables(dev, s, &tb))) return rc;
   auto* c = (const uint8_t*)codes;
-  if (kind == FO_MOMENTUM && codec == FO_COMPANDED) hipLaunchKernelGGL((k_dequantize<0, COMPANDED>), grid, WG, 0, s, c, scales, n, x_out, tb);
-  else if (kind == FO_MOMENTUM) hipLaunchKernelGGL((k_dequantize<0, LINEAR>), grid, WG, 0, s, c, scales, n, x_out, tb);
-  else if (codec == FO_COMPANDED) hipLaunchKernelGGL((k_dequantize<1, COMPANDED>), grid, WG, 0, s, c, scales, n, x_out, tb);
-  else hipLaunchKernelGGL((k_dequantize<1, LINEAR>), grid, WG, 0, s, c, scales, n, x_out, tb);
+  void (*kern)(const uint8_t*, const uint16_t*, int64_t, float*, const CodecTables*) =
+      (kind == FO_MOMENTUM) ? (codec == FO_COMPANDED ? k_dequantize<0, COMPANDED>
+                               : codec == FO_LINEAR  ? k_dequantize<0, LINEAR>
+                                                     : k_dequantize<0, COMPANDED4>)
+                            : (codec == FO_COMPANDED ? k_dequantize<1, COMPANDED>
+                               : codec == FO_LINEAR  ? k_dequantize<1, LINEAR>
+                                                     : k_dequantize<1, COMPANDED4>);
+  hipLaunchKernelGGL(kern, grid, WG, 0, s, c, scales, n, x_out, tb);
   return launch_check("k_dequantize launch");
 }
 
@@ -578,28 +600,32 @@ static int list_table(const std::vector<uint8_t>& key, int32_t count, int na, co
   return get_table(dev, key, descs, buckets, tiles, stream, entry);
 }
 
-static void fill_adamw_arrays(const fo_adamw_tensor* list, int32_t count, int ecc_bits, ArraySpec* arrays,
+static void fill_adamw_arrays(const fo_adamw_tensor* list, int32_t count, int ecc_bits, int codec, ArraySpec* arrays,
                               int64_t* ns) {
-  const size_t eb = (size_t)ecc_bits / 8;
+  const size_t eb = (size_t)ecc_bits / 8, qb = code_elem_bytes(codec);
   for (int i = 0; i < count; ++i) {
     const fo_adamw_tensor& t = list[i];
     ns[i] = t.n;
     ArraySpec* a = arrays + (size_t)i * kArraysPerTensor;
     a[0] = {t.w16, 2, false, "w16"}; a[1] = {t.ecc, eb, false, "ecc"}; a[2] = {t.grad, 2, false, "grad"};
-    a[3] = {t.m_q, 1, false, "m_q"}; a[4] = {t.m_s, 2, true, "m_s"}; a[5] = {t.v_q, 1, false, "v_q"};
+    a[3] = {t.m_q, qb, false, "m_q"}; a[4] = {t.m_s, 2, true, "m_s"}; a[5] = {t.v_q, qb, false, "v_q"};
     a[6] = {t.v_s, 2, true, "v_s"};
   }
 }
 
-static int adamw_like_table(const fo_adamw_tensor* list, int32_t count, int wfmt, int ecc_bits, uint8_t tag,
-                            hipStream_t stream, TableEntry** entry) {
-  std::vector<uint8_t> key(1 + sizeof(int32_t) * 2 + (size_t)count * sizeof(fo_adamw_tensor));
+// The cache key holds what the validation depends on: the entry point, the
+// formats (array extents) and the list itself.
+static int adamw_like_table(const fo_adamw_tensor* list, int32_t count, int wfmt, int ecc_bits, int codec,
+                            uint8_t tag, hipStream_t stream, TableEntry** entry) {
+  const int32_t qb = (int32_t)code_elem_bytes(codec);
+  std::vector<uint8_t> key(1 + sizeof(int32_t) * 3 + (size_t)count * sizeof(fo_adamw_tensor));
   key[0] = tag;
   std::memcpy(&key[1], &wfmt, 4);
   std::memcpy(&key[5], &ecc_bits, 4);
-  if (count) std::memcpy(&key[9], list, (size_t)count * sizeof(fo_adamw_tensor));
+  std::memcpy(&key[9], &qb, 4);
+  if (count) std::memcpy(&key[13], list, (size_t)count * sizeof(fo_adamw_tensor));
   return list_table(key, count, 7, [&](ArraySpec* arrays, int64_t* ns) {
-    fill_adamw_arrays(list, count, ecc_bits, arrays, ns);
+    fill_adamw_arrays(list, count, ecc_bits, codec, arrays, ns);
   }, stream, entry);
 }
 
@@ -610,7 +636,7 @@ static int adamw_check_args(const fo_adamw_tensor* list, int32_t count, const fo
   if (count < 0) return fail(FO_EINVAL, "count < 0");
   if (count > 0 && !list) return fail(FO_EINVAL, "list is NULL");
   if (!fmt_ok(hp->wfmt, hp->ecc_bits)) return fail(FO_EINVAL, "unsupported format/ECC combination (%d, %d)", hp->wfmt, hp->ecc_bits);
-  if (hp->codec != FO_COMPANDED && hp->codec != FO_LINEAR) return fail(FO_EINVAL, "bad codec %d", hp->codec);
+  if (!codec_ok(hp->codec)) return fail(FO_EINVAL, "bad codec %d", hp->codec);
   if (hp->step < 1) return fail(FO_EINVAL, "step must be >= 1");
   if (hp->l2_decay != 0 && hp->l2_decay != 1) return fail(FO_EINVAL, "l2_decay must be 0 or 1");
   if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0 && hp->beta2 >= 0.0 && hp->beta2 < 1.0))
@@ -661,7 +687,7 @@ int fo_fused_adamw_step(const fo_adamw_tensor* list, int32_t count, const fo_ada
   hipStream_t s = as_stream(stream);
   std::lock_guard<std::mutex> lk(g_tab_mu);   // table slot stays ours until the use is recorded
   TableEntry* e = nullptr;
-  rc = adamw_like_table(list, count, hp->wfmt, hp->ecc_bits, 'A', s, &e);
+  rc = adamw_like_table(list, count, hp->wfmt, hp->ecc_bits, hp->codec, 'A', s, &e);
   if (rc) return rc;
   if (!e || e->total_tiles == 0) return FO_OK;
   int dev;
@@ -741,7 +767,7 @@ int fo_fused_adamw_step_noalloc(const fo_adamw_tensor* list, int32_t count, cons
     return fail(FO_EINVAL, "the allocation-free step takes at most %d tensors (got %d)", kNoAllocMaxTensors, count);
   hipStream_t s = as_stream(stream);
   std::lock_guard<std::mutex> lk(g_na_mu);
-  fill_adamw_arrays(list, count, hp->ecc_bits, g_na_arrays, g_na_ns);
+  fill_adamw_arrays(list, count, hp->ecc_bits, hp->codec, g_na_arrays, g_na_ns);
   int nd = 0, nbk = 0;
   int64_t tiles = 0;
   rc = build_descs_into(count, 7, g_na_arrays, g_na_ns, g_na_body, g_na_ranges, g_na_descs, &nd, g_na_buckets, &nbk,
@@ -781,7 +807,7 @@ int fo_stream_probe(const fo_adamw_tensor* list, int32_t count, int32_t wfmt, in
   hipStream_t s = as_stream(stream);
   std::lock_guard<std::mutex> lk(g_tab_mu);
   TableEntry* e = nullptr;
-  int rc = adamw_like_table(list, count, wfmt, ecc_bits, 'A', s, &e);
+  int rc = adamw_like_table(list, count, wfmt, ecc_bits, FO_COMPANDED, 'A', s, &e);
   if (rc) return rc;
   if (!e || e->total_tiles == 0) return FO_OK;
   void (*kern)(const TensorDesc*, int, int64_t, int64_t, uint32_t) = (ecc_bits == 8) ? k_stream_probe<8> : k_stream_probe<16>;
@@ -830,7 +856,7 @@ int fo_fused_sgdm_step(const fo_sgdm_tensor* list, int32_t count, const fo_sgdm_
   if (count < 0) return fail(FO_EINVAL, "count < 0");
   if (count > 0 && !list) return fail(FO_EINVAL, "list is NULL");
   if (!fmt_ok(hp->wfmt, hp->ecc_bits)) return fail(FO_EINVAL, "unsupported format/ECC combination (%d, %d)", hp->wfmt, hp->ecc_bits);
-  if (hp->codec != FO_COMPANDED && hp->codec != FO_LINEAR) return fail(FO_EINVAL, "bad codec %d", hp->codec);
+  if (!codec_ok(hp->codec)) return fail(FO_EINVAL, "bad codec %d", hp->codec);
   if (hp->step < 1) return fail(FO_EINVAL, "step must be >= 1");
   if (!(hp->lr >= 0.0) || !(hp->momentum >= 0.0) || !(hp->weight_decay >= 0.0))
     return fail(FO_EINVAL, "lr, momentum and weight_decay must be >= 0");
@@ -840,11 +866,13 @@ int fo_fused_sgdm_step(const fo_sgdm_tensor* list, int32_t count, const fo_sgdm_
     return fail(FO_EINVAL, "Nesterov momentum needs momentum > 0 and dampening 0");
   if (count == 0) return FO_OK;
   hipStream_t s = as_stream(stream);
-  std::vector<uint8_t> key(1 + 8 + (size_t)count * sizeof(fo_sgdm_tensor));
+  const int32_t qb = (int32_t)code_elem_bytes(hp->codec);
+  std::vector<uint8_t> key(1 + 12 + (size_t)count * sizeof(fo_sgdm_tensor));
   key[0] = 'S';
   std::memcpy(&key[1], &hp->wfmt, 4);
   std::memcpy(&key[5], &hp->ecc_bits, 4);
-  std::memcpy(&key[9], list, (size_t)count * sizeof(fo_sgdm_tensor));
+  std::memcpy(&key[9], &qb, 4);
+  std::memcpy(&key[13], list, (size_t)count * sizeof(fo_sgdm_tensor));
   TableEntry* e = nullptr;
   std::lock_guard<std::mutex> lk(g_tab_mu);
   const size_t eb = (size_t)hp->ecc_bits / 8;
@@ -854,7 +882,7 @@ int fo_fused_sgdm_step(const fo_sgdm_tensor* list, int32_t count, const fo_sgdm_
       ns[i] = t.n;
       ArraySpec* a = arrays + (size_t)i * kArraysPerTensor;
       a[0] = {t.w16, 2, false, "w16"}; a[1] = {t.ecc, eb, false, "ecc"}; a[2] = {t.grad, 2, false, "grad"};
-      a[3] = {t.b_q, 1, false, "b_q"}; a[4] = {t.b_s, 2, true, "b_s"};
+      a[3] = {t.b_q, (size_t)qb, false, "b_q"}; a[4] = {t.b_s, 2, true, "b_s"};
     }
   }, s, &e);
   if (rc) return rc;

@@ -15,6 +15,8 @@ that many small tensors share one fused call.
 All arithmetic runs in the HIP library (fo_fused_adamw_step /
 fo_fused_sgdm_step); this module only groups tensors and keeps step counts.
 FlashAdamW, FlashAdam and FlashSGD follow torch.optim.AdamW, Adam and SGD.
+codec="companded4" keeps 4-bit state codes instead (two per byte; the
+blog's Conclusion & Perspective names lower-bit states as the next step).
 
 Between steps the optimizers keep the device addresses of each parameter's
 state tensors (ECC, codes, scales); only theta' and gradient addresses are
@@ -91,7 +93,7 @@ class _FlashBase(torch.optim.Optimizer):
     def __init__(self, params, defaults, wfmt, ecc_bits, codec, grad_release, release_bucket=1 << 26):
         if (wfmt, ecc_bits) not in (("bf16", 8), ("bf16", 16), ("fp16", 8)):
             raise ValueError(f"unsupported weight format {wfmt}+ECC{ecc_bits}")
-        if codec not in ("companded", "linear"):
+        if codec not in ("companded", "linear", "companded4"):
             raise ValueError(f"unknown codec {codec}")
         self.wfmt, self.ecc_bits, self.codec = wfmt, ecc_bits, codec
         self.grad_release = grad_release
@@ -131,7 +133,10 @@ class _FlashBase(torch.optim.Optimizer):
         st["step"] = 0
         st["ecc"] = ecc
         for key, dt, per_block in self._state_keys:
-            st[key] = torch.zeros(_nb(n) if per_block else n, dtype=dt, device=p.device)
+            if per_block or self.codec != "companded4":
+                st[key] = torch.zeros(_nb(n) if per_block else n, dtype=dt, device=p.device)
+            else:                                        # two 4-bit codes per byte
+                st[key] = torch.zeros((n + 1) // 2, dtype=torch.uint8, device=p.device)
 
     # -- master weights -------------------------------------------------------
     @torch.no_grad()

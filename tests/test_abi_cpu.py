@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(B.EXPORTS)
-    assert lib.fo_abi_version() == B.ABI_VERSION == 4
+    assert lib.fo_abi_version() == B.ABI_VERSION == 5
 
 
 def test_struct_layouts_match_header():
@@ -98,3 +98,36 @@ def test_binding_rejects_host_tensors():
         B.AdamWList([st])
     with pytest.raises(ValueError, match="GPU"):
         B.SGDMList([{k: st[k] for k in ("w16", "ecc", "grad", "m_q", "m_s")} | {"b_q": st["m_q"], "b_s": st["m_s"]}])
+
+
+def test_4bit_code_arrays_are_validated_at_half_size():
+    """Under FO_COMPANDED4 a code array spans ceil(n/2) bytes: two code arrays
+    n/2 bytes apart are disjoint there (validation passes; with no GPU the
+    call then fails at the device, not with FO_EALIAS) and overlap under the
+    8-bit codecs (FO_EALIAS).  The same extents hold for quantize."""
+    lib = B.load()
+    P = ctypes.c_void_p
+    n = 4096
+    base = 1 << 24
+    w16, ecc, grad, mq, ms, vs = base, base + 2 * n, base + 3 * n, base + 5 * n, base + 7 * n, base + 8 * n
+    vq = mq + n // 2
+    t = (B.AdamWTensor * 1)(B.AdamWTensor(w16, ecc, grad, mq, ms, vq, vs, n))
+    for codec, alias in (("companded4", False), ("companded", True), ("linear", True)):
+        hp = B.adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.0, 1, codec=codec)
+        rc = lib.fo_fused_adamw_step(t, 1, ctypes.byref(hp), None)
+        assert (rc == B.FO_EALIAS) == alias, (codec, rc, B.fo_last_error())
+        assert rc != B.FO_OK
+    # n - 1 = 4095 codes: 2048 bytes at 4 bits, so the SGD-M buffer ends at vq
+    s2 = (B.SGDMTensor * 2)(B.SGDMTensor(w16, ecc, grad, mq, ms, n - 1),
+                            B.SGDMTensor(w16 + (1 << 20), ecc + (1 << 20), grad + (1 << 20), vq, vs, 16))
+    for codec, alias in (("companded4", False), ("companded", True)):
+        sh = B.sgdm_hparams(0.1, 0.9, 1e-4, 1, codec=codec)
+        rc = lib.fo_fused_sgdm_step(s2, 2, ctypes.byref(sh), None)
+        assert (rc == B.FO_EALIAS) == alias, (codec, rc, B.fo_last_error())
+    # quantize: codes of ceil(n/2) bytes right below the input are disjoint at 4 bits only
+    x = base + (1 << 20)
+    assert lib.fo_companded_quantize(P(x), n, 0, B.FO_COMPANDED, P(x - n // 2), P(base), None) == B.FO_EALIAS
+    assert lib.fo_companded_quantize(P(x), n, 0, B.FO_COMPANDED4, P(x - n // 2), P(base), None) != B.FO_EALIAS
+    assert lib.fo_companded_quantize(P(x), n, 0, 3, P(x - n // 2), P(base), None) == B.FO_EINVAL
+    assert lib.fo_dequantize(P(x - n // 2), P(base), n, 1, B.FO_COMPANDED4, P(x), None) != B.FO_EALIAS
+    assert lib.fo_dequantize(P(x - n // 2), P(base), n, 1, B.FO_COMPANDED, P(x), None) == B.FO_EALIAS

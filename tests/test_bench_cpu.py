@@ -7,6 +7,8 @@ import os
 import subprocess
 import sys
 
+import pytest
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
@@ -31,14 +33,15 @@ def test_launch_count_follows_the_tile_ranges():
     assert sum(bench.launches_per_call([m]) for m in RELEASE_CHUNKS) == len(RELEASE_CHUNKS)
 
 
-def test_cpu_baseline_is_a_measured_wall_rate():
+@pytest.mark.parametrize("name", ["c1_flat1m", "c3_llama8b_s4", "c4_resnet50_s4"])
+def test_cpu_baseline_is_a_measured_wall_rate(name):
     # the oracle leg runs in worker processes released together at a barrier;
     # its value is elements / wall time of the compute phase, and every worker
-    # is joined (none terminated)
+    # is joined (none terminated); 4-bit configs run the oracle on packed states
     sys.path.insert(0, ROOT)
     import bench
     from workloads import config
-    res = bench.cpu_baseline(config("c1_flat1m"), segments=6, seg=4096, log=lambda m: None)
+    res = bench.cpu_baseline(config(name), segments=6, seg=4096, log=lambda m: None)
     assert res["kind"] == "oracle" and res["unit"] == "params/s"
     assert 1 <= res["cores"] <= 16 and res["value"] > 0
     assert "6 segments" in res["sample"] and "wall" in res["sample"]

@@ -30,10 +30,11 @@ class Config:
     def read_write_bytes_per_param(self):
         """Algorithmic HBM bytes (read, written) per parameter by one fused step."""
         e = self.ecc_bits // 8
+        q = 0.5 if self.codec == "companded4" else 1      # bytes per state code
         if self.optimizer == "adamw":
-            # read: grad 2, w16 2, ecc E, m 1, v 1, scales 4/32; write: w16 2, ecc E, m 1, v 1, scales 4/32
-            return (2 + 2 + e + 1 + 1 + 4 / 32), (2 + e + 1 + 1 + 4 / 32)
-        return (2 + 2 + e + 1 + 2 / 32), (2 + e + 1 + 2 / 32)
+            # read: grad 2, w16 2, ecc E, m q, v q, scales 4/32; write: w16 2, ecc E, m q, v q, scales 4/32
+            return (2 + 2 + e + 2 * q + 4 / 32), (2 + e + 2 * q + 4 / 32)
+        return (2 + 2 + e + q + 2 / 32), (2 + e + q + 2 / 32)
 
     def bytes_per_param(self) -> float:
         """Algorithmic HBM bytes moved per parameter by one fused step."""
@@ -59,6 +60,12 @@ CONFIGS = {
     "c5_flat1g_fp16e8": Config("c5_flat1g_fp16e8", "adamw", (("flat", (FLAT_1G,)),), ADAMW_C1, steps=2, wfmt="fp16"),
     "c5_flat1g_bf16e16": Config("c5_flat1g_bf16e16", "adamw", (("flat", (FLAT_1G,)),), ADAMW_C1, steps=2, ecc_bits=16),
     "c5_flat1g_linear": Config("c5_flat1g_linear", "adamw", (("flat", (FLAT_1G,)),), ADAMW_C1, steps=2, codec="linear"),
+    # 4-bit companded states on the same lists
+    "c3_llama8b_s4": Config("c3_llama8b_s4", "adamw", tuple(llama31_8b_shapes()), ADAMW_LM, steps=3,
+                            grad_kind="t3_lognormal", codec="companded4"),
+    "c4_resnet50_s4": Config("c4_resnet50_s4", "sgdm", tuple(resnet50_shapes()), SGDM_C4, steps=20,
+                             grad_kind="normal_outliers", codec="companded4"),
+    "c5_flat1g_s4": Config("c5_flat1g_s4", "adamw", (("flat", (FLAT_1G,)),), ADAMW_C1, steps=2, codec="companded4"),
 }
 
 
