@@ -448,12 +448,12 @@ static_assert(MENC_CAP > MENC_NAN, "interval table capacity");
 //   lut[q + 128]  = RN32(q / (254 - |q|)) for q in [-127, 127]: momentum levels;
 //                   lut[0] (code -128, never written by the encoder) = lut[1]
 //   menc[k]       = interval table of the momentum code as above
-//   lut4[q + 8]   = RN32(q / (14 - |q|)) for q in [-7, 7]: 4-bit momentum
-//                   levels; lut4[0] (pattern -8, never written) = lut4[1]
+//   lut4[c]       = RN32(q / (14 - |q|)) for the 4-bit pattern c = 0..15 of
+//                   the code q (two's complement; pattern 8, the code -8, is
+//                   never written and decodes as -7): 4-bit momentum levels
 //   menc4[k]      = interval table of the 4-bit momentum code
 struct CodecTables { float lut[256]; MEnc menc[MENC_CAP]; float lut4[16]; MEnc menc4[M4_CAP]; };
 constexpr int LUT_BIAS = 128;
-constexpr int LUT4_BIAS = 8;
 static_assert(sizeof(CodecTables) == 6 * 1024, "six 1-KiB chunks: one 64-lane x 16-B load each");
 
 // thr[k] = smallest f32 >= (2k+1)/(4L-1-2k), the a at which round(L*phi(a))
@@ -483,7 +483,7 @@ __device__ __forceinline__ void build_tables(FO_GLOBAL CodecTables* out, float* 
     out->lut[i] = (float)q / (float)(254 - aq);         // IEEE division
   }
   for (int i = tid; i < 16; i += nthreads) {
-    const int q = max(i - LUT4_BIAS, -7);
+    const int q = (i < 8) ? i : max(i - 16, -7);
     const int aq = q < 0 ? -q : q;
     out->lut4[i] = (float)q / (float)(14 - aq);
   }

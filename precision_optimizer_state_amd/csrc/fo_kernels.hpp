@@ -186,9 +186,28 @@ __device__ __forceinline__ void store_codes(gp<uint8_t> base, const uint32_t* w,
   else store8<1, FULL>(base, w, cnt);
 }
 
-// element k of a packed group
-__device__ __forceinline__ int32_t s4(uint32_t w, int k) { return ((int32_t)(w << (28 - 4 * k))) >> 28; }
-__device__ __forceinline__ uint32_t u4(uint32_t w, int k) { return (w >> (4 * k)) & 0xFu; }
+// element k of a packed group.  A nibble word splits once into the nibbles
+// of its even and of its odd elements, one per byte (NibHalves), so each
+// element is then a byte select, which the byte-operand forms of the
+// conversions and shifts take at no cost.  The empty asm statements emit
+// nothing; they keep the compiler from folding the split back into one bit
+// extract per element.
+struct NibHalves { uint32_t ev, od; };
+__device__ __forceinline__ NibHalves nib_halves(uint32_t w) {
+  NibHalves h{w & 0x0F0F0F0Fu, (w >> 4) & 0x0F0F0F0Fu};
+  asm("" : "+v"(h.ev));
+  asm("" : "+v"(h.od));
+  return h;
+}
+__device__ __forceinline__ uint32_t nib4(const NibHalves& h, int k) {
+  return (((k & 1) ? h.od : h.ev) >> (8 * (k >> 1))) & 0xFFu;
+}
+// the decode operand of a lane's loaded code words
+template <int CODEC>
+__device__ __forceinline__ auto code_operand(const DW<code_words<CODEC>>& q) {
+  if constexpr (CODEC == COMPANDED4) return nib_halves(q.w[0]);
+  else return q;
+}
 __device__ __forceinline__ int32_t s8(const DW<2>& v, int k) {
   return ((int32_t)(v.w[k >> 2] << (24 - 8 * (k & 3)))) >> 24;
 }
@@ -231,13 +250,15 @@ __device__ __forceinline__ float decode_mult(float s) {
                                              : div_refined(x, 255.0f, R255);
   return (fabsf(x) <= 0x1p126f) ? q : x;
 }
-template <int KIND, int CODEC, int NDW>
-__device__ __forceinline__ float decode_state(const DW<NDW>& q, int i, float dm, const CodecTables& T) {
+// q: the lane's code words of 8 elements (DW<2> of bytes, or the NibHalves
+// of one nibble word under COMPANDED4)
+template <int KIND, int CODEC, class QW>
+__device__ __forceinline__ float decode_state(const QW& q, int i, float dm, const CodecTables& T) {
   if constexpr (CODEC == COMPANDED4) {
     if constexpr (KIND == MOMENTUM_STATE) {
-      return dm * T.lut4[s4(q.w[0], i) + LUT4_BIAS];
+      return dm * T.lut4[nib4(q, i)];
     } else {
-      const float t = dm * (float)u4(q.w[0], i);
+      const float t = dm * (float)nib4(q, i);
       return t * t;
     }
   } else if constexpr (KIND == MOMENTUM_STATE) {
@@ -521,6 +542,8 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
     float dm[NS];
 #pragma unroll
     for (int k = 0; k < NS; ++k) dm[k] = bcast_j(dm_own[k], j);
+    const auto q0 = code_operand<CODEC>(SQ[0][j]);
+    const auto q1 = code_operand<CODEC>(SQ[NS - 1][j]);
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       g[i] = wid<WFMT>(G[j], i);
@@ -528,8 +551,8 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
         th[i] = ecc_decode_bf16_packed<ECC>(W[j].w[i >> 1], E[j].w[(i * ECC) >> 5], i & 1, (ECC == 8) ? (i & 3) : (i & 1));
       else
         th[i] = ecc_decode<WFMT, ECC>(wid<WFMT>(W[j], i), rho_at<ECC>(E[j], i));
-      st[0][i] = decode_state<K0, CODEC>(SQ[0][j], i, dm[0], tabs);
-      if constexpr (NS == 2) st[NS - 1][i] = decode_state<K1, CODEC>(SQ[NS - 1][j], i, dm[NS - 1], tabs);
+      st[0][i] = decode_state<K0, CODEC>(q0, i, dm[0], tabs);
+      if constexpr (NS == 2) st[NS - 1][i] = decode_state<K1, CODEC>(q1, i, dm[NS - 1], tabs);
     }
     R::update(c, ieee, th, g, st, root);
     if (j == 0) {                       // the barriers keep the second half here
@@ -994,8 +1017,9 @@ __global__ void __launch_bounds__(WG) k_dequantize(const uint8_t* __restrict__ c
     // the 8 elements of a thread lie in one 32-element block
     const float dm = decode_mult<SK, CODEC>(h2f(((gp<const uint16_t>)scales)[i >> 5]));
     float v[8];
+    const auto qo = code_operand<CODEC>(q);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = decode_state<SK, CODEC>(q, k, dm, tabs);
+    for (int k = 0; k < 8; ++k) v[k] = decode_state<SK, CODEC>(qo, k, dm, tabs);
     if (cnt == 8) {
       *(gp<f32x4>)(o + i) = f32x4{v[0], v[1], v[2], v[3]};
       *(gp<f32x4>)(o + i + 4) = f32x4{v[4], v[5], v[6], v[7]};

@@ -18,10 +18,10 @@ KEYS = ("w16", "ecc", "m_q", "m_s", "v_q", "v_s")
 HP = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
 
 
-def _states(sizes, tag):
+def _states(sizes, tag, codec="companded"):
     out = []
     for i, n in enumerate(sizes):
-        st = alloc_adamw_state(n)
+        st = alloc_adamw_state(n, codec=codec)
         B.fo_split_weights(device_weights(tag, i, n), st["w16"], st["ecc"], "bf16", 8)
         device_grads(tag, i, 1, n, "t3", "bf16", out=st["grad"])
         out.append(st)
@@ -53,6 +53,22 @@ def test_noalloc_step_equals_cached_step(sizes_a, sizes_b):
                 assert torch.equal(sa[k].view(torch.uint8), sb[k].view(torch.uint8)), (call, i, k)
         del a, b
         torch.cuda.empty_cache()
+
+
+def test_noalloc_step_equals_cached_step_4bit_states():
+    """The same with 4-bit state codes (two per byte), odd lengths included."""
+    for call, sizes in enumerate(([(1 << 20) + 77, 33, 4097, 2049], [5001, 31])):
+        print(f"no-alloc 4-bit call {call}: sizes {sizes}", flush=True)
+        a = _states(sizes, f"noalloc4_{call}", "companded4")
+        b = _clone(a)
+        for step in (1, 2):
+            hp = dict(HP, step=step, codec="companded4")
+            B.fo_fused_adamw_step(a, hp)
+            B.fo_fused_adamw_step_noalloc(b, hp)
+        torch.cuda.synchronize()
+        for i, (sa, sb) in enumerate(zip(a, b)):
+            for k in KEYS:
+                assert torch.equal(sa[k].view(torch.uint8), sb[k].view(torch.uint8)), (call, i, k)
 
 
 def test_noalloc_rejects_lists_over_the_limit():
