@@ -15,22 +15,24 @@ pytestmark = pytest.mark.gpu
 KEYS = ("w16", "ecc", "m_q", "m_s", "v_q", "v_s")
 
 
-def _state(n, tag):
-    st = alloc_adamw_state(n)
+def _state(n, tag, codec="companded"):
+    st = alloc_adamw_state(n, codec=codec)
     w = device_weights(tag, 0, n)
     B.fo_split_weights(w, st["w16"], st["ecc"], "bf16", 8)
     device_grads(tag, 0, 1, n, "t3", "bf16", out=st["grad"])
     return st
 
 
-@pytest.mark.parametrize("sizes", [[300_000 + 77],
-                                   # two tensors over more than 2^18 wave tiles: the step is
-                                   # two launches (two kernel nodes in the graph)
-                                   [(1 << 29) - 5000, 3 * (1 << 20) + 77]],
-                         ids=["one_launch", "two_launches"])
-def test_captured_step_replays_match_eager_calls(sizes):
-    hp = B.adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 5)
-    al = [_state(n, f"graph{i}") for i, n in enumerate(sizes)]
+@pytest.mark.parametrize("sizes,codec", [([300_000 + 77], "companded"),
+                                         # two tensors over more than 2^18 wave tiles: the step is
+                                         # two launches (two kernel nodes in the graph)
+                                         ([(1 << 29) - 5000, 3 * (1 << 20) + 77], "companded"),
+                                         # 4-bit state codes, odd length
+                                         ([300_000 + 77, 4097], "companded4")],
+                         ids=["one_launch", "two_launches", "one_launch_4bit"])
+def test_captured_step_replays_match_eager_calls(sizes, codec):
+    hp = B.adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.01, 5, codec=codec)
+    al = [_state(n, f"graph{i}", codec) for i, n in enumerate(sizes)]
     tl_a = B.AdamWList(al)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
