@@ -35,6 +35,8 @@ from .numerics import (  # noqa: F401
 )
 from .codecs import (  # noqa: F401
     ru_fp16_bits,
+    ru_bf16_bits,
+    scale_to_f32,
     block_scales,
     encode_momentum,
     decode_momentum,

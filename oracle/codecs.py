@@ -1,4 +1,5 @@
-"""Oracle: blockwise state codecs (8-bit companded and linear, 4-bit companded).
+"""Oracle: blockwise state codecs (8-bit companded and linear, 4-bit companded,
+8-bit companded with bfloat16 block scales).
 
 TEST INFRASTRUCTURE ONLY -- see the package docstring for who may import it.
 
@@ -73,6 +74,17 @@ C8  4-bit states.  The pages name lower-bit states only as an outlook (blog,
     two's complement; an odd-length tensor's last byte has a zero high
     nibble.  Only the companded codec has a 4-bit form (the pages report
     that plain linear codes diverge already at 8 bits).
+C9  bfloat16 block scales (codec "companded_bf16scale").  The pages fix a
+    16-bit scale per 32 elements and name no format; C2 reads binary16.  The
+    other 16-bit format the method already uses for weights is bfloat16,
+    which keeps float32's exponent range at 8 significand bits.  The variant
+    keeps everything of C1-C7 and changes only the scale:
+    s = RUbf16(max |m|) or RUbf16(sqrt_rn(max v)), RUbf16 = smallest
+    bfloat16 >= the value (subnormal bfloat16 values included), saturating
+    at the largest finite bfloat16 (0x7F7F); NaN -> 0x7FC0.  Blocks far below
+    binary16's smallest subnormal keep nonzero codes, and a block's codes do
+    not change when its values are scaled by a power of two (four for v)
+    anywhere in the normal range.
 
 RN32(.) is one IEEE float32 rounding; numpy float32 arithmetic provides it
 (its division and square root are the correctly rounded IEEE operations).
@@ -83,7 +95,10 @@ for its float32 argument (float64 is exact for that decision:
 |127*phi(a) - (k+1/2)| >= 2^-35 for every float32 a near a threshold, far
 above float64's error).
 
-Parity status: pinned (for both code widths: invertibility, monotone decode, phi(0)=0 and
+Parity status: pinned (C9: RUbf16 against a search of the sorted table of
+every bfloat16 value, codes equal to the binary16-scale codec wherever the
+two scales coincide, power-of-two scale invariance, tiny blocks;
+tests/test_oracle_bf16scale.py; the rest for both code widths: invertibility, monotone decode, phi(0)=0 and
 phi(+-1)=+-1, exhaustive half-step bound over float32 z in [-1, 1] sampled
 densely, hand-computed golden codes, exact-rational codes for inputs where a
 reciprocal-multiply would differ from the division, RU16 against numpy's
@@ -96,12 +111,18 @@ from __future__ import annotations
 
 import numpy as np
 
-from .numerics import FORMATS, _exponent, f16_bits_to_f32
+from .numerics import FORMATS, _exponent, bf16_bits_to_f32, f16_bits_to_f32
 
 BLOCK = 32
 F16 = FORMATS["fp16"]
 F16_MAX = 65504.0
+BF16 = FORMATS["bf16"]
 F32 = np.float32
+
+# codecs whose codes come from the companders (C3, C4, C8, C9)
+COMPANDED_CODECS = ("companded", "companded4", "companded_bf16scale")
+# the format of each codec's block scales (C2, C9)
+SCALE_FORMAT = {"companded": "fp16", "linear": "fp16", "companded4": "fp16", "companded_bf16scale": "bf16"}
 
 
 def ru_fp16_bits(x32: np.ndarray) -> np.ndarray:
@@ -117,6 +138,28 @@ def ru_fp16_bits(x32: np.ndarray) -> np.ndarray:
     return bits
 
 
+def ru_bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """Smallest bfloat16 >= x (x >= 0 or NaN), saturating at the largest finite
+    bfloat16; NaN -> 0x7FC0 (C9)."""
+    x = np.asarray(x32, dtype=np.float32).astype(np.float64)
+    nan = np.isnan(x)
+    xf = np.where(nan, 0.0, np.minimum(x, BF16.max_finite))
+    q = np.ldexp(1.0, _exponent(xf, BF16) - (BF16.p - 1))  # spacing of x's binade (subnormals: 2^-133)
+    a = np.ceil(xf / q) * q                                 # exact: power-of-two scaling
+    a = np.minimum(a, BF16.max_finite)
+    bits = (a.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)   # a is a bfloat16 value
+    bits[nan] = 0x7FC0
+    return bits
+
+
+def scale_to_f32(scale_bits: np.ndarray, codec: str = "companded") -> np.ndarray:
+    """Stored block-scale patterns -> float32 (exact), in the codec's scale
+    format (C2, C9)."""
+    if SCALE_FORMAT[codec] == "bf16":
+        return bf16_bits_to_f32(scale_bits)
+    return f16_bits_to_f32(scale_bits)
+
+
 def _blocks(x: np.ndarray) -> np.ndarray:
     """(n,) -> (ceil(n/32), 32); the short last block is padded with NaN, which
     the maxNum reductions skip, so only its valid elements count (C1)."""
@@ -127,9 +170,9 @@ def _blocks(x: np.ndarray) -> np.ndarray:
     return pad.reshape(nb, BLOCK)
 
 
-def block_scales(x: np.ndarray, kind: str) -> np.ndarray:
-    """fp16 scale bits per 32-element block for a momentum ('m') or variance ('v')
-    state (C1, C2)."""
+def block_scales(x: np.ndarray, kind: str, codec: str = "companded") -> np.ndarray:
+    """Scale bits per 32-element block for a momentum ('m') or variance ('v')
+    state (C1, C2; binary16, or bfloat16 under C9)."""
     b = _blocks(x)
     if b.shape[0] == 0:
         return np.zeros(0, dtype=np.uint16)
@@ -140,16 +183,18 @@ def block_scales(x: np.ndarray, kind: str) -> np.ndarray:
             amax = np.sqrt(np.fmax.reduce(b, axis=1))      # float32 sqrt: correctly rounded
         else:
             raise ValueError(kind)
-    return ru_fp16_bits(amax.astype(np.float32))
+    ru = ru_bf16_bits if SCALE_FORMAT[codec] == "bf16" else ru_fp16_bits
+    return ru(amax.astype(np.float32))
 
 
-def _per_elem(scale_bits: np.ndarray, n: int) -> np.ndarray:
-    s = f16_bits_to_f32(scale_bits)
+def _per_elem(scale_bits: np.ndarray, n: int, codec: str) -> np.ndarray:
+    s = scale_to_f32(scale_bits, codec)
     return np.repeat(s, BLOCK)[:n]
 
 
-# largest momentum code L and largest variance code of each codec (C3-C5, C8)
-CODE_MAX = {"companded": (127, 255), "linear": (127, 255), "companded4": (7, 15)}
+# largest momentum code L and largest variance code of each codec (C3-C5, C8, C9)
+CODE_MAX = {"companded": (127, 255), "linear": (127, 255), "companded4": (7, 15),
+            "companded_bf16scale": (127, 255)}
 
 
 def code_bytes(n: int, codec: str) -> int:
@@ -159,8 +204,8 @@ def code_bytes(n: int, codec: str) -> int:
 
 def momentum_lut(codec: str = "companded") -> np.ndarray:
     """LUT[q + L] = RN32(q / (2L - |q|)) for q in [-L, L], the inverse of phi
-    at q/L: L = 127 (C3) or 7 (C8)."""
-    if codec not in ("companded", "companded4"):
+    at q/L: L = 127 (C3, C9) or 7 (C8)."""
+    if codec not in COMPANDED_CODECS:
         raise ValueError("the momentum LUT exists for the companded codecs only")
     L = CODE_MAX[codec][0]
     q = np.arange(-L, L + 1, dtype=np.float32)
@@ -196,9 +241,9 @@ def level_spacing(scale_bits: np.ndarray, kind: str, codec: str) -> np.ndarray:
     block): RN32(s/255) (variance, companded), RN32(s/15) (variance,
     companded4), RN32(s/127) (momentum, linear), RN32(RN32(s*s)/255)
     (variance, linear)."""
-    s = f16_bits_to_f32(scale_bits)
+    s = scale_to_f32(scale_bits, codec)
     with np.errstate(all="ignore"):
-        if kind == "v" and codec in ("companded", "companded4"):
+        if kind == "v" and codec in COMPANDED_CODECS:
             return (s / F32(CODE_MAX[codec][1])).astype(F32)
         if kind == "m" and codec == "linear":
             return (s / F32(127.0)).astype(F32)
@@ -224,10 +269,10 @@ def _saturating_code(y: np.ndarray, lo: int, hi: int) -> np.ndarray:
 
 def encode_momentum(m: np.ndarray, scale_bits: np.ndarray, codec: str = "companded") -> np.ndarray:
     m = np.asarray(m, dtype=np.float32).ravel()
-    s = _per_elem(scale_bits, m.size)
+    s = _per_elem(scale_bits, m.size, codec)
     with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
         z = (m / s).astype(F32)                                   # one float32 division (C3, C5)
-        if codec in ("companded", "companded4"):
+        if codec in COMPANDED_CODECS:
             nan = np.isnan(z)
             a = np.fmin(np.abs(np.where(nan, F32(0), z)), F32(1.0)).astype(np.float64)
             q = _phi_code(a, CODE_MAX[codec][0])
@@ -242,9 +287,9 @@ def encode_momentum(m: np.ndarray, scale_bits: np.ndarray, codec: str = "compand
 
 def decode_momentum(q: np.ndarray, scale_bits: np.ndarray, codec: str = "companded") -> np.ndarray:
     q = np.asarray(q, dtype=np.int8).ravel()
-    if codec in ("companded", "companded4"):
+    if codec in COMPANDED_CODECS:
         L = CODE_MAX[codec][0]
-        s = _per_elem(scale_bits, q.size)
+        s = _per_elem(scale_bits, q.size, codec)
         lut = momentum_lut(codec)
         return (s * lut[np.maximum(q.astype(np.int64), -L) + L]).astype(F32)   # C7, C8
     if codec == "linear":
@@ -255,9 +300,9 @@ def decode_momentum(q: np.ndarray, scale_bits: np.ndarray, codec: str = "compand
 
 def encode_variance(v: np.ndarray, scale_bits: np.ndarray, codec: str = "companded") -> np.ndarray:
     v = np.asarray(v, dtype=np.float32).ravel()
-    s = _per_elem(scale_bits, v.size)
+    s = _per_elem(scale_bits, v.size, codec)
     with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
-        if codec in ("companded", "companded4"):
+        if codec in COMPANDED_CODECS:
             w = np.sqrt(v).astype(F32)                            # correctly rounded (C4, C8)
             z = (w / s).astype(F32)
         elif codec == "linear":
@@ -275,7 +320,7 @@ def decode_variance(q: np.ndarray, scale_bits: np.ndarray, codec: str = "compand
     q = np.asarray(q, dtype=np.uint8).ravel()
     d = np.repeat(level_spacing(scale_bits, "v", codec), BLOCK)[: q.size]
     qf = q.astype(F32)
-    if codec in ("companded", "companded4"):
+    if codec in COMPANDED_CODECS:
         t = (d * qf).astype(F32)
         return (t * t).astype(F32)
     if codec == "linear":
@@ -284,9 +329,9 @@ def decode_variance(q: np.ndarray, scale_bits: np.ndarray, codec: str = "compand
 
 
 def quantize_state(x: np.ndarray, kind: str, codec: str = "companded"):
-    """f32 state -> (codes, fp16 scale bits); one code per element (4-bit
-    codes unpacked: pack_nibbles gives their stored bytes)."""
-    s = block_scales(x, kind)
+    """f32 state -> (codes, scale bits); one code per element (4-bit codes
+    unpacked: pack_nibbles gives their stored bytes)."""
+    s = block_scales(x, kind, codec)
     if kind == "m":
         return encode_momentum(x, s, codec), s
     return encode_variance(x, s, codec), s

@@ -186,8 +186,8 @@ def adamw_step(state: dict, grad_bits: np.ndarray, hp: dict, fmt: str = "bf16",
     v = decode_variance(_stored_codes(state["v_q"], n, codec, False), state["v_s"], codec)
     th, m1, v1, _ = adamw_update(theta, g, m, v, S)
     w16, ecc = split_weights(th, fmt, ecc_bits)
-    m_s = block_scales(m1, "m")
-    v_s = block_scales(v1, "v")
+    m_s = block_scales(m1, "m", codec)
+    v_s = block_scales(v1, "v", codec)
     return {
         "w16": w16, "ecc": ecc,
         "m_q": _stored_form(encode_momentum(m1, m_s, codec), codec), "m_s": m_s,
@@ -209,7 +209,7 @@ def sgdm_step(state: dict, grad_bits: np.ndarray, hp: dict, fmt: str = "bf16",
     b = decode_momentum(_stored_codes(state["b_q"], theta.size, codec, True), state["b_s"], codec)
     th, b1 = sgdm_update(theta, g, b, S, first=sgdm_first(hp["step"], hp["momentum"]))
     w16, ecc = split_weights(th, fmt, ecc_bits)
-    b_s = block_scales(b1, "m")
+    b_s = block_scales(b1, "m", codec)
     return {"w16": w16, "ecc": ecc, "b_q": _stored_form(encode_momentum(b1, b_s, codec), codec), "b_s": b_s}
 
 
