@@ -624,6 +624,8 @@ def main(argv=None):
                 "c4_resnet50_s4": "ResNet-50-shaped parameter list, fused SGD-M, bf16 + 8-bit ECC, "
                                   "companded 4-bit states",
                 "c5_flat1g_s4": "one 2^30-element tensor, fused AdamW, bf16 + 8-bit ECC, companded 4-bit states",
+                "c3_llama8b_bs": "Llama-3.1-8B-shaped parameter list, fused AdamW, bf16 + 8-bit ECC, "
+                                 "companded 8-bit states with bfloat16 block scales",
             }.get(cfg.name, cfg.name),
             "name": cfg.name,
             "optimizer": cfg.optimizer,

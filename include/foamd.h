@@ -54,6 +54,11 @@
  *     D = RN(s / 15)).  Two codes per byte: element 2i in the low nibble,
  *     2i+1 in the high one, momentum codes in 4-bit two's complement; a code
  *     array holds ceil(n/2) bytes and an odd n leaves the last high nibble 0.
+ *   bfloat16 block scales [STATE] (FO_COMPANDED_BF16SCALE): the companded
+ *     8-bit codes with scale = the smallest bfloat16 >= the block's maximum
+ *     (subnormal values included), saturating at the largest finite
+ *     bfloat16 (0x7F7F); NaN maximum -> 0x7FC0.  The pages fix a 16-bit scale
+ *     without naming its format; this one keeps float32's exponent range.
  *   A NaN state element gets code 0 (the rule of saturating float-to-integer
  *   conversion); +-Inf takes the end codes.
  *   Updates: see fo_fused_adamw_step and fo_fused_sgdm_step.
@@ -102,11 +107,12 @@
 extern "C" {
 #endif
 
-#define FO_ABI_VERSION 5   /* 2: l2_decay in fo_adamw_hparams; dampening, nesterov in fo_sgdm_hparams;
+#define FO_ABI_VERSION 6   /* 2: l2_decay in fo_adamw_hparams; dampening, nesterov in fo_sgdm_hparams;
                               3: correctly rounded quotients in the update and the codecs, NaN codes 0,
                                  NaN-only short last blocks keep a NaN scale, SGD momentum 0 as torch;
                               4: fo_hbm_probe takes a chunk size (and an in-place mode);
-                              5: FO_COMPANDED4, 4-bit state codes */
+                              5: FO_COMPANDED4, 4-bit state codes;
+                              6: FO_COMPANDED_BF16SCALE, bfloat16 block scales */
 
 enum fo_status {
   FO_OK = 0,
@@ -119,9 +125,10 @@ enum fo_status {
 /* 16-bit downcast format of theta' (and of the gradients). */
 enum fo_wfmt { FO_BF16 = 0, FO_FP16 = 1 };
 /* State code mapping: companded (softsign-like momentum, square-root
- * variance), the linear ablation with the same scales, or the companded
- * mapping onto 4-bit codes, two per byte. */
-enum fo_codec { FO_COMPANDED = 0, FO_LINEAR = 1, FO_COMPANDED4 = 2 };
+ * variance), the linear ablation with the same scales, the companded
+ * mapping onto 4-bit codes, two per byte, or the companded 8-bit codes with
+ * bfloat16 block scales instead of binary16 ones. */
+enum fo_codec { FO_COMPANDED = 0, FO_LINEAR = 1, FO_COMPANDED4 = 2, FO_COMPANDED_BF16SCALE = 3 };
 /* State kind: signed momentum-like (int8 codes in [-127,127]; [-7,7] as
  * 4-bit codes) or unsigned variance-like (uint8 codes in [0,255]; [0,15]). */
 enum fo_kind { FO_MOMENTUM = 0, FO_VARIANCE = 1 };
@@ -157,25 +164,29 @@ int fo_reconstruct_weights(const void* w16, const void* ecc, int64_t n, int wfmt
 
 /*
  * fo_companded_quantize -- [STATE], [LOWER]
- * Quantises an f32 state to 8-bit (or 4-bit) codes plus one fp16 scale per
+ * Quantises an f32 state to 8-bit (or 4-bit) codes plus one 16-bit scale per
  * 32 elements.
  *   x          : n float32 (read); variance states must be >= 0
  *   kind       : FO_MOMENTUM (int8 codes) or FO_VARIANCE (uint8 codes)
- *   codec      : FO_COMPANDED, FO_LINEAR or FO_COMPANDED4
+ *   codec      : FO_COMPANDED, FO_LINEAR, FO_COMPANDED4 or FO_COMPANDED_BF16SCALE
  *   codes_out  : n bytes, or ceil(n/2) under FO_COMPANDED4 (written)
- *   scales_out : ceil(n/32) fp16 bit patterns (written)
+ *   scales_out : ceil(n/32) fp16 bit patterns, bfloat16 ones under
+ *                FO_COMPANDED_BF16SCALE (written)
  * Momentum scale = smallest fp16 >= max|x| of the block; variance scale =
- * smallest fp16 >= sqrt(max x) of the block (both saturate at 65504).
+ * smallest fp16 >= sqrt(max x) of the block (both saturate at 65504); under
+ * FO_COMPANDED_BF16SCALE the smallest bfloat16 instead (saturating at its
+ * largest finite value).
  */
 int fo_companded_quantize(const float* x, int64_t n, int kind, int codec,
                           void* codes_out, uint16_t* scales_out, void* stream);
 
 /*
  * fo_dequantize -- [STATE]
- * Decodes 8-bit (or 4-bit) codes and fp16 block scales back to f32 (inverse
+ * Decodes 8-bit (or 4-bit) codes and 16-bit block scales back to f32 (inverse
  * mapping of fo_companded_quantize for the same kind and codec).
  *   codes : n bytes, or ceil(n/2) under FO_COMPANDED4 (read);
- *   scales : ceil(n/32) fp16 (read);  x_out : n float32 (written)
+ *   scales : ceil(n/32) fp16, or bfloat16 under FO_COMPANDED_BF16SCALE (read);
+ *   x_out : n float32 (written)
  */
 int fo_dequantize(const void* codes, const uint16_t* scales, int64_t n, int kind,
                   int codec, float* x_out, void* stream);
@@ -189,9 +200,9 @@ typedef struct fo_adamw_tensor {
   void*        ecc;   /* int8 or int16 */
   const void*  grad;  /* bf16 or fp16, same format as w16 */
   int8_t*      m_q;   /* momentum codes */
-  uint16_t*    m_s;   /* momentum scales (fp16 bits) */
+  uint16_t*    m_s;   /* momentum scales (fp16 bits; bfloat16 under FO_COMPANDED_BF16SCALE) */
   uint8_t*     v_q;   /* variance codes */
-  uint16_t*    v_s;   /* variance scales (fp16 bits) */
+  uint16_t*    v_s;   /* variance scales (fp16 bits; bfloat16 under FO_COMPANDED_BF16SCALE) */
   int64_t      n;
 } fo_adamw_tensor;
 
@@ -260,7 +271,7 @@ typedef struct fo_sgdm_tensor {
   void*        ecc;
   const void*  grad;
   int8_t*      b_q;   /* momentum-buffer codes (ceil(n/2) bytes under FO_COMPANDED4) */
-  uint16_t*    b_s;   /* momentum-buffer scales (fp16 bits) */
+  uint16_t*    b_s;   /* momentum-buffer scales (fp16 bits; bfloat16 under FO_COMPANDED_BF16SCALE) */
   int64_t      n;
 } fo_sgdm_tensor;
 

@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libf
 
 FO_OK, FO_EINVAL, FO_EALIAS, FO_EHIP, FO_ENOMEM = 0, -1, -2, -3, -4
 FO_BF16, FO_FP16 = 0, 1
-FO_COMPANDED, FO_LINEAR, FO_COMPANDED4 = 0, 1, 2
+FO_COMPANDED, FO_LINEAR, FO_COMPANDED4, FO_COMPANDED_BF16SCALE = 0, 1, 2, 3
 FO_MOMENTUM, FO_VARIANCE = 0, 1
 
 EXPORTS = (
@@ -27,7 +27,8 @@ EXPORTS = (
 )
 
 WFMT = {"bf16": FO_BF16, "fp16": FO_FP16}
-CODEC = {"companded": FO_COMPANDED, "linear": FO_LINEAR, "companded4": FO_COMPANDED4}
+CODEC = {"companded": FO_COMPANDED, "linear": FO_LINEAR, "companded4": FO_COMPANDED4,
+         "companded_bf16scale": FO_COMPANDED_BF16SCALE}
 KIND = {"m": FO_MOMENTUM, "v": FO_VARIANCE}
 
 
@@ -60,7 +61,7 @@ class SGDMHParams(ctypes.Structure):
 
 
 _lib = None
-ABI_VERSION = 5          # FO_ABI_VERSION of include/foamd.h (struct layouts below)
+ABI_VERSION = 6          # FO_ABI_VERSION of include/foamd.h (struct layouts below)
 
 
 def load(path: str = LIB_PATH) -> ctypes.CDLL:

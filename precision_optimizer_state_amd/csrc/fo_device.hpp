@@ -32,8 +32,12 @@
 namespace fo {
 
 enum { BF16 = 0, FP16 = 1 };
-// state codecs: 8-bit companded, 8-bit linear, 4-bit companded (two codes a byte)
-enum { COMPANDED = 0, LINEAR = 1, COMPANDED4 = 2 };
+// state codecs: 8-bit companded, 8-bit linear, 4-bit companded (two codes a
+// byte), and 8-bit companded with bfloat16 block scales (binary16 otherwise)
+enum { COMPANDED = 0, LINEAR = 1, COMPANDED4 = 2, COMPANDED_BF16S = 3 };
+// the codec of a state's codes, and whether its block scales are bfloat16
+template <int CODEC> constexpr int code_codec = (CODEC == COMPANDED_BF16S) ? COMPANDED : CODEC;
+template <int CODEC> constexpr bool scale_bf16 = (CODEC == COMPANDED_BF16S);
 template <int CODEC> constexpr int code_bits = (CODEC == COMPANDED4) ? 4 : 8;
 
 // Pointers into device memory are declared in the global address space so the
@@ -294,6 +298,35 @@ __device__ __forceinline__ uint32_t ru_fp16(float x) {
   const int s = e ? (126 - (int)e) : 125;              // value = M / 2^s units of 2^-24
   if (s >= 25) return M ? 1u : 0u;
   return (M + (1u << s) - 1u) >> s;                    // ceil
+}
+
+// Block scales of the bfloat16-scale codec: smallest bfloat16 >= x (x >= 0,
+// subnormal values included), saturating at the largest finite bfloat16
+// 0x7F7F; NaN -> 0x7FC0.  On non-negative patterns the bfloat16 pattern of a
+// value is the high half of its f32 pattern, so rounding up is adding
+// 0xFFFF before taking the high half.
+__device__ __forceinline__ uint32_t ru_bf16(float x) {
+  const uint32_t ux = f2u(x) & 0x7FFFFFFFu;            // callers pass |.| or sqrt: sign ignored
+  if (ux > 0x7F800000u) return 0x7FC0u;                // NaN
+  return min((ux + 0xFFFFu) >> 16, 0x7F7Fu);           // +inf and values past 0x7F7F saturate
+}
+// stored scale pattern -> f32 (exact) in the codec's scale format
+template <int CODEC>
+__device__ __forceinline__ float scale_f32(uint32_t bits) {
+  if constexpr (scale_bf16<CODEC>) return u2f(bits << 16);
+  else return h2f(bits);
+}
+// The fast forms of the steps take block scales in binary16's range only:
+// zero, or [2^-24, 65504].  There the fast division and reciprocal are exact
+// for every divisor with at most 22 significand bits (bfloat16 has 8), and
+// the decoded states keep the magnitudes the fast update is valid for.  A
+// bfloat16 scale outside it (NaN and +-Inf included) sends its wave to the
+// IEEE forms.  Tested on the pattern, without short-circuit branches (which
+// split the scale loads of a tile): +0, or 0x33800000 (2^-24) through
+// 0x477FE000 (65504); -0, negative values and NaN fall outside.
+__device__ __forceinline__ bool scale_in_fast_range(float s) {
+  const uint32_t u = f2u(s);
+  return (u == 0u) | (u - 0x33800000u <= 0x477FE000u - 0x33800000u);
 }
 
 // ---------------------------------------------------------------------------

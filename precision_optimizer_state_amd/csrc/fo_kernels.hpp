@@ -238,16 +238,20 @@ enum { MOMENTUM_STATE = 0, VARIANCE_STATE = 1 };
 // fo_device.hpp).  The level spacings RN(s/127), RN(s/255), RN(s*s/255) are
 // correctly rounded divisions by a constant: div_refined with the constant's
 // rounded reciprocal (exact for every dividend: the CPU check covers all
-// divisors with 11-bit significands).  A non-finite s divides to itself.
+// divisors with 11-bit significands).  A non-finite s divides to itself.  A
+// bfloat16 scale may lie below the fast division's dividend range (2^-100):
+// such a block's spacing is one IEEE division.
 template <int KIND, int CODEC>
 __device__ __forceinline__ float decode_mult(float s) {
+  constexpr int CC = code_codec<CODEC>;
   // RN(1/127), RN(1/255), RN(1/15)
   constexpr float R127 = 1.0f / 127.0f, R255 = 1.0f / 255.0f, R15 = 1.0f / 15.0f;
-  if constexpr (KIND == MOMENTUM_STATE && CODEC != LINEAR) return s;
-  const float x = (KIND == VARIANCE_STATE && CODEC == LINEAR) ? s * s : s;
-  const float q = (CODEC == COMPANDED4)       ? div_refined(x, 15.0f, R15)
+  if constexpr (KIND == MOMENTUM_STATE && CC != LINEAR) return s;
+  const float x = (KIND == VARIANCE_STATE && CC == LINEAR) ? s * s : s;
+  const float q = (CC == COMPANDED4)          ? div_refined(x, 15.0f, R15)
                   : (KIND == MOMENTUM_STATE) ? div_refined(x, 127.0f, R127)
                                              : div_refined(x, 255.0f, R255);
+  if constexpr (scale_bf16<CODEC>) return (fabsf(x) >= 0x1p-100f && fabsf(x) <= 0x1p126f) ? q : x / 255.0f;
   return (fabsf(x) <= 0x1p126f) ? q : x;
 }
 // q: the lane's code words of 8 elements (DW<2> of bytes, or the NibHalves
@@ -474,7 +478,9 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
   constexpr int EB = ECC / 8;                                  // ECC bytes per element
   constexpr int K0 = R::template KIND<0>;
   constexpr int K1 = R::template KIND<NS - 1>;
-  constexpr int QW = code_words<CODEC>;                        // code words per lane and sub-tile
+  constexpr int CC = code_codec<CODEC>;                        // the codes' codec
+  constexpr bool SBF = scale_bf16<CODEC>;                      // bfloat16 block scales
+  constexpr int QW = code_words<CC>;                           // code words per lane and sub-tile
   const int Q = lane >> 2, p = lane & 3;
   const gp<const uint8_t> grad = (gp<const uint8_t>)d.grad + e0 * 2;
   const gp<uint8_t> w16 = (gp<uint8_t>)d.w16 + e0 * 2;
@@ -510,7 +516,7 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
     W[j] = load8<2, FULL>(w16 + off * 2, cnt[j]);
     E[j] = load8<EB, FULL>(ecc + off * EB, cnt[j]);
 #pragma unroll
-    for (int k = 0; k < NS; ++k) SQ[k][j] = load_codes<CODEC, FULL>(qp[k] + off * QW / 2, cnt[j]);
+    for (int k = 0; k < NS; ++k) SQ[k][j] = load_codes<CC, FULL>(qp[k] + off * QW / 2, cnt[j]);
   };
   // the first half now, the second half once sub-tile 0 is updated: fewer
   // bytes in flight per wave at once measure about 0.7% faster on every
@@ -522,13 +528,14 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
   bool nonfinite = false;
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
-    const float sold = h2f(own_ok ? (uint32_t)__builtin_nontemporal_load(sp[k] + own) : 0u);
+    const float sold = scale_f32<CODEC>(own_ok ? (uint32_t)__builtin_nontemporal_load(sp[k] + own) : 0u);
     dm_own[k] = (k == 0) ? decode_mult<K0, CODEC>(sold) : decode_mult<K1, CODEC>(sold);
-    nonfinite |= !(fabsf(sold) <= 65504.0f);
+    nonfinite |= SBF ? !scale_in_fast_range(sold) : !(fabsf(sold) <= 65504.0f);
   }
   // a NaN or infinite stored scale (the encoder writes NaN only for an all-NaN
-  // block) makes NaN or infinite states: the rule then takes its IEEE form
-  // (or the rule finds the tile's gradients outside its fast range)
+  // block) makes NaN or infinite states, and a bfloat16 scale outside the
+  // fast range states the fast update does not take: the rule then takes its
+  // IEEE form (or the rule finds the tile's gradients outside its fast range)
   const bool ieee = (__builtin_amdgcn_ballot_w64(nonfinite) != 0) || R::tile_slow(c, G);
 
   float X[NS][NSUB][EPL];                  // what each state's codes are taken from
@@ -542,8 +549,8 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
     float dm[NS];
 #pragma unroll
     for (int k = 0; k < NS; ++k) dm[k] = bcast_j(dm_own[k], j);
-    const auto q0 = code_operand<CODEC>(SQ[0][j]);
-    const auto q1 = code_operand<CODEC>(SQ[NS - 1][j]);
+    const auto q0 = code_operand<CC>(SQ[0][j]);
+    const auto q1 = code_operand<CC>(SQ[NS - 1][j]);
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
       g[i] = wid<WFMT>(G[j], i);
@@ -551,8 +558,8 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
         th[i] = ecc_decode_bf16_packed<ECC>(W[j].w[i >> 1], E[j].w[(i * ECC) >> 5], i & 1, (ECC == 8) ? (i & 3) : (i & 1));
       else
         th[i] = ecc_decode<WFMT, ECC>(wid<WFMT>(W[j], i), rho_at<ECC>(E[j], i));
-      st[0][i] = decode_state<K0, CODEC>(q0, i, dm[0], tabs);
-      if constexpr (NS == 2) st[NS - 1][i] = decode_state<K1, CODEC>(q1, i, dm[NS - 1], tabs);
+      st[0][i] = decode_state<K0, CC>(q0, i, dm[0], tabs);
+      if constexpr (NS == 2) st[NS - 1][i] = decode_state<K1, CC>(q1, i, dm[NS - 1], tabs);
     }
     R::update(c, ieee, th, g, st, root);
     if (j == 0) {                       // the barriers keep the second half here
@@ -574,7 +581,7 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
     // whose valid elements are all NaN keeps a NaN maximum (and scale)
 #pragma unroll
     for (int k = 0; k < NS; ++k) {
-      const bool root_k = (k == 0) ? encodes_root<K0, CODEC> : encodes_root<K1, CODEC>;
+      const bool root_k = (k == 0) ? encodes_root<K0, CC> : encodes_root<K1, CC>;
       const bool mom_k = ((k == 0) ? K0 : K1) == MOMENTUM_STATE;
       float a[EPL];
 #pragma unroll
@@ -598,18 +605,19 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
 #pragma unroll
   for (int k = 0; k < NS; ++k) {
     const int kind = (k == 0) ? K0 : K1;
-    const bool lin_var = (kind == VARIANCE_STATE && CODEC == LINEAR);
-    const uint32_t sb = ru_fp16(lin_var ? __builtin_sqrtf(own_max[k]) : own_max[k]);
+    const bool lin_var = (kind == VARIANCE_STATE && CC == LINEAR);
+    const uint32_t sb = SBF ? ru_bf16(own_max[k]) : ru_fp16(lin_var ? __builtin_sqrtf(own_max[k]) : own_max[k]);
     if (own_ok) __builtin_nontemporal_store((uint16_t)sb, sp[k] + own);
-    const float sf = h2f(sb);
+    const float sf = scale_f32<CODEC>(sb);
     s_own[k] = lin_var ? sf * sf : sf;                       // the divisor of the normalisation (exact)
     // RN(1/divisor) for the fast encodes; a zero divisor gives NaN, which
     // codes the block's zeros (and NaNs) 0 as the division 0/0 would
     r_own[k] = rcp_refined(s_own[k]);
     // the fast encodes need |x| <= s (momentum, and 4-bit variance, whose
     // conversion saturates at 255 instead of 15) or a finite x (variance)
-    sat |= (kind == MOMENTUM_STATE || CODEC == COMPANDED4) ? (own_max[k] > 65504.0f)
-                                                           : (own_max[k] == __builtin_inff());
+    sat |= (kind == MOMENTUM_STATE || CC == COMPANDED4) ? (own_max[k] > 65504.0f)
+                                                        : (own_max[k] == __builtin_inff());
+    if constexpr (SBF) sat |= !scale_in_fast_range(sf);
   }
   const bool sat_wave = __builtin_amdgcn_ballot_w64(sat) != 0;
 
@@ -621,8 +629,8 @@ __device__ __forceinline__ void fused_tile(const TensorDesc& d, int64_t e0, int 
       const int kind = (k == 0) ? K0 : K1;
       const float sdiv = bcast_j(s_own[k], j), rdiv = bcast_j(r_own[k], j);
       uint32_t o[QW];
-      encode_group<CODEC>(kind, X[k][j], sdiv, rdiv, sat_wave, tabs, o);
-      store_codes<CODEC, FULL>(qp[k] + off * QW / 2, o, cnt[j]);
+      encode_group<CC>(kind, X[k][j], sdiv, rdiv, sat_wave, tabs, o);
+      store_codes<CC, FULL>(qp[k] + off * QW / 2, o, cnt[j]);
     }
   }
 }
@@ -948,6 +956,7 @@ __global__ void __launch_bounds__(WG) k_quantize(const float* __restrict__ x, in
                                                  const CodecTables* __restrict__ gtabs) {
   __shared__ CodecTables tabs;
   load_tables(tabs, gtabs);
+  constexpr int CC = code_codec<CODEC>;
   const gp<const float> xs = (gp<const float>)x;
   const int64_t stride = (int64_t)gridDim.x * WG * EPL;
   // all lanes iterate together (stride multiple of 512), so the 4 lanes of a
@@ -965,7 +974,7 @@ __global__ void __launch_bounds__(WG) k_quantize(const float* __restrict__ x, in
       for (int k = 0; k < 8; ++k) v[k] = (k < cnt) ? xs[i + k] : __builtin_nanf("");
     }
     float e[8];
-    if (KIND == 1 && CODEC != LINEAR) {
+    if (KIND == 1 && CC != LINEAR) {
       uint64_t slow = 0;
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -984,19 +993,20 @@ __global__ void __launch_bounds__(WG) k_quantize(const float* __restrict__ x, in
 #pragma unroll
     for (int k = 0; k < 8; ++k) mx = fmaxf(mx, (KIND == 0) ? fabsf(e[k]) : e[k]);
     mx = quad_max(mx);
-    const uint32_t sb = ru_fp16((KIND == 1 && CODEC == LINEAR) ? __builtin_sqrtf(mx) : mx);
+    const uint32_t sb = scale_bf16<CODEC> ? ru_bf16(mx) : ru_fp16((KIND == 1 && CC == LINEAR) ? __builtin_sqrtf(mx) : mx);
     if ((threadIdx.x & 3) == 0 && cnt > 0) ((gp<uint16_t>)scales)[i >> 5] = (uint16_t)sb;
-    const float sf = h2f(sb);
-    const float sdiv = (KIND == 1 && CODEC == LINEAR) ? sf * sf : sf;
+    const float sf = scale_f32<CODEC>(sb);
+    const float sdiv = (KIND == 1 && CC == LINEAR) ? sf * sf : sf;
     const float rdiv = 1.0f / sdiv;
-    const bool sat_wave =
-        __builtin_amdgcn_ballot_w64((KIND == 0 || CODEC == COMPANDED4) ? (mx > 65504.0f) : (mx == __builtin_inff())) != 0;
-    constexpr int QW = code_words<CODEC>;
+    const bool sat = ((KIND == 0 || CC == COMPANDED4) ? (mx > 65504.0f) : (mx == __builtin_inff())) ||
+                     (scale_bf16<CODEC> && !scale_in_fast_range(sf));
+    const bool sat_wave = __builtin_amdgcn_ballot_w64(sat) != 0;
+    constexpr int QW = code_words<CC>;
     uint32_t o[QW];
-    encode_group<CODEC>(KIND == 0 ? MOMENTUM_STATE : VARIANCE_STATE, e, sdiv, rdiv, sat_wave, tabs, o);
+    encode_group<CC>(KIND == 0 ? MOMENTUM_STATE : VARIANCE_STATE, e, sdiv, rdiv, sat_wave, tabs, o);
     const gp<uint8_t> cp = (gp<uint8_t>)codes + i * QW / 2;
-    if (cnt == 8) store_codes<CODEC, true>(cp, o, 8);
-    else if (cnt > 0) store_codes<CODEC, false>(cp, o, cnt);
+    if (cnt == 8) store_codes<CC, true>(cp, o, 8);
+    else if (cnt > 0) store_codes<CC, false>(cp, o, cnt);
   }
 }
 
@@ -1011,15 +1021,16 @@ __global__ void __launch_bounds__(WG) k_dequantize(const uint8_t* __restrict__ c
   constexpr int SK = (KIND == 0) ? MOMENTUM_STATE : VARIANCE_STATE;
   for (int64_t i = ((int64_t)blockIdx.x * WG + threadIdx.x) * EPL; i < n; i += stride) {
     const int cnt = (int)min((int64_t)8, n - i);
-    constexpr int QW = code_words<CODEC>;
+    constexpr int CC = code_codec<CODEC>;
+    constexpr int QW = code_words<CC>;
     const gp<const uint8_t> cp = (gp<const uint8_t>)codes + i * QW / 2;
-    const DW<QW> q = (cnt == 8) ? load_codes<CODEC, true>(cp, 8) : load_codes<CODEC, false>(cp, cnt);
+    const DW<QW> q = (cnt == 8) ? load_codes<CC, true>(cp, 8) : load_codes<CC, false>(cp, cnt);
     // the 8 elements of a thread lie in one 32-element block
-    const float dm = decode_mult<SK, CODEC>(h2f(((gp<const uint16_t>)scales)[i >> 5]));
+    const float dm = decode_mult<SK, CODEC>(scale_f32<CODEC>(((gp<const uint16_t>)scales)[i >> 5]));
     float v[8];
-    const auto qo = code_operand<CODEC>(q);
+    const auto qo = code_operand<CC>(q);
 #pragma unroll
-    for (int k = 0; k < 8; ++k) v[k] = decode_state<SK, CODEC>(qo, k, dm, tabs);
+    for (int k = 0; k < 8; ++k) v[k] = decode_state<SK, CC>(qo, k, dm, tabs);
     if (cnt == 8) {
       *(gp<f32x4>)(o + i) = f32x4{v[0], v[1], v[2], v[3]};
       *(gp<f32x4>)(o + i + 4) = f32x4{v[4], v[5], v[6], v[7]};

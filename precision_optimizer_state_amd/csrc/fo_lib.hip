@@ -286,7 +286,9 @@ inline int64_t array_extent(const ArraySpec& s, int64_t n, int64_t nb) {
 }
 // bytes per element of a codec's code array (0 = two codes per byte)
 inline size_t code_elem_bytes(int codec) { return codec == FO_COMPANDED4 ? 0 : 1; }
-inline bool codec_ok(int codec) { return codec == FO_COMPANDED || codec == FO_LINEAR || codec == FO_COMPANDED4; }
+inline bool codec_ok(int codec) {
+  return codec == FO_COMPANDED || codec == FO_LINEAR || codec == FO_COMPANDED4 || codec == FO_COMPANDED_BF16SCALE;
+}
 
 // Element counts above 2^56 cannot describe device memory; rejecting them
 // keeps every byte-range computation below within int64 / uintptr_t.
@@ -399,6 +401,9 @@ hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
     else if (wfmt == FO_BF16 && ecc == 8 && codec == FO_COMPANDED4) OUT = KERNEL<BF16, 8, COMPANDED4>; \
     else if (wfmt == FO_BF16 && ecc == 16 && codec == FO_COMPANDED4) OUT = KERNEL<BF16, 16, COMPANDED4>; \
     else if (wfmt == FO_FP16 && ecc == 8 && codec == FO_COMPANDED4) OUT = KERNEL<FP16, 8, COMPANDED4>; \
+    else if (wfmt == FO_BF16 && ecc == 8 && codec == FO_COMPANDED_BF16SCALE) OUT = KERNEL<BF16, 8, COMPANDED_BF16S>; \
+    else if (wfmt == FO_BF16 && ecc == 16 && codec == FO_COMPANDED_BF16SCALE) OUT = KERNEL<BF16, 16, COMPANDED_BF16S>; \
+    else if (wfmt == FO_FP16 && ecc == 8 && codec == FO_COMPANDED_BF16SCALE) OUT = KERNEL<FP16, 8, COMPANDED_BF16S>; \
   } while (0)
 
 // AdamW (decoupled decay) and Adam (L2 decay folded into the gradient)
@@ -534,12 +539,14 @@ int fo_companded_quantize(const float* x, int64_t n, int kind, int codec, void* 
   if ((rc = current_device(&dev)) || (rc = elementwise_grid(dev, n, &grid)) || (rc = device_tables(dev, s, &tb))) return rc;
   auto* c = (uint8_t*)codes_out;
   void (*kern)(const float*, int64_t, uint8_t*, uint16_t*, const CodecTables*) =
-      (kind == FO_MOMENTUM) ? (codec == FO_COMPANDED ? k_quantize<0, COMPANDED>
-                               : codec == FO_LINEAR  ? k_quantize<0, LINEAR>
-                                                     : k_quantize<0, COMPANDED4>)
-                            : (codec == FO_COMPANDED ? k_quantize<1, COMPANDED>
-                               : codec == FO_LINEAR  ? k_quantize<1, LINEAR>
-                                                     : k_quantize<1, COMPANDED4>);
+      (kind == FO_MOMENTUM) ? (codec == FO_COMPANDED   ? k_quantize<0, COMPANDED>
+                               : codec == FO_LINEAR    ? k_quantize<0, LINEAR>
+                               : codec == FO_COMPANDED4 ? k_quantize<0, COMPANDED4>
+                                                        : k_quantize<0, COMPANDED_BF16S>)
+                            : (codec == FO_COMPANDED   ? k_quantize<1, COMPANDED>
+                               : codec == FO_LINEAR    ? k_quantize<1, LINEAR>
+                               : codec == FO_COMPANDED4 ? k_quantize<1, COMPANDED4>
+                                                        : k_quantize<1, COMPANDED_BF16S>);
   hipLaunchKernelGGL(kern, grid, WG, 0, s, x, n, c, scales_out, tb);
   return launch_check("k_quantize launch");
 }
@@ -564,12 +571,14 @@ int fo_dequantize(const void* codes, const uint16_t* scales, int64_t n, int kind
   if ((rc = current_device(&dev)) || (rc = elementwise_grid(dev, n, &grid)) || (rc = device_tables(dev, s, &tb))) return rc;
   auto* c = (const uint8_t*)codes;
   void (*kern)(const uint8_t*, const uint16_t*, int64_t, float*, const CodecTables*) =
-      (kind == FO_MOMENTUM) ? (codec == FO_COMPANDED ? k_dequantize<0, COMPANDED>
-                               : codec == FO_LINEAR  ? k_dequantize<0, LINEAR>
-                                                     : k_dequantize<0, COMPANDED4>)
-                            : (codec == FO_COMPANDED ? k_dequantize<1, COMPANDED>
-                               : codec == FO_LINEAR  ? k_dequantize<1, LINEAR>
-                                                     : k_dequantize<1, COMPANDED4>);
+      (kind == FO_MOMENTUM) ? (codec == FO_COMPANDED   ? k_dequantize<0, COMPANDED>
+                               : codec == FO_LINEAR    ? k_dequantize<0, LINEAR>
+                               : codec == FO_COMPANDED4 ? k_dequantize<0, COMPANDED4>
+                                                        : k_dequantize<0, COMPANDED_BF16S>)
+                            : (codec == FO_COMPANDED   ? k_dequantize<1, COMPANDED>
+                               : codec == FO_LINEAR    ? k_dequantize<1, LINEAR>
+                               : codec == FO_COMPANDED4 ? k_dequantize<1, COMPANDED4>
+                                                        : k_dequantize<1, COMPANDED_BF16S>);
   hipLaunchKernelGGL(kern, grid, WG, 0, s, c, scales, n, x_out, tb);
   return launch_check("k_dequantize launch");
 }

@@ -16,7 +16,8 @@ All arithmetic runs in the HIP library (fo_fused_adamw_step /
 fo_fused_sgdm_step); this module only groups tensors and keeps step counts.
 FlashAdamW, FlashAdam and FlashSGD follow torch.optim.AdamW, Adam and SGD.
 codec="companded4" keeps 4-bit state codes instead (two per byte; the
-blog's Conclusion & Perspective names lower-bit states as the next step).
+blog's Conclusion & Perspective names lower-bit states as the next step), and
+codec="companded_bf16scale" keeps the 8-bit codes with bfloat16 block scales.
 
 Between steps the optimizers keep the device addresses of each parameter's
 state tensors (ECC, codes, scales); only theta' and gradient addresses are
@@ -93,7 +94,7 @@ class _FlashBase(torch.optim.Optimizer):
     def __init__(self, params, defaults, wfmt, ecc_bits, codec, grad_release, release_bucket=1 << 26):
         if (wfmt, ecc_bits) not in (("bf16", 8), ("bf16", 16), ("fp16", 8)):
             raise ValueError(f"unsupported weight format {wfmt}+ECC{ecc_bits}")
-        if codec not in ("companded", "linear", "companded4"):
+        if codec not in ("companded", "linear", "companded4", "companded_bf16scale"):
             raise ValueError(f"unknown codec {codec}")
         self.wfmt, self.ecc_bits, self.codec = wfmt, ecc_bits, codec
         self.grad_release = grad_release
@@ -364,7 +365,7 @@ class FlashAdamW(_FlashBase):
         m = torch.empty(p.numel(), dtype=torch.float32, device=p.device)
         v = torch.empty_like(m)
         B.fo_dequantize(st["m_q"], st["m_s"], m, "m", self.codec)
-        B.fo_dequantize(st["v_q"], st["v_s"], v, "v", self.codec)   # scale patterns read as fp16 bits
+        B.fo_dequantize(st["v_q"], st["v_s"], v, "v", self.codec)   # scale patterns in the codec's format
         return m.view(p.shape), v.view(p.shape)
 
     @torch.no_grad()

@@ -25,7 +25,7 @@ def test_library_exports_every_declared_symbol():
     for name in names:
         assert hasattr(lib, name), name
     assert set(names) == set(B.EXPORTS)
-    assert lib.fo_abi_version() == B.ABI_VERSION == 5
+    assert lib.fo_abi_version() == B.ABI_VERSION == 6
 
 
 def test_struct_layouts_match_header():
@@ -112,7 +112,7 @@ def test_4bit_code_arrays_are_validated_at_half_size():
     w16, ecc, grad, mq, ms, vs = base, base + 2 * n, base + 3 * n, base + 5 * n, base + 7 * n, base + 8 * n
     vq = mq + n // 2
     t = (B.AdamWTensor * 1)(B.AdamWTensor(w16, ecc, grad, mq, ms, vq, vs, n))
-    for codec, alias in (("companded4", False), ("companded", True), ("linear", True)):
+    for codec, alias in (("companded4", False), ("companded", True), ("linear", True), ("companded_bf16scale", True)):
         hp = B.adamw_hparams(1e-3, 0.9, 0.999, 1e-8, 0.0, 1, codec=codec)
         rc = lib.fo_fused_adamw_step(t, 1, ctypes.byref(hp), None)
         assert (rc == B.FO_EALIAS) == alias, (codec, rc, B.fo_last_error())
@@ -128,6 +128,8 @@ def test_4bit_code_arrays_are_validated_at_half_size():
     x = base + (1 << 20)
     assert lib.fo_companded_quantize(P(x), n, 0, B.FO_COMPANDED, P(x - n // 2), P(base), None) == B.FO_EALIAS
     assert lib.fo_companded_quantize(P(x), n, 0, B.FO_COMPANDED4, P(x - n // 2), P(base), None) != B.FO_EALIAS
-    assert lib.fo_companded_quantize(P(x), n, 0, 3, P(x - n // 2), P(base), None) == B.FO_EINVAL
+    assert lib.fo_companded_quantize(P(x), n, 0, B.FO_COMPANDED_BF16SCALE, P(x - n // 2), P(base),
+                                     None) == B.FO_EALIAS
+    assert lib.fo_companded_quantize(P(x), n, 0, 4, P(x - n // 2), P(base), None) == B.FO_EINVAL
     assert lib.fo_dequantize(P(x - n // 2), P(base), n, 1, B.FO_COMPANDED4, P(x), None) != B.FO_EALIAS
     assert lib.fo_dequantize(P(x - n // 2), P(base), n, 1, B.FO_COMPANDED, P(x), None) == B.FO_EALIAS

@@ -55,7 +55,7 @@ def _check_initial_split(opt, params, x0):
                       w_ref, e_ref, "bf16", 8)
 
 
-def _lockstep(model, opt, steps, hp_of, adam=True, tag=""):
+def _lockstep(model, opt, steps, hp_of, adam=True, tag="", codec="companded"):
     """Run `steps` optimizer steps; before each one the oracle takes a host
     copy of every parameter's state, and after it the states must match."""
     params = list(model.parameters())
@@ -68,7 +68,8 @@ def _lockstep(model, opt, steps, hp_of, adam=True, tag=""):
         torch.cuda.synchronize()
         for i, p in enumerate(params):
             hp = dict(hp_of(p), step=step)
-            want = O.adamw_step(before[i], grads[i], hp) if adam else O.sgdm_step(before[i], grads[i], hp)
+            want = (O.adamw_step(before[i], grads[i], hp, codec=codec) if adam
+                    else O.sgdm_step(before[i], grads[i], hp, codec=codec))
             check_state(f"{tag} step {step} param {i}", _host_state(opt, p, adam), want)
 
 
@@ -95,6 +96,19 @@ def test_flash_sgd_matches_oracle_every_step(extra):
     opt = FlashSGD(model.parameters(), **kw)
     _check_initial_split(opt, list(model.parameters()), x0)
     _lockstep(model, opt, 5, lambda p: kw, adam=False, tag=f"FlashSGD {extra}")
+
+
+def test_flash_optimizers_with_bf16_block_scales():
+    """The drop-in classes with codec="companded_bf16scale" (bfloat16 block
+    scales) step like the oracle, AdamW and SGD."""
+    model = _model(3)
+    opt = FlashAdamW(model.parameters(), **HP, codec="companded_bf16scale")
+    hp = dict(lr=HP["lr"], beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+    _lockstep(model, opt, 4, lambda p: hp, tag="FlashAdamW bf16 scales", codec="companded_bf16scale")
+    model = _model(4)
+    kw = dict(lr=0.05, momentum=0.9, weight_decay=1e-4)
+    opt = FlashSGD(model.parameters(), **kw, codec="companded_bf16scale")
+    _lockstep(model, opt, 4, lambda p: kw, adam=False, tag="FlashSGD bf16 scales", codec="companded_bf16scale")
 
 
 def _train(model, opt, steps, start=1):

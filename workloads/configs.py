@@ -66,6 +66,9 @@ CONFIGS = {
     "c4_resnet50_s4": Config("c4_resnet50_s4", "sgdm", tuple(resnet50_shapes()), SGDM_C4, steps=20,
                              grad_kind="normal_outliers", codec="companded4"),
     "c5_flat1g_s4": Config("c5_flat1g_s4", "adamw", (("flat", (FLAT_1G,)),), ADAMW_C1, steps=2, codec="companded4"),
+    # bfloat16 block scales on the 8B list
+    "c3_llama8b_bs": Config("c3_llama8b_bs", "adamw", tuple(llama31_8b_shapes()), ADAMW_LM, steps=3,
+                            grad_kind="t3_lognormal", codec="companded_bf16scale"),
 }
 
 
