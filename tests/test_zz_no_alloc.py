@@ -55,14 +55,16 @@ def test_noalloc_step_equals_cached_step(sizes_a, sizes_b):
         torch.cuda.empty_cache()
 
 
-def test_noalloc_step_equals_cached_step_4bit_states():
-    """The same with 4-bit state codes (two per byte), odd lengths included."""
+@pytest.mark.parametrize("codec", ["companded4", "companded_bf16scale"])
+def test_noalloc_step_equals_cached_step_other_codecs(codec):
+    """The same with 4-bit state codes (two per byte, odd lengths included)
+    and with bfloat16 block scales."""
     for call, sizes in enumerate(([(1 << 20) + 77, 33, 4097, 2049], [5001, 31])):
-        print(f"no-alloc 4-bit call {call}: sizes {sizes}", flush=True)
-        a = _states(sizes, f"noalloc4_{call}", "companded4")
+        print(f"no-alloc {codec} call {call}: sizes {sizes}", flush=True)
+        a = _states(sizes, f"noalloc_{codec}_{call}", codec)
         b = _clone(a)
         for step in (1, 2):
-            hp = dict(HP, step=step, codec="companded4")
+            hp = dict(HP, step=step, codec=codec)
             B.fo_fused_adamw_step(a, hp)
             B.fo_fused_adamw_step_noalloc(b, hp)
         torch.cuda.synchronize()
